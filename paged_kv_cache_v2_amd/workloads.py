@@ -1,0 +1,244 @@
+"""Seeded synthetic inputs for paged single-query decode attention.
+
+This module only *constructs inputs*: shapes, sequence lengths, a shuffled
+physical-block assignment and normally distributed query/key/value values.
+It holds none of the attention arithmetic, so both the HIP path and the fp64
+oracle can consume the same tensors without sharing any code of the method.
+
+Layouts follow the problem statement of the Triton PagedAttention V2 page
+(argument comments of the phase-1 partition kernel):
+
+* query        ``[S, H, D]``
+* key_cache    ``[B, KH, D/x, BS, x]`` with ``x = 16 / sizeof(dtype)``
+* value_cache  ``[B, KH, D, BS]``
+* block_tables ``[S, MB]`` int32, padded with -1 past a sequence's blocks
+* seq_lens     ``[S]`` int32
+
+Random numbers come from numpy's PCG64, one independent stream per
+(tensor, 4 Mi-element chunk), keyed by ``SeedSequence(seed, spawn_key=...)``.
+The values therefore do not depend on how many threads generate them.
+Normals are drawn in float32 and rounded to the storage dtype with
+round-to-nearest-even (torch's ``.to``), so every consumer reads the same bits.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+
+# Stream keys (first element of spawn_key) for each random quantity.
+_KEY_LENS, _KEY_PERM, _KEY_Q, _KEY_K, _KEY_V = 0, 1, 2, 3, 4
+_CHUNK = 1 << 22
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    """One decode workload: head structure, cache geometry and length mix."""
+
+    name: str
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_size: int
+    block_size: int
+    partition_size: int
+    dtype: str
+    len_lo: int = 0  # inclusive lower bound of uniform integer lengths
+    len_hi: int = 0  # inclusive upper bound; also sizes max_blocks and P
+    fixed_lens: Optional[Sequence[int]] = None
+    sigma: float = 1.0
+    scale: Optional[float] = None  # None means 1/sqrt(head_size)
+    num_blocks: Optional[int] = None  # None means exactly the blocks used
+
+    @property
+    def x(self) -> int:
+        return 16 // torch.tensor([], dtype=DTYPES[self.dtype]).element_size()
+
+    @property
+    def group(self) -> int:
+        return self.num_heads // self.num_kv_heads
+
+    @property
+    def max_len(self) -> int:
+        if self.fixed_lens is not None:
+            return max(self.fixed_lens)
+        return self.len_hi
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return max(1, -(-self.max_len // self.block_size))
+
+    @property
+    def max_num_partitions(self) -> int:
+        return max(1, -(-self.max_len // self.partition_size))
+
+    @property
+    def scale_f32(self) -> float:
+        s = self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_size)
+        return float(np.float32(s))
+
+    def replace(self, **kw) -> "DecodeConfig":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads the measurements are quoted on, named by what they are.
+CONFIGS: Dict[str, DecodeConfig] = {
+    "tiny_f32_d64": DecodeConfig(
+        "tiny_f32_d64", num_seqs=2, num_heads=4, num_kv_heads=4, head_size=64,
+        block_size=16, partition_size=64, dtype="f32", fixed_lens=(37, 100),
+        scale=1.0 / 8.0, num_blocks=32),
+    "mha_f16_d128": DecodeConfig(
+        "mha_f16_d128", num_seqs=64, num_heads=32, num_kv_heads=32, head_size=128,
+        block_size=16, partition_size=512, dtype="f16", len_lo=512, len_hi=2048),
+    "gqa_bf16_g4": DecodeConfig(
+        "gqa_bf16_g4", num_seqs=128, num_heads=32, num_kv_heads=8, head_size=128,
+        block_size=16, partition_size=512, dtype="bf16", len_lo=1, len_hi=4096),
+    "longctx_bf16_g8": DecodeConfig(
+        "longctx_bf16_g8", num_seqs=8, num_heads=64, num_kv_heads=8, head_size=128,
+        block_size=16, partition_size=512, dtype="bf16", fixed_lens=(32768,) * 8,
+        sigma=0.5),
+    "wide_f16_d256": DecodeConfig(
+        "wide_f16_d256", num_seqs=32, num_heads=16, num_kv_heads=16, head_size=256,
+        block_size=32, partition_size=512, dtype="f16", len_lo=4096, len_hi=8192,
+        scale=1.0 / 16.0),
+}
+CONFIG_ORDER = ["tiny_f32_d64", "mha_f16_d128", "gqa_bf16_g4", "longctx_bf16_g8",
+                "wide_f16_d256"]
+
+
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _normals(seed: int, key: int, n: int, sigma: float) -> np.ndarray:
+    """n float32 normals N(0, sigma^2), chunked PCG64 streams, thread-count independent."""
+    out = np.empty(n, dtype=np.float32)
+    nchunks = -(-n // _CHUNK) if n else 0
+
+    def work(i: int) -> None:
+        ss = np.random.SeedSequence(seed, spawn_key=(key, i))
+        rng = np.random.Generator(np.random.PCG64(ss))
+        lo = i * _CHUNK
+        hi = min(n, lo + _CHUNK)
+        rng.standard_normal(hi - lo, dtype=np.float32, out=out[lo:hi])
+
+    if nchunks <= 1:
+        for i in range(nchunks):
+            work(i)
+    else:
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(work, range(nchunks)))
+    if sigma != 1.0:
+        out *= np.float32(sigma)
+    return out
+
+
+def _rng(seed: int, key: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(key,))))
+
+
+def draw_lengths(cfg: DecodeConfig, seed: int) -> np.ndarray:
+    if cfg.fixed_lens is not None:
+        lens = np.asarray(cfg.fixed_lens, dtype=np.int64)
+        assert lens.shape == (cfg.num_seqs,)
+        return lens
+    return _rng(seed, _KEY_LENS).integers(cfg.len_lo, cfg.len_hi + 1, size=cfg.num_seqs)
+
+
+def make_inputs(cfg: DecodeConfig, seed: int, lens: Optional[Sequence[int]] = None,
+                device: str = "cpu") -> Dict[str, object]:
+    """Build one seeded input set for ``cfg``.
+
+    Returns a dict with torch tensors ``query``, ``key_cache``, ``value_cache``,
+    ``block_tables``, ``seq_lens`` plus the integer sizes the C-ABI takes.
+    ``lens`` overrides the drawn lengths (edge-case tests).
+    """
+    S, H, KH, D, BS = (cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_size,
+                       cfg.block_size)
+    x = cfg.x
+    assert H % KH == 0 and D % x == 0
+    seq_lens = np.asarray(lens if lens is not None else draw_lengths(cfg, seed), dtype=np.int64)
+    assert seq_lens.shape == (S,)
+    MB = cfg.max_blocks_per_seq
+    P = cfg.max_num_partitions
+    assert int(seq_lens.max(initial=0)) <= min(MB * BS, P * cfg.partition_size)
+    blocks_per_seq = [-(-int(n) // BS) for n in seq_lens]
+    used = sum(blocks_per_seq)
+    NB = cfg.num_blocks if cfg.num_blocks is not None else max(1, used)
+    assert NB >= used, "num_blocks too small for the drawn lengths"
+    perm = _rng(seed, _KEY_PERM).permutation(NB).astype(np.int32)
+    bt = np.full((S, MB), -1, dtype=np.int32)
+    pos = 0
+    for s, nb in enumerate(blocks_per_seq):
+        bt[s, :nb] = perm[pos:pos + nb]
+        pos += nb
+
+    tdt = DTYPES[cfg.dtype]
+
+    def tensor(key: int, shape) -> torch.Tensor:
+        n = int(np.prod(shape))
+        vals = torch.from_numpy(_normals(seed, key, n, cfg.sigma)).reshape(shape)
+        return vals.to(tdt)
+
+    q = tensor(_KEY_Q, (S, H, D))
+    kc = tensor(_KEY_K, (NB, KH, D // x, BS, x))
+    vc = tensor(_KEY_V, (NB, KH, D, BS))
+    out = dict(
+        query=q, key_cache=kc, value_cache=vc,
+        block_tables=torch.from_numpy(bt), seq_lens=torch.from_numpy(seq_lens.astype(np.int32)),
+        num_seqs=S, num_heads=H, num_kv_heads=KH, head_size=D, block_size=BS,
+        num_blocks=NB, max_blocks_per_seq=MB, max_num_partitions=P,
+        partition_size=cfg.partition_size, scale=cfg.scale_f32, dtype=cfg.dtype,
+        x=x, used_blocks=used)
+    if device != "cpu":
+        for k in ("query", "key_cache", "value_cache", "block_tables", "seq_lens"):
+            out[k] = out[k].to(device)
+    return out
+
+
+def poison_unused(inp: Dict[str, object], value: float = float("nan")) -> None:
+    """Fill every cache slot no sequence may read with ``value`` (in place, CPU tensors).
+
+    That is: physical blocks no block table references, and the slots of each
+    sequence's last block at or past its length.
+    """
+    kc, vc = inp["key_cache"], inp["value_cache"]
+    bt, sl = inp["block_tables"], inp["seq_lens"]
+    BS = inp["block_size"]
+    NB = kc.shape[0]
+    referenced = torch.zeros(NB, dtype=torch.bool)
+    for s in range(bt.shape[0]):
+        n = int(sl[s])
+        nb = -(-n // BS)
+        for i in range(nb):
+            referenced[int(bt[s, i])] = True
+        if n % BS:
+            last = int(bt[s, nb - 1])
+            kc[last, :, :, n % BS:, :] = value
+            vc[last, :, :, n % BS:] = value
+    kc[~referenced] = value
+    vc[~referenced] = value
+
+
+def kv_bytes(inp: Dict[str, object]) -> int:
+    """Algorithmic K+V bytes one decode step reads: 2*D*sizeof per (token, kv-head)."""
+    esz = inp["key_cache"].element_size()
+    return int(inp["seq_lens"].to(torch.int64).sum()) * inp["num_kv_heads"] * 2 * \
+        inp["head_size"] * esz
+
+
+def qhead_tokens(inp: Dict[str, object]) -> int:
+    """Query-head x token pairs one decode step scores."""
+    return int(inp["seq_lens"].to(torch.int64).sum()) * inp["num_heads"]

@@ -1,0 +1,84 @@
+"""The oracle's pins are sharp: each plausible mistake planted in a copy of the
+oracle source (CPU only, compiled into a temp dir) makes at least one pin fail.
+
+Every mutation keeps all memory accesses in bounds, so a mutant fails by
+giving wrong numbers, never by crashing the test process.
+"""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "paged_decode_oracle.c")
+
+# (name, text in the oracle source, replacement)
+MUTANTS = [
+    ("gqa_mapping_modulo", "int32_t h = kh * G + g;", "int32_t h = g * pr->KH + kh;"),
+    ("query_indexed_by_kv_head", "dot += query_at(pr, s, h, d)", "dot += query_at(pr, s, kh, d)"),
+    ("key_layout_token_major",
+     "int64_t idx = ((((int64_t)b * pr->KH + kh) * (pr->D / x) + d / x) * pr->BS + o) * x + d % x;",
+     "int64_t idx = ((((int64_t)b * pr->KH + kh) * pr->BS + o) * (pr->D / x) + d / x) * x + d % x;"),
+    ("value_layout_token_major",
+     "int64_t idx = (((int64_t)b * pr->KH + kh) * pr->D + d) * pr->BS + o;",
+     "int64_t idx = (((int64_t)b * pr->KH + kh) * pr->BS + o) * pr->D + d;"),
+    ("slot_off_by_one", "*slot = t % pr->BS;", "*slot = (t + 1) % pr->BS;"),
+    ("scale_dropped", "score[t] = pr->scale * dot;", "score[t] = dot;"),
+    ("softmax_sign", "double w = exp(score[t] - m);", "double w = exp(m - score[t]);"),
+    ("partition_end_short", "int32_t t1 = t0 + pr->PS < L ? t0 + pr->PS : L;",
+     "int32_t t1 = t0 + pr->PS - 1 < L ? t0 + pr->PS - 1 : L;"),
+    ("partition_not_normalised", "for (int32_t d = 0; d < pr->D; ++d) o[d] /= l;", ""),
+    ("sentinel_max_zero", "double m = -INFINITY, l = 0.0;", "double m = 0.0, l = 0.0;"),
+    ("combine_drops_exp_sums", "Z += exp(ml[base + p] - M) * es[base + p];",
+     "Z += exp(ml[base + p] - M);"),
+    ("combine_weight_sign", "double w = exp(ml[base + p] - M) * es[base + p] / Z;",
+     "double w = exp(M - ml[base + p]) * es[base + p] / Z;"),
+    ("combine_floor_partitions", "int32_t n = (seq_lens[s] + PS - 1) / PS;",
+     "int32_t n = seq_lens[s] / PS;"),
+    ("binary16_bias", "v = ldexp((double)(1024 + f), e - 25);",
+     "v = ldexp((double)(1024 + f), e - 24);"),
+    ("bfloat16_subnormal", "v = ldexp((double)f, -133);", "v = ldexp((double)f, -126);"),
+]
+
+
+def battery():
+    """The pins, as plain calls; returns the names of those that fail."""
+    checks = {
+        "binary16": PINS.test_binary16_decoder_exhaustive,
+        "bfloat16": PINS.test_bfloat16_decoder_exhaustive,
+        "golden_uniform": PINS.test_golden_uniform_scores,
+        "golden_argmax": PINS.test_golden_argmax_selection,
+        "brute_force": lambda: PINS.test_brute_force_tiny("bf16", 4, 2, 16, 2),
+        "library_dense": lambda: PINS.test_library_routine_dense("bf16", 8, 1, 64, 32, 0),
+        "library_partitions": lambda: PINS.test_library_routine_partitions("bf16", 4),
+        "partition_combine": lambda: PINS.test_partition_combine_equals_dense(32),
+        "zero_length": PINS.test_zero_length_gives_zero_and_sentinels,
+        "gather": PINS.test_gather_indices_brute_force,
+    }
+    failed = []
+    for name, fn in checks.items():
+        try:
+            fn()
+        except Exception:  # an assertion or a shape error both count as caught
+            failed.append(name)
+    return failed
+
+
+def test_unmutated_oracle_passes_battery():
+    assert battery() == []
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    with tempfile.TemporaryDirectory() as d:
+        csrc = os.path.join(d, f"{name}.c")
+        with open(csrc, "w") as f:
+            f.write(src.replace(old, new))
+        lib = oracle.compile_source(csrc, os.path.join(d, f"{name}.so"))
+        with oracle.using_library(lib):
+            failed = battery()
+    assert failed, f"no pin catches mutant {name}"
