@@ -1,0 +1,148 @@
+/*
+ * paged_attn.h -- C ABI of the MI355X (gfx950) paged single-query decode
+ * attention library, V2 split: per-partition online-softmax attention, then
+ * a cross-partition log-sum-exp reduce, with grouped-query head mapping.
+ *
+ * The operation is the one defined on the page "paged_attention_v2_triton.py
+ * -- Triton PagedAttention V2 for BI-V100": its phase-1 partition kernel,
+ * its phase-2 reduce kernel, and the host launcher that fixes the tensor
+ * layouts and the caller-allocated outputs.
+ *
+ * Conventions for every entry point below
+ *  - All tensor pointers are DEVICE pointers on the current HIP device, in
+ *    the dense row-major layouts stated per argument. The caller owns every
+ *    buffer; the library never allocates, frees, copies to the host or
+ *    synchronises. Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    null stream) and the call returns.
+ *  - x = 16 / sizeof(kv element): 4 for fp32, 8 for fp16 / bf16.
+ *  - S = num_seqs, H = num_heads, KH = num_kv_heads, G = H / KH (query heads
+ *    per kv head; query head h reads kv head h / G), D = head_size,
+ *    BS = block_size, B = num_blocks, MB = max_blocks_per_seq,
+ *    P = max_num_partitions, PS = partition_size.
+ *  - Return value: PA_OK, or a negative PA_ERR_* code with a message readable
+ *    through paged_attn_last_error() on the calling thread. Argument errors
+ *    are detected on the host before anything is enqueued.
+ *  - Preconditions the library cannot check without synchronising (the
+ *    caller guarantees them): 0 <= seq_lens[s] <= min(P * PS, MB * BS);
+ *    block_tables[s][i] in [0, B) for i < ceil(seq_lens[s] / BS); entries past
+ *    that are never read and may hold anything (e.g. -1). Cache slots that no
+ *    sequence reads (unreferenced blocks, tail slots of a last block) never
+ *    influence any result, whatever they hold (NaN included).
+ *  - Outputs must not alias inputs. Calls on one stream are ordered; the
+ *    functions keep no state between calls and are safe to call from several
+ *    threads on different streams.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define PA_API __attribute__((visibility("default")))
+#else
+#define PA_API
+#endif
+
+/* Element types of query / key_cache / value_cache (and of `out`). */
+enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 };
+
+/* Status codes. */
+enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                              */
+  PA_ERR_SHAPE = -2,       /* negative size, H % KH, D % x, PS <= 0 or PS % BS, P < 1,
+                              MB < 1, B < 1                                            */
+  PA_ERR_UNSUPPORTED = -3, /* D not in {64,128,256}, BS not in {16,32}, G outside the
+                              built range, PS / BS > 1024, unknown dtype, or out_dtype
+                              neither PA_F32 nor kv_dtype                              */
+  PA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned                  */
+  PA_ERR_HIP = -5          /* the HIP runtime rejected a launch                        */
+};
+
+/*
+ * Phase 1 (the page's partition kernel). For every sequence s, kv head kh and
+ * partition p < P, over the tokens t in [p*PS, min((p+1)*PS, seq_lens[s])):
+ *   score(h, t)       = scale * dot(query[s][h], K_t)   for the G heads h of kh
+ *   max_logits[s][h][p] = max_t score
+ *   exp_sums[s][h][p]   = sum_t exp(score - max)
+ *   tmp_output[s][h][p] = sum_t exp(score - max) * V_t / exp_sums  (normalised)
+ * where K_t / V_t are gathered from physical block block_tables[s][t / BS],
+ * slot t % BS. A partition with no tokens gets max_logits = -inf,
+ * exp_sums = 0 and its tmp_output row is left untouched.
+ *
+ *   tmp_output   [S, H, P, D] fp32, written
+ *   exp_sums     [S, H, P]    fp32, written
+ *   max_logits   [S, H, P]    fp32, written
+ *   query        [S, H, D]            kv_dtype
+ *   key_cache    [B, KH, D/x, BS, x]  kv_dtype
+ *   value_cache  [B, KH, D, BS]       kv_dtype
+ *   block_tables [S, MB] int32
+ *   seq_lens     [S]     int32
+ *   scale        multiplies q.k (applied after the dot product)
+ *   kv_dtype     PA_F32, PA_F16 or PA_BF16
+ * num_seqs == 0 is a successful no-op.
+ */
+PA_API int paged_attn_v2_partition(float* tmp_output, float* exp_sums, float* max_logits,
+                                   const void* query, const void* key_cache, const void* value_cache,
+                                   const int32_t* block_tables, const int32_t* seq_lens,
+                                   int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size, int32_t num_blocks,
+                                   int32_t max_blocks_per_seq, int32_t max_num_partitions,
+                                   int32_t partition_size, float scale, int32_t kv_dtype,
+                                   void* stream);
+
+/*
+ * Phase 2 (the page's reduce kernel). For every (s, h), over the
+ * n = ceil(seq_lens[s] / PS) partitions the sequence uses:
+ *   M = max_p max_logits, Z = sum_p exp(max_logits - M) * exp_sums,
+ *   out[s][h] = sum_p exp(max_logits - M) * exp_sums / Z * tmp_output[s][h][p]
+ * and out[s][h] = 0 when n == 0. Entries of partitions p >= n are not read.
+ *
+ *   out          [S, H, D] in out_dtype (PA_F32, or the kv dtype: round to
+ *                nearest even from the fp32 result), written
+ *   tmp_output, exp_sums, max_logits, seq_lens: as written by phase 1
+ * num_seqs == 0 is a successful no-op.
+ */
+PA_API int paged_attn_v2_reduce(void* out, const float* tmp_output, const float* exp_sums,
+                                const float* max_logits, const int32_t* seq_lens,
+                                int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                int32_t max_num_partitions, int32_t partition_size,
+                                int32_t out_dtype, void* stream);
+
+/*
+ * Phase 1 then phase 2 on one stream (the page's host launcher): the same
+ * arguments as the two calls above. tmp_output / exp_sums / max_logits are
+ * workspace the caller allocates ([S,H,P,D], [S,H,P], [S,H,P] fp32) and may
+ * reuse across calls on the same stream.
+ */
+PA_API int paged_attn_decode(void* out, float* tmp_output, float* exp_sums, float* max_logits,
+                             const void* query, const void* key_cache, const void* value_cache,
+                             const int32_t* block_tables, const int32_t* seq_lens,
+                             int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                             int32_t head_size, int32_t block_size, int32_t num_blocks,
+                             int32_t max_blocks_per_seq, int32_t max_num_partitions,
+                             int32_t partition_size, float scale, int32_t kv_dtype,
+                             int32_t out_dtype, void* stream);
+
+/* Text of the last nonzero return on this thread ("" if none). Owned by the
+ * library; valid until the next call on the same thread. */
+PA_API const char* paged_attn_last_error(void);
+
+/* Version of this ABI (incremented on any incompatible change). */
+PA_API int paged_attn_abi_version(void);
+
+/* Partition size the library is tuned for at this geometry (a multiple of
+ * block_size); results do not depend on the partition size beyond rounding.
+ * Returns a PA_ERR_* code for an unsupported geometry. */
+PA_API int paged_attn_default_partition_size(int32_t head_size, int32_t block_size, int32_t kv_dtype,
+                                             int32_t group);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

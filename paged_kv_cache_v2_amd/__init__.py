@@ -1,1 +1,10 @@
-"""MI355X-native paged single-query decode attention (V2 partition + LSE reduce, GQA)."""
+"""MI355X-native paged single-query decode attention (V2 partition + LSE reduce, GQA).
+
+The computation lives in libpaged_attn.so (hand-written gfx950 HIP kernels
+behind the C ABI of include/paged_attn.h); this package is its Python binding
+plus the seeded synthetic-input generator.
+"""
+from .binding import (PA_BF16, PA_ERR_ALIGN, PA_ERR_HIP, PA_ERR_NULL, PA_ERR_SHAPE,  # noqa: F401
+                      PA_ERR_UNSUPPORTED, PA_F16, PA_F32, PA_OK, abi_version,
+                      default_partition_size, ensure_built, last_error, lib, paged_attn_decode,
+                      paged_attn_v2_partition, paged_attn_v2_reduce, workspace)

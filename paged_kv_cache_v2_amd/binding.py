@@ -1,0 +1,173 @@
+"""Thin Python binding of libpaged_attn.so (the C ABI in include/paged_attn.h).
+
+Argument marshalling only: shapes are read off torch tensors, pointers and
+the current HIP stream are passed through, and a nonzero status becomes a
+RuntimeError carrying the library's message. Every step of the computation
+runs in the HIP kernels; there is no other implementation to fall back on,
+and a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # noqa: F401  (load torch's HIP runtime first so both share one runtime)
+
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_ALIGN, PA_ERR_HIP = 0, -1, -2, -3, -4, -5
+_DT = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpaged_attn.so")
+_LIB = None
+
+_P, _I32, _F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+_SIGS = {
+    "paged_attn_v2_partition": [_P, _P, _P, _P, _P, _P, _P, _P] + [_I32] * 9 + [_F32, _I32, _P],
+    "paged_attn_v2_reduce": [_P, _P, _P, _P, _P] + [_I32] * 6 + [_P],
+    "paged_attn_decode": [_P, _P, _P, _P, _P, _P, _P, _P, _P] + [_I32] * 9 + [_F32, _I32, _I32, _P],
+    "paged_attn_last_error": [],
+    "paged_attn_abi_version": [],
+    "paged_attn_default_partition_size": [_I32, _I32, _I32, _I32],
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m paged_kv_cache_v2_amd.build`. "
+                "There is no fallback implementation.")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name == "paged_attn_last_error" else ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def last_error() -> str:
+    return lib().paged_attn_last_error().decode()
+
+
+def abi_version() -> int:
+    return lib().paged_attn_abi_version()
+
+
+def default_partition_size(head_size: int, block_size: int, dtype: torch.dtype, group: int) -> int:
+    rc = lib().paged_attn_default_partition_size(head_size, block_size, _DT[dtype], group)
+    if rc < 0:
+        raise RuntimeError(f"paged_attn_default_partition_size: {last_error()} (code {rc})")
+    return rc
+
+
+def _check(name: str, rc: int) -> None:
+    if rc != PA_OK:
+        raise RuntimeError(f"{name}: {last_error()} (code {rc})")
+
+
+def _stream(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _kv_geometry(query, key_cache, value_cache, block_tables, seq_lens):
+    _need(query.dim() == 3 and key_cache.dim() == 5 and value_cache.dim() == 4,
+          "query [S,H,D], key_cache [B,KH,D/x,BS,x], value_cache [B,KH,D,BS] expected")
+    _need(query.dtype in _DT and key_cache.dtype == query.dtype and value_cache.dtype == query.dtype,
+          "query, key_cache and value_cache must share one dtype (f32, f16 or bf16)")
+    _need(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32,
+          "block_tables and seq_lens must be int32")
+    for t in (query, key_cache, value_cache, block_tables, seq_lens):
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    S, H, D = query.shape
+    B, KH, Dx, BS, x = key_cache.shape
+    _need(x == 16 // query.element_size() and Dx * x == D, "key_cache packing must be x = 16/sizeof")
+    _need(tuple(value_cache.shape) == (B, KH, D, BS), "value_cache shape mismatch")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == S and seq_lens.shape == (S,),
+          "block_tables [S, MB] and seq_lens [S] expected")
+    return S, H, KH, D, BS, B, block_tables.shape[1]
+
+
+def _stats_geometry(tmp_output, exp_sums, max_logits, S, H, D):
+    _need(all(t.dtype == torch.float32 and t.is_cuda and t.is_contiguous()
+              for t in (tmp_output, exp_sums, max_logits)),
+          "tmp_output, exp_sums, max_logits must be contiguous fp32 device tensors")
+    _need(tmp_output.dim() == 4 and tuple(tmp_output.shape[:2]) == (S, H) and tmp_output.shape[3] == D,
+          "tmp_output must be [S, H, P, D]")
+    P = tmp_output.shape[2]
+    _need(tuple(exp_sums.shape) == (S, H, P) and tuple(max_logits.shape) == (S, H, P),
+          "exp_sums and max_logits must be [S, H, P]")
+    return P
+
+
+def paged_attn_v2_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                            block_tables, seq_lens, scale: float, partition_size: int,
+                            stream=None) -> None:
+    """Phase 1: per-partition attention into tmp_output / exp_sums / max_logits."""
+    S, H, KH, D, BS, B, MB = _kv_geometry(query, key_cache, value_cache, block_tables, seq_lens)
+    P = _stats_geometry(tmp_output, exp_sums, max_logits, S, H, D)
+    rc = lib().paged_attn_v2_partition(
+        tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(), query.data_ptr(),
+        key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+        seq_lens.data_ptr(), S, H, KH, D, BS, B, MB, P, partition_size, float(scale),
+        _DT[query.dtype], _stream(query, stream))
+    _check("paged_attn_v2_partition", rc)
+
+
+def paged_attn_v2_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, partition_size: int,
+                         stream=None) -> None:
+    """Phase 2: cross-partition log-sum-exp combine into out [S, H, D]."""
+    _need(out.dim() == 3 and out.dtype in _DT and out.is_cuda and out.is_contiguous(),
+          "out must be a contiguous [S, H, D] f32/f16/bf16 device tensor")
+    S, H, D = out.shape
+    P = _stats_geometry(tmp_output, exp_sums, max_logits, S, H, D)
+    _need(seq_lens.dtype == torch.int32 and seq_lens.is_cuda and seq_lens.shape == (S,),
+          "seq_lens must be an int32 [S] device tensor")
+    rc = lib().paged_attn_v2_reduce(
+        out.data_ptr(), tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
+        seq_lens.data_ptr(), S, H, D, P, partition_size, _DT[out.dtype], _stream(out, stream))
+    _check("paged_attn_v2_reduce", rc)
+
+
+def paged_attn_decode(out, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                      block_tables, seq_lens, scale: float, partition_size: int,
+                      stream=None) -> None:
+    """Phase 1 then phase 2 on one stream."""
+    S, H, KH, D, BS, B, MB = _kv_geometry(query, key_cache, value_cache, block_tables, seq_lens)
+    P = _stats_geometry(tmp_output, exp_sums, max_logits, S, H, D)
+    _need(out.dim() == 3 and tuple(out.shape) == (S, H, D) and out.dtype in _DT and out.is_cuda
+          and out.is_contiguous(), "out must be a contiguous [S, H, D] device tensor")
+    rc = lib().paged_attn_decode(
+        out.data_ptr(), tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
+        query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+        seq_lens.data_ptr(), S, H, KH, D, BS, B, MB, P, partition_size, float(scale),
+        _DT[query.dtype], _DT[out.dtype], _stream(query, stream))
+    _check("paged_attn_decode", rc)
+
+
+def workspace(num_seqs: int, num_heads: int, head_size: int, max_num_partitions: int,
+              device) -> tuple:
+    """Allocate (tmp_output, exp_sums, max_logits) for a decode call (torch memory)."""
+    tmp = torch.empty(num_seqs, num_heads, max_num_partitions, head_size, dtype=torch.float32,
+                      device=device)
+    es = torch.empty(num_seqs, num_heads, max_num_partitions, dtype=torch.float32, device=device)
+    ml = torch.empty(num_seqs, num_heads, max_num_partitions, dtype=torch.float32, device=device)
+    return tmp, es, ml
+
+
+def ensure_built() -> str:
+    """Build the library if no built copy exists (tests, smoke and bench use this)."""
+    if not os.path.exists(LIB_PATH):
+        from . import build
+        build.build()
+    return LIB_PATH

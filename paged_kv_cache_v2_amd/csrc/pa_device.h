@@ -1,0 +1,139 @@
+// Device helpers for the gfx950 paged decode kernels: element codecs,
+// MFMA wrappers, wavefront reductions. wave64 only (CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- codecs
+// Two 16-bit elements packed in one 32-bit word: element 0 in the low half.
+template <int DT> struct codec;
+
+template <> struct codec<DT_BF16> {
+  static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  // Round-to-nearest-even pack of two floats.
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ uint16_t one(float a) {
+    return __builtin_bit_cast(uint16_t, (__bf16)a);
+  }
+  // fp32 += a.lo*b.lo + a.hi*b.hi
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+  }
+};
+
+template <> struct codec<DT_F16> {
+  static __device__ __forceinline__ float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ uint16_t one(float a) {
+    return __builtin_bit_cast(uint16_t, (_Float16)a);
+  }
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c,
+                                  false);
+  }
+};
+
+// ---------------------------------------------------------------- MFMA
+// QK: 16x16x32 (A = 16 token rows x 32 d, B = 32 d x 16 head columns).
+// PV: 16x16x16 (A = 16 d rows x 16 tokens, B = 16 tokens x 16 head columns).
+// Operand layout (CDNA3/CDNA4): A[i][k] lives in lane i + 16*(k / kpl), element
+// k % kpl (kpl = k-values per lane: 8 for x32, 4 for x16); B[k][j] in lane
+// j + 16*(k / kpl); C[i][j] in lane j + 16*(i / 4), register i % 4.
+template <int DT> struct mma;
+
+template <> struct mma<DT_BF16> {
+  static __device__ __forceinline__ f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+  }
+};
+
+template <> struct mma<DT_F16> {
+  static __device__ __forceinline__ f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// Max / sum over the four 16-lane rows of a wavefront (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float rows_max(float v) {
+  v = fmaxf(v, shfl_xor(v, 16));
+  return fmaxf(v, shfl_xor(v, 32));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  v += shfl_xor(v, 16);
+  return v + shfl_xor(v, 32);
+}
+// Max / sum within each 16-lane row.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, shfl_xor(v, 1));
+  v = fmaxf(v, shfl_xor(v, 2));
+  v = fmaxf(v, shfl_xor(v, 4));
+  return fmaxf(v, shfl_xor(v, 8));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += shfl_xor(v, 1);
+  v += shfl_xor(v, 2);
+  v += shfl_xor(v, 4);
+  return v + shfl_xor(v, 8);
+}
+// Whole-wavefront max / sum.
+__device__ __forceinline__ float wave_max(float v) { return rows_max(row16_max(v)); }
+__device__ __forceinline__ float wave_sum(float v) { return rows_sum(row16_sum(v)); }
+
+// Element e of a lane's run of tokens is a real token iff e < nvalid.
+__device__ __forceinline__ bool e_valid(int e, int nvalid) { return e < nvalid; }
+
+// Zero the 16-bit elements of a packed pair of words at positions >= nvalid (0..4).
+__device__ __forceinline__ u32x2 keep_first(u32x2 v, int nvalid) {
+  const uint32_t mx = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0x0000ffffu : 0u);
+  const uint32_t my = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0x0000ffffu : 0u);
+  return u32x2{v.x & mx, v.y & my};
+}
+
+}  // namespace pa

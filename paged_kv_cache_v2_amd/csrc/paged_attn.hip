@@ -1,0 +1,306 @@
+// Host side of the C ABI declared in include/paged_attn.h: argument
+// validation, kernel selection and launch. No allocation, no host copies, no
+// synchronisation: everything is enqueued on the caller's stream.
+//
+// The two phases are the page "paged_attention_v2_triton.py -- Triton
+// PagedAttention V2 for BI-V100": phase-1 partition kernel and phase-2
+// reduce kernel, launched back to back on one stream by its host launcher.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "paged_attn.h"
+#include "pa_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_size(int32_t dt) { return dt == PA_F32 ? 4 : 2; }
+
+using pa::PartitionArgs;
+using pa::ReduceArgs;
+typedef void (*partition_fn)(PartitionArgs);
+typedef void (*reduce_fn)(ReduceArgs);
+
+int d_index(int D) { return D == 64 ? 0 : D == 128 ? 1 : D == 256 ? 2 : -1; }
+int bs_index(int BS) { return BS == 16 ? 0 : BS == 32 ? 1 : -1; }
+
+// ---------------------------------------------------------------- kernel tables
+template <int DT, int D, int BS>
+constexpr partition_fn mfma_k() { return pa::partition_mfma_kernel<DT, D, BS>; }
+template <int DT, int D, int BS, int GM>
+constexpr partition_fn vec_k() { return pa::partition_vec_kernel<DT, D, BS, GM>; }
+
+// [dtype 1..2 -> 0..1][D][BS]
+const partition_fn kMfma[2][3][2] = {
+    {{mfma_k<pa::DT_F16, 64, 16>(), mfma_k<pa::DT_F16, 64, 32>()},
+     {mfma_k<pa::DT_F16, 128, 16>(), mfma_k<pa::DT_F16, 128, 32>()},
+     {mfma_k<pa::DT_F16, 256, 16>(), mfma_k<pa::DT_F16, 256, 32>()}},
+    {{mfma_k<pa::DT_BF16, 64, 16>(), mfma_k<pa::DT_BF16, 64, 32>()},
+     {mfma_k<pa::DT_BF16, 128, 16>(), mfma_k<pa::DT_BF16, 128, 32>()},
+     {mfma_k<pa::DT_BF16, 256, 16>(), mfma_k<pa::DT_BF16, 256, 32>()}},
+};
+
+#define PA_VEC_GM(DT, D, BS) {vec_k<DT, D, BS, 1>(), vec_k<DT, D, BS, 2>(), vec_k<DT, D, BS, 4>()}
+#define PA_VEC_BS(DT, D) {PA_VEC_GM(DT, D, 16), PA_VEC_GM(DT, D, 32)}
+#define PA_VEC_D(DT) {PA_VEC_BS(DT, 64), PA_VEC_BS(DT, 128), PA_VEC_BS(DT, 256)}
+// [dtype][D][BS][GM = 1, 2, 4]
+const partition_fn kVec[3][3][2][3] = {PA_VEC_D(pa::DT_F32), PA_VEC_D(pa::DT_F16),
+                                       PA_VEC_D(pa::DT_BF16)};
+#undef PA_VEC_D
+#undef PA_VEC_BS
+#undef PA_VEC_GM
+
+// [out dtype][D]
+const reduce_fn kReduce[3][3] = {
+    {pa::reduce_kernel<64, pa::DT_F32>, pa::reduce_kernel<128, pa::DT_F32>,
+     pa::reduce_kernel<256, pa::DT_F32>},
+    {pa::reduce_kernel<64, pa::DT_F16>, pa::reduce_kernel<128, pa::DT_F16>,
+     pa::reduce_kernel<256, pa::DT_F16>},
+    {pa::reduce_kernel<64, pa::DT_BF16>, pa::reduce_kernel<128, pa::DT_BF16>,
+     pa::reduce_kernel<256, pa::DT_BF16>},
+};
+
+// Per-device limit on dynamic LDS per workgroup (read once per device).
+int max_lds_per_block() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+      v = 65536;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+struct Plan {
+  partition_fn fn;
+  int lds_bytes;
+  int grid;
+};
+
+// Host checks shared by the partition entry points; fills `plan`.
+int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const void* query,
+                    const void* key_cache, const void* value_cache, const int32_t* block_tables,
+                    const int32_t* seq_lens, int32_t S, int32_t H, int32_t KH, int32_t D,
+                    int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS, int32_t dt,
+                    Plan* plan) {
+  if (S < 0 || H < 0 || KH < 0 || D < 0 || BS < 0 || NB < 0 || MB < 0 || P < 0)
+    return fail(PA_ERR_SHAPE, "negative size argument");
+  if (S == 0) {
+    plan->fn = nullptr;
+    return PA_OK;  // nothing to do; pointers of empty tensors may be NULL
+  }
+  if (dt != PA_F32 && dt != PA_F16 && dt != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "unknown kv dtype %d", dt);
+  if (!tmp_output || !exp_sums || !max_logits || !query || !key_cache || !value_cache ||
+      !block_tables || !seq_lens)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  const int x = 16 / elem_size(dt);
+  if (H < 1 || KH < 1 || H % KH) return fail(PA_ERR_SHAPE, "num_heads %d not a multiple of num_kv_heads %d", H, KH);
+  if (D < 1 || D % x) return fail(PA_ERR_SHAPE, "head_size %d not a multiple of x = %d", D, x);
+  if (BS < 1 || PS <= 0 || PS % BS)
+    return fail(PA_ERR_SHAPE, "partition_size %d must be a positive multiple of block_size %d", PS, BS);
+  if (P < 1) return fail(PA_ERR_SHAPE, "max_num_partitions must be >= 1");
+  if (MB < 1) return fail(PA_ERR_SHAPE, "max_blocks_per_seq must be >= 1");
+  if (NB < 1) return fail(PA_ERR_SHAPE, "num_blocks must be >= 1");
+  const int di = d_index(D), bi = bs_index(BS);
+  if (di < 0) return fail(PA_ERR_UNSUPPORTED, "head_size %d not in {64, 128, 256}", D);
+  if (bi < 0) return fail(PA_ERR_UNSUPPORTED, "block_size %d not in {16, 32}", BS);
+  if (PS / BS > 1024) return fail(PA_ERR_UNSUPPORTED, "partition_size / block_size > 1024");
+  const int G = H / KH;
+  partition_fn fn = nullptr;
+  int gm_vec = 0;
+  if (dt != PA_F32 && G >= 4 && G <= 16) {
+    fn = kMfma[dt - 1][di][bi];
+  } else if (G <= 4) {
+    const int gi = G == 1 ? 0 : G == 2 ? 1 : 2;
+    gm_vec = G == 1 ? 1 : G == 2 ? 2 : 4;
+    fn = kVec[dt][di][bi][gi];
+  } else {
+    return fail(PA_ERR_UNSUPPORTED, "group size %d not supported for this dtype", G);
+  }
+  if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      !aligned16(tmp_output))
+    return fail(PA_ERR_ALIGN, "query, key_cache, value_cache and tmp_output must be 16-byte aligned");
+  const long long grid = (long long)S * KH * P;
+  if (grid > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many work units");
+  const int lds = pa::lds_layout(PS, BS, G, D, gm_vec).total;
+  if (lds > max_lds_per_block())
+    return fail(PA_ERR_UNSUPPORTED, "needs %d bytes of LDS per workgroup, device allows %d", lds,
+                max_lds_per_block());
+  plan->fn = fn;
+  plan->lds_bytes = lds;
+  plan->grid = (int)grid;
+  return PA_OK;
+}
+
+int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float* max_logits,
+                     const void* query, const void* key_cache, const void* value_cache,
+                     const int32_t* block_tables, const int32_t* seq_lens, int32_t S, int32_t H,
+                     int32_t KH, int32_t MB, int32_t P, int32_t PS, float scale,
+                     hipStream_t stream) {
+  PartitionArgs a;
+  a.tmp_out = tmp_output;
+  a.exp_sums = exp_sums;
+  a.max_logits = max_logits;
+  a.q = query;
+  a.kc = key_cache;
+  a.vc = value_cache;
+  a.bt = block_tables;
+  a.sl = seq_lens;
+  a.S = S;
+  a.H = H;
+  a.KH = KH;
+  a.MB = MB;
+  a.P = P;
+  a.PS = PS;
+  a.qk_scale = scale * pa::kLog2e;
+  hipLaunchKernelGGL(plan.fn, dim3(plan.grid), dim3(pa::kWaves * 64), plan.lds_bytes, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "partition launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int check_reduce(void* out, const float* tmp_output, const float* exp_sums,
+                 const float* max_logits, const int32_t* seq_lens, int32_t S, int32_t H,
+                 int32_t D, int32_t P, int32_t PS, int32_t odt, reduce_fn* fn) {
+  if (S < 0 || H < 0 || D < 0 || P < 0) return fail(PA_ERR_SHAPE, "negative size argument");
+  if (S == 0) {
+    *fn = nullptr;
+    return PA_OK;
+  }
+  if (odt != PA_F32 && odt != PA_F16 && odt != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "unknown out dtype %d", odt);
+  if (!out || !tmp_output || !exp_sums || !max_logits || !seq_lens)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  if (H < 1) return fail(PA_ERR_SHAPE, "num_heads must be >= 1");
+  if (PS <= 0) return fail(PA_ERR_SHAPE, "partition_size must be positive");
+  if (P < 1) return fail(PA_ERR_SHAPE, "max_num_partitions must be >= 1");
+  const int di = d_index(D);
+  if (di < 0) return fail(PA_ERR_UNSUPPORTED, "head_size %d not in {64, 128, 256}", D);
+  if (!aligned16(out) || !aligned16(tmp_output))
+    return fail(PA_ERR_ALIGN, "out and tmp_output must be 16-byte aligned");
+  if ((long long)S * H > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many rows");
+  *fn = kReduce[odt][di];
+  return PA_OK;
+}
+
+int launch_reduce(reduce_fn fn, void* out, const float* tmp_output, const float* exp_sums,
+                  const float* max_logits, const int32_t* seq_lens, int32_t S, int32_t H,
+                  int32_t P, int32_t PS, hipStream_t stream) {
+  ReduceArgs a;
+  a.out = out;
+  a.tmp_out = tmp_output;
+  a.exp_sums = exp_sums;
+  a.max_logits = max_logits;
+  a.sl = seq_lens;
+  a.S = S;
+  a.H = H;
+  a.P = P;
+  a.PS = PS;
+  const int rows = S * H;
+  hipLaunchKernelGGL(fn, dim3((rows + 3) / 4), dim3(256), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "reduce launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_v2_partition(float* tmp_output, float* exp_sums, float* max_logits,
+                            const void* query, const void* key_cache, const void* value_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_size, int32_t block_size, int32_t num_blocks,
+                            int32_t max_blocks_per_seq, int32_t max_num_partitions,
+                            int32_t partition_size, float scale, int32_t kv_dtype,
+                            void* stream) {
+  g_err[0] = 0;
+  Plan plan;
+  int rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                           block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                           block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
+                           partition_size, kv_dtype, &plan);
+  if (rc != PA_OK || num_seqs == 0) return rc;
+  return launch_partition(plan, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                          block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
+                          max_blocks_per_seq, max_num_partitions, partition_size, scale,
+                          (hipStream_t)stream);
+}
+
+int paged_attn_v2_reduce(void* out, const float* tmp_output, const float* exp_sums,
+                         const float* max_logits, const int32_t* seq_lens, int32_t num_seqs,
+                         int32_t num_heads, int32_t head_size, int32_t max_num_partitions,
+                         int32_t partition_size, int32_t out_dtype, void* stream) {
+  g_err[0] = 0;
+  reduce_fn fn = nullptr;
+  int rc = check_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, num_seqs, num_heads,
+                        head_size, max_num_partitions, partition_size, out_dtype, &fn);
+  if (rc != PA_OK || num_seqs == 0) return rc;
+  return launch_reduce(fn, out, tmp_output, exp_sums, max_logits, seq_lens, num_seqs, num_heads,
+                       max_num_partitions, partition_size, (hipStream_t)stream);
+}
+
+int paged_attn_decode(void* out, float* tmp_output, float* exp_sums, float* max_logits,
+                      const void* query, const void* key_cache, const void* value_cache,
+                      const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                      int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                      int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                      int32_t max_num_partitions, int32_t partition_size, float scale,
+                      int32_t kv_dtype, int32_t out_dtype, void* stream) {
+  g_err[0] = 0;
+  Plan plan;
+  int rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                           block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                           block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
+                           partition_size, kv_dtype, &plan);
+  if (rc != PA_OK || num_seqs == 0) return rc;
+  if (out_dtype != PA_F32 && out_dtype != kv_dtype)
+    return fail(PA_ERR_UNSUPPORTED, "out dtype must be PA_F32 or the kv dtype");
+  reduce_fn fn = nullptr;
+  rc = check_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, num_seqs, num_heads,
+                    head_size, max_num_partitions, partition_size, out_dtype, &fn);
+  if (rc != PA_OK || num_seqs == 0) return rc;
+  rc = launch_partition(plan, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                        block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
+                        max_blocks_per_seq, max_num_partitions, partition_size, scale,
+                        (hipStream_t)stream);
+  if (rc != PA_OK) return rc;
+  return launch_reduce(fn, out, tmp_output, exp_sums, max_logits, seq_lens, num_seqs, num_heads,
+                       max_num_partitions, partition_size, (hipStream_t)stream);
+}
+
+const char* paged_attn_last_error(void) { return g_err; }
+
+int paged_attn_abi_version(void) { return 1; }
+
+int paged_attn_default_partition_size(int32_t head_size, int32_t block_size, int32_t kv_dtype,
+                                      int32_t group) {
+  if (d_index(head_size) < 0 || bs_index(block_size) < 0)
+    return fail(PA_ERR_UNSUPPORTED, "unsupported head_size / block_size");
+  if (kv_dtype != PA_F32 && kv_dtype != PA_F16 && kv_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "unknown kv dtype %d", kv_dtype);
+  if (group < 1 || group > 16) return fail(PA_ERR_UNSUPPORTED, "group size %d", group);
+  return 512;
+}
+
+}  // extern "C"

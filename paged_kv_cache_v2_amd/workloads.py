@@ -157,18 +157,14 @@ def draw_lengths(cfg: DecodeConfig, seed: int) -> np.ndarray:
     return _rng(seed, _KEY_LENS).integers(cfg.len_lo, cfg.len_hi + 1, size=cfg.num_seqs)
 
 
-def make_inputs(cfg: DecodeConfig, seed: int, lens: Optional[Sequence[int]] = None,
-                device: str = "cpu") -> Dict[str, object]:
-    """Build one seeded input set for ``cfg``.
+def make_metadata(cfg: DecodeConfig, seed: int, lens: Optional[Sequence[int]] = None,
+                  extra_blocks: int = 0) -> Dict[str, object]:
+    """Lengths, shuffled block tables and sizes of one input set (no K/V values).
 
-    Returns a dict with torch tensors ``query``, ``key_cache``, ``value_cache``,
-    ``block_tables``, ``seq_lens`` plus the integer sizes the C-ABI takes.
-    ``lens`` overrides the drawn lengths (edge-case tests).
+    ``lens`` overrides the drawn lengths; ``extra_blocks`` adds physical blocks
+    that no sequence references (decoys).
     """
-    S, H, KH, D, BS = (cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_size,
-                       cfg.block_size)
-    x = cfg.x
-    assert H % KH == 0 and D % x == 0
+    S, BS = cfg.num_seqs, cfg.block_size
     seq_lens = np.asarray(lens if lens is not None else draw_lengths(cfg, seed), dtype=np.int64)
     assert seq_lens.shape == (S,)
     MB = cfg.max_blocks_per_seq
@@ -176,7 +172,7 @@ def make_inputs(cfg: DecodeConfig, seed: int, lens: Optional[Sequence[int]] = No
     assert int(seq_lens.max(initial=0)) <= min(MB * BS, P * cfg.partition_size)
     blocks_per_seq = [-(-int(n) // BS) for n in seq_lens]
     used = sum(blocks_per_seq)
-    NB = cfg.num_blocks if cfg.num_blocks is not None else max(1, used)
+    NB = (cfg.num_blocks if cfg.num_blocks is not None else max(1, used)) + extra_blocks
     assert NB >= used, "num_blocks too small for the drawn lengths"
     perm = _rng(seed, _KEY_PERM).permutation(NB).astype(np.int32)
     bt = np.full((S, MB), -1, dtype=np.int32)
@@ -184,7 +180,28 @@ def make_inputs(cfg: DecodeConfig, seed: int, lens: Optional[Sequence[int]] = No
     for s, nb in enumerate(blocks_per_seq):
         bt[s, :nb] = perm[pos:pos + nb]
         pos += nb
+    return dict(block_tables=torch.from_numpy(bt),
+                seq_lens=torch.from_numpy(seq_lens.astype(np.int32)),
+                num_seqs=S, num_heads=cfg.num_heads, num_kv_heads=cfg.num_kv_heads,
+                head_size=cfg.head_size, block_size=BS, num_blocks=NB, max_blocks_per_seq=MB,
+                max_num_partitions=P, partition_size=cfg.partition_size, scale=cfg.scale_f32,
+                dtype=cfg.dtype, x=cfg.x, used_blocks=used)
 
+
+def make_inputs(cfg: DecodeConfig, seed: int, lens: Optional[Sequence[int]] = None,
+                device: str = "cpu", extra_blocks: int = 0) -> Dict[str, object]:
+    """Build one seeded input set for ``cfg``.
+
+    Returns the metadata of ``make_metadata`` plus torch tensors ``query``,
+    ``key_cache`` and ``value_cache`` drawn N(0, sigma^2) and rounded to the
+    workload's dtype.
+    """
+    S, H, KH, D, BS = (cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_size,
+                       cfg.block_size)
+    x = cfg.x
+    assert H % KH == 0 and D % x == 0
+    out = make_metadata(cfg, seed, lens, extra_blocks)
+    NB = out["num_blocks"]
     tdt = DTYPES[cfg.dtype]
 
     def tensor(key: int, shape) -> torch.Tensor:
@@ -192,16 +209,9 @@ def make_inputs(cfg: DecodeConfig, seed: int, lens: Optional[Sequence[int]] = No
         vals = torch.from_numpy(_normals(seed, key, n, cfg.sigma)).reshape(shape)
         return vals.to(tdt)
 
-    q = tensor(_KEY_Q, (S, H, D))
-    kc = tensor(_KEY_K, (NB, KH, D // x, BS, x))
-    vc = tensor(_KEY_V, (NB, KH, D, BS))
-    out = dict(
-        query=q, key_cache=kc, value_cache=vc,
-        block_tables=torch.from_numpy(bt), seq_lens=torch.from_numpy(seq_lens.astype(np.int32)),
-        num_seqs=S, num_heads=H, num_kv_heads=KH, head_size=D, block_size=BS,
-        num_blocks=NB, max_blocks_per_seq=MB, max_num_partitions=P,
-        partition_size=cfg.partition_size, scale=cfg.scale_f32, dtype=cfg.dtype,
-        x=x, used_blocks=used)
+    out["query"] = tensor(_KEY_Q, (S, H, D))
+    out["key_cache"] = tensor(_KEY_K, (NB, KH, D // x, BS, x))
+    out["value_cache"] = tensor(_KEY_V, (NB, KH, D, BS))
     if device != "cpu":
         for k in ("query", "key_cache", "value_cache", "block_tables", "seq_lens"):
             out[k] = out[k].to(device)

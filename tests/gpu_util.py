@@ -1,0 +1,116 @@
+"""Helpers for the GPU parity tests: run the HIP path, compare with the oracle.
+
+The comparison bar is the one the measurements are quoted against:
+|gpu - oracle| <= 1e-3 + 1e-3 * |oracle| elementwise on fp32 results, exact
+sentinels for empty partitions, bit-exact integer / index work.
+"""
+from __future__ import annotations
+
+import math
+import sys
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_v2_amd as pa
+from paged_kv_cache_v2_amd import workloads as W
+
+ATOL = 1e-3
+RTOL = 1e-3
+DEV = "cuda"
+
+
+def note(msg: str) -> None:
+    """Name the case on stdout before a GPU step (survives a crash of the step)."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(inp: Dict[str, object]) -> Dict[str, object]:
+    out = dict(inp)
+    for k in ("query", "key_cache", "value_cache", "block_tables", "seq_lens"):
+        out[k] = inp[k].to(DEV)
+    return out
+
+
+def num_partitions(inp, PS: int) -> int:
+    return max(1, -(-int(inp["seq_lens"].max()) // PS))
+
+
+def run_decode(dinp: Dict[str, object], PS: Optional[int] = None, P: Optional[int] = None,
+               out_dtype=torch.float32, split: bool = False) -> Dict[str, torch.Tensor]:
+    """One decode through the C ABI; workspace pre-filled with NaN. Host copies back."""
+    q = dinp["query"]
+    S, H, D = q.shape
+    PS = PS or dinp["partition_size"]
+    P = P or max(dinp["max_num_partitions"] if PS == dinp["partition_size"] else 1,
+                 num_partitions(dinp, PS))
+    tmp = torch.full((S, H, P, D), float("nan"), device=DEV)
+    es = torch.full((S, H, P), float("nan"), device=DEV)
+    ml = torch.full((S, H, P), float("nan"), device=DEV)
+    out = torch.full((S, H, D), float("nan"), device=DEV).to(out_dtype)
+    args = (q, dinp["key_cache"], dinp["value_cache"], dinp["block_tables"], dinp["seq_lens"])
+    if split:
+        pa.paged_attn_v2_partition(tmp, es, ml, *args, dinp["scale"], PS)
+        pa.paged_attn_v2_reduce(out, tmp, es, ml, dinp["seq_lens"], PS)
+    else:
+        pa.paged_attn_decode(out, tmp, es, ml, *args, dinp["scale"], PS)
+    torch.cuda.synchronize()
+    return dict(out=out.cpu(), tmp=tmp.cpu(), es=es.cpu(), ml=ml.cpu(), P=P, PS=PS)
+
+
+def assert_close(name: str, got, ref, atol: float = ATOL, rtol: float = RTOL) -> float:
+    got = np.asarray(got.double().numpy() if isinstance(got, torch.Tensor) else got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    err = np.abs(got - ref)
+    lim = atol + rtol * np.abs(ref)
+    bad = ~(err <= lim)  # NaN counts as bad
+    if bad.any():
+        idx = np.unravel_index(np.argmax(np.where(bad, err - lim, -np.inf)), bad.shape)
+        raise AssertionError(f"{name}: {int(bad.sum())}/{bad.size} outside tolerance; worst at "
+                             f"{idx}: gpu={got[idx]!r} ref={ref[idx]!r}")
+    return float(np.max(err / lim)) if err.size else 0.0
+
+
+def check_against_oracle(inp: Dict[str, object], res: Dict[str, torch.Tensor],
+                         seqs: Optional[Sequence[int]] = None, label: str = "") -> None:
+    """Compare out and the partition intermediates of `seqs` (all if None) with the oracle."""
+    S = inp["query"].shape[0]
+    rows = list(range(S)) if seqs is None else sorted(set(int(s) for s in seqs))
+    args = (inp["query"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
+            inp["seq_lens"], inp["scale"])
+    ref = oracle.attention(*args, seqs=rows)
+    assert_close(f"{label} out", res["out"][rows].float(), ref[rows])
+    tmp, es, ml = oracle.partition_stats(*args, res["P"], res["PS"], seqs=rows)
+    sl = inp["seq_lens"].tolist()
+    for s in rows:
+        n = -(-sl[s] // res["PS"]) if sl[s] > 0 else 0
+        if n:
+            assert_close(f"{label} max_logits s={s}", res["ml"][s, :, :n], ml[s, :, :n])
+            assert_close(f"{label} exp_sums s={s}", res["es"][s, :, :n], es[s, :, :n])
+            assert_close(f"{label} tmp_output s={s}", res["tmp"][s, :, :n], tmp[s, :, :n])
+        # empty partitions: exact sentinels, tmp_output untouched (still NaN)
+        assert torch.all(res["ml"][s, :, n:] == -math.inf), f"{label} sentinel max s={s}"
+        assert torch.all(res["es"][s, :, n:] == 0), f"{label} sentinel sum s={s}"
+        assert torch.all(torch.isnan(res["tmp"][s, :, n:])), f"{label} tmp written s={s}"
+
+
+def small_config(name: str) -> W.DecodeConfig:
+    """A reduced-size version of a named workload: same heads, dims, dtype and
+    block/partition geometry; fewer and shorter sequences (several tiles,
+    several partitions and a ragged tail each)."""
+    cfg = W.CONFIGS[name]
+    if name == "tiny_f32_d64":
+        return cfg
+    if name == "mha_f16_d128":
+        return cfg.replace(num_seqs=5, len_lo=1, len_hi=1100)
+    if name == "gqa_bf16_g4":
+        return cfg.replace(num_seqs=6, len_lo=1, len_hi=1600)
+    if name == "longctx_bf16_g8":
+        return cfg.replace(num_seqs=2, fixed_lens=(2500, 1300))
+    if name == "wide_f16_d256":
+        return cfg.replace(num_seqs=3, len_lo=100, len_hi=1800)
+    raise KeyError(name)

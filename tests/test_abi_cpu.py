@@ -1,0 +1,166 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and rejects bad arguments on the host with the documented status
+codes and a message. Every call here fails validation (or is the documented
+num_seqs == 0 no-op), so nothing is ever enqueued on a device.
+"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+import torch
+
+import paged_kv_cache_v2_amd as pa
+from paged_kv_cache_v2_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 40  # a 16-byte aligned, never dereferenced address
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    pa.ensure_built()
+
+
+def declared_symbols():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        names += re.findall(r"PA_API\s+[\w\s\*]+?\b(\w+)\s*\(", open(h).read())
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_symbols()
+    for n in ("paged_attn_v2_partition", "paged_attn_v2_reduce", "paged_attn_decode",
+              "paged_attn_last_error", "paged_attn_abi_version",
+              "paged_attn_default_partition_size"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for n in declared_symbols():
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_default_partition_size():
+    assert pa.abi_version() == 1
+    for D, BS, dt, G in [(128, 16, torch.bfloat16, 4), (256, 32, torch.float16, 1),
+                         (64, 16, torch.float32, 1)]:
+        ps = pa.default_partition_size(D, BS, dt, G)
+        assert ps > 0 and ps % BS == 0
+    with pytest.raises(RuntimeError):
+        pa.default_partition_size(96, 16, torch.float16, 1)
+
+
+# Valid baseline: bf16, S=2, H=8, KH=2, D=128, BS=16, B=64, MB=8, P=1, PS=512
+BASE = dict(S=2, H=8, KH=2, D=128, BS=16, B=64, MB=8, P=1, PS=512, dt=binding.PA_BF16)
+
+
+def part(ptrs=None, **kw):
+    a = dict(BASE, **kw)
+    p = [FAKE] * 8 if ptrs is None else ptrs
+    return pa.lib().paged_attn_v2_partition(*p, a["S"], a["H"], a["KH"], a["D"], a["BS"], a["B"],
+                                            a["MB"], a["P"], a["PS"], 0.125, a["dt"], None)
+
+
+def decode(odt, **kw):
+    a = dict(BASE, **kw)
+    return pa.lib().paged_attn_decode(*([FAKE] * 9), a["S"], a["H"], a["KH"], a["D"], a["BS"],
+                                      a["B"], a["MB"], a["P"], a["PS"], 0.125, a["dt"], odt, None)
+
+
+def reduce(ptrs=None, S=2, H=8, D=128, P=1, PS=512, odt=binding.PA_F32):
+    p = [FAKE] * 5 if ptrs is None else ptrs
+    return pa.lib().paged_attn_v2_reduce(*p, S, H, D, P, PS, odt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=-1), binding.PA_ERR_SHAPE),
+    (dict(H=6, KH=4), binding.PA_ERR_SHAPE),
+    (dict(D=100), binding.PA_ERR_SHAPE),               # 100 % 8 != 0
+    (dict(PS=500), binding.PA_ERR_SHAPE),              # 500 % 16 != 0
+    (dict(PS=0), binding.PA_ERR_SHAPE),
+    (dict(P=0), binding.PA_ERR_SHAPE),
+    (dict(MB=0), binding.PA_ERR_SHAPE),
+    (dict(B=0), binding.PA_ERR_SHAPE),
+    (dict(D=96), binding.PA_ERR_UNSUPPORTED),
+    (dict(D=512), binding.PA_ERR_UNSUPPORTED),
+    (dict(BS=8, PS=512), binding.PA_ERR_UNSUPPORTED),
+    (dict(dt=7), binding.PA_ERR_UNSUPPORTED),
+    (dict(H=64, KH=2), binding.PA_ERR_UNSUPPORTED),    # G = 32
+    (dict(H=16, KH=2, dt=binding.PA_F32), binding.PA_ERR_UNSUPPORTED),  # fp32, G = 8
+    (dict(PS=16 * 2048), binding.PA_ERR_UNSUPPORTED),  # PS / BS > 1024
+])
+def test_partition_rejects(kw, code):
+    assert part(**kw) == code
+    assert pa.last_error() != ""
+
+
+@pytest.mark.parametrize("which", range(8))
+def test_partition_null_pointer(which):
+    ptrs = [FAKE] * 8
+    ptrs[which] = None
+    assert part(ptrs) == binding.PA_ERR_NULL
+    assert "NULL" in pa.last_error()
+
+
+@pytest.mark.parametrize("which", [0, 3, 4, 5])  # tmp_output, query, key_cache, value_cache
+def test_partition_misaligned(which):
+    ptrs = [FAKE] * 8
+    ptrs[which] = FAKE + 2
+    assert part(ptrs) == binding.PA_ERR_ALIGN
+
+
+def test_num_seqs_zero_is_noop_even_with_null_pointers():
+    assert part([None] * 8, S=0) == binding.PA_OK
+    assert pa.last_error() == ""
+    assert reduce([None] * 5, S=0) == binding.PA_OK
+    assert pa.lib().paged_attn_decode(*([None] * 9), 0, 8, 2, 128, 16, 64, 8, 1, 512, 0.125,
+                                      binding.PA_BF16, binding.PA_F32, None) == binding.PA_OK
+
+
+def test_decode_out_dtype_must_be_f32_or_kv():
+    assert decode(binding.PA_F16) == binding.PA_ERR_UNSUPPORTED
+    assert decode(binding.PA_BF16, D=96) == binding.PA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=-2), binding.PA_ERR_SHAPE),
+    (dict(H=0), binding.PA_ERR_SHAPE),
+    (dict(P=0), binding.PA_ERR_SHAPE),
+    (dict(PS=0), binding.PA_ERR_SHAPE),
+    (dict(D=96), binding.PA_ERR_UNSUPPORTED),
+    (dict(odt=9), binding.PA_ERR_UNSUPPORTED),
+])
+def test_reduce_rejects(kw, code):
+    assert reduce(**kw) == code
+
+
+def test_reduce_null_and_align():
+    for i in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[i] = None
+        assert reduce(ptrs) == binding.PA_ERR_NULL
+    ptrs = [FAKE] * 5
+    ptrs[0] = FAKE + 4
+    assert reduce(ptrs) == binding.PA_ERR_ALIGN
+
+
+def test_binding_rejects_host_tensors():
+    q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    kc = torch.zeros(4, 2, 16, 16, 8, dtype=torch.bfloat16)
+    vc = torch.zeros(4, 2, 128, 16, dtype=torch.bfloat16)
+    bt = torch.zeros(2, 8, dtype=torch.int32)
+    sl = torch.zeros(2, dtype=torch.int32)
+    tmp, es, ml = (torch.zeros(2, 8, 1, 128), torch.zeros(2, 8, 1), torch.zeros(2, 8, 1))
+    with pytest.raises(ValueError):
+        pa.paged_attn_v2_partition(tmp, es, ml, q, kc, vc, bt, sl, 0.1, 512)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(binding, "_LIB", None)
+    monkeypatch.setattr(binding, "LIB_PATH", "/nonexistent/libpaged_attn.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.lib()
