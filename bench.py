@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Benchmark of paged single-query decode attention (V2 split, GQA) on one MI355X.
+
+One step is the whole hot path over one batch: paged_attn_v2_partition then
+paged_attn_v2_reduce on one stream, inputs already resident in HBM. W warmup
+steps, then exactly K timed steps between two torch.cuda.synchronize() calls.
+Prints ONE JSON line:
+
+  value      = algorithmic K+V bytes per step / step time (GB/s), the metric's
+               "achieved HBM GB/s"; the line also carries the % of the 8 TB/s
+               peak and query-heads x tokens / s.
+  roofline   = the dominant kernel (the partition kernel): algorithmic K+V
+               bytes per launch / its average duration, measured with HIP events
+               recorded around every launch on the launch stream inside the timed
+               region; `traffic` = HBM bytes per launch from the committed
+               rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the
+               current kernel source (else null).
+  cpu_baseline = the fp64 oracle (partition stats + combine) timed on this
+               host's cores over a bounded sample of the same workload.
+
+Only one GPU is used; --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "decode attention achieved HBM GB/s (% of peak) + query-heads×tokens/s, GQA cfg"
+DEFAULT_WORKLOAD = "gqa_bf16_g4"
+TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "*hbm_traffic*.md")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "paged_kv_cache_v2_amd", "csrc", "*")) +
+                   glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from a committed counter summary taken on this source."""
+    want = source_hash()
+    for path in sorted(glob.glob(TRAFFIC_GLOB)):
+        text = open(path).read()
+        fields = dict(re.findall(r"^- (\w+): `?([^`\n]+)`?$", text, re.M))
+        if (fields.get("kernel_source_hash") == want and fields.get("workload") == workload
+                and fields.get("kernel") == kernel and "traffic_bytes_per_launch" in fields):
+            return int(float(fields["traffic_bytes_per_launch"])), os.path.relpath(path, ROOT)
+    return None, None
+
+
+def cpu_baseline(inp, W, min_seconds: float):
+    import oracle
+    import torch  # noqa: F401
+    threads = oracle.default_threads()
+    args = (inp["query"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
+            inp["seq_lens"], inp["scale"])
+    P, PS = inp["max_num_partitions"], inp["partition_size"]
+    runs, t_total = 0, 0.0
+    while runs == 0 or t_total < min_seconds:
+        t0 = time.perf_counter()
+        tmp, es, ml = oracle.partition_stats(*args, P, PS, nthreads=threads)
+        oracle.combine(tmp, es, ml, inp["seq_lens"], PS)
+        t_total += time.perf_counter() - t0
+        runs += 1
+        del tmp, es, ml
+    per_run = t_total / runs
+    return {
+        "value": round(W.kv_bytes(inp) / per_run / 1e9, 4), "unit": "GB/s", "cores": threads,
+        "kind": "oracle",
+        "sample": (f"whole workload ({inp['num_seqs']} sequences, "
+                   f"{int(inp['seq_lens'].sum())} tokens) x {runs} run(s), fp64 partition "
+                   f"stats + combine, {per_run:.2f} s per run"),
+    }
+
+
+def run(args) -> dict:
+    import torch
+
+    import paged_kv_cache_v2_amd as pa
+    from paged_kv_cache_v2_amd import workloads as W
+
+    pa.ensure_built()
+    cfg = W.CONFIGS[args.workload]
+    seed = W.CONFIG_ORDER.index(args.workload) + 1
+    inp = W.make_inputs(cfg, seed=seed)
+    PS = args.partition_size or cfg.partition_size
+    P = max(1, -(-int(inp["seq_lens"].max()) // PS))
+    P = max(P, cfg.max_num_partitions) if PS == cfg.partition_size else P
+    dev = torch.device("cuda", 0)
+    q, kc, vc = (inp[k].to(dev) for k in ("query", "key_cache", "value_cache"))
+    bt, sl = inp["block_tables"].to(dev), inp["seq_lens"].to(dev)
+    S, H, D = q.shape
+    out = torch.empty(S, H, D, dtype=torch.float32, device=dev)
+    tmp, es, ml = pa.workspace(S, H, D, P, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        pa.paged_attn_v2_partition(tmp, es, ml, q, kc, vc, bt, sl, inp["scale"], PS, stream)
+        pa.paged_attn_v2_reduce(out, tmp, es, ml, sl, PS, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        pa.paged_attn_v2_partition(tmp, es, ml, q, kc, vc, bt, sl, inp["scale"], PS, stream)
+        ev[i][1].record(stream)
+        pa.paged_attn_v2_reduce(out, tmp, es, ml, sl, PS, stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    part_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    part_avg_s = sum(part_ms) / len(part_ms) / 1e3
+
+    kvb = W.kv_bytes(inp)
+    step_s = elapsed / K
+    gbs = kvb / step_s / 1e9
+    achieved = kvb / part_avg_s / 1e9
+    kernel = ("partition_mfma_kernel" if (cfg.dtype != "f32" and 4 <= cfg.group <= 16)
+              else "partition_vec_kernel")
+    traffic, traffic_src = committed_traffic(args.workload, kernel)
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "qheads_tokens_per_s": round(W.qhead_tokens(inp) / step_s, 1),
+        "config": {
+            "workload": args.workload, "num_seqs": S, "num_heads": H,
+            "num_kv_heads": cfg.num_kv_heads, "head_size": D, "block_size": cfg.block_size,
+            "partition_size": PS, "max_num_partitions": P,
+            "seq_lens": (f"fixed {list(cfg.fixed_lens)[:2]}..." if cfg.fixed_lens else
+                         f"uniform[{cfg.len_lo},{cfg.len_hi}] seed {seed}"),
+            "total_tokens": int(inp["seq_lens"].sum()), "kv_bytes_per_step": kvb,
+            "num_blocks": inp["num_blocks"],
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "kernel": kernel, "kernel_avg_us": round(part_avg_s * 1e6, 3),
+            "kernel_p10_us": round(part_ms[len(part_ms) // 10] * 1e3, 3),
+            "kernel_p90_us": round(part_ms[(9 * len(part_ms)) // 10] * 1e3, 3),
+            "bytes_per_launch": kvb, "traffic_source": traffic_src,
+            "kernel_source_hash": source_hash(),
+        },
+    }
+    if args.calibrate_copy:
+        n = 1 << 28  # 1 GiB of fp32: FETCH_SIZE / WRITE_SIZE calibration for the counters
+        a = torch.ones(n, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = 4 * n
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, W, args.cpu_min_seconds)
+    return res
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration under rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU mode; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        return 2
+    res = run(args)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -126,6 +126,11 @@ __device__ __forceinline__ float row16_sum(float v) {
 __device__ __forceinline__ float wave_max(float v) { return rows_max(row16_max(v)); }
 __device__ __forceinline__ float wave_sum(float v) { return rows_sum(row16_sum(v)); }
 
+// Value of `v` in lane `src` (wavefront-uniform src): v_readlane into an SGPR.
+__device__ __forceinline__ float lane_value(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
 // Element e of a lane's run of tokens is a real token iff e < nvalid.
 __device__ __forceinline__ bool e_valid(int e, int nvalid) { return e < nvalid; }
 

@@ -51,17 +51,16 @@ struct PartitionArgs {
 
 // LDS carve-up shared by both partition kernels (byte offsets).
 struct LdsLayout {
-  int bt_off, m_off, l_off, acc_off, p_off, total;
+  int bt_off, m_off, l_off, acc_off, total;
 };
-__host__ __device__ inline LdsLayout lds_layout(int PS, int BS, int G, int D, int GM_vec) {
+__host__ __device__ inline LdsLayout lds_layout(int PS, int BS, int G, int D) {
   LdsLayout o;
   auto up16 = [](int v) { return (v + 15) & ~15; };
   o.bt_off = 0;
   o.m_off = up16((PS / BS) * 4);
   o.l_off = o.m_off + up16(kWaves * G * 4);
   o.acc_off = o.l_off + up16(kWaves * G * 4);
-  o.p_off = o.acc_off + kWaves * G * D * 4;
-  o.total = o.p_off + kWaves * GM_vec * 16 * 4;
+  o.total = o.acc_off + kWaves * G * D * 4;
   return o;
 }
 
@@ -158,7 +157,7 @@ partition_mfma_kernel(PartitionArgs a) {
   Unit u;
   if (!unit_setup<BS>(a, (int32_t*)smem, u)) return;
   const int G = u.G;
-  const LdsLayout lay = lds_layout(a.PS, BS, G, D, 0);
+  const LdsLayout lay = lds_layout(a.PS, BS, G, D);
   const int32_t* s_bt = (const int32_t*)(smem + lay.bt_off);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -276,7 +275,8 @@ partition_mfma_kernel(PartitionArgs a) {
 // QK: each lane dots its d-chunks of one token with the packed query
 // (v_dot2 for 16-bit, fma for fp32), then a sum across the four 16-lane rows.
 // PV: lane l owns X consecutive tokens (one 16-byte V chunk) of one d; the
-// tile's probabilities reach it through a per-wavefront LDS slot.
+// tile's 16 probabilities are read out of lanes 0..15 with v_readlane
+// (wavefront-uniform) and each lane selects the X of its chunk.
 // =====================================================================
 template <int DT> struct vec_elem {
   static constexpr int X = 8;
@@ -301,7 +301,7 @@ partition_vec_kernel(PartitionArgs a) {
   Unit u;
   if (!unit_setup<BS>(a, (int32_t*)smem, u)) return;
   const int G = u.G;
-  const LdsLayout lay = lds_layout(a.PS, BS, G, D, GM);
+  const LdsLayout lay = lds_layout(a.PS, BS, G, D);
   const int32_t* s_bt = (const int32_t*)(smem + lay.bt_off);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -328,8 +328,6 @@ partition_vec_kernel(PartitionArgs a) {
   const uint8_t* vbase = (const uint8_t*)a.vc + head_off;
   const uint32_t k_lane = (uint32_t)(grp * BS + t) * 16;
   const uint32_t v_lane = (uint32_t)(dl * BS + h * X) * ESZ;
-
-  float* s_p = (float*)(smem + lay.p_off) + wave * GM * 16;
 
   const int my_pages = u.npages > wave ? (u.npages - wave + kWaves - 1) / kWaves : 0;
   const int ntiles = my_pages * TPP;
@@ -387,21 +385,23 @@ partition_vec_kernel(PartitionArgs a) {
 #pragma unroll
       for (int j = 0; j < VJ; ++j) acc[gg][j] *= alpha;
     }
-    // Publish the tile's probabilities (one copy per token) and read back the
-    // X this lane's V chunks need.
-    if (grp == 0) {
-#pragma unroll
-      for (int gg = 0; gg < GM; ++gg) s_p[gg * 16 + t] = p[gg];
-    }
     const int nv = u.L - (tok0 + h * X);  // valid tokens among this lane's X
 #pragma unroll
     for (int gg = 0; gg < GM; ++gg) {
+      // p of token k sits in lane k (rows repeat it); lane picks tokens h*X .. h*X+X-1.
+      float sp[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) sp[k] = lane_value(p[gg], k);
       float pw[X];
 #pragma unroll
-      for (int e4 = 0; e4 < X / 4; ++e4) {
-        const f32x4 v = *(const f32x4*)&s_p[gg * 16 + h * X + 4 * e4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pw[4 * e4 + e] = v[e];
+      for (int e = 0; e < X; ++e) {
+        if constexpr (CPR == 2) {
+          pw[e] = h ? sp[8 + e] : sp[e];
+        } else {
+          const float lo = (h & 1) ? sp[4 + e] : sp[e];
+          const float hi = (h & 1) ? sp[12 + e] : sp[8 + e];
+          pw[e] = (h & 2) ? hi : lo;
+        }
       }
 #pragma unroll
       for (int j = 0; j < VJ; ++j) {
@@ -464,7 +464,9 @@ partition_vec_kernel(PartitionArgs a) {
 
 // =====================================================================
 // Reduce: one wavefront per (sequence, query head); the page's phase-2
-// log-sum-exp combine over the partitions the sequence uses.
+// log-sum-exp combine over the partitions the sequence uses. Lane i computes
+// the weight of partition base+i; the d-parallel accumulation reads each
+// weight back with v_readlane.
 // =====================================================================
 struct ReduceArgs {
   void* out;
@@ -479,7 +481,6 @@ template <int D, int ODT>
 __global__ void __launch_bounds__(256) reduce_kernel(ReduceArgs a) {
   constexpr int NWR = 4;
   constexpr int DPL = D / 64;  // consecutive d per lane
-  __shared__ float s_w[NWR][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sh = blockIdx.x * NWR + wave;
   if (sh >= a.S * a.H) return;  // whole wavefront; only wavefront-local LDS below
@@ -501,7 +502,7 @@ __global__ void __launch_bounds__(256) reduce_kernel(ReduceArgs a) {
     const float* trow = a.tmp_out + (size_t)sh * a.P * D + lane * DPL;
     for (int base = 0; base < n; base += 64) {
       const int i = base + lane;
-      s_w[wave][lane] = i < n ? fast_exp2((mlr[i] - M) * kLog2e) * esr[i] / Z : 0.0f;
+      const float wl = i < n ? fast_exp2((mlr[i] - M) * kLog2e) * esr[i] / Z : 0.0f;
       const int cnt = min(64, n - base);
       int k = 0;
       for (; k + 4 <= cnt; k += 4) {
@@ -514,13 +515,13 @@ __global__ void __launch_bounds__(256) reduce_kernel(ReduceArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float w = s_w[wave][k + u];
+          const float w = lane_value(wl, k + u);
 #pragma unroll
           for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, v[u][e], acc[e]);
         }
       }
       for (; k < cnt; ++k) {
-        const float w = s_w[wave][k];
+        const float w = lane_value(wl, k);
         const float* src = trow + (size_t)(base + k) * D;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, src[e], acc[e]);

@@ -126,12 +126,10 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   if (PS / BS > 1024) return fail(PA_ERR_UNSUPPORTED, "partition_size / block_size > 1024");
   const int G = H / KH;
   partition_fn fn = nullptr;
-  int gm_vec = 0;
   if (dt != PA_F32 && G >= 4 && G <= 16) {
     fn = kMfma[dt - 1][di][bi];
   } else if (G <= 4) {
     const int gi = G == 1 ? 0 : G == 2 ? 1 : 2;
-    gm_vec = G == 1 ? 1 : G == 2 ? 2 : 4;
     fn = kVec[dt][di][bi][gi];
   } else {
     return fail(PA_ERR_UNSUPPORTED, "group size %d not supported for this dtype", G);
@@ -141,7 +139,7 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
     return fail(PA_ERR_ALIGN, "query, key_cache, value_cache and tmp_output must be 16-byte aligned");
   const long long grid = (long long)S * KH * P;
   if (grid > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many work units");
-  const int lds = pa::lds_layout(PS, BS, G, D, gm_vec).total;
+  const int lds = pa::lds_layout(PS, BS, G, D).total;
   if (lds > max_lds_per_block())
     return fail(PA_ERR_UNSUPPORTED, "needs %d bytes of LDS per workgroup, device allows %d", lds,
                 max_lds_per_block());
