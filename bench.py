@@ -10,9 +10,10 @@ Prints ONE JSON line:
                "achieved HBM GB/s"; the line also carries the % of the 8 TB/s
                peak and query-heads x tokens / s.
   roofline   = the dominant kernel (the partition kernel): algorithmic K+V
-               bytes per launch / its average duration, measured with HIP events
-               recorded around every launch on the launch stream inside the timed
-               region; `traffic` = HBM bytes per launch from the committed
+               bytes per launch / its average duration, measured with a HIP event
+               pair on the launch stream around every partition launch of a
+               second pass of the same K steps; `traffic` = HBM bytes per launch
+               from the committed
                rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the
                current kernel source (else null).
   cpu_baseline = the fp64 oracle (partition stats + combine) timed on this
@@ -117,17 +118,24 @@ def run(args) -> dict:
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
+    # Timed region: exactly K whole-path steps between two synchronisations.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # Kernel timing: the same K steps again, with a HIP event pair on the launch
+    # stream around every partition launch (events inside the timed region above
+    # would add their own gaps to the step time).
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
     for i in range(K):
         ev[i][0].record(stream)
         pa.paged_attn_v2_partition(tmp, es, ml, q, kc, vc, bt, sl, inp["scale"], PS, stream)
         ev[i][1].record(stream)
         pa.paged_attn_v2_reduce(out, tmp, es, ml, sl, PS, stream)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     part_ms = sorted(a.elapsed_time(b) for a, b in ev)
     part_avg_s = sum(part_ms) / len(part_ms) / 1e3
 

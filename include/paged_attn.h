@@ -57,7 +57,7 @@ enum {
   PA_ERR_SHAPE = -2,       /* negative size, H % KH, D % x, PS <= 0 or PS % BS, P < 1,
                               MB < 1, B < 1                                            */
   PA_ERR_UNSUPPORTED = -3, /* D not in {64,128,256}, BS not in {16,32}, G outside the
-                              built range, PS / BS > 1024, unknown dtype, or out_dtype
+                              built range, PS / BS > 256, unknown dtype, or out_dtype
                               neither PA_F32 nor kv_dtype                              */
   PA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned                  */
   PA_ERR_HIP = -5          /* the HIP runtime rejected a launch                        */

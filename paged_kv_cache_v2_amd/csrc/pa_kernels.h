@@ -13,12 +13,19 @@
 //  - blockIdx.x = (p * S + s) * KH + kh: kv head fastest, partition slowest, so
 //    the last-dispatched workgroups are the cheap tail/empty partitions.
 //  - A unit covers pages [p*PS/BS, ceil(min((p+1)*PS, L)/BS)); PS % BS == 0 so
-//    partition edges are page edges. The unit's block-table slice is hoisted
-//    into LDS once; NW wavefronts take pages wave, wave+NW, ...
-//  - A page is processed as BS/16 tiles of 16 tokens. K tile: lane l holds
-//    token l%16 and d-chunks c = 4j + l/16 (16-byte dwordx4 loads; each 16 lanes
-//    read 256 contiguous bytes per chunk row). That register image is exactly
-//    the A operand of a 16x16x32 MFMA with the token as row.
+//    partition edges are page edges. The unit's block-table slice is loaded
+//    together with the sequence length (no dependent round trip) and hoisted
+//    into LDS; NW wavefronts take pages wave, wave+NW, ...
+//  - The page is the unit of fetch and compute; it is BS/16 sub-tiles of 16
+//    tokens. K sub-tile: lane l holds token l%16 and d-chunks c = 4j + l/16
+//    (16-byte dwordx4 loads; each 16 lanes read 256 contiguous bytes per chunk
+//    row). That register image is exactly the A operand of a 16x16x32 MFMA
+//    with the token as row. All of a page's loads are issued together, so the
+//    two halves of every cache line of a 32-token page are requested
+//    back to back.
+//  - K/V loads carry the non-temporal hint: every byte is read exactly once,
+//    and streaming them past the caches measured ~12 % faster on MI355X than
+//    letting them allocate normally.
 //  - Each wavefront keeps its own running (max, sum, unnormalised accumulator)
 //    in the log2 domain (scores pre-multiplied by scale*log2(e)); at the end the
 //    NW partial states are merged through LDS with the same log-sum-exp rule
@@ -34,7 +41,98 @@
 
 namespace pa {
 
-constexpr int kWaves = 4;  // wavefronts per partition workgroup
+// Compile-time tuning (measured on MI355X).
+#ifndef PA_WAVES
+#define PA_WAVES 4           // wavefronts per partition workgroup
+#endif
+#ifndef PA_PREFETCH
+#define PA_PREFETCH 1        // pages in flight ahead of the one being computed
+#endif
+#ifndef PA_PF_REG_BUDGET
+#define PA_PF_REG_BUDGET 32  // prefetch only if a page fits in this many VGPRs
+#endif
+#ifndef PA_MIN_WAVES
+#define PA_MIN_WAVES 0       // >0: ask the compiler for this many waves per SIMD
+#endif
+#if PA_MIN_WAVES > 0
+#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_MIN_WAVES)))
+#else
+#define PA_OCCUPANCY
+#endif
+#ifndef PA_PIN_PREFETCH
+#define PA_PIN_PREFETCH 1    // scheduling barrier between prefetch issue and compute
+#endif
+#ifndef PA_NT_LOADS
+#define PA_NT_LOADS 1        // K/V loads carry the non-temporal (streaming) hint
+#endif
+constexpr int kWaves = PA_WAVES;
+
+template <typename T>
+__device__ __forceinline__ T stream_load(const void* p) {
+#if PA_NT_LOADS
+  return __builtin_nontemporal_load((const T*)p);
+#else
+  return *(const T*)p;
+#endif
+}
+
+// Software pipeline over a wavefront's pages: fetch(i, buf) is issued PF pages
+// ahead of process(i, buf); buffers rotate through a ring whose indices are
+// compile-time constants after unrolling, so they stay in registers.
+template <int PF, typename Buf, typename Fetch, typename Process>
+__device__ __forceinline__ void pipeline(int n, Buf (&buf)[PF + 1], Fetch&& fetch,
+                                         Process&& process) {
+  constexpr int NB = PF + 1;
+#pragma unroll
+  for (int b = 0; b < PF; ++b)
+    if (b < n) fetch(b, buf[b]);
+  for (int t0 = 0; t0 < n; t0 += NB) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int t = t0 + b;
+      if (t < n) {
+        if (t + PF < n) fetch(t + PF, buf[(b + PF) % NB]);
+#if PA_PIN_PREFETCH
+        // Keep the prefetch loads ahead of this page's compute: left free, the
+        // scheduler may sink them past it, which serialises load and compute.
+        __builtin_amdgcn_sched_barrier(0);
+#endif
+        process(t, buf[b]);
+      }
+    }
+  }
+}
+
+constexpr int prefetch_for(int page_regs) {
+  return page_regs <= PA_PF_REG_BUDGET ? PA_PREFETCH : 0;
+}
+
+// cand(h) for a lane-varying h in [0, N) as a tree of selects over scalars.
+// Every candidate is evaluated unconditionally first: cand() reads other lanes
+// (v_readlane, a convergent operation), so a short-circuit `b ? cand(1) :
+// cand(0)` would become a divergent branch. Candidates are kept in scalars,
+// not an array, which the compiler could fold into an indexed stack load.
+template <int N, typename F>
+__device__ __forceinline__ float pick(int h, F&& cand) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8, "pick: N in {1, 2, 4, 8}");
+  const bool b0 = h & 1, b1 = h & 2, b2 = h & 4;
+  if constexpr (N == 1) {
+    return cand(0);
+  } else if constexpr (N == 2) {
+    const float c0 = cand(0), c1 = cand(1);
+    return b0 ? c1 : c0;
+  } else if constexpr (N == 4) {
+    const float c0 = cand(0), c1 = cand(1), c2 = cand(2), c3 = cand(3);
+    const float lo = b0 ? c1 : c0, hi = b0 ? c3 : c2;
+    return b1 ? hi : lo;
+  } else {
+    const float c0 = cand(0), c1 = cand(1), c2 = cand(2), c3 = cand(3);
+    const float c4 = cand(4), c5 = cand(5), c6 = cand(6), c7 = cand(7);
+    const float c01 = b0 ? c1 : c0, c23 = b0 ? c3 : c2, c45 = b0 ? c5 : c4, c67 = b0 ? c7 : c6;
+    const float lo = b1 ? c23 : c01, hi = b1 ? c67 : c45;
+    return b2 ? hi : lo;
+  }
+}
 
 struct PartitionArgs {
   float* tmp_out;
@@ -105,61 +203,72 @@ __device__ __forceinline__ void merge_store(const PartitionArgs& a, const float*
   }
 }
 
-// Decode the unit index and hoist the block-table slice. Returns false for an
-// empty partition (after writing its sentinels).
+// A work unit: sequence s, kv head kh, partition p.
 struct Unit {
   int s, kh, p, G, L, pg0, npages;
+  int32_t bt_val;  // this thread's entry of the unit's block-table slice
 };
+
+// Decode the unit and issue its first loads together: the sequence length and
+// the block-table slice of the whole partition (clamped to the row, so always
+// in bounds; entries past the sequence's last block are loaded but never
+// used). Nothing here waits on the length, so the loads overlap.
 template <int BS>
-__device__ __forceinline__ bool unit_setup(const PartitionArgs& a, int32_t* s_bt, Unit& u) {
+__device__ __forceinline__ void unit_begin(const PartitionArgs& a, Unit& u) {
   const int unit = blockIdx.x;
   u.kh = unit % a.KH;
   const int rest = unit / a.KH;
   u.s = rest % a.S;
   u.p = rest / a.S;
   u.G = a.H / a.KH;
+  const int pps = a.PS / BS;
+  u.pg0 = u.p * pps;
+  const int nspec = min(pps, a.MB - u.pg0);
+  u.bt_val = (int)threadIdx.x < nspec ? a.bt[(size_t)u.s * a.MB + u.pg0 + threadIdx.x] : 0;
   u.L = a.sl[u.s];
+}
+
+// After unit_begin: false for an empty partition (sentinels written);
+// otherwise publish the block-table slice to LDS for the whole workgroup.
+template <int BS>
+__device__ __forceinline__ bool unit_hoist(const PartitionArgs& a, int32_t* s_bt, Unit& u) {
   const int t0 = u.p * a.PS;
   if (t0 >= u.L) {
     write_sentinels(a, u.s, u.kh, u.p, u.G);
     return false;
   }
   const int t1 = min(t0 + a.PS, u.L);
-  u.pg0 = t0 / BS;
   u.npages = (t1 - t0 + BS - 1) / BS;
-  const int32_t* row = a.bt + (size_t)u.s * a.MB + u.pg0;
-  for (int i = threadIdx.x; i < u.npages; i += kWaves * 64) s_bt[i] = row[i];
+  if ((int)threadIdx.x < u.npages) s_bt[threadIdx.x] = u.bt_val;
   __syncthreads();
   return true;
 }
 
 // =====================================================================
 // MFMA path: 16-bit K/V, G in [4, 16] query heads per kv head.
-// QK^T per tile: D/32 MFMA 16x16x32, token rows x head columns (heads >= G are
-// zero-padded). The fp32 C tile (lane l: tokens 4*(l/16)+r, head l%16) is
-// exactly the B operand layout of a 16x16x16 MFMA with tokens as k, so P
-// feeds PV without any data movement. V is read as 8-byte pieces (4 tokens
-// of one d) that form the matching A operand. P is split into a 16-bit high
-// part and a 16-bit residual (two PV MFMAs) so the probabilities keep ~16
-// bits of mantissa instead of bf16's 8.
+// QK^T per 16-token sub-tile: D/32 MFMA 16x16x32, token rows x head columns
+// (heads >= G are zero-padded). The fp32 C tile (lane l: tokens 4*(l/16)+r,
+// head l%16) is exactly the B operand layout of a 16x16x16 MFMA with tokens as
+// k, so P feeds PV without any data movement. V is read as 8-byte pieces (4
+// tokens of one d) that form the matching A operand. P is split into a 16-bit
+// high part and a 16-bit residual (two PV MFMAs) so the probabilities keep
+// ~16 bits of mantissa instead of bf16's 8.
 // =====================================================================
 template <int DT, int D, int BS>
-__global__ void __launch_bounds__(kWaves * 64)
+__global__ void __launch_bounds__(kWaves * 64) PA_OCCUPANCY
 partition_mfma_kernel(PartitionArgs a) {
-  constexpr int KJ = D / 32;  // K dwordx4 per lane per tile = QK k-steps
-  constexpr int VB = D / 16;  // V dwordx2 per lane per tile = PV d-blocks
-  constexpr int TPP = BS / 16;
+  constexpr int SUB = BS / 16;  // 16-token sub-tiles per page
+  constexpr int KJ = D / 32;    // K dwordx4 per lane per sub-tile = QK k-steps
+  constexpr int VB = D / 16;    // V dwordx2 per lane per sub-tile = PV d-blocks
   constexpr size_t PAGE = (size_t)D * BS * 2;  // bytes of one (block, kv head) page
+  constexpr int PF = prefetch_for(SUB * (KJ * 4 + VB * 2));
   using C = codec<DT>;
   using M = mma<DT>;
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   Unit u;
-  if (!unit_setup<BS>(a, (int32_t*)smem, u)) return;
+  unit_begin<BS>(a, u);
   const int G = u.G;
-  const LdsLayout lay = lds_layout(a.PS, BS, G, D);
-  const int32_t* s_bt = (const int32_t*)(smem + lay.bt_off);
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane & 15, grp = lane >> 4;
 
@@ -174,16 +283,18 @@ partition_mfma_kernel(PartitionArgs a) {
       qb[j] = g < G ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
+  if (!unit_hoist<BS>(a, (int32_t*)smem, u)) return;
+  const LdsLayout lay = lds_layout(a.PS, BS, G, D);
+  const int32_t* s_bt = (const int32_t*)(smem + lay.bt_off);
 
   const size_t head_off = (size_t)u.kh * PAGE;
   const size_t blk_stride = (size_t)a.KH * PAGE;
   const uint8_t* kbase = (const uint8_t*)a.kc + head_off;
   const uint8_t* vbase = (const uint8_t*)a.vc + head_off;
-  const uint32_t k_lane = (uint32_t)(grp * BS + g) * 16;          // + j*4*BS*16 + tt*256
-  const uint32_t v_lane = (uint32_t)(g * BS + 4 * grp) * 2;       // + mb*16*BS*2 + tt*32
+  const uint32_t k_lane = (uint32_t)(grp * BS + g) * 16;     // + j*4*BS*16 + st*256
+  const uint32_t v_lane = (uint32_t)(g * BS + 4 * grp) * 2;  // + mb*16*BS*2 + st*32
 
-  const int my_pages = u.npages > wave ? (u.npages - wave + kWaves - 1) / kWaves : 0;
-  const int ntiles = my_pages * TPP;
+  const int npg = u.npages > wave ? (u.npages - wave + kWaves - 1) / kWaves : 0;
 
   float m = kNegInf;  // running max (log2 domain), uniform over a head column
   float lsum = 0.0f;  // this lane's share of the running exp sum
@@ -191,64 +302,79 @@ partition_mfma_kernel(PartitionArgs a) {
 #pragma unroll
   for (int i = 0; i < VB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto fetch = [&](int ti, u32x4(&kr)[KJ], u32x2(&vr)[VB]) {
-    const int pi = wave + (ti / TPP) * kWaves;
-    const int tt = ti % TPP;
-    const int blk = __builtin_amdgcn_readfirstlane(s_bt[pi]);
-    const uint8_t* kp = kbase + (size_t)blk * blk_stride + tt * 256 + k_lane;
-    const uint8_t* vp = vbase + (size_t)blk * blk_stride + tt * 32 + v_lane;
+  struct Page {
+    u32x4 k[SUB][KJ];
+    u32x2 v[SUB][VB];
+  };
+  auto fetch = [&](int i, Page& pg) {
+    const int blk = __builtin_amdgcn_readfirstlane(s_bt[wave + i * kWaves]);
+    const uint8_t* kp = kbase + (size_t)blk * blk_stride + k_lane;
+    const uint8_t* vp = vbase + (size_t)blk * blk_stride + v_lane;
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) kr[j] = *(const u32x4*)(kp + j * 4 * BS * 16);
+    for (int j = 0; j < KJ; ++j) {
 #pragma unroll
-    for (int mb = 0; mb < VB; ++mb) vr[mb] = *(const u32x2*)(vp + mb * 16 * BS * 2);
+      for (int st = 0; st < SUB; ++st)
+        pg.k[st][j] = stream_load<u32x4>(kp + j * 4 * BS * 16 + st * 256);
+    }
+#pragma unroll
+    for (int mb = 0; mb < VB; ++mb) {
+#pragma unroll
+      for (int st = 0; st < SUB; ++st)
+        pg.v[st][mb] = stream_load<u32x2>(vp + mb * 16 * BS * 2 + st * 32);
+    }
   };
 
-  auto process = [&](int ti, const u32x4(&kr)[KJ], const u32x2(&vr)[VB]) {
-    const int pi = wave + (ti / TPP) * kWaves;
-    const int tt = ti % TPP;
-    const int tok = (u.pg0 + pi) * BS + tt * 16 + 4 * grp;  // token of row 4*grp
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+  auto process = [&](int i, const Page& pg) {
+    const int tok0 = (u.pg0 + wave + i * kWaves) * BS;  // first token of the page
+    float s2[SUB][4];
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) sc = M::qk(kr[j], qb[j], sc);
-    const int nvalid = u.L - tok;  // rows 4*grp+r valid iff r < nvalid
-    float s2[4];
+    for (int st = 0; st < SUB; ++st) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s2[r] = r < nvalid ? sc[r] * a.qk_scale : kNegInf;
-    float mt = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
+      for (int j = 0; j < KJ; ++j) sc = M::qk(pg.k[st][j], qb[j], sc);
+      const int nvalid = u.L - (tok0 + 16 * st + 4 * grp);  // row 4*grp+r valid iff r < nvalid
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s2[st][r] = r < nvalid ? sc[r] * a.qk_scale : kNegInf;
+    }
+    float mt = kNegInf;
+#pragma unroll
+    for (int st = 0; st < SUB; ++st)
+      mt = fmaxf(mt, fmaxf(fmaxf(s2[st][0], s2[st][1]), fmaxf(s2[st][2], s2[st][3])));
     mt = rows_max(mt);
     const float mn = fmaxf(m, mt);
     const float mu = mn == kNegInf ? 0.0f : mn;
     const float alpha = fast_exp2(m - mu);
-    float pr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(s2[r] - mu);
-    lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     m = mn;
-    const uint32_t h01 = C::pack(pr[0], pr[1]), h23 = C::pack(pr[2], pr[3]);
-    const u32x2 phi = {h01, h23};
-    const u32x2 plo = {C::pack(pr[0] - C::lo(h01), pr[1] - C::hi(h01)),
-                       C::pack(pr[2] - C::lo(h23), pr[3] - C::hi(h23))};
-    const bool partial = (u.pg0 + pi) * BS + tt * 16 + 16 > u.L;  // wavefront-uniform
+    u32x2 phi[SUB], plo[SUB];
+    float psum = 0.0f;
+#pragma unroll
+    for (int st = 0; st < SUB; ++st) {
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(s2[st][r] - mu);
+      psum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      const uint32_t h01 = C::pack(pr[0], pr[1]), h23 = C::pack(pr[2], pr[3]);
+      phi[st] = u32x2{h01, h23};
+      plo[st] = u32x2{C::pack(pr[0] - C::lo(h01), pr[1] - C::hi(h01)),
+                      C::pack(pr[2] - C::lo(h23), pr[3] - C::hi(h23))};
+    }
+    lsum = lsum * alpha + psum;
+    const bool partial = tok0 + BS > u.L;  // wavefront-uniform
 #pragma unroll
     for (int mb = 0; mb < VB; ++mb) {
-      const u32x2 v = partial ? keep_first(vr[mb], nvalid) : vr[mb];
       acc[mb] *= alpha;
-      acc[mb] = M::pv(v, phi, acc[mb]);
-      acc[mb] = M::pv(v, plo, acc[mb]);
+#pragma unroll
+      for (int st = 0; st < SUB; ++st) {
+        const u32x2 v = partial ? keep_first(pg.v[st][mb], u.L - (tok0 + 16 * st + 4 * grp))
+                                : pg.v[st][mb];
+        acc[mb] = M::pv(v, phi[st], acc[mb]);
+        acc[mb] = M::pv(v, plo[st], acc[mb]);
+      }
     }
   };
 
-  u32x4 kA[KJ], kB[KJ];
-  u32x2 vA[VB], vB[VB];
-  if (ntiles > 0) fetch(0, kA, vA);
-  int ti = 0;
-  for (; ti + 1 < ntiles; ti += 2) {
-    fetch(ti + 1, kB, vB);
-    process(ti, kA, vA);
-    if (ti + 2 < ntiles) fetch(ti + 2, kA, vA);
-    process(ti + 1, kB, vB);
-  }
-  if (ti < ntiles) process(ti, kA, vA);
+  Page ring[PF + 1];
+  pipeline<PF>(npg, ring, fetch, process);
 
   lsum = rows_sum(lsum);
   float* s_m = (float*)(smem + lay.m_off);
@@ -275,7 +401,7 @@ partition_mfma_kernel(PartitionArgs a) {
 // QK: each lane dots its d-chunks of one token with the packed query
 // (v_dot2 for 16-bit, fma for fp32), then a sum across the four 16-lane rows.
 // PV: lane l owns X consecutive tokens (one 16-byte V chunk) of one d; the
-// tile's 16 probabilities are read out of lanes 0..15 with v_readlane
+// page's probabilities are read out of lanes 0..15 with v_readlane
 // (wavefront-uniform) and each lane selects the X of its chunk.
 // =====================================================================
 template <int DT> struct vec_elem {
@@ -286,23 +412,23 @@ template <> struct vec_elem<DT_F32> {
 };
 
 template <int DT, int D, int BS, int GM>
-__global__ void __launch_bounds__(kWaves * 64)
+__global__ void __launch_bounds__(kWaves * 64) PA_OCCUPANCY
 partition_vec_kernel(PartitionArgs a) {
   constexpr int X = vec_elem<DT>::X;
   constexpr int ESZ = 16 / X;
-  constexpr int KJ = D / X / 4;     // K chunks per lane per tile (c = 4j + row)
-  constexpr int CPR = 16 / X;       // V chunks per d-row of a 16-token tile
-  constexpr int DPL = 64 / CPR;     // d distance between one lane's V chunks
-  constexpr int VJ = D / DPL;       // V chunks per lane per tile
-  constexpr int TPP = BS / 16;
+  constexpr int SUB = BS / 16;       // 16-token sub-tiles per page
+  constexpr int KJ = D / X / 4;      // K chunks per lane per sub-tile (c = 4j + row)
+  constexpr int CPS = 16 / X;        // V chunks per d-row of one sub-tile
+  constexpr int CPR = SUB * CPS;     // V chunks per d-row of a page
+  constexpr int DPL = 64 / CPR;      // d distance between one lane's V chunks
+  constexpr int VJ = D / DPL;        // V chunks per lane per page
   constexpr size_t PAGE = (size_t)D * BS * ESZ;
+  constexpr int PF = prefetch_for((SUB * KJ + VJ) * 4);
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   Unit u;
-  if (!unit_setup<BS>(a, (int32_t*)smem, u)) return;
+  unit_begin<BS>(a, u);
   const int G = u.G;
-  const LdsLayout lay = lds_layout(a.PS, BS, G, D);
-  const int32_t* s_bt = (const int32_t*)(smem + lay.bt_off);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = lane & 15, grp = lane >> 4;     // K: token, chunk row
@@ -321,6 +447,9 @@ partition_vec_kernel(PartitionArgs a) {
       for (int w = 0; w < 4; ++w) qw[gg][j][w] = gg < G ? v[w] : 0u;
     }
   }
+  if (!unit_hoist<BS>(a, (int32_t*)smem, u)) return;
+  const LdsLayout lay = lds_layout(a.PS, BS, G, D);
+  const int32_t* s_bt = (const int32_t*)(smem + lay.bt_off);
 
   const size_t head_off = (size_t)u.kh * PAGE;
   const size_t blk_stride = (size_t)a.KH * PAGE;
@@ -329,8 +458,7 @@ partition_vec_kernel(PartitionArgs a) {
   const uint32_t k_lane = (uint32_t)(grp * BS + t) * 16;
   const uint32_t v_lane = (uint32_t)(dl * BS + h * X) * ESZ;
 
-  const int my_pages = u.npages > wave ? (u.npages - wave + kWaves - 1) / kWaves : 0;
-  const int ntiles = my_pages * TPP;
+  const int npg = u.npages > wave ? (u.npages - wave + kWaves - 1) / kWaves : 0;
 
   float m[GM], lpart[GM], acc[GM][VJ];
 #pragma unroll
@@ -341,46 +469,60 @@ partition_vec_kernel(PartitionArgs a) {
     for (int j = 0; j < VJ; ++j) acc[gg][j] = 0.0f;
   }
 
-  auto fetch = [&](int ti, u32x4(&kr)[KJ], u32x4(&vr)[VJ]) {
-    const int pi = wave + (ti / TPP) * kWaves;
-    const int tt = ti % TPP;
-    const int blk = __builtin_amdgcn_readfirstlane(s_bt[pi]);
-    const uint8_t* kp = kbase + (size_t)blk * blk_stride + tt * 256 + k_lane;
-    const uint8_t* vp = vbase + (size_t)blk * blk_stride + tt * 16 * ESZ + v_lane;
+  struct Page {
+    u32x4 k[SUB][KJ];
+    u32x4 v[VJ];
+  };
+  auto fetch = [&](int i, Page& pg) {
+    const int blk = __builtin_amdgcn_readfirstlane(s_bt[wave + i * kWaves]);
+    const uint8_t* kp = kbase + (size_t)blk * blk_stride + k_lane;
+    const uint8_t* vp = vbase + (size_t)blk * blk_stride + v_lane;
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) kr[j] = *(const u32x4*)(kp + j * 4 * BS * 16);
+    for (int j = 0; j < KJ; ++j) {
 #pragma unroll
-    for (int j = 0; j < VJ; ++j) vr[j] = *(const u32x4*)(vp + j * DPL * BS * ESZ);
+      for (int st = 0; st < SUB; ++st)
+        pg.k[st][j] = stream_load<u32x4>(kp + j * 4 * BS * 16 + st * 256);
+    }
+#pragma unroll
+    for (int j = 0; j < VJ; ++j) pg.v[j] = stream_load<u32x4>(vp + j * DPL * BS * ESZ);
   };
 
-  auto process = [&](int ti, const u32x4(&kr)[KJ], const u32x4(&vr)[VJ]) {
-    const int pi = wave + (ti / TPP) * kWaves;
-    const int tt = ti % TPP;
-    const int tok0 = (u.pg0 + pi) * BS + tt * 16;  // token of tile row 0
-    const bool valid = tok0 + t < u.L;
-    float p[GM];
+  auto process = [&](int i, const Page& pg) {
+    const int tok0 = (u.pg0 + wave + i * kWaves) * BS;  // first token of the page
+    float p[GM][SUB];
 #pragma unroll
     for (int gg = 0; gg < GM; ++gg) {
-      float dot = 0.0f;
+      float s2[SUB];
+      float mt = kNegInf;
 #pragma unroll
-      for (int j = 0; j < KJ; ++j) {
+      for (int st = 0; st < SUB; ++st) {
+        float dot = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          if constexpr (DT == DT_F32) {
-            dot = fmaf(__uint_as_float(kr[j][w]), __uint_as_float(qw[gg][j][w]), dot);
-          } else {
-            dot = codec<DT>::dot2(kr[j][w], qw[gg][j][w], dot);
+        for (int j = 0; j < KJ; ++j) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            if constexpr (DT == DT_F32) {
+              dot = fmaf(__uint_as_float(pg.k[st][j][w]), __uint_as_float(qw[gg][j][w]), dot);
+            } else {
+              dot = codec<DT>::dot2(pg.k[st][j][w], qw[gg][j][w], dot);
+            }
           }
         }
+        dot = rows_sum(dot);
+        s2[st] = tok0 + 16 * st + t < u.L ? dot * a.qk_scale : kNegInf;
+        mt = fmaxf(mt, s2[st]);
       }
-      dot = rows_sum(dot);
-      const float s2 = valid ? dot * a.qk_scale : kNegInf;
-      const float mt = row16_max(s2);
+      mt = row16_max(mt);
       const float mn = fmaxf(m[gg], mt);
       const float mu = mn == kNegInf ? 0.0f : mn;
       const float alpha = fast_exp2(m[gg] - mu);
-      p[gg] = fast_exp2(s2 - mu);
-      lpart[gg] = lpart[gg] * alpha + p[gg];
+      float ps = 0.0f;
+#pragma unroll
+      for (int st = 0; st < SUB; ++st) {
+        p[gg][st] = fast_exp2(s2[st] - mu);
+        ps += p[gg][st];
+      }
+      lpart[gg] = lpart[gg] * alpha + ps;
       m[gg] = mn;
 #pragma unroll
       for (int j = 0; j < VJ; ++j) acc[gg][j] *= alpha;
@@ -388,20 +530,14 @@ partition_vec_kernel(PartitionArgs a) {
     const int nv = u.L - (tok0 + h * X);  // valid tokens among this lane's X
 #pragma unroll
     for (int gg = 0; gg < GM; ++gg) {
-      // p of token k sits in lane k (rows repeat it); lane picks tokens h*X .. h*X+X-1.
-      float sp[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) sp[k] = lane_value(p[gg], k);
+      // p of page token 16*st + k sits in lane k (rows repeat it); this lane
+      // needs tokens h*X .. h*X+X-1, i.e. chunk h of the page row.
       float pw[X];
 #pragma unroll
       for (int e = 0; e < X; ++e) {
-        if constexpr (CPR == 2) {
-          pw[e] = h ? sp[8 + e] : sp[e];
-        } else {
-          const float lo = (h & 1) ? sp[4 + e] : sp[e];
-          const float hi = (h & 1) ? sp[12 + e] : sp[8 + e];
-          pw[e] = (h & 2) ? hi : lo;
-        }
+        pw[e] = pick<CPR>(h, [&](int hh) {
+          return lane_value(p[gg][hh / CPS], (hh % CPS) * X + e);
+        });
       }
 #pragma unroll
       for (int j = 0; j < VJ; ++j) {
@@ -409,11 +545,11 @@ partition_vec_kernel(PartitionArgs a) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           if constexpr (DT == DT_F32) {
-            const float v = e_valid(w, nv) ? __uint_as_float(vr[j][w]) : 0.0f;
+            const float v = e_valid(w, nv) ? __uint_as_float(pg.v[j][w]) : 0.0f;
             sum = fmaf(pw[w], v, sum);
           } else {
-            const float v0 = e_valid(2 * w, nv) ? codec<DT>::lo(vr[j][w]) : 0.0f;
-            const float v1 = e_valid(2 * w + 1, nv) ? codec<DT>::hi(vr[j][w]) : 0.0f;
+            const float v0 = e_valid(2 * w, nv) ? codec<DT>::lo(pg.v[j][w]) : 0.0f;
+            const float v1 = e_valid(2 * w + 1, nv) ? codec<DT>::hi(pg.v[j][w]) : 0.0f;
             sum = fmaf(pw[2 * w], v0, sum);
             sum = fmaf(pw[2 * w + 1], v1, sum);
           }
@@ -423,16 +559,8 @@ partition_vec_kernel(PartitionArgs a) {
     }
   };
 
-  u32x4 kA[KJ], kB[KJ], vA[VJ], vB[VJ];
-  if (ntiles > 0) fetch(0, kA, vA);
-  int ti = 0;
-  for (; ti + 1 < ntiles; ti += 2) {
-    fetch(ti + 1, kB, vB);
-    process(ti, kA, vA);
-    if (ti + 2 < ntiles) fetch(ti + 2, kA, vA);
-    process(ti + 1, kB, vB);
-  }
-  if (ti < ntiles) process(ti, kA, vA);
+  Page ring[PF + 1];
+  pipeline<PF>(npg, ring, fetch, process);
 
   float* s_m = (float*)(smem + lay.m_off);
   float* s_l = (float*)(smem + lay.l_off);
@@ -443,8 +571,8 @@ partition_vec_kernel(PartitionArgs a) {
 #pragma unroll
     for (int j = 0; j < VJ; ++j) {
       float v = acc[gg][j];
-      v += __shfl_xor(v, 1, 64);
-      if constexpr (CPR == 4) v += __shfl_xor(v, 2, 64);
+#pragma unroll
+      for (int x = 1; x < CPR; x <<= 1) v += __shfl_xor(v, x, 64);
       acc[gg][j] = v;
     }
     if (gg < G) {
@@ -464,9 +592,12 @@ partition_vec_kernel(PartitionArgs a) {
 
 // =====================================================================
 // Reduce: one wavefront per (sequence, query head); the page's phase-2
-// log-sum-exp combine over the partitions the sequence uses. Lane i computes
-// the weight of partition base+i; the d-parallel accumulation reads each
-// weight back with v_readlane.
+// log-sum-exp combine over the n = ceil(L / PS) partitions the sequence uses.
+// Lane i holds partition i's statistics; the d-parallel accumulation reads
+// each weight back with v_readlane. The sequence length, the statistics of
+// the first 64 partitions and the rows of the first kChunk partitions are all
+// requested before any of them is needed (rows past n are loaded but selected
+// away, never multiplied), so the common case costs one memory round trip.
 // =====================================================================
 struct ReduceArgs {
   void* out;
@@ -480,51 +611,68 @@ struct ReduceArgs {
 template <int D, int ODT>
 __global__ void __launch_bounds__(256) reduce_kernel(ReduceArgs a) {
   constexpr int NWR = 4;
-  constexpr int DPL = D / 64;  // consecutive d per lane
+  constexpr int DPL = D / 64;   // consecutive d per lane
+  constexpr int kChunk = 8;     // partition rows in flight per wavefront
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sh = blockIdx.x * NWR + wave;
-  if (sh >= a.S * a.H) return;  // whole wavefront; only wavefront-local LDS below
+  if (sh >= a.S * a.H) return;  // whole wavefront; no LDS, no barrier below
   const int s = sh / a.H;
+  const float* mlr = a.max_logits + (size_t)sh * a.P;
+  const float* esr = a.exp_sums + (size_t)sh * a.P;
+  const float* trow = a.tmp_out + (size_t)sh * a.P * D + lane * DPL;
+
+  // Independent loads: length, first 64 partitions' statistics, first rows.
   const int L = a.sl[s];
+  float mi = lane < a.P ? mlr[lane] : kNegInf;
+  float li = lane < a.P ? esr[lane] : 0.0f;
+  float v[kChunk][DPL];
+#pragma unroll
+  for (int u = 0; u < kChunk; ++u) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) v[u][e] = u < a.P ? trow[(size_t)u * D + e] : 0.0f;
+  }
+
   const int n = L > 0 ? (L + a.PS - 1) / a.PS : 0;
   float acc[DPL];
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
   if (n > 0) {
-    const float* mlr = a.max_logits + (size_t)sh * a.P;
-    const float* esr = a.exp_sums + (size_t)sh * a.P;
-    float M = kNegInf;
-    for (int i = lane; i < n; i += 64) M = fmaxf(M, mlr[i]);
+    if (lane >= n) {
+      mi = kNegInf;
+      li = 0.0f;
+    }
+    float M = mi;
+    for (int i = lane + 64; i < n; i += 64) M = fmaxf(M, mlr[i]);
     M = wave_max(M);
-    float Z = 0.0f;
-    for (int i = lane; i < n; i += 64) Z += fast_exp2((mlr[i] - M) * kLog2e) * esr[i];
+    float Z = lane < n ? fast_exp2((mi - M) * kLog2e) * li : 0.0f;
+    for (int i = lane + 64; i < n; i += 64) Z += fast_exp2((mlr[i] - M) * kLog2e) * esr[i];
     Z = wave_sum(Z);
-    const float* trow = a.tmp_out + (size_t)sh * a.P * D + lane * DPL;
+    float wl = lane < n ? fast_exp2((mi - M) * kLog2e) * li / Z : 0.0f;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const float w = lane_value(wl, u);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = u < n ? fmaf(w, v[u][e], acc[e]) : acc[e];
+    }
     for (int base = 0; base < n; base += 64) {
-      const int i = base + lane;
-      const float wl = i < n ? fast_exp2((mlr[i] - M) * kLog2e) * esr[i] / Z : 0.0f;
-      const int cnt = min(64, n - base);
-      int k = 0;
-      for (; k + 4 <= cnt; k += 4) {
-        float v[4][DPL];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float* src = trow + (size_t)(base + k + u) * D;
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) v[u][e] = src[e];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float w = lane_value(wl, k + u);
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, v[u][e], acc[e]);
-        }
+      if (base > 0) {
+        const int i = base + lane;
+        wl = i < n ? fast_exp2((mlr[i] - M) * kLog2e) * esr[i] / Z : 0.0f;
       }
-      for (; k < cnt; ++k) {
-        const float w = lane_value(wl, k);
-        const float* src = trow + (size_t)(base + k) * D;
+      const int cnt = min(64, n - base);
+      for (int k = base == 0 ? kChunk : 0; k < cnt; k += kChunk) {
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, src[e], acc[e]);
+        for (int u = 0; u < kChunk; ++u) {
+#pragma unroll
+          for (int e = 0; e < DPL; ++e)
+            v[u][e] = k + u < cnt ? trow[(size_t)(base + k + u) * D + e] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+          const float w = lane_value(wl, (k + u) & 63);
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[e] = k + u < cnt ? fmaf(w, v[u][e], acc[e]) : acc[e];
+        }
       }
     }
   }

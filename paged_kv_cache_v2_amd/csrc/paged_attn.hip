@@ -123,7 +123,8 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   const int di = d_index(D), bi = bs_index(BS);
   if (di < 0) return fail(PA_ERR_UNSUPPORTED, "head_size %d not in {64, 128, 256}", D);
   if (bi < 0) return fail(PA_ERR_UNSUPPORTED, "block_size %d not in {16, 32}", BS);
-  if (PS / BS > 1024) return fail(PA_ERR_UNSUPPORTED, "partition_size / block_size > 1024");
+  if (PS / BS > pa::kWaves * 64)
+    return fail(PA_ERR_UNSUPPORTED, "partition_size / block_size > %d", pa::kWaves * 64);
   const int G = H / KH;
   partition_fn fn = nullptr;
   if (dt != PA_F32 && G >= 4 && G <= 16) {

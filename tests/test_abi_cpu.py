@@ -91,7 +91,7 @@ def reduce(ptrs=None, S=2, H=8, D=128, P=1, PS=512, odt=binding.PA_F32):
     (dict(dt=7), binding.PA_ERR_UNSUPPORTED),
     (dict(H=64, KH=2), binding.PA_ERR_UNSUPPORTED),    # G = 32
     (dict(H=16, KH=2, dt=binding.PA_F32), binding.PA_ERR_UNSUPPORTED),  # fp32, G = 8
-    (dict(PS=16 * 2048), binding.PA_ERR_UNSUPPORTED),  # PS / BS > 1024
+    (dict(PS=16 * 512), binding.PA_ERR_UNSUPPORTED),   # PS / BS > 256
 ])
 def test_partition_rejects(kw, code):
     assert part(**kw) == code
