@@ -128,16 +128,18 @@ def run(args) -> dict:
     # Kernel timing: the same K steps again, with a HIP event pair on the launch
     # stream around every partition launch (events inside the timed region above
     # would add their own gaps to the step time).
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     for i in range(K):
         ev[i][0].record(stream)
         pa.paged_attn_v2_partition(tmp, es, ml, q, kc, vc, bt, sl, inp["scale"], PS, stream)
         ev[i][1].record(stream)
         pa.paged_attn_v2_reduce(out, tmp, es, ml, sl, PS, stream)
+        ev[i][2].record(stream)
     torch.cuda.synchronize()
-    part_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    part_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    red_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
     part_avg_s = sum(part_ms) / len(part_ms) / 1e3
+    red_avg_s = sum(red_ms) / len(red_ms) / 1e3
 
     kvb = W.kv_bytes(inp)
     step_s = elapsed / K
@@ -178,6 +180,9 @@ def run(args) -> dict:
             "kernel_p90_us": round(part_ms[(9 * len(part_ms)) // 10] * 1e3, 3),
             "bytes_per_launch": kvb, "traffic_source": traffic_src,
             "kernel_source_hash": source_hash(),
+            "reduce_avg_us": round(red_avg_s * 1e6, 3),
+            "partition_span": pa.partition_span(S, H, cfg.num_kv_heads, D, cfg.block_size, P, PS,
+                                                W.DTYPES[cfg.dtype]),
         },
     }
     if args.calibrate_copy:

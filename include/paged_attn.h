@@ -141,6 +141,17 @@ PA_API int paged_attn_abi_version(void);
 PA_API int paged_attn_default_partition_size(int32_t head_size, int32_t block_size, int32_t kv_dtype,
                                              int32_t group);
 
+/* Launch plan inspection: how many consecutive partitions of one (sequence,
+ * kv head) a workgroup of paged_attn_v2_partition / paged_attn_decode handles
+ * for these sizes (1 or 2). Results do not depend on it (each partition is
+ * computed and stored on its own); it only groups work. Host-side, no device
+ * work; returns a PA_ERR_* code for arguments the launchers would reject on
+ * shape or support grounds. */
+PA_API int paged_attn_partition_span(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                     int32_t head_size, int32_t block_size,
+                                     int32_t max_num_partitions, int32_t partition_size,
+                                     int32_t kv_dtype);
+
 #ifdef __cplusplus
 }
 #endif

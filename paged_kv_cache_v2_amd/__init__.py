@@ -7,4 +7,4 @@ plus the seeded synthetic-input generator.
 from .binding import (PA_BF16, PA_ERR_ALIGN, PA_ERR_HIP, PA_ERR_NULL, PA_ERR_SHAPE,  # noqa: F401
                       PA_ERR_UNSUPPORTED, PA_F16, PA_F32, PA_OK, abi_version,
                       default_partition_size, ensure_built, last_error, lib, paged_attn_decode,
-                      paged_attn_v2_partition, paged_attn_v2_reduce, workspace)
+                      paged_attn_v2_partition, paged_attn_v2_reduce, partition_span, workspace)

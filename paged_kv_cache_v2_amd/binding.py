@@ -29,6 +29,7 @@ _SIGS = {
     "paged_attn_last_error": [],
     "paged_attn_abi_version": [],
     "paged_attn_default_partition_size": [_I32, _I32, _I32, _I32],
+    "paged_attn_partition_span": [_I32] * 8,
 }
 
 
@@ -61,6 +62,17 @@ def default_partition_size(head_size: int, block_size: int, dtype: torch.dtype, 
     rc = lib().paged_attn_default_partition_size(head_size, block_size, _DT[dtype], group)
     if rc < 0:
         raise RuntimeError(f"paged_attn_default_partition_size: {last_error()} (code {rc})")
+    return rc
+
+
+def partition_span(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int,
+                   block_size: int, max_num_partitions: int, partition_size: int,
+                   dtype: torch.dtype) -> int:
+    """Partitions per workgroup the launchers use for these sizes (plan inspection)."""
+    rc = lib().paged_attn_partition_span(num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                                         max_num_partitions, partition_size, _DT[dtype])
+    if rc < 0:
+        raise RuntimeError(f"paged_attn_partition_span: {last_error()} (code {rc})")
     return rc
 
 

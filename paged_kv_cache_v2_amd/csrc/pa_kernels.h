@@ -10,12 +10,22 @@
 // G query heads of the group share every K/V fetch.
 //
 // Work unit and layout
-//  - blockIdx.x = (p * S + s) * KH + kh: kv head fastest, partition slowest, so
-//    the last-dispatched workgroups are the cheap tail/empty partitions.
-//  - A unit covers pages [p*PS/BS, ceil(min((p+1)*PS, L)/BS)); PS % BS == 0 so
-//    partition edges are page edges. The unit's block-table slice is loaded
-//    together with the sequence length (no dependent round trip) and hoisted
-//    into LDS; NW wavefronts take pages wave, wave+NW, ...
+//  - A workgroup owns a span of C consecutive partitions p0 .. p0+C-1 of one
+//    (sequence, kv head); blockIdx.x = (q * S + s) * KH + kh with p0 = q * C:
+//    kv head fastest, partition span slowest, so the last-dispatched
+//    workgroups are the cheap tail/empty partitions. Each partition is still
+//    computed and stored on its own (outputs do not depend on C); spanning
+//    only amortises the unit's prologue (length and block-table loads) and
+//    epilogue (LDS merge, stores) over C partitions, lets the stores of
+//    adjacent partitions (adjacent rows of tmp_output) go out together, and
+//    retires the empty partitions of a sequence in the same workgroup as its
+//    last used one.
+//  - Partition p covers pages [p*PS/BS, ceil(min((p+1)*PS, L)/BS)); PS % BS
+//    == 0 so partition edges are page edges, and the used pages of a span are
+//    contiguous. The span's block-table slice is loaded together with the
+//    sequence length (no dependent round trip) and hoisted into LDS; NW
+//    wavefronts take the span's pages wave, wave+NW, ... and park their
+//    running state in LDS each time they cross into the next partition.
 //  - The page is the unit of fetch and compute; it is BS/16 sub-tiles of 16
 //    tokens. K sub-tile: lane l holds token l%16 and d-chunks c = 4j + l/16
 //    (16-byte dwordx4 loads; each 16 lanes read 256 contiguous bytes per chunk
@@ -28,9 +38,9 @@
 //    letting them allocate normally.
 //  - Each wavefront keeps its own running (max, sum, unnormalised accumulator)
 //    in the log2 domain (scores pre-multiplied by scale*log2(e)); at the end the
-//    NW partial states are merged through LDS with the same log-sum-exp rule
-//    the reduce uses, normalised, and stored with max_logits back in natural
-//    units. Keeping the accumulator unnormalised and dividing once is the
+//    NW partial states of every partition are merged through LDS with the same
+//    log-sum-exp rule the reduce uses, normalised, and stored with max_logits
+//    back in natural units. Keeping the accumulator unnormalised and dividing once is the
 //    partition kernel's normalised recurrence in exact arithmetic.
 //  - Masked tokens (t >= seq_len in the last page) are selected out: score
 //    -inf and value 0, never multiplied by a zero weight, so NaN in unread
@@ -144,58 +154,79 @@ struct PartitionArgs {
   const int32_t* bt;
   const int32_t* sl;
   int S, H, KH, MB, P, PS;
+  int NB;          // physical blocks; block-table entries are clamped into [0, NB)
+  int C;           // consecutive partitions per workgroup (span), 1 .. kMaxSpan
   float qk_scale;  // scale * log2(e)
 };
 
-// LDS carve-up shared by both partition kernels (byte offsets).
+constexpr int kMaxSpan = 2;
+
+// LDS carve-up shared by both partition kernels (byte offsets): the span's
+// block-table slice, then per (partition of the span, wavefront, head) the
+// parked running max, sum and accumulator.
 struct LdsLayout {
   int bt_off, m_off, l_off, acc_off, total;
 };
-__host__ __device__ inline LdsLayout lds_layout(int PS, int BS, int G, int D) {
+__host__ __device__ inline LdsLayout lds_layout(int PS, int BS, int G, int D, int C) {
   LdsLayout o;
   auto up16 = [](int v) { return (v + 15) & ~15; };
   o.bt_off = 0;
-  o.m_off = up16((PS / BS) * 4);
-  o.l_off = o.m_off + up16(kWaves * G * 4);
-  o.acc_off = o.l_off + up16(kWaves * G * 4);
-  o.total = o.acc_off + kWaves * G * D * 4;
+  o.m_off = up16(C * (PS / BS) * 4);
+  o.l_off = o.m_off + up16(C * kWaves * G * 4);
+  o.acc_off = o.l_off + up16(C * kWaves * G * 4);
+  o.total = o.acc_off + C * kWaves * G * D * 4;
   return o;
 }
 
-// Empty partition: the sentinels of the page's partition kernel.
-__device__ __forceinline__ void write_sentinels(const PartitionArgs& a, int s, int kh, int p,
-                                                int G) {
-  if ((int)threadIdx.x < G) {
-    const size_t row = ((size_t)s * a.H + kh * G + threadIdx.x) * a.P + p;
-    a.max_logits[row] = kNegInf;
-    a.exp_sums[row] = 0.0f;
-  }
+// Stores of the partition outputs. They are written once and read once by the
+// reduce; issued with device-scope (sc1) policy they measured up to ~6 % faster
+// on the long-context workload than default write-back stores (interleaved with
+// the streaming K/V reads, written-back tmp lines cost several times their
+// size in read bandwidth) and neutral elsewhere.
+#ifndef PA_TMP_POLICY
+#define PA_TMP_POLICY 16  // buffer-instruction cache-policy bits: sc0 = 1, nt = 2, sc1 = 16
+#endif
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer resource: 32-bit format, no swizzle
+__device__ __forceinline__ void store_row(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0,
+                                          PA_TMP_POLICY);
 }
 
-// Merge the NW per-wavefront states (log2-domain max m, sum l, unnormalised
-// accumulators acc[w][g][D]) and store the unit's normalised outputs.
+// Slot of (partition j of the span, wavefront w, head g) in the parked state.
+__device__ __forceinline__ int slot(int j, int w, int g, int G) { return (j * kWaves + w) * G + g; }
+
+// Merge the NW parked states of each of the span's ne used partitions
+// (log2-domain max m, sum l, unnormalised accumulator) and store the
+// normalised outputs. Threads walk (head, partition, d) in memory order, so
+// the rows of adjacent partitions of one head are written together.
 template <int D>
 __device__ __forceinline__ void merge_store(const PartitionArgs& a, const float* s_m,
                                             const float* s_l, const float* s_acc, int s, int kh,
-                                            int p, int G) {
+                                            int p0, int ne, int G) {
   constexpr int D4 = D / 4;
-  for (int i = threadIdx.x; i < G * D4; i += kWaves * 64) {
-    const int g = i / D4, d4 = i % D4;
+  const int per_head = ne * D4;
+  // The unit's G heads x P rows of tmp_output, addressed by 32-bit offsets.
+  const __amdgpu_buffer_rsrc_t tmp = __builtin_amdgcn_make_buffer_rsrc(
+      a.tmp_out + ((size_t)s * a.H + kh * G) * a.P * D, (short)0, G * a.P * D * 4, kRsrcFlags);
+  for (int i = threadIdx.x; i < G * per_head; i += kWaves * 64) {
+    const int g = i / per_head, rem = i - g * per_head;
+    const int j = rem / D4, d4 = rem - j * D4;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * G + g]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[slot(j, w, g, G)]);
     float Z = 0.0f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float e = fast_exp2(s_m[w * G + g] - M);  // 0 for a wavefront with no tokens
-      Z += e * s_l[w * G + g];
-      const f32x4 v = *(const f32x4*)&s_acc[(w * G + g) * D + 4 * d4];
+      const int k = slot(j, w, g, G);
+      const float e = fast_exp2(s_m[k] - M);  // 0 for a wavefront with no tokens
+      Z += e * s_l[k];
+      const f32x4 v = *(const f32x4*)&s_acc[k * D + 4 * d4];
       o += e * v;
     }
     const float inv = 1.0f / Z;
-    const size_t row = ((size_t)s * a.H + kh * G + g) * a.P + p;
-    *(f32x4*)&a.tmp_out[row * D + 4 * d4] = o * inv;
+    const size_t row = ((size_t)s * a.H + kh * G + g) * a.P + p0 + j;
+    store_row(tmp, (uint32_t)(((g * a.P + p0 + j) * D + 4 * d4) * 4), o * inv);
     if (d4 == 0) {
       a.exp_sums[row] = Z;
       a.max_logits[row] = M * kLn2;
@@ -203,42 +234,52 @@ __device__ __forceinline__ void merge_store(const PartitionArgs& a, const float*
   }
 }
 
-// A work unit: sequence s, kv head kh, partition p.
+// A work unit: sequence s, kv head kh, partitions p0 .. p0+nparts-1.
 struct Unit {
-  int s, kh, p, G, L, pg0, npages;
-  int32_t bt_val;  // this thread's entry of the unit's block-table slice
+  int s, kh, p0, nparts, G, L, pg0;
+  int npages;      // used pages of the span (contiguous from its first page)
+  int ne;          // used partitions of the span
+  int32_t bt_val;  // this thread's entry of the span's block-table slice
 };
 
 // Decode the unit and issue its first loads together: the sequence length and
-// the block-table slice of the whole partition (clamped to the row, so always
-// in bounds; entries past the sequence's last block are loaded but never
-// used). Nothing here waits on the length, so the loads overlap.
+// the block-table slice of the whole span (clamped to the row, so always in
+// bounds; entries past the sequence's last block are loaded but never used).
+// Nothing here waits on the length, so the loads overlap.
 template <int BS>
 __device__ __forceinline__ void unit_begin(const PartitionArgs& a, Unit& u) {
   const int unit = blockIdx.x;
   u.kh = unit % a.KH;
   const int rest = unit / a.KH;
   u.s = rest % a.S;
-  u.p = rest / a.S;
+  u.p0 = (rest / a.S) * a.C;
+  u.nparts = min(a.C, a.P - u.p0);
   u.G = a.H / a.KH;
   const int pps = a.PS / BS;
-  u.pg0 = u.p * pps;
-  const int nspec = min(pps, a.MB - u.pg0);
+  u.pg0 = u.p0 * pps;
+  const int nspec = min(u.nparts * pps, a.MB - u.pg0);
   u.bt_val = (int)threadIdx.x < nspec ? a.bt[(size_t)u.s * a.MB + u.pg0 + threadIdx.x] : 0;
   u.L = a.sl[u.s];
 }
 
-// After unit_begin: false for an empty partition (sentinels written);
-// otherwise publish the block-table slice to LDS for the whole workgroup.
+// After unit_begin: sentinels (max -inf, sum 0) for the span's empty
+// partitions; false if the whole span is empty, otherwise publish the span's
+// block-table slice to LDS for the whole workgroup.
 template <int BS>
 __device__ __forceinline__ bool unit_hoist(const PartitionArgs& a, int32_t* s_bt, Unit& u) {
-  const int t0 = u.p * a.PS;
-  if (t0 >= u.L) {
-    write_sentinels(a, u.s, u.kh, u.p, u.G);
-    return false;
+  if ((int)threadIdx.x < u.nparts * u.G) {
+    const int j = threadIdx.x / u.G, g = threadIdx.x % u.G;
+    if ((u.p0 + j) * a.PS >= u.L) {
+      const size_t row = ((size_t)u.s * a.H + u.kh * u.G + g) * a.P + u.p0 + j;
+      a.max_logits[row] = kNegInf;
+      a.exp_sums[row] = 0.0f;
+    }
   }
-  const int t1 = min(t0 + a.PS, u.L);
+  const int t0 = u.p0 * a.PS;
+  if (t0 >= u.L) return false;
+  const int t1 = min(t0 + u.nparts * a.PS, u.L);
   u.npages = (t1 - t0 + BS - 1) / BS;
+  u.ne = (t1 - t0 + a.PS - 1) / a.PS;
   if ((int)threadIdx.x < u.npages) s_bt[threadIdx.x] = u.bt_val;
   __syncthreads();
   return true;
@@ -284,8 +325,12 @@ partition_mfma_kernel(PartitionArgs a) {
     }
   }
   if (!unit_hoist<BS>(a, (int32_t*)smem, u)) return;
-  const LdsLayout lay = lds_layout(a.PS, BS, G, D);
+  const LdsLayout lay = lds_layout(a.PS, BS, G, D, a.C);
   const int32_t* s_bt = (const int32_t*)(smem + lay.bt_off);
+  float* s_m = (float*)(smem + lay.m_off);
+  float* s_l = (float*)(smem + lay.l_off);
+  float* s_acc = (float*)(smem + lay.acc_off);
+  const int pps = a.PS / BS;
 
   const size_t head_off = (size_t)u.kh * PAGE;
   const size_t blk_stride = (size_t)a.KH * PAGE;
@@ -302,12 +347,38 @@ partition_mfma_kernel(PartitionArgs a) {
 #pragma unroll
   for (int i = 0; i < VB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Park this wavefront's state of partition jcur of the span in LDS and
+  // start the next partition empty (wavefront-uniform control flow).
+  int jcur = 0, next_edge = pps;  // next_edge: first page of partition jcur + 1
+  auto park = [&]() {
+    const float ls = rows_sum(lsum);
+    if (g < G) {
+      const int k = slot(jcur, wave, g, G);
+      if (grp == 0) {
+        s_m[k] = m;
+        s_l[k] = ls;
+      }
+      float* dst = s_acc + k * D + 4 * grp;
+#pragma unroll
+      for (int mb = 0; mb < VB; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[16 * mb + r] = acc[mb][r];
+      }
+    }
+    m = kNegInf;
+    lsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ++jcur;
+    next_edge += pps;
+  };
+
   struct Page {
     u32x4 k[SUB][KJ];
     u32x2 v[SUB][VB];
   };
   auto fetch = [&](int i, Page& pg) {
-    const int blk = __builtin_amdgcn_readfirstlane(s_bt[wave + i * kWaves]);
+    const int blk = min(max(__builtin_amdgcn_readfirstlane(s_bt[wave + i * kWaves]), 0), a.NB - 1);
     const uint8_t* kp = kbase + (size_t)blk * blk_stride + k_lane;
     const uint8_t* vp = vbase + (size_t)blk * blk_stride + v_lane;
 #pragma unroll
@@ -325,7 +396,9 @@ partition_mfma_kernel(PartitionArgs a) {
   };
 
   auto process = [&](int i, const Page& pg) {
-    const int tok0 = (u.pg0 + wave + i * kWaves) * BS;  // first token of the page
+    const int page = wave + i * kWaves;  // page of the span
+    while (page >= next_edge) park();
+    const int tok0 = (u.pg0 + page) * BS;  // first token of the page
     float s2[SUB][4];
 #pragma unroll
     for (int st = 0; st < SUB; ++st) {
@@ -375,25 +448,9 @@ partition_mfma_kernel(PartitionArgs a) {
 
   Page ring[PF + 1];
   pipeline<PF>(npg, ring, fetch, process);
-
-  lsum = rows_sum(lsum);
-  float* s_m = (float*)(smem + lay.m_off);
-  float* s_l = (float*)(smem + lay.l_off);
-  float* s_acc = (float*)(smem + lay.acc_off);
-  if (g < G) {
-    if (grp == 0) {
-      s_m[wave * G + g] = m;
-      s_l[wave * G + g] = lsum;
-    }
-    float* dst = s_acc + (wave * G + g) * D + 4 * grp;
-#pragma unroll
-    for (int mb = 0; mb < VB; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[16 * mb + r] = acc[mb][r];
-    }
-  }
+  while (jcur < u.ne) park();
   __syncthreads();
-  merge_store<D>(a, s_m, s_l, s_acc, u.s, u.kh, u.p, G);
+  merge_store<D>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G);
 }
 
 // =====================================================================
@@ -448,8 +505,12 @@ partition_vec_kernel(PartitionArgs a) {
     }
   }
   if (!unit_hoist<BS>(a, (int32_t*)smem, u)) return;
-  const LdsLayout lay = lds_layout(a.PS, BS, G, D);
+  const LdsLayout lay = lds_layout(a.PS, BS, G, D, a.C);
   const int32_t* s_bt = (const int32_t*)(smem + lay.bt_off);
+  float* s_m = (float*)(smem + lay.m_off);
+  float* s_l = (float*)(smem + lay.l_off);
+  float* s_acc = (float*)(smem + lay.acc_off);
+  const int pps = a.PS / BS;
 
   const size_t head_off = (size_t)u.kh * PAGE;
   const size_t blk_stride = (size_t)a.KH * PAGE;
@@ -469,12 +530,46 @@ partition_vec_kernel(PartitionArgs a) {
     for (int j = 0; j < VJ; ++j) acc[gg][j] = 0.0f;
   }
 
+  // Park this wavefront's state of partition jcur of the span in LDS and
+  // start the next partition empty (wavefront-uniform control flow).
+  int jcur = 0, next_edge = pps;  // next_edge: first page of partition jcur + 1
+  auto park = [&]() {
+#pragma unroll
+    for (int gg = 0; gg < GM; ++gg) {
+      const float ls = row16_sum(lpart[gg]);
+#pragma unroll
+      for (int j = 0; j < VJ; ++j) {
+        float v = acc[gg][j];
+#pragma unroll
+        for (int x = 1; x < CPR; x <<= 1) v += __shfl_xor(v, x, 64);
+        acc[gg][j] = v;
+      }
+      if (gg < G) {
+        const int k = slot(jcur, wave, gg, G);
+        if (lane == 0) {
+          s_m[k] = m[gg];
+          s_l[k] = ls;
+        }
+        if (h == 0) {
+#pragma unroll
+          for (int j = 0; j < VJ; ++j) s_acc[k * D + j * DPL + dl] = acc[gg][j];
+        }
+      }
+      m[gg] = kNegInf;
+      lpart[gg] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < VJ; ++j) acc[gg][j] = 0.0f;
+    }
+    ++jcur;
+    next_edge += pps;
+  };
+
   struct Page {
     u32x4 k[SUB][KJ];
     u32x4 v[VJ];
   };
   auto fetch = [&](int i, Page& pg) {
-    const int blk = __builtin_amdgcn_readfirstlane(s_bt[wave + i * kWaves]);
+    const int blk = min(max(__builtin_amdgcn_readfirstlane(s_bt[wave + i * kWaves]), 0), a.NB - 1);
     const uint8_t* kp = kbase + (size_t)blk * blk_stride + k_lane;
     const uint8_t* vp = vbase + (size_t)blk * blk_stride + v_lane;
 #pragma unroll
@@ -488,7 +583,9 @@ partition_vec_kernel(PartitionArgs a) {
   };
 
   auto process = [&](int i, const Page& pg) {
-    const int tok0 = (u.pg0 + wave + i * kWaves) * BS;  // first token of the page
+    const int page = wave + i * kWaves;  // page of the span
+    while (page >= next_edge) park();
+    const int tok0 = (u.pg0 + page) * BS;  // first token of the page
     float p[GM][SUB];
 #pragma unroll
     for (int gg = 0; gg < GM; ++gg) {
@@ -561,43 +658,27 @@ partition_vec_kernel(PartitionArgs a) {
 
   Page ring[PF + 1];
   pipeline<PF>(npg, ring, fetch, process);
-
-  float* s_m = (float*)(smem + lay.m_off);
-  float* s_l = (float*)(smem + lay.l_off);
-  float* s_acc = (float*)(smem + lay.acc_off);
-#pragma unroll
-  for (int gg = 0; gg < GM; ++gg) {
-    const float ls = row16_sum(lpart[gg]);
-#pragma unroll
-    for (int j = 0; j < VJ; ++j) {
-      float v = acc[gg][j];
-#pragma unroll
-      for (int x = 1; x < CPR; x <<= 1) v += __shfl_xor(v, x, 64);
-      acc[gg][j] = v;
-    }
-    if (gg < G) {
-      if (lane == 0) {
-        s_m[wave * G + gg] = m[gg];
-        s_l[wave * G + gg] = ls;
-      }
-      if (h == 0) {
-#pragma unroll
-        for (int j = 0; j < VJ; ++j) s_acc[(wave * G + gg) * D + j * DPL + dl] = acc[gg][j];
-      }
-    }
-  }
+  while (jcur < u.ne) park();
   __syncthreads();
-  merge_store<D>(a, s_m, s_l, s_acc, u.s, u.kh, u.p, G);
+  merge_store<D>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G);
 }
 
 // =====================================================================
-// Reduce: one wavefront per (sequence, query head); the page's phase-2
-// log-sum-exp combine over the n = ceil(L / PS) partitions the sequence uses.
-// Lane i holds partition i's statistics; the d-parallel accumulation reads
-// each weight back with v_readlane. The sequence length, the statistics of
-// the first 64 partitions and the rows of the first kChunk partitions are all
-// requested before any of them is needed (rows past n are loaded but selected
-// away, never multiplied), so the common case costs one memory round trip.
+// Reduce: the page's phase-2 log-sum-exp combine over the n = ceil(L / PS)
+// partitions a sequence uses, for one (sequence, query head) row per WPI
+// wavefronts (WPI = 1, 2 or 4, from the partition count, so that long
+// sequences spread their rows over a whole workgroup).
+//  - First round trip: the sequence length and the first 64 partitions'
+//    statistics (lane i holds partition i); every wavefront of the row forms
+//    the global max M and sum Z itself.
+//  - Second round trip: the rows of the used partitions only (never the
+//    unspecified rows of empty ones), 16 bytes per lane, D/4 lanes per row,
+//    kU rows per lane in flight. Row r of a 64-partition chunk belongs to
+//    wavefront (r / R) % WPI; its weight e^(m_r - M) l_r / Z is read from lane
+//    r with a cross-lane permute.
+//  - The per-lane sums are folded over the rows of a load with xor shuffles
+//    and over the WPI wavefronts through LDS, in a fixed order (the result is
+//    run-to-run identical).
 // =====================================================================
 struct ReduceArgs {
   void* out;
@@ -606,83 +687,100 @@ struct ReduceArgs {
   const float* max_logits;
   const int32_t* sl;
   int S, H, P, PS;
+  int WPI;  // wavefronts per (sequence, head) row: 1, 2 or 4
 };
 
+constexpr int kReduceU = 8;  // partition rows per lane in flight
+
+// Wavefronts per row for a given partition count and head size (host side).
+__host__ __device__ constexpr int reduce_waves_per_row(int P, int D) {
+  const int rows_per_wave = (256 / D) * kReduceU;
+  const int p = P < 64 ? P : 64;
+  return p <= rows_per_wave ? 1 : p <= 2 * rows_per_wave ? 2 : 4;
+}
+
 template <int D, int ODT>
-__global__ void __launch_bounds__(256) reduce_kernel(ReduceArgs a) {
-  constexpr int NWR = 4;
-  constexpr int DPL = D / 64;   // consecutive d per lane
-  constexpr int kChunk = 8;     // partition rows in flight per wavefront
+__global__ void __launch_bounds__(kWaves * 64) reduce_kernel(ReduceArgs a) {
+  constexpr int LPR = D / 4;   // lanes per row, one f32x4 each
+  constexpr int R = 64 / LPR;  // rows per wavefront load
+  __shared__ f32x4 s_part[kWaves][LPR];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sh = blockIdx.x * NWR + wave;
-  if (sh >= a.S * a.H) return;  // whole wavefront; no LDS, no barrier below
-  const int s = sh / a.H;
-  const float* mlr = a.max_logits + (size_t)sh * a.P;
-  const float* esr = a.exp_sums + (size_t)sh * a.P;
-  const float* trow = a.tmp_out + (size_t)sh * a.P * D + lane * DPL;
+  const int WPI = a.WPI;
+  const int sh = blockIdx.x * (kWaves / WPI) + wave / WPI;
+  const int wi = wave % WPI;
+  const int sub = lane / LPR, c4 = lane % LPR;
+  const bool live = sh < a.S * a.H;
 
-  // Independent loads: length, first 64 partitions' statistics, first rows.
-  const int L = a.sl[s];
-  float mi = lane < a.P ? mlr[lane] : kNegInf;
-  float li = lane < a.P ? esr[lane] : 0.0f;
-  float v[kChunk][DPL];
-#pragma unroll
-  for (int u = 0; u < kChunk; ++u) {
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) v[u][e] = u < a.P ? trow[(size_t)u * D + e] : 0.0f;
-  }
-
-  const int n = L > 0 ? (L + a.PS - 1) / a.PS : 0;
-  float acc[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
-  if (n > 0) {
-    if (lane >= n) {
-      mi = kNegInf;
-      li = 0.0f;
-    }
-    float M = mi;
-    for (int i = lane + 64; i < n; i += 64) M = fmaxf(M, mlr[i]);
-    M = wave_max(M);
-    float Z = lane < n ? fast_exp2((mi - M) * kLog2e) * li : 0.0f;
-    for (int i = lane + 64; i < n; i += 64) Z += fast_exp2((mlr[i] - M) * kLog2e) * esr[i];
-    Z = wave_sum(Z);
-    float wl = lane < n ? fast_exp2((mi - M) * kLog2e) * li / Z : 0.0f;
-#pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
-      const float w = lane_value(wl, u);
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] = u < n ? fmaf(w, v[u][e], acc[e]) : acc[e];
-    }
-    for (int base = 0; base < n; base += 64) {
-      if (base > 0) {
-        const int i = base + lane;
-        wl = i < n ? fast_exp2((mlr[i] - M) * kLog2e) * esr[i] / Z : 0.0f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    const int s = sh / a.H;
+    const float* mlr = a.max_logits + (size_t)sh * a.P;
+    const float* esr = a.exp_sums + (size_t)sh * a.P;
+    const float* trow = a.tmp_out + (size_t)sh * a.P * D + 4 * c4;
+    // Independent loads: length and the first 64 partitions' statistics.
+    const int L = a.sl[s];
+    float mi = lane < a.P ? mlr[lane] : kNegInf;
+    float li = lane < a.P ? esr[lane] : 0.0f;
+    const int n = L > 0 ? min((L - 1) / a.PS + 1, a.P) : 0;  // P bounds a length past P*PS
+    if (n > 0) {
+      if (lane >= n) {
+        mi = kNegInf;
+        li = 0.0f;
       }
-      const int cnt = min(64, n - base);
-      for (int k = base == 0 ? kChunk : 0; k < cnt; k += kChunk) {
-#pragma unroll
-        for (int u = 0; u < kChunk; ++u) {
-#pragma unroll
-          for (int e = 0; e < DPL; ++e)
-            v[u][e] = k + u < cnt ? trow[(size_t)(base + k + u) * D + e] : 0.0f;
+      float M = mi;
+      for (int i = lane + 64; i < n; i += 64) M = fmaxf(M, mlr[i]);
+      M = wave_max(M);
+      float Z = lane < n ? fast_exp2((mi - M) * kLog2e) * li : 0.0f;
+      for (int i = lane + 64; i < n; i += 64) Z += fast_exp2((mlr[i] - M) * kLog2e) * esr[i];
+      Z = wave_sum(Z);
+      for (int base = 0; base < n; base += 64) {
+        // Weight of partition base + lane.
+        float wl;
+        if (base == 0) {
+          wl = lane < n ? fast_exp2((mi - M) * kLog2e) * li / Z : 0.0f;
+        } else {
+          const int i = base + lane;
+          wl = i < n ? fast_exp2((mlr[i] - M) * kLog2e) * esr[i] / Z : 0.0f;
         }
+        const int cnt = min(64, n - base);
+        const float* crow = trow + (size_t)base * D;
+        for (int k0 = 0; (k0 * WPI + wi) * R < cnt; k0 += kReduceU) {
+          f32x4 v[kReduceU];
 #pragma unroll
-        for (int u = 0; u < kChunk; ++u) {
-          const float w = lane_value(wl, (k + u) & 63);
+          for (int k = 0; k < kReduceU; ++k) {
+            const int r = ((k0 + k) * WPI + wi) * R + sub;
+            v[k] = r < cnt ? *(const f32x4*)(crow + (size_t)r * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+          }
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) acc[e] = k + u < cnt ? fmaf(w, v[u][e], acc[e]) : acc[e];
+          for (int k = 0; k < kReduceU; ++k) {
+            const int r = ((k0 + k) * WPI + wi) * R + sub;
+            const float w = __shfl(wl, r & 63, 64);
+            if (r < cnt) acc += w * v[k];
+          }
         }
       }
     }
+#pragma unroll
+    for (int x = LPR; x < 64; x <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += shfl_xor(acc[e], x);
+    }
   }
-  const size_t o = (size_t)sh * D + lane * DPL;
-  if constexpr (ODT == DT_F32) {
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) ((float*)a.out)[o + e] = acc[e];
-  } else {
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) ((uint16_t*)a.out)[o + e] = codec<ODT>::one(acc[e]);
+  if (WPI > 1) {  // uniform over the workgroup
+    if (sub == 0) s_part[wave][c4] = acc;
+    __syncthreads();
+    if (sub == 0 && wi == 0) {
+      for (int w = 1; w < WPI; ++w) acc += s_part[wave + w][c4];
+    }
+  }
+  if (live && wi == 0 && sub == 0) {
+    const size_t o = (size_t)sh * D + 4 * c4;
+    if constexpr (ODT == DT_F32) {
+      *(f32x4*)((float*)a.out + o) = acc;
+    } else {
+      using Cd = codec<ODT>;
+      *(u32x2*)((uint16_t*)a.out + o) = u32x2{Cd::pack(acc[0], acc[1]), Cd::pack(acc[2], acc[3])};
+    }
   }
 }
 

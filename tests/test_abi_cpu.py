@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     names = declared_symbols()
     for n in ("paged_attn_v2_partition", "paged_attn_v2_reduce", "paged_attn_decode",
               "paged_attn_last_error", "paged_attn_abi_version",
-              "paged_attn_default_partition_size"):
+              "paged_attn_default_partition_size", "paged_attn_partition_span"):
         assert n in names
 
 
@@ -52,6 +52,21 @@ def test_abi_version_and_default_partition_size():
         assert ps > 0 and ps % BS == 0
     with pytest.raises(RuntimeError):
         pa.default_partition_size(96, 16, torch.float16, 1)
+
+
+def test_partition_span_plan():
+    """Span 2 for large grids of short partitions, 1 for small grids or long spans."""
+    bf, f16, f32 = torch.bfloat16, torch.float16, torch.float32
+    assert pa.partition_span(128, 32, 8, 128, 16, 8, 512, bf) == 2     # GQA, 512-token partitions
+    assert pa.partition_span(8, 64, 8, 128, 16, 64, 512, bf) == 2      # long context
+    assert pa.partition_span(128, 32, 8, 128, 16, 4, 1024, bf) == 1    # 2048-token span too long
+    assert pa.partition_span(32, 16, 16, 256, 32, 16, 512, f16) == 1   # 1 MiB span too long
+    assert pa.partition_span(2, 4, 4, 64, 16, 2, 64, f32) == 1         # small grid
+    assert pa.partition_span(128, 8, 8, 64, 16, 4, 64, f32) == 2
+    with pytest.raises(RuntimeError):
+        pa.partition_span(2, 4, 3, 64, 16, 2, 64, f32)                  # H % KH
+    with pytest.raises(RuntimeError):
+        pa.partition_span(2, 4, 4, 96, 16, 2, 64, f32)                  # head size
 
 
 # Valid baseline: bf16, S=2, H=8, KH=2, D=128, BS=16, B=64, MB=8, P=1, PS=512

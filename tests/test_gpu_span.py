@@ -1,0 +1,120 @@
+"""Workgroups that span two partitions, and the multi-wavefront reduce.
+
+A partition workgroup may own two consecutive partitions of one (sequence, kv
+head); each partition is still computed and stored on its own, so every
+intermediate must match the oracle exactly as for one partition per
+workgroup. The shapes below are chosen so that the launch plan takes the
+two-partition span (asserted through paged_attn_partition_span) on every
+kernel family, with odd partition counts (a last span of one partition),
+partitions that are not a multiple of four pages (wavefronts cross a
+partition edge between two of their pages), and sequence lengths at every
+span edge. The reduce cases cover one, two and four wavefronts per row and
+more than 64 partitions (a second chunk of statistics).
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_v2_amd as pa
+from paged_kv_cache_v2_amd import workloads as W
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    pa.ensure_built()
+    import oracle
+    oracle.build(force=False)
+
+
+def span_lens(S, BS, PS, P, seed):
+    edges = [0, 1, BS - 1, BS, PS - 1, PS, PS + 1, 2 * PS - 1, 2 * PS, 2 * PS + 1, 3 * PS,
+             P * PS - 1, P * PS]
+    edges = [e for e in edges if 0 <= e <= P * PS]
+    rng = np.random.default_rng(seed)
+    rest = rng.integers(0, P * PS + 1, size=max(0, S - len(edges))).tolist()
+    return (edges + rest)[:S]
+
+
+# dtype, H, KH, D, BS, PS, P, S
+SPAN_CASES = [
+    ("bf16", 32, 8, 128, 16, 64, 5, 104),   # MFMA G=4, odd P: last span has one partition
+    ("bf16", 32, 8, 128, 16, 48, 6, 96),    # MFMA G=4, 3 pages per partition
+    ("bf16", 64, 8, 128, 16, 64, 8, 64),    # MFMA G=8
+    ("f16", 32, 32, 128, 16, 64, 8, 32),    # vector G=1
+    ("bf16", 16, 8, 64, 32, 64, 4, 256),    # vector G=2, D=64, BS=32
+    ("f32", 8, 8, 64, 16, 64, 4, 128),      # vector fp32
+    ("f16", 16, 16, 256, 32, 64, 4, 64),    # vector D=256, BS=32
+]
+
+
+@pytest.mark.parametrize("c", SPAN_CASES, ids=lambda c: "_".join(map(str, c)))
+@pytest.mark.parametrize("split", [False, True], ids=["decode", "split"])
+def test_two_partition_span(c, split):
+    dtype, H, KH, D, BS, PS, P, S = c
+    span = pa.partition_span(S, H, KH, D, BS, P, PS, W.DTYPES[dtype])
+    assert span == 2, f"plan chose span {span}; the case no longer exercises two-partition spans"
+    cfg = W.DecodeConfig(f"span_{dtype}", num_seqs=S, num_heads=H, num_kv_heads=KH, head_size=D,
+                         block_size=BS, partition_size=PS, dtype=dtype, len_lo=0,
+                         len_hi=P * PS)
+    lens = span_lens(S, BS, PS, P, seed=S + P)
+    inp = W.make_inputs(cfg, seed=41, lens=lens, extra_blocks=3)
+    W.poison_unused(inp)
+    U.note(f"span case {c} split={split}")
+    res = U.run_decode(U.to_device(inp), split=split)
+    assert res["P"] == P
+    U.check_against_oracle(inp, res, label=f"span {c}")
+
+
+# dtype, H, KH, D, BS, PS, P, lens: reduce rows over 1, 2 and 4 wavefronts, > 64 partitions
+REDUCE_CASES = [
+    ("bf16", 16, 4, 128, 16, 16, 130, [2080, 1030, 5]),  # 4 wavefronts per row, 3 chunks
+    ("f16", 8, 8, 256, 16, 16, 70, [1120, 1000]),        # D=256: 4 wavefronts, 2 chunks
+    ("f32", 4, 4, 64, 16, 16, 20, [320, 17]),            # D=64: one wavefront per row
+    ("bf16", 32, 8, 128, 16, 16, 24, [384, 200, 0]),     # 2 wavefronts per row
+]
+
+
+@pytest.mark.parametrize("c", REDUCE_CASES, ids=lambda c: "_".join(map(str, c[:7])))
+def test_reduce_row_spread(c):
+    dtype, H, KH, D, BS, PS, P, lens = c
+    cfg = W.DecodeConfig(f"red_{dtype}", num_seqs=len(lens), num_heads=H, num_kv_heads=KH,
+                         head_size=D, block_size=BS, partition_size=PS, dtype=dtype, len_lo=0,
+                         len_hi=P * PS)
+    inp = W.make_inputs(cfg, seed=43, lens=lens, extra_blocks=2)
+    W.poison_unused(inp)
+    U.note(f"reduce case {c[:7]}")
+    res = U.run_decode(U.to_device(inp), split=True)
+    assert res["P"] == P
+    U.check_against_oracle(inp, res, label=f"reduce {c[:7]}")
+
+
+def test_span_results_match_single_partition_workgroups():
+    """Same inputs, one and two partitions per workgroup: tmp/statistics identical.
+
+    The two plans differ only in how units are grouped; each partition's
+    arithmetic is the same, so the intermediates agree bit for bit. The
+    single-partition plan is reached by a small batch of the same sequences."""
+    dtype, H, KH, D, BS, PS, P = "bf16", 32, 8, 128, 16, 64, 5
+    S_big = 104
+    cfg = W.DecodeConfig("span_eq", num_seqs=S_big, num_heads=H, num_kv_heads=KH, head_size=D,
+                         block_size=BS, partition_size=PS, dtype=dtype, len_lo=0, len_hi=P * PS)
+    lens = span_lens(S_big, BS, PS, P, seed=5)
+    inp = W.make_inputs(cfg, seed=47, lens=lens)
+    assert pa.partition_span(S_big, H, KH, D, BS, P, PS, torch.bfloat16) == 2
+    assert pa.partition_span(4, H, KH, D, BS, P, PS, torch.bfloat16) == 1
+    U.note("span vs single-partition plan")
+    big = U.run_decode(U.to_device(inp), split=True)
+    small_inp = dict(inp)
+    small_inp["query"] = inp["query"][:4]
+    small_inp["block_tables"] = inp["block_tables"][:4]
+    small_inp["seq_lens"] = inp["seq_lens"][:4]
+    small = U.run_decode(U.to_device(small_inp), split=True)
+    for k in ("es", "ml"):
+        assert torch.equal(small[k], big[k][:4]), k
+    n = [-(-int(L) // PS) for L in lens[:4]]
+    for s in range(4):
+        assert torch.equal(small["tmp"][s, :, :n[s]], big["tmp"][s, :, :n[s]]), s
+    assert torch.equal(small["out"], big["out"][:4])
