@@ -7,8 +7,12 @@ steps, then exactly K timed steps between two torch.cuda.synchronize() calls.
 Prints ONE JSON line:
 
   value      = algorithmic K+V bytes per step / step time (GB/s), the metric's
-               "achieved HBM GB/s"; the line also carries the % of the 8 TB/s
-               peak and query-heads x tokens / s.
+               "achieved HBM GB/s", at the workload's configured partition
+               size; the line also carries the % of the 8 TB/s peak and
+               query-heads x tokens / s.
+  tuned      = the same batch through paged_attn_decode at the partition size
+               the library recommends (paged_attn_default_partition_size);
+               same K+V bytes, same output up to rounding.
   roofline   = the dominant kernel (the partition kernel): algorithmic K+V
                bytes per launch / its average duration, measured with a HIP event
                pair on the launch stream around every partition launch of a
@@ -141,6 +145,27 @@ def run(args) -> dict:
     part_avg_s = sum(part_ms) / len(part_ms) / 1e3
     red_avg_s = sum(red_ms) / len(red_ms) / 1e3
 
+    # The same batch through paged_attn_decode (one ABI call, partition +
+    # reduce) at the partition size the library recommends for this geometry;
+    # out does not depend on the partition size beyond rounding.
+    PS_t = pa.default_partition_size(D, cfg.block_size, W.DTYPES[cfg.dtype], cfg.group)
+    P_t = max(1, -(-cfg.max_len // PS_t))
+    tmp_t, es_t, ml_t = pa.workspace(S, H, D, P_t, dev)
+
+    def step_tuned():
+        pa.paged_attn_decode(out, tmp_t, es_t, ml_t, q, kc, vc, bt, sl, inp["scale"], PS_t,
+                             stream=stream)
+
+    for _ in range(args.warmup):
+        step_tuned()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step_tuned()
+    torch.cuda.synchronize()
+    tuned_s = (time.perf_counter() - t0) / K
+    del tmp_t, es_t, ml_t
+
     kvb = W.kv_bytes(inp)
     step_s = elapsed / K
     gbs = kvb / step_s / 1e9
@@ -171,6 +196,14 @@ def run(args) -> dict:
                          f"uniform[{cfg.len_lo},{cfg.len_hi}] seed {seed}"),
             "total_tokens": int(inp["seq_lens"].sum()), "kv_bytes_per_step": kvb,
             "num_blocks": inp["num_blocks"],
+        },
+        "tuned": {
+            "entry": "paged_attn_decode", "partition_size": PS_t, "max_num_partitions": P_t,
+            "partition_span": pa.partition_span(S, H, cfg.num_kv_heads, D, cfg.block_size, P_t,
+                                                PS_t, W.DTYPES[cfg.dtype]),
+            "ms_per_step": round(tuned_s * 1e3, 5), "value": round(kvb / tuned_s / 1e9, 2),
+            "unit": "GB/s", "pct_of_peak_hbm": round(100.0 * kvb / tuned_s / 1e9 / PEAK_HBM_GBS, 2),
+            "qheads_tokens_per_s": round(W.qhead_tokens(inp) / tuned_s, 1),
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,

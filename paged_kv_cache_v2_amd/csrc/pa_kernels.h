@@ -156,6 +156,7 @@ struct PartitionArgs {
   int S, H, KH, MB, P, PS;
   int NB;          // physical blocks; block-table entries are clamped into [0, NB)
   int C;           // consecutive partitions per workgroup (span), 1 .. kMaxSpan
+  int through;     // 1: tmp_output stores with device-scope (sc1) policy
   float qk_scale;  // scale * log2(e)
 };
 
@@ -178,18 +179,21 @@ __host__ __device__ inline LdsLayout lds_layout(int PS, int BS, int G, int D, in
   return o;
 }
 
-// Stores of the partition outputs. They are written once and read once by the
-// reduce; issued with device-scope (sc1) policy they measured up to ~6 % faster
-// on the long-context workload than default write-back stores (interleaved with
-// the streaming K/V reads, written-back tmp lines cost several times their
-// size in read bandwidth) and neutral elsewhere.
-#ifndef PA_TMP_POLICY
-#define PA_TMP_POLICY 16  // buffer-instruction cache-policy bits: sc0 = 1, nt = 2, sc1 = 16
-#endif
+// Stores of the partition outputs (written once, read once by the reduce).
+// Interleaved with the streaming K/V reads, written-back tmp lines cost
+// several times their size in read bandwidth. Device-scope (sc1) stores
+// measured up to ~6 % faster where each row has many partitions (64: long
+// context, 16: 256-wide heads) and up to ~2.5 % slower where it has few (4-8:
+// ragged GQA batches), so the host picks the policy per launch (`through`).
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer resource: 32-bit format, no swizzle
-__device__ __forceinline__ void store_row(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0,
-                                          PA_TMP_POLICY);
+constexpr int kStoreThrough = 16;       // buffer-instruction cache policy: sc1
+__device__ __forceinline__ void store_row(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v,
+                                          bool through) {
+  const u32x4 w = __builtin_bit_cast(u32x4, v);
+  if (through)
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, kStoreThrough);
+  else
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, 0);
 }
 
 // Slot of (partition j of the span, wavefront w, head g) in the parked state.
@@ -226,7 +230,7 @@ __device__ __forceinline__ void merge_store(const PartitionArgs& a, const float*
     }
     const float inv = 1.0f / Z;
     const size_t row = ((size_t)s * a.H + kh * G + g) * a.P + p0 + j;
-    store_row(tmp, (uint32_t)(((g * a.P + p0 + j) * D + 4 * d4) * 4), o * inv);
+    store_row(tmp, (uint32_t)(((g * a.P + p0 + j) * D + 4 * d4) * 4), o * inv, a.through);
     if (d4 == 0) {
       a.exp_sums[row] = Z;
       a.max_logits[row] = M * kLn2;

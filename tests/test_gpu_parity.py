@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import paged_kv_cache_v2_amd as pa
 from paged_kv_cache_v2_amd import workloads as W
 from tests import gpu_util as U
 
@@ -75,11 +76,22 @@ def sample_seqs(inp, k=3, seed=0):
 
 
 @pytest.mark.parametrize("name", W.CONFIG_ORDER)
-def test_parity_full_size_sampled(name):
+@pytest.mark.parametrize("ps", ["config", "default"])
+def test_parity_full_size_sampled(name, ps):
+    """Full-size inputs, in the launch configurations bench.py times: the
+    configured partition size through the two calls, and the library's
+    recommended partition size through paged_attn_decode."""
     inp, d = full_inputs(name)
+    cfg = W.CONFIGS[name]
     seqs = sample_seqs(inp, k=1 if name == "longctx_bf16_g8" else 3)
-    U.note(f"parity full {name} S={inp['num_seqs']} blocks={inp['num_blocks']} seqs={seqs}")
-    res = U.run_decode(d)
+    PS = None
+    if ps == "default":
+        PS = pa.default_partition_size(cfg.head_size, cfg.block_size, W.DTYPES[cfg.dtype],
+                                       cfg.group)
+    U.note(f"parity full {name} ps={ps} S={inp['num_seqs']} blocks={inp['num_blocks']} "
+           f"seqs={seqs}")
+    res = U.run_decode(d, PS=PS, P=max(1, -(-cfg.max_len // PS)) if PS else None,
+                       split=(ps == "config"))
     assert torch.isfinite(res["out"]).all()
     U.check_against_oracle(inp, res, seqs=seqs, label=f"{name} full")
     # properties at every row: sentinels exact, valid partitions finite and l >= 1
