@@ -22,7 +22,7 @@ _SRC = os.path.join(_HERE, "paged_decode_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _LIB = None
 
-DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
 
 
 def compile_source(src: str, out: str) -> str:
@@ -77,6 +77,8 @@ def _bind(path: str):
     lib.oracle_decode_binary16.argtypes = [ctypes.c_uint16]
     lib.oracle_decode_bfloat16.restype = ctypes.c_double
     lib.oracle_decode_bfloat16.argtypes = [ctypes.c_uint16]
+    lib.oracle_decode_e4m3.restype = ctypes.c_double
+    lib.oracle_decode_e4m3.argtypes = [ctypes.c_uint8]
     lib.oracle_decode_array.restype = None
     lib.oracle_decode_array.argtypes = [P, P, I64, ctypes.c_int]
     lib.oracle_attention.restype = ctypes.c_int
@@ -85,6 +87,13 @@ def _bind(path: str):
     lib.oracle_partition_stats.restype = ctypes.c_int
     lib.oracle_partition_stats.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32,
                                            I32, I32, I32, F32, I32, P, I32, I32]
+    lib.oracle_attention_ex.restype = ctypes.c_int
+    lib.oracle_attention_ex.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, F32,
+                                        I32, I32, F32, F32, P, I32, I32]
+    lib.oracle_partition_stats_ex.restype = ctypes.c_int
+    lib.oracle_partition_stats_ex.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32,
+                                              I32, I32, I32, F32, I32, I32, F32, F32, P, I32,
+                                              I32]
     lib.oracle_combine.restype = None
     lib.oracle_combine.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32]
     lib.oracle_gather_indices.restype = I64
@@ -107,6 +116,8 @@ def _np(t) -> np.ndarray:
             t = t.detach().cpu().contiguous()
             if t.dtype in (torch.float16, torch.bfloat16):
                 return t.view(torch.int16).numpy().view(np.uint16)
+            if t.dtype == torch.float8_e4m3fn:
+                return t.view(torch.uint8).numpy()
             return t.numpy()
     except ImportError:  # pragma: no cover
         pass
@@ -115,7 +126,7 @@ def _np(t) -> np.ndarray:
 
 def _dtype_code(q) -> int:
     import torch
-    m = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    m = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float8_e4m3fn: 3}
     return m[q.dtype]
 
 
@@ -124,7 +135,7 @@ def _ptr(a: np.ndarray) -> int:
 
 
 def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """Decode an array of stored 16-bit patterns (or float32) to float64."""
+    """Decode an array of stored 8/16-bit patterns (or float32) to float64."""
     a = np.ascontiguousarray(bits)
     out = np.empty(a.size, dtype=np.float64)
     _lib().oracle_decode_array(_ptr(out), _ptr(a), a.size, DTYPE_CODES[dtype])
@@ -139,10 +150,13 @@ def _seq_arg(seqs: Optional[Sequence[int]]):
 
 
 def attention(query, key_cache, value_cache, block_tables, seq_lens, scale: float,
-              seqs: Optional[Sequence[int]] = None, nthreads: Optional[int] = None) -> np.ndarray:
+              seqs: Optional[Sequence[int]] = None, nthreads: Optional[int] = None,
+              k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Dense softmax attention over the block-table-gathered tokens: out[S, H, D] float64.
 
-    Rows of sequences not in ``seqs`` are NaN.
+    Rows of sequences not in ``seqs`` are NaN. The query dtype and the cache
+    dtype are read off the tensors; an e4m3fn cache stands for its decoded
+    values times ``k_scale`` / ``v_scale``.
     """
     q, kc, vc = _np(query), _np(key_cache), _np(value_cache)
     bt, sl = _np(block_tables).astype(np.int32, copy=False), _np(seq_lens).astype(np.int32, copy=False)
@@ -151,9 +165,11 @@ def attention(query, key_cache, value_cache, block_tables, seq_lens, scale: floa
     MB = bt.shape[1]
     out = np.full((S, H, D), np.nan)
     sp, ns, keep = _seq_arg(seqs)
-    rc = _lib().oracle_attention(_ptr(out), _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl),
-                                 S, H, KH, D, BS, MB, float(np.float32(scale)),
-                                 _dtype_code(query), sp, ns, nthreads or default_threads())
+    rc = _lib().oracle_attention_ex(_ptr(out), _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl),
+                                    S, H, KH, D, BS, MB, float(np.float32(scale)),
+                                    _dtype_code(query), _dtype_code(key_cache),
+                                    float(np.float32(k_scale)), float(np.float32(v_scale)),
+                                    sp, ns, nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_attention: unsupported shape")
     del keep
@@ -163,7 +179,8 @@ def attention(query, key_cache, value_cache, block_tables, seq_lens, scale: floa
 def partition_stats(query, key_cache, value_cache, block_tables, seq_lens, scale: float,
                     max_num_partitions: int, partition_size: int,
                     seqs: Optional[Sequence[int]] = None,
-                    nthreads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                    nthreads: Optional[int] = None, k_scale: float = 1.0,
+                    v_scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Phase-1 intermediates (tmp_output[S,H,P,D], exp_sums[S,H,P], max_logits[S,H,P])."""
     q, kc, vc = _np(query), _np(key_cache), _np(value_cache)
     bt, sl = _np(block_tables).astype(np.int32, copy=False), _np(seq_lens).astype(np.int32, copy=False)
@@ -175,10 +192,11 @@ def partition_stats(query, key_cache, value_cache, block_tables, seq_lens, scale
     es = np.full((S, H, P), np.nan)
     ml = np.full((S, H, P), np.nan)
     sp, ns, keep = _seq_arg(seqs)
-    rc = _lib().oracle_partition_stats(_ptr(tmp), _ptr(es), _ptr(ml), _ptr(q), _ptr(kc), _ptr(vc),
-                                       _ptr(bt), _ptr(sl), S, H, KH, D, BS, MB, P, partition_size,
-                                       float(np.float32(scale)), _dtype_code(query), sp, ns,
-                                       nthreads or default_threads())
+    rc = _lib().oracle_partition_stats_ex(
+        _ptr(tmp), _ptr(es), _ptr(ml), _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl), S, H, KH,
+        D, BS, MB, P, partition_size, float(np.float32(scale)), _dtype_code(query),
+        _dtype_code(key_cache), float(np.float32(k_scale)), float(np.float32(v_scale)), sp, ns,
+        nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_partition_stats: unsupported shape or length > P*PS")
     del keep

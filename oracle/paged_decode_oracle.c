@@ -15,6 +15,8 @@
  *              (cross-partition log-sum-exp combine).
  *  [METAL-FA]  "Flash Attention Metal Shaders": forward kernel (the same
  *              softmax recurrence in unnormalised form; an empty row gives 0).
+ *  [CUDA-A2A]  "all2all_heads.cu": its kernels move tensors of e4m3fn
+ *              elements (only the element format is taken from it).
  *
  * What is computed. V2 is an exact reformulation of dense softmax attention
  * over the tokens a sequence's block table gathers, so the plain definition is:
@@ -39,7 +41,16 @@
  *  - the 1024-partition cap of the launcher is an implementation limit of
  *    that GPU, not semantics; any P is accepted.
  * All arithmetic is IEEE double; stored inputs are decoded exactly from
- * their bits using the binary16 and bfloat16 format definitions.
+ * their bits using the binary16, bfloat16 and OCP 8-bit E4M3 format
+ * definitions.
+ *
+ * 8-bit KV caches. The launcher of [TRITON-V2] carries a cache dtype string
+ * and per-tensor key / value scales (its kernels do not use them), and
+ * [CUDA-A2A] "all2all_heads.cu" moves e4m3fn tensors. The plainest reading,
+ * taken here: key and value elements are stored as OCP FP8 E4M3 bytes and
+ * stand for decode(byte) * k_scale and decode(byte) * v_scale (scales are
+ * fp32 scalars, applied in double); the query keeps its own 16-bit dtype and
+ * the cache packing factor is x = 16 / 1 = 16. Everything else is unchanged.
  */
 #include <math.h>
 #include <pthread.h>
@@ -47,7 +58,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2, ORACLE_FP8_E4M3 = 3 };
 
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
  * exponent 0 -> subnormal (fraction * 2^-24), 31 -> inf / NaN. */
@@ -83,8 +94,28 @@ double oracle_decode_bfloat16(uint16_t bits) {
     return sign ? -v : v;
 }
 
+/* OCP 8-bit floating point, E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits
+ * (bias 7), 3 fraction bits; exponent 0 -> subnormal (fraction * 2^-9); no
+ * infinities: only S.1111.111 is NaN, so exponent 15 with fraction < 7 is a
+ * normal number (largest 1.75 * 2^8 = 448). */
+double oracle_decode_e4m3(uint8_t bits) {
+    int sign = (bits >> 7) & 1;
+    int e = (bits >> 3) & 0xf;
+    int f = bits & 0x7;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -9);
+    } else if (e == 15 && f == 7) {
+        v = NAN;
+    } else {
+        v = ldexp((double)(8 + f), e - 10);
+    }
+    return sign ? -v : v;
+}
+
 static double load_elem(const void* base, int64_t idx, int dtype) {
     if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
+    if (dtype == ORACLE_FP8_E4M3) return oracle_decode_e4m3(((const uint8_t*)base)[idx]);
     uint16_t b = ((const uint16_t*)base)[idx];
     return dtype == ORACLE_F16 ? oracle_decode_binary16(b) : oracle_decode_bfloat16(b);
 }
@@ -93,7 +124,9 @@ void oracle_decode_array(double* out, const void* src, int64_t n, int dtype) {
     for (int64_t i = 0; i < n; ++i) out[i] = load_elem(src, i, dtype);
 }
 
-static int elem_size(int dtype) { return dtype == ORACLE_F32 ? 4 : 2; }
+static int elem_size(int dtype) {
+    return dtype == ORACLE_F32 ? 4 : dtype == ORACLE_FP8_E4M3 ? 1 : 2;
+}
 
 /* Problem description shared by the entry points. */
 typedef struct {
@@ -102,8 +135,10 @@ typedef struct {
     const void* vc;     /* [B, KH, D, BS]          */
     const int32_t* bt;  /* [S, MB]                 */
     const int32_t* sl;  /* [S]                     */
-    int32_t S, H, KH, D, BS, MB, P, PS, dtype;
+    int32_t S, H, KH, D, BS, MB, P, PS;
+    int32_t qdtype, kvdtype;  /* query dtype; key / value cache dtype */
     double scale;
+    double kscale, vscale;    /* cache dequantisation scales (1 for 16/32-bit caches) */
     /* outputs (any may be NULL) */
     double* out;        /* [S, H, D]     dense attention      */
     double* tmp;        /* [S, H, P, D]  partition outputs    */
@@ -123,19 +158,19 @@ static void gather_index(const problem_t* pr, int32_t s, int32_t t, int32_t* blk
 
 /* K element d of (block b, kv head kh, slot o): key_cache[b][kh][d / x][o][d % x]. */
 static double key_at(const problem_t* pr, int32_t b, int32_t kh, int32_t o, int32_t d) {
-    int32_t x = 16 / elem_size(pr->dtype);
+    int32_t x = 16 / elem_size(pr->kvdtype);
     int64_t idx = ((((int64_t)b * pr->KH + kh) * (pr->D / x) + d / x) * pr->BS + o) * x + d % x;
-    return load_elem(pr->kc, idx, pr->dtype);
+    return load_elem(pr->kc, idx, pr->kvdtype) * pr->kscale;
 }
 
 /* V element d of (block b, kv head kh, slot o): value_cache[b][kh][d][o]. */
 static double value_at(const problem_t* pr, int32_t b, int32_t kh, int32_t o, int32_t d) {
     int64_t idx = (((int64_t)b * pr->KH + kh) * pr->D + d) * pr->BS + o;
-    return load_elem(pr->vc, idx, pr->dtype);
+    return load_elem(pr->vc, idx, pr->kvdtype) * pr->vscale;
 }
 
 static double query_at(const problem_t* pr, int32_t s, int32_t h, int32_t d) {
-    return load_elem(pr->q, ((int64_t)s * pr->H + h) * pr->D + d, pr->dtype);
+    return load_elem(pr->q, ((int64_t)s * pr->H + h) * pr->D + d, pr->qdtype);
 }
 
 /* Softmax-weighted value mix of tokens [t0, t1) given their scores.
@@ -235,44 +270,79 @@ static void run_all(problem_t* pr, const int32_t* seqs, int32_t n_seqs, int nthr
     free(all);
 }
 
+static int valid_dtypes(int32_t qdtype, int32_t kvdtype) {
+    if (qdtype < ORACLE_F32 || qdtype > ORACLE_BF16) return 0;
+    if (kvdtype == ORACLE_FP8_E4M3) return qdtype != ORACLE_F32;
+    return kvdtype == qdtype;
+}
+
 /* Dense attention over the gathered tokens. out[S,H,D]: only rows of the
- * listed sequences are written (seqs == NULL means all). Returns 0, or -1 on
- * a shape the definition does not cover. */
-int oracle_attention(double* out, const void* q, const void* kc, const void* vc,
-                     const int32_t* block_tables, const int32_t* seq_lens,
-                     int32_t S, int32_t H, int32_t KH, int32_t D, int32_t BS, int32_t MB,
-                     float scale, int32_t dtype, const int32_t* seqs, int32_t n_seqs,
-                     int32_t nthreads) {
-    if (KH <= 0 || H % KH || D % (16 / elem_size(dtype))) return -1;
+ * listed sequences are written (seqs == NULL means all). The query is
+ * decoded as qdtype, the caches as kvdtype scaled by k_scale / v_scale.
+ * Returns 0, or -1 on a shape or dtype pair the definition does not cover. */
+int oracle_attention_ex(double* out, const void* q, const void* kc, const void* vc,
+                        const int32_t* block_tables, const int32_t* seq_lens,
+                        int32_t S, int32_t H, int32_t KH, int32_t D, int32_t BS, int32_t MB,
+                        float scale, int32_t qdtype, int32_t kvdtype, float k_scale,
+                        float v_scale, const int32_t* seqs, int32_t n_seqs, int32_t nthreads) {
+    if (!valid_dtypes(qdtype, kvdtype)) return -1;
+    if (KH <= 0 || H % KH || D % (16 / elem_size(kvdtype))) return -1;
     problem_t pr;
     memset(&pr, 0, sizeof pr);
     pr.q = q; pr.kc = kc; pr.vc = vc; pr.bt = block_tables; pr.sl = seq_lens;
-    pr.S = S; pr.H = H; pr.KH = KH; pr.D = D; pr.BS = BS; pr.MB = MB; pr.dtype = dtype;
+    pr.S = S; pr.H = H; pr.KH = KH; pr.D = D; pr.BS = BS; pr.MB = MB;
+    pr.qdtype = qdtype; pr.kvdtype = kvdtype;
     pr.scale = (double)scale;
+    pr.kscale = (double)k_scale; pr.vscale = (double)v_scale;
     pr.out = out;
     run_all(&pr, seqs, n_seqs, nthreads);
     return 0;
 }
 
+/* Same, one dtype for query and caches, no cache scales. */
+int oracle_attention(double* out, const void* q, const void* kc, const void* vc,
+                     const int32_t* block_tables, const int32_t* seq_lens,
+                     int32_t S, int32_t H, int32_t KH, int32_t D, int32_t BS, int32_t MB,
+                     float scale, int32_t dtype, const int32_t* seqs, int32_t n_seqs,
+                     int32_t nthreads) {
+    return oracle_attention_ex(out, q, kc, vc, block_tables, seq_lens, S, H, KH, D, BS, MB,
+                               scale, dtype, dtype, 1.0f, 1.0f, seqs, n_seqs, nthreads);
+}
+
 /* Phase-1 intermediates: tmp[S,H,P,D], es[S,H,P], ml[S,H,P] for the listed
  * sequences. Returns -1 if a length exceeds P*PS. */
-int oracle_partition_stats(double* tmp, double* es, double* ml, const void* q, const void* kc,
-                           const void* vc, const int32_t* block_tables, const int32_t* seq_lens,
-                           int32_t S, int32_t H, int32_t KH, int32_t D, int32_t BS, int32_t MB,
-                           int32_t P, int32_t PS, float scale, int32_t dtype,
-                           const int32_t* seqs, int32_t n_seqs, int32_t nthreads) {
-    if (KH <= 0 || H % KH || D % (16 / elem_size(dtype)) || PS <= 0 || P < 1) return -1;
+int oracle_partition_stats_ex(double* tmp, double* es, double* ml, const void* q,
+                              const void* kc, const void* vc, const int32_t* block_tables,
+                              const int32_t* seq_lens, int32_t S, int32_t H, int32_t KH,
+                              int32_t D, int32_t BS, int32_t MB, int32_t P, int32_t PS,
+                              float scale, int32_t qdtype, int32_t kvdtype, float k_scale,
+                              float v_scale, const int32_t* seqs, int32_t n_seqs,
+                              int32_t nthreads) {
+    if (!valid_dtypes(qdtype, kvdtype)) return -1;
+    if (KH <= 0 || H % KH || D % (16 / elem_size(kvdtype)) || PS <= 0 || P < 1) return -1;
     for (int32_t s = 0; s < S; ++s)
         if (seq_lens[s] > (int64_t)P * PS) return -1;
     problem_t pr;
     memset(&pr, 0, sizeof pr);
     pr.q = q; pr.kc = kc; pr.vc = vc; pr.bt = block_tables; pr.sl = seq_lens;
-    pr.S = S; pr.H = H; pr.KH = KH; pr.D = D; pr.BS = BS; pr.MB = MB; pr.dtype = dtype;
+    pr.S = S; pr.H = H; pr.KH = KH; pr.D = D; pr.BS = BS; pr.MB = MB;
+    pr.qdtype = qdtype; pr.kvdtype = kvdtype;
     pr.P = P; pr.PS = PS;
     pr.scale = (double)scale;
+    pr.kscale = (double)k_scale; pr.vscale = (double)v_scale;
     pr.tmp = tmp; pr.es = es; pr.ml = ml;
     run_all(&pr, seqs, n_seqs, nthreads);
     return 0;
+}
+
+int oracle_partition_stats(double* tmp, double* es, double* ml, const void* q, const void* kc,
+                           const void* vc, const int32_t* block_tables, const int32_t* seq_lens,
+                           int32_t S, int32_t H, int32_t KH, int32_t D, int32_t BS, int32_t MB,
+                           int32_t P, int32_t PS, float scale, int32_t dtype,
+                           const int32_t* seqs, int32_t n_seqs, int32_t nthreads) {
+    return oracle_partition_stats_ex(tmp, es, ml, q, kc, vc, block_tables, seq_lens, S, H, KH,
+                                     D, BS, MB, P, PS, scale, dtype, dtype, 1.0f, 1.0f, seqs,
+                                     n_seqs, nthreads);
 }
 
 /* Phase-2 cross-partition log-sum-exp combine, per (s, h), over the

@@ -31,8 +31,10 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 import torch
 
-DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
-DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+          "fp8": torch.float8_e4m3fn}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
+FP8_MAX = 448.0  # largest finite OCP E4M3 value
 
 # Stream keys (first element of spawn_key) for each random quantity.
 _KEY_LENS, _KEY_PERM, _KEY_Q, _KEY_K, _KEY_V = 0, 1, 2, 3, 4
@@ -57,6 +59,13 @@ class DecodeConfig:
     sigma: float = 1.0
     scale: Optional[float] = None  # None means 1/sqrt(head_size)
     num_blocks: Optional[int] = None  # None means exactly the blocks used
+    q_dtype: Optional[str] = None  # None means the cache dtype
+    k_scale: float = 1.0  # 8-bit caches: a stored key byte stands for decode(byte) * k_scale
+    v_scale: float = 1.0
+
+    @property
+    def query_dtype(self) -> str:
+        return self.q_dtype or self.dtype
 
     @property
     def x(self) -> int:
@@ -112,6 +121,28 @@ CONFIGS: Dict[str, DecodeConfig] = {
 }
 CONFIG_ORDER = ["tiny_f32_d64", "mha_f16_d128", "gqa_bf16_g4", "longctx_bf16_g8",
                 "wide_f16_d256"]
+
+# 8-bit (OCP E4M3) key/value caches with per-tensor scales: the GQA, long-context
+# and MHA shapes above with the caches stored in one byte per element and the
+# query kept in its 16-bit dtype. The scales are deliberately not powers of two.
+FP8_CONFIGS: Dict[str, DecodeConfig] = {
+    "gqa_fp8_g4": CONFIGS["gqa_bf16_g4"].replace(
+        name="gqa_fp8_g4", dtype="fp8", q_dtype="bf16", k_scale=0.015, v_scale=0.02),
+    "longctx_fp8_g8": CONFIGS["longctx_bf16_g8"].replace(
+        name="longctx_fp8_g8", dtype="fp8", q_dtype="bf16", k_scale=0.0075, v_scale=0.01),
+    "mha_fp8_d128": CONFIGS["mha_f16_d128"].replace(
+        name="mha_fp8_d128", dtype="fp8", q_dtype="f16", k_scale=0.015, v_scale=0.02),
+}
+FP8_ORDER = ["gqa_fp8_g4", "longctx_fp8_g8", "mha_fp8_d128"]
+CONFIGS.update(FP8_CONFIGS)
+
+
+def workload_seed(name: str) -> int:
+    """Seed of a named workload's reported runs: its index in its list, plus 1
+    (the 8-bit workloads from 101)."""
+    if name in CONFIG_ORDER:
+        return CONFIG_ORDER.index(name) + 1
+    return FP8_ORDER.index(name) + 101
 
 
 def _workers() -> int:
@@ -185,7 +216,8 @@ def make_metadata(cfg: DecodeConfig, seed: int, lens: Optional[Sequence[int]] = 
                 num_seqs=S, num_heads=cfg.num_heads, num_kv_heads=cfg.num_kv_heads,
                 head_size=cfg.head_size, block_size=BS, num_blocks=NB, max_blocks_per_seq=MB,
                 max_num_partitions=P, partition_size=cfg.partition_size, scale=cfg.scale_f32,
-                dtype=cfg.dtype, x=cfg.x, used_blocks=used)
+                dtype=cfg.dtype, q_dtype=cfg.query_dtype, x=cfg.x, used_blocks=used,
+                k_scale=float(np.float32(cfg.k_scale)), v_scale=float(np.float32(cfg.v_scale)))
 
 
 def make_inputs(cfg: DecodeConfig, seed: int, lens: Optional[Sequence[int]] = None,
@@ -194,7 +226,9 @@ def make_inputs(cfg: DecodeConfig, seed: int, lens: Optional[Sequence[int]] = No
 
     Returns the metadata of ``make_metadata`` plus torch tensors ``query``,
     ``key_cache`` and ``value_cache`` drawn N(0, sigma^2) and rounded to the
-    workload's dtype.
+    workload's dtypes. For an 8-bit cache the drawn values are divided by the
+    cache scale, clamped to the format's finite range and rounded to E4M3
+    (the stored bytes then stand for roughly N(0, sigma^2) values).
     """
     S, H, KH, D, BS = (cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_size,
                        cfg.block_size)
@@ -202,16 +236,17 @@ def make_inputs(cfg: DecodeConfig, seed: int, lens: Optional[Sequence[int]] = No
     assert H % KH == 0 and D % x == 0
     out = make_metadata(cfg, seed, lens, extra_blocks)
     NB = out["num_blocks"]
-    tdt = DTYPES[cfg.dtype]
 
-    def tensor(key: int, shape) -> torch.Tensor:
+    def tensor(key: int, shape, dtype: str, cache_scale: float = 1.0) -> torch.Tensor:
         n = int(np.prod(shape))
         vals = torch.from_numpy(_normals(seed, key, n, cfg.sigma)).reshape(shape)
-        return vals.to(tdt)
+        if dtype == "fp8":
+            vals = (vals / np.float32(cache_scale)).clamp_(-FP8_MAX, FP8_MAX)
+        return vals.to(DTYPES[dtype])
 
-    out["query"] = tensor(_KEY_Q, (S, H, D))
-    out["key_cache"] = tensor(_KEY_K, (NB, KH, D // x, BS, x))
-    out["value_cache"] = tensor(_KEY_V, (NB, KH, D, BS))
+    out["query"] = tensor(_KEY_Q, (S, H, D), cfg.query_dtype)
+    out["key_cache"] = tensor(_KEY_K, (NB, KH, D // x, BS, x), cfg.dtype, cfg.k_scale)
+    out["value_cache"] = tensor(_KEY_V, (NB, KH, D, BS), cfg.dtype, cfg.v_scale)
     if device != "cpu":
         for k in ("query", "key_cache", "value_cache", "block_tables", "seq_lens"):
             out[k] = out[k].to(device)
@@ -225,6 +260,9 @@ def poison_unused(inp: Dict[str, object], value: float = float("nan")) -> None:
     sequence's last block at or past its length.
     """
     kc, vc = inp["key_cache"], inp["value_cache"]
+    if kc.dtype == torch.float8_e4m3fn:  # fill through the byte view (same storage)
+        value = int(torch.tensor([value]).to(kc.dtype).view(torch.uint8)[0])
+        kc, vc = kc.view(torch.uint8), vc.view(torch.uint8)
     bt, sl = inp["block_tables"], inp["seq_lens"]
     BS = inp["block_size"]
     NB = kc.shape[0]

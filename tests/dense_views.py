@@ -13,17 +13,20 @@ from typing import Dict, List, Tuple
 import torch
 
 
-def token_major(key_cache: torch.Tensor, value_cache: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
-    """[B, KH, D/x, BS, x] and [B, KH, D, BS] -> two [B, BS, KH, D] float64 tensors."""
+def token_major(key_cache: torch.Tensor, value_cache: torch.Tensor, k_scale: float = 1.0,
+                v_scale: float = 1.0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """[B, KH, D/x, BS, x] and [B, KH, D, BS] -> two [B, BS, KH, D] float64 tensors
+    (torch's own casts decode the stored dtype; 8-bit caches are then scaled)."""
     B, KH, Dx, BS, x = key_cache.shape
     k = key_cache.permute(0, 3, 1, 2, 4).reshape(B, BS, KH, Dx * x).to(torch.float64)
     v = value_cache.permute(0, 3, 1, 2).to(torch.float64)
-    return k, v
+    return k * float(k_scale), v * float(v_scale)
 
 
 def gathered(inp: Dict[str, object], s: int) -> Tuple[torch.Tensor, torch.Tensor]:
     """Dense [L, KH, D] float64 K and V of sequence s via the block table."""
-    k, v = token_major(inp["key_cache"], inp["value_cache"])
+    k, v = token_major(inp["key_cache"], inp["value_cache"], inp.get("k_scale", 1.0),
+                       inp.get("v_scale", 1.0))
     BS = k.shape[1]
     L = int(inp["seq_lens"][s])
     nb = -(-L // BS)
@@ -83,8 +86,8 @@ def library_partitions(inp: Dict[str, object], scale: float, P: int, PS: int):
 def brute_force_attention(inp: Dict[str, object], scale: float) -> List[List[List[float]]]:
     """Pure-Python loops on tiny inputs: nested lists, math.exp and math.fsum."""
     q = inp["query"].to(torch.float64).tolist()
-    kc = inp["key_cache"].to(torch.float64).tolist()
-    vc = inp["value_cache"].to(torch.float64).tolist()
+    kc = (inp["key_cache"].to(torch.float64) * float(inp.get("k_scale", 1.0))).tolist()
+    vc = (inp["value_cache"].to(torch.float64) * float(inp.get("v_scale", 1.0))).tolist()
     bt = inp["block_tables"].tolist()
     sl = inp["seq_lens"].tolist()
     S, H, D = len(q), len(q[0]), len(q[0][0])

@@ -10,6 +10,7 @@ import tempfile
 import pytest
 
 import oracle
+from tests import test_oracle_fp8 as FP8
 from tests import test_oracle_pins as PINS
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "paged_decode_oracle.c")
@@ -40,6 +41,19 @@ MUTANTS = [
     ("binary16_bias", "v = ldexp((double)(1024 + f), e - 25);",
      "v = ldexp((double)(1024 + f), e - 24);"),
     ("bfloat16_subnormal", "v = ldexp((double)f, -133);", "v = ldexp((double)f, -126);"),
+    ("e4m3_bias", "v = ldexp((double)(8 + f), e - 10);", "v = ldexp((double)(8 + f), e - 11);"),
+    ("e4m3_exponent_15_is_nan", "} else if (e == 15 && f == 7) {", "} else if (e == 15) {"),
+    ("e4m3_subnormal", "v = ldexp((double)f, -9);", "v = ldexp((double)f, -10);"),
+    ("k_scale_dropped", "return load_elem(pr->kc, idx, pr->kvdtype) * pr->kscale;",
+     "return load_elem(pr->kc, idx, pr->kvdtype);"),
+    ("v_scale_on_keys", "return load_elem(pr->kc, idx, pr->kvdtype) * pr->kscale;",
+     "return load_elem(pr->kc, idx, pr->kvdtype) * pr->vscale;"),
+    ("v_scale_dropped", "return load_elem(pr->vc, idx, pr->kvdtype) * pr->vscale;",
+     "return load_elem(pr->vc, idx, pr->kvdtype);"),
+    ("fp8_key_packing_8", "int32_t x = 16 / elem_size(pr->kvdtype);",
+     "int32_t x = pr->kvdtype == ORACLE_FP8_E4M3 ? 8 : 16 / elem_size(pr->kvdtype);"),
+    ("query_decoded_as_cache", "((int64_t)s * pr->H + h) * pr->D + d, pr->qdtype)",
+     "((int64_t)s * pr->H + h) * pr->D + d, pr->kvdtype)"),
 ]
 
 
@@ -56,6 +70,10 @@ def battery():
         "partition_combine": lambda: PINS.test_partition_combine_equals_dense(32),
         "zero_length": PINS.test_zero_length_gives_zero_and_sentinels,
         "gather": PINS.test_gather_indices_brute_force,
+        "e4m3": FP8.test_e4m3_decoder_exhaustive,
+        "fp8_brute_force": lambda: FP8.test_fp8_brute_force_tiny("bf16", 4, 2, 16, 2),
+        "fp8_library_dense": lambda: FP8.test_fp8_library_routine_dense("bf16", 8, 2, 128, 16, 0),
+        "fp8_repacked": FP8.test_fp8_equals_repacked_fp32_cache,
     }
     failed = []
     for name, fn in checks.items():
