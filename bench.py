@@ -77,7 +77,8 @@ def cpu_baseline(inp, W, min_seconds: float):
     runs, t_total = 0, 0.0
     while runs == 0 or t_total < min_seconds:
         t0 = time.perf_counter()
-        tmp, es, ml = oracle.partition_stats(*args, P, PS, nthreads=threads)
+        tmp, es, ml = oracle.partition_stats(*args, P, PS, nthreads=threads,
+                                             k_scale=inp["k_scale"], v_scale=inp["v_scale"])
         oracle.combine(tmp, es, ml, inp["seq_lens"], PS)
         t_total += time.perf_counter() - t0
         runs += 1
@@ -100,7 +101,7 @@ def run(args) -> dict:
 
     pa.ensure_built()
     cfg = W.CONFIGS[args.workload]
-    seed = W.CONFIG_ORDER.index(args.workload) + 1
+    seed = W.workload_seed(args.workload)
     inp = W.make_inputs(cfg, seed=seed)
     PS = args.partition_size or cfg.partition_size
     P = max(1, -(-int(inp["seq_lens"].max()) // PS))
@@ -113,8 +114,19 @@ def run(args) -> dict:
     tmp, es, ml = pa.workspace(S, H, D, P, dev)
     stream = torch.cuda.current_stream(dev)
 
+    fp8 = cfg.dtype == "fp8"
+    ks, vs = inp["k_scale"], inp["v_scale"]
+
+    def partition(tmp_, es_, ml_, PS_):
+        if fp8:
+            pa.paged_attn_v2_partition_fp8(tmp_, es_, ml_, q, kc, vc, bt, sl, inp["scale"], ks, vs,
+                                           PS_, stream)
+        else:
+            pa.paged_attn_v2_partition(tmp_, es_, ml_, q, kc, vc, bt, sl, inp["scale"], PS_,
+                                       stream)
+
     def step():
-        pa.paged_attn_v2_partition(tmp, es, ml, q, kc, vc, bt, sl, inp["scale"], PS, stream)
+        partition(tmp, es, ml, PS)
         pa.paged_attn_v2_reduce(out, tmp, es, ml, sl, PS, stream)
 
     for _ in range(args.warmup):
@@ -135,7 +147,7 @@ def run(args) -> dict:
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     for i in range(K):
         ev[i][0].record(stream)
-        pa.paged_attn_v2_partition(tmp, es, ml, q, kc, vc, bt, sl, inp["scale"], PS, stream)
+        partition(tmp, es, ml, PS)
         ev[i][1].record(stream)
         pa.paged_attn_v2_reduce(out, tmp, es, ml, sl, PS, stream)
         ev[i][2].record(stream)
@@ -153,8 +165,12 @@ def run(args) -> dict:
     tmp_t, es_t, ml_t = pa.workspace(S, H, D, P_t, dev)
 
     def step_tuned():
-        pa.paged_attn_decode(out, tmp_t, es_t, ml_t, q, kc, vc, bt, sl, inp["scale"], PS_t,
-                             stream=stream)
+        if fp8:
+            pa.paged_attn_decode_fp8(out, tmp_t, es_t, ml_t, q, kc, vc, bt, sl, inp["scale"], ks,
+                                     vs, PS_t, stream=stream)
+        else:
+            pa.paged_attn_decode(out, tmp_t, es_t, ml_t, q, kc, vc, bt, sl, inp["scale"], PS_t,
+                                 stream=stream)
 
     for _ in range(args.warmup):
         step_tuned()
@@ -170,7 +186,7 @@ def run(args) -> dict:
     step_s = elapsed / K
     gbs = kvb / step_s / 1e9
     achieved = kvb / part_avg_s / 1e9
-    kernel = ("partition_mfma_kernel" if (cfg.dtype != "f32" and 4 <= cfg.group <= 16)
+    kernel = ("partition_mfma_kernel" if (cfg.query_dtype != "f32" and 4 <= cfg.group <= 16)
               else "partition_vec_kernel")
     traffic, traffic_src = committed_traffic(args.workload, kernel)
     res = {
@@ -184,7 +200,7 @@ def run(args) -> dict:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": cfg.dtype if not fp8 else f"fp8_e4m3 cache, {cfg.query_dtype} query",
         "data": "synthetic",
         "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "qheads_tokens_per_s": round(W.qhead_tokens(inp) / step_s, 1),
@@ -196,9 +212,11 @@ def run(args) -> dict:
                          f"uniform[{cfg.len_lo},{cfg.len_hi}] seed {seed}"),
             "total_tokens": int(inp["seq_lens"].sum()), "kv_bytes_per_step": kvb,
             "num_blocks": inp["num_blocks"],
+            **({"k_scale": inp["k_scale"], "v_scale": inp["v_scale"]} if fp8 else {}),
         },
         "tuned": {
-            "entry": "paged_attn_decode", "partition_size": PS_t, "max_num_partitions": P_t,
+            "entry": "paged_attn_decode_fp8" if fp8 else "paged_attn_decode",
+            "partition_size": PS_t, "max_num_partitions": P_t,
             "partition_span": pa.partition_span(S, H, cfg.num_kv_heads, D, cfg.block_size, P_t,
                                                 PS_t, W.DTYPES[cfg.dtype]),
             "ms_per_step": round(tuned_s * 1e3, 5), "value": round(kvb / tuned_s / 1e9, 2),

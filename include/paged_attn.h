@@ -47,8 +47,11 @@ extern "C" {
 #define PA_API
 #endif
 
-/* Element types of query / key_cache / value_cache (and of `out`). */
-enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 };
+/* Element types of query / key_cache / value_cache (and of `out`).
+ * PA_FP8_E4M3 is the OCP 8-bit E4M3 format ("e4m3fn": bias 7, no infinities,
+ * largest finite 448); it is a cache type only, taken by the *_fp8 entry
+ * points below and by the two sizing queries at the end. */
+enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 };
 
 /* Status codes. */
 enum {
@@ -127,6 +130,45 @@ PA_API int paged_attn_decode(void* out, float* tmp_output, float* exp_sums, floa
                              int32_t max_blocks_per_seq, int32_t max_num_partitions,
                              int32_t partition_size, float scale, int32_t kv_dtype,
                              int32_t out_dtype, void* stream);
+
+/*
+ * 8-bit key/value caches with per-tensor scales. The page's launcher carries
+ * a cache dtype and scalar k_scale / v_scale arguments (Triton PagedAttention
+ * V2 for BI-V100, host launcher) and the head all-to-all page moves e4m3fn
+ * tensors; neither states the arithmetic, so the reading taken is the plain
+ * one: a stored key byte stands for decode(byte) * k_scale and a value byte
+ * for decode(byte) * v_scale, everything else as in the two phases above.
+ *
+ *   query        [S, H, D]           q_dtype: PA_F16 or PA_BF16
+ *   key_cache    [B, KH, D/16, BS, 16] E4M3 bytes (x = 16 / 1)
+ *   value_cache  [B, KH, D, BS]      E4M3 bytes
+ *   k_scale, v_scale                 finite fp32 scalars (PA_ERR_SHAPE otherwise)
+ *   outputs as above (fp32 tmp_output / exp_sums / max_logits); the reduce is
+ *   the ordinary paged_attn_v2_reduce; out_dtype of the decode is PA_F32 or
+ *   q_dtype. Stored NaN bytes in slots the sequences reference are not
+ *   covered; slots past a sequence's length may hold anything.
+ * The same errors as the 16-bit calls; the plain entry points reject
+ * kv_dtype == PA_FP8_E4M3 with PA_ERR_UNSUPPORTED.
+ */
+PA_API int paged_attn_v2_partition_fp8(float* tmp_output, float* exp_sums, float* max_logits,
+                                       const void* query, const void* key_cache,
+                                       const void* value_cache, const int32_t* block_tables,
+                                       const int32_t* seq_lens, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_size, int32_t block_size, int32_t num_blocks,
+                                       int32_t max_blocks_per_seq, int32_t max_num_partitions,
+                                       int32_t partition_size, float scale, float k_scale,
+                                       float v_scale, int32_t q_dtype, void* stream);
+
+PA_API int paged_attn_decode_fp8(void* out, float* tmp_output, float* exp_sums,
+                                 float* max_logits, const void* query, const void* key_cache,
+                                 const void* value_cache, const int32_t* block_tables,
+                                 const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                 int32_t num_blocks, int32_t max_blocks_per_seq,
+                                 int32_t max_num_partitions, int32_t partition_size, float scale,
+                                 float k_scale, float v_scale, int32_t q_dtype, int32_t out_dtype,
+                                 void* stream);
 
 /* Text of the last nonzero return on this thread ("" if none). Owned by the
  * library; valid until the next call on the same thread. */

@@ -14,9 +14,10 @@ from typing import Optional
 
 import torch  # noqa: F401  (load torch's HIP runtime first so both share one runtime)
 
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_ALIGN, PA_ERR_HIP = 0, -1, -2, -3, -4, -5
 _DT = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+_CACHE_DT = {**_DT, torch.float8_e4m3fn: PA_FP8_E4M3}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpaged_attn.so")
 _LIB = None
@@ -30,6 +31,8 @@ _SIGS = {
     "paged_attn_abi_version": [],
     "paged_attn_default_partition_size": [_I32, _I32, _I32, _I32],
     "paged_attn_partition_span": [_I32] * 8,
+    "paged_attn_v2_partition_fp8": [_P] * 8 + [_I32] * 9 + [_F32, _F32, _F32, _I32, _P],
+    "paged_attn_decode_fp8": [_P] * 9 + [_I32] * 9 + [_F32, _F32, _F32, _I32, _I32, _P],
 }
 
 
@@ -59,7 +62,7 @@ def abi_version() -> int:
 
 
 def default_partition_size(head_size: int, block_size: int, dtype: torch.dtype, group: int) -> int:
-    rc = lib().paged_attn_default_partition_size(head_size, block_size, _DT[dtype], group)
+    rc = lib().paged_attn_default_partition_size(head_size, block_size, _CACHE_DT[dtype], group)
     if rc < 0:
         raise RuntimeError(f"paged_attn_default_partition_size: {last_error()} (code {rc})")
     return rc
@@ -70,7 +73,7 @@ def partition_span(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: 
                    dtype: torch.dtype) -> int:
     """Partitions per workgroup the launchers use for these sizes (plan inspection)."""
     rc = lib().paged_attn_partition_span(num_seqs, num_heads, num_kv_heads, head_size, block_size,
-                                         max_num_partitions, partition_size, _DT[dtype])
+                                         max_num_partitions, partition_size, _CACHE_DT[dtype])
     if rc < 0:
         raise RuntimeError(f"paged_attn_partition_span: {last_error()} (code {rc})")
     return rc
@@ -92,18 +95,26 @@ def _need(cond: bool, msg: str) -> None:
         raise ValueError(msg)
 
 
-def _kv_geometry(query, key_cache, value_cache, block_tables, seq_lens):
+def _kv_geometry(query, key_cache, value_cache, block_tables, seq_lens, fp8: bool = False):
     _need(query.dim() == 3 and key_cache.dim() == 5 and value_cache.dim() == 4,
           "query [S,H,D], key_cache [B,KH,D/x,BS,x], value_cache [B,KH,D,BS] expected")
-    _need(query.dtype in _DT and key_cache.dtype == query.dtype and value_cache.dtype == query.dtype,
-          "query, key_cache and value_cache must share one dtype (f32, f16 or bf16)")
+    if fp8:
+        _need(query.dtype in (torch.float16, torch.bfloat16) and
+              key_cache.dtype == torch.float8_e4m3fn and value_cache.dtype == torch.float8_e4m3fn,
+              "the fp8 calls take an f16/bf16 query and float8_e4m3fn key/value caches")
+    else:
+        _need(query.dtype in _DT and key_cache.dtype == query.dtype and
+              value_cache.dtype == query.dtype,
+              "query, key_cache and value_cache must share one dtype (f32, f16 or bf16); "
+              "float8_e4m3fn caches go through the *_fp8 calls")
     _need(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32,
           "block_tables and seq_lens must be int32")
     for t in (query, key_cache, value_cache, block_tables, seq_lens):
         _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
     S, H, D = query.shape
     B, KH, Dx, BS, x = key_cache.shape
-    _need(x == 16 // query.element_size() and Dx * x == D, "key_cache packing must be x = 16/sizeof")
+    _need(x == 16 // key_cache.element_size() and Dx * x == D,
+          "key_cache packing must be x = 16/sizeof(cache element)")
     _need(tuple(value_cache.shape) == (B, KH, D, BS), "value_cache shape mismatch")
     _need(block_tables.dim() == 2 and block_tables.shape[0] == S and seq_lens.shape == (S,),
           "block_tables [S, MB] and seq_lens [S] expected")
@@ -165,6 +176,38 @@ def paged_attn_decode(out, tmp_output, exp_sums, max_logits, query, key_cache, v
         seq_lens.data_ptr(), S, H, KH, D, BS, B, MB, P, partition_size, float(scale),
         _DT[query.dtype], _DT[out.dtype], _stream(query, stream))
     _check("paged_attn_decode", rc)
+
+
+def paged_attn_v2_partition_fp8(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                                block_tables, seq_lens, scale: float, k_scale: float,
+                                v_scale: float, partition_size: int, stream=None) -> None:
+    """Phase 1 over float8_e4m3fn caches (key = byte * k_scale, value = byte * v_scale)."""
+    S, H, KH, D, BS, B, MB = _kv_geometry(query, key_cache, value_cache, block_tables, seq_lens,
+                                          fp8=True)
+    P = _stats_geometry(tmp_output, exp_sums, max_logits, S, H, D)
+    rc = lib().paged_attn_v2_partition_fp8(
+        tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(), query.data_ptr(),
+        key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+        seq_lens.data_ptr(), S, H, KH, D, BS, B, MB, P, partition_size, float(scale),
+        float(k_scale), float(v_scale), _DT[query.dtype], _stream(query, stream))
+    _check("paged_attn_v2_partition_fp8", rc)
+
+
+def paged_attn_decode_fp8(out, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                          block_tables, seq_lens, scale: float, k_scale: float, v_scale: float,
+                          partition_size: int, stream=None) -> None:
+    """Phase 1 then phase 2 over float8_e4m3fn caches, on one stream."""
+    S, H, KH, D, BS, B, MB = _kv_geometry(query, key_cache, value_cache, block_tables, seq_lens,
+                                          fp8=True)
+    P = _stats_geometry(tmp_output, exp_sums, max_logits, S, H, D)
+    _need(out.dim() == 3 and tuple(out.shape) == (S, H, D) and out.dtype in _DT and out.is_cuda
+          and out.is_contiguous(), "out must be a contiguous [S, H, D] device tensor")
+    rc = lib().paged_attn_decode_fp8(
+        out.data_ptr(), tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
+        query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+        seq_lens.data_ptr(), S, H, KH, D, BS, B, MB, P, partition_size, float(scale),
+        float(k_scale), float(v_scale), _DT[query.dtype], _DT[out.dtype], _stream(query, stream))
+    _check("paged_attn_decode_fp8", rc)
 
 
 def workspace(num_seqs: int, num_heads: int, head_size: int, max_num_partitions: int,

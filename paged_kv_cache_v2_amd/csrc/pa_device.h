@@ -7,9 +7,10 @@
 
 namespace pa {
 
-enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };  // DT_FP8: OCP E4M3 (e4m3fn)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -67,6 +68,29 @@ template <> struct codec<DT_F16> {
   }
 };
 
+// ---------------------------------------------------------------- 8-bit caches
+// OCP FP8 E4M3 bytes, four per 32-bit word (element 0 in the low byte). Every
+// E4M3 value (subnormals included) is exactly representable in bf16 and in
+// f16, and gfx950's conversions decode exactly this format (checked on every
+// code by the GPU tests), so a cache page converted to the query's 16-bit
+// type feeds the same MFMA / dot2 arithmetic as a 16-bit cache.
+template <int DT> struct fp8cvt;
+template <> struct fp8cvt<DT_BF16> {
+  // Elements 2*HI, 2*HI+1 of w -> two packed bf16 (v_cvt_scalef32_pk_bf16_fp8, scale 1).
+  template <bool HI> static __device__ __forceinline__ uint32_t pair(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  }
+};
+template <> struct fp8cvt<DT_F16> {
+  template <bool HI> static __device__ __forceinline__ uint32_t pair(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+  }
+};
+// Elements 2*HI, 2*HI+1 of w as two floats (v_cvt_pk_f32_fp8).
+template <bool HI> __device__ __forceinline__ f32x2 fp8_pair_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+
 // ---------------------------------------------------------------- MFMA
 // QK: 16x16x32 (A = 16 token rows x 32 d, B = 32 d x 16 head columns).
 // PV: 16x16x16 (A = 16 d rows x 16 tokens, B = 16 tokens x 16 head columns).
@@ -100,14 +124,37 @@ template <> struct mma<DT_F16> {
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// Exchange across 16-lane rows with gfx950's v_permlane16_swap / v_permlane32_swap
+// (register-to-register, no LDS round trip). Called with the same value in
+// both operands, each returns, in every lane l, the pair (x_a, x_b) = the
+// values of lanes {l, l ^ 16} (resp. {l, l ^ 32}) with a the lower of the two
+// lanes -- the same operands in the same order in both lanes of the pair, so a
+// reduction step gives both lanes the identical result.
+__device__ __forceinline__ void pair16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
 // Max / sum over the four 16-lane rows of a wavefront (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float rows_max(float v) {
-  v = fmaxf(v, shfl_xor(v, 16));
-  return fmaxf(v, shfl_xor(v, 32));
+  float a, b;
+  pair16(v, a, b);
+  pair32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float rows_sum(float v) {
-  v += shfl_xor(v, 16);
-  return v + shfl_xor(v, 32);
+  float a, b;
+  pair16(v, a, b);
+  pair32(a + b, a, b);
+  return a + b;
 }
 // Max / sum within each 16-lane row.
 __device__ __forceinline__ float row16_max(float v) {
@@ -133,6 +180,16 @@ __device__ __forceinline__ float lane_value(float v, int src) {
 
 // Element e of a lane's run of tokens is a real token iff e < nvalid.
 __device__ __forceinline__ bool e_valid(int e, int nvalid) { return e < nvalid; }
+
+// Zero the bytes of a word at positions >= nvalid (0..4): the 8-bit-cache form
+// of keep_first.
+__device__ __forceinline__ uint32_t keep_first_bytes(uint32_t w, int nvalid) {
+  const uint32_t m = nvalid >= 4 ? 0xffffffffu : nvalid <= 0 ? 0u : (1u << (8 * nvalid)) - 1u;
+  return w & m;
+}
+
+// True in every lane if cond holds in any active lane (wavefront-uniform).
+__device__ __forceinline__ bool any_lane(bool cond) { return __builtin_amdgcn_ballot_w64(cond) != 0; }
 
 // Zero the 16-bit elements of a packed pair of words at positions >= nvalid (0..4).
 __device__ __forceinline__ u32x2 keep_first(u32x2 v, int nvalid) {

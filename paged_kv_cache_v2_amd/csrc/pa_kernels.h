@@ -47,6 +47,8 @@
 //    cache slots cannot leak.
 #pragma once
 
+#include <type_traits>
+
 #include "pa_device.h"
 
 namespace pa {
@@ -157,7 +159,8 @@ struct PartitionArgs {
   int NB;          // physical blocks; block-table entries are clamped into [0, NB)
   int C;           // consecutive partitions per workgroup (span), 1 .. kMaxSpan
   int through;     // 1: tmp_output stores with device-scope (sc1) policy
-  float qk_scale;  // scale * log2(e)
+  float qk_scale;  // scale * log2(e) (times k_scale for an 8-bit cache)
+  float v_scale;   // 1, or v_scale for an 8-bit cache (applied once, at the merge)
 };
 
 constexpr int kMaxSpan = 2;
@@ -228,7 +231,7 @@ __device__ __forceinline__ void merge_store(const PartitionArgs& a, const float*
       const f32x4 v = *(const f32x4*)&s_acc[k * D + 4 * d4];
       o += e * v;
     }
-    const float inv = 1.0f / Z;
+    const float inv = a.v_scale / Z;
     const size_t row = ((size_t)s * a.H + kh * G + g) * a.P + p0 + j;
     store_row(tmp, (uint32_t)(((g * a.P + p0 + j) * D + 4 * d4) * 4), o * inv, a.through);
     if (d4 == 0) {
@@ -290,25 +293,62 @@ __device__ __forceinline__ bool unit_hoist(const PartitionArgs& a, int32_t* s_bt
 }
 
 // =====================================================================
-// MFMA path: 16-bit K/V, G in [4, 16] query heads per kv head.
+// MFMA path: 16-bit query, G in [4, 16] query heads per kv head; the cache is
+// 16-bit (KV8 = false) or OCP E4M3 bytes converted to the query's type in
+// registers (KV8 = true).
 // QK^T per 16-token sub-tile: D/32 MFMA 16x16x32, token rows x head columns
 // (heads >= G are zero-padded). The fp32 C tile (lane l: tokens 4*(l/16)+r,
 // head l%16) is exactly the B operand layout of a 16x16x16 MFMA with tokens as
-// k, so P feeds PV without any data movement. V is read as 8-byte pieces (4
-// tokens of one d) that form the matching A operand. P is split into a 16-bit
-// high part and a 16-bit residual (two PV MFMAs) so the probabilities keep
-// ~16 bits of mantissa instead of bf16's 8.
+// k, so P feeds PV without any data movement. V is read as 4 tokens of one d
+// (8 bytes, or 4 bytes for an 8-bit cache) that form the matching A operand.
+// P is split into a 16-bit high part and a 16-bit residual (two PV MFMAs) so
+// the probabilities keep ~16 bits of mantissa instead of bf16's 8.
+// K k-steps: a 16-bit cache chunk is 8 d of one token (one k-step per 16-byte
+// load); an 8-bit chunk is 16 d (two k-steps per load: its low and high 8 d).
+// The query B operand follows the same d assignment, so the contraction over
+// d is unchanged.
 // =====================================================================
-template <int DT, int D, int BS>
-__global__ void __launch_bounds__(kWaves * 64) PA_OCCUPANCY
+template <bool KV8, int SUB, int D> struct MfmaPage {
+  u32x4 k[SUB][D / 32];  // 16-bit K: one 16-byte load per k-step
+  u32x2 v[SUB][D / 16];  // 16-bit V: 4 tokens x 2 bytes per d-block
+};
+template <int SUB, int D> struct MfmaPage<true, SUB, D> {
+  u32x4 k[SUB][D / 64];  // 8-bit K: one 16-byte load per two k-steps
+  uint32_t v[SUB][D / 16];  // 8-bit V: 4 tokens x 1 byte per d-block
+};
+
+// Pages in flight for an 8-bit cache page of `page_regs` VGPRs. An 8-bit page
+// carries twice the arithmetic per byte of a 16-bit one, so occupancy matters
+// more than depth (three pages ahead at 2 wavefronts per SIMD measured ~20 %
+// slower than one page ahead at 3 or 4): one page ahead for small pages,
+// none for larger ones.
+#ifndef PA_PREFETCH_FP8
+#define PA_PREFETCH_FP8 1
+#endif
+constexpr int prefetch_fp8(int page_regs) { return page_regs <= 16 ? PA_PREFETCH_FP8 : 0; }
+
+// Wavefronts per SIMD the 8-bit MFMA kernel is register-budgeted for: its
+// pages carry twice the arithmetic per byte of a 16-bit cache's, so latency
+// hiding needs more resident wavefronts (D = 128, BS = 16: 4 per SIMD
+// measured ~10 % faster than 3 and ~25 % faster than 2). Larger pages need
+// more registers; the budget shrinks so that nothing spills.
+constexpr int fp8_waves(int D, int BS) { return D * BS <= 2048 ? 4 : D <= 128 ? 3 : 2; }
+
+template <int DT, int D, int BS, bool KV8>
+__global__ void __launch_bounds__(kWaves * 64)
+__attribute__((amdgpu_waves_per_eu(KV8 ? fp8_waves(D, BS) : (PA_MIN_WAVES > 0 ? PA_MIN_WAVES : 1))))
 partition_mfma_kernel(PartitionArgs a) {
   constexpr int SUB = BS / 16;  // 16-token sub-tiles per page
-  constexpr int KJ = D / 32;    // K dwordx4 per lane per sub-tile = QK k-steps
-  constexpr int VB = D / 16;    // V dwordx2 per lane per sub-tile = PV d-blocks
-  constexpr size_t PAGE = (size_t)D * BS * 2;  // bytes of one (block, kv head) page
-  constexpr int PF = prefetch_for(SUB * (KJ * 4 + VB * 2));
+  constexpr int KS = D / 32;    // QK k-steps (32 d each) per sub-tile
+  constexpr int KL = KV8 ? D / 64 : D / 32;  // K 16-byte loads per lane per sub-tile
+  constexpr int VB = D / 16;    // PV d-blocks (16 d each)
+  constexpr int ESZ = KV8 ? 1 : 2;
+  constexpr size_t PAGE = (size_t)D * BS * ESZ;  // bytes of one (block, kv head) page
+  constexpr int PREGS = SUB * (KL * 4 + VB * (KV8 ? 1 : 2));
+  constexpr int PF = KV8 ? prefetch_fp8(PREGS) : prefetch_for(PREGS);
   using C = codec<DT>;
   using M = mma<DT>;
+  using Page = MfmaPage<KV8, SUB, D>;
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   Unit u;
@@ -317,15 +357,17 @@ partition_mfma_kernel(PartitionArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane & 15, grp = lane >> 4;
 
-  // Q group as the QK B operand: lane holds q[head g][32j + 8*grp .. +7].
-  u32x4 qb[KJ];
+  // Q group as the QK B operand, k-step m: lane holds 8 consecutive d of head
+  // g, d = 32m + 8*grp (16-bit cache) or 16*(4*(m/2) + grp) + 8*(m%2) (8-bit).
+  u32x4 qb[KS];
   {
     const uint16_t* qrow =
         (const uint16_t*)a.q + ((size_t)u.s * a.H + u.kh * G + (g < G ? g : 0)) * D;
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) {
-      u32x4 v = *(const u32x4*)(qrow + 32 * j + 8 * grp);
-      qb[j] = g < G ? v : u32x4{0u, 0u, 0u, 0u};
+    for (int m = 0; m < KS; ++m) {
+      const int d0 = KV8 ? 16 * (4 * (m / 2) + grp) + 8 * (m % 2) : 32 * m + 8 * grp;
+      u32x4 v = *(const u32x4*)(qrow + d0);
+      qb[m] = g < G ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
   if (!unit_hoist<BS>(a, (int32_t*)smem, u)) return;
@@ -340,8 +382,10 @@ partition_mfma_kernel(PartitionArgs a) {
   const size_t blk_stride = (size_t)a.KH * PAGE;
   const uint8_t* kbase = (const uint8_t*)a.kc + head_off;
   const uint8_t* vbase = (const uint8_t*)a.vc + head_off;
-  const uint32_t k_lane = (uint32_t)(grp * BS + g) * 16;     // + j*4*BS*16 + st*256
-  const uint32_t v_lane = (uint32_t)(g * BS + 4 * grp) * 2;  // + mb*16*BS*2 + st*32
+  // K: chunk c = 4j + grp of token g at (c*BS + g)*16 bytes (+ st*256).
+  const uint32_t k_lane = (uint32_t)(grp * BS + g) * 16;
+  // V: d-row 16*mb + g, tokens 16*st + 4*grp .. +3.
+  const uint32_t v_lane = (uint32_t)(g * BS + 4 * grp) * ESZ;
 
   const int npg = u.npages > wave ? (u.npages - wave + kWaves - 1) / kWaves : 0;
 
@@ -377,16 +421,12 @@ partition_mfma_kernel(PartitionArgs a) {
     next_edge += pps;
   };
 
-  struct Page {
-    u32x4 k[SUB][KJ];
-    u32x2 v[SUB][VB];
-  };
   auto fetch = [&](int i, Page& pg) {
     const int blk = min(max(__builtin_amdgcn_readfirstlane(s_bt[wave + i * kWaves]), 0), a.NB - 1);
     const uint8_t* kp = kbase + (size_t)blk * blk_stride + k_lane;
     const uint8_t* vp = vbase + (size_t)blk * blk_stride + v_lane;
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) {
+    for (int j = 0; j < KL; ++j) {
 #pragma unroll
       for (int st = 0; st < SUB; ++st)
         pg.k[st][j] = stream_load<u32x4>(kp + j * 4 * BS * 16 + st * 256);
@@ -394,8 +434,34 @@ partition_mfma_kernel(PartitionArgs a) {
 #pragma unroll
     for (int mb = 0; mb < VB; ++mb) {
 #pragma unroll
-      for (int st = 0; st < SUB; ++st)
-        pg.v[st][mb] = stream_load<u32x2>(vp + mb * 16 * BS * 2 + st * 32);
+      for (int st = 0; st < SUB; ++st) {
+        if constexpr (KV8)
+          pg.v[st][mb] = stream_load<uint32_t>(vp + mb * 16 * BS + st * 16);
+        else
+          pg.v[st][mb] = stream_load<u32x2>(vp + mb * 16 * BS * 2 + st * 32);
+      }
+    }
+  };
+
+  // A operand of QK k-step mk of sub-tile st (8-bit: low or high 8 d of a chunk).
+  auto k_operand = [&](const Page& pg, int st, int mk) -> u32x4 {
+    if constexpr (KV8) {
+      using F = fp8cvt<DT>;
+      const u32x4 w = pg.k[st][mk / 2];
+      const uint32_t w0 = (mk % 2) ? w[2] : w[0], w1 = (mk % 2) ? w[3] : w[1];
+      return u32x4{F::template pair<false>(w0), F::template pair<true>(w0),
+                   F::template pair<false>(w1), F::template pair<true>(w1)};
+    } else {
+      return pg.k[st][mk];
+    }
+  };
+  using VWord = typename std::remove_reference<decltype(Page::v[0][0])>::type;
+  auto v_operand = [&](VWord w) -> u32x2 {
+    if constexpr (KV8) {
+      using F = fp8cvt<DT>;
+      return u32x2{F::template pair<false>(w), F::template pair<true>(w)};
+    } else {
+      return w;
     }
   };
 
@@ -408,7 +474,7 @@ partition_mfma_kernel(PartitionArgs a) {
     for (int st = 0; st < SUB; ++st) {
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < KJ; ++j) sc = M::qk(pg.k[st][j], qb[j], sc);
+      for (int mk = 0; mk < KS; ++mk) sc = M::qk(k_operand(pg, st, mk), qb[mk], sc);
       const int nvalid = u.L - (tok0 + 16 * st + 4 * grp);  // row 4*grp+r valid iff r < nvalid
 #pragma unroll
       for (int r = 0; r < 4; ++r) s2[st][r] = r < nvalid ? sc[r] * a.qk_scale : kNegInf;
@@ -436,14 +502,40 @@ partition_mfma_kernel(PartitionArgs a) {
                       C::pack(pr[2] - C::lo(h23), pr[3] - C::hi(h23))};
     }
     lsum = lsum * alpha + psum;
-    const bool partial = tok0 + BS > u.L;  // wavefront-uniform
+    // Rescale the accumulator only if some head's running max moved: alpha is
+    // exactly 1 otherwise, so skipping is bit-identical and saves 4*VB
+    // multiplies on most pages.
+    if (any_lane(alpha != 1.0f)) {
 #pragma unroll
-    for (int mb = 0; mb < VB; ++mb) {
-      acc[mb] *= alpha;
+      for (int mb = 0; mb < VB; ++mb) acc[mb] *= alpha;
+    }
+    // V tail slots past the sequence end are zeroed (selected, never multiplied
+    // by a zero weight: they may hold NaN). Only the last page of a sequence is
+    // partial, so the masking is a separate, wavefront-uniform branch.
+    VWord vw[SUB][VB];
+#pragma unroll
+    for (int st = 0; st < SUB; ++st) {
+#pragma unroll
+      for (int mb = 0; mb < VB; ++mb) vw[st][mb] = pg.v[st][mb];
+    }
+    if (tok0 + BS > u.L) {
 #pragma unroll
       for (int st = 0; st < SUB; ++st) {
-        const u32x2 v = partial ? keep_first(pg.v[st][mb], u.L - (tok0 + 16 * st + 4 * grp))
-                                : pg.v[st][mb];
+        const int nv = u.L - (tok0 + 16 * st + 4 * grp);  // valid among this lane's 4 tokens
+#pragma unroll
+        for (int mb = 0; mb < VB; ++mb) {
+          if constexpr (KV8)
+            vw[st][mb] = keep_first_bytes(vw[st][mb], nv);
+          else
+            vw[st][mb] = keep_first(vw[st][mb], nv);
+        }
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < VB; ++mb) {
+#pragma unroll
+      for (int st = 0; st < SUB; ++st) {
+        const u32x2 v = v_operand(vw[st][mb]);
         acc[mb] = M::pv(v, phi[st], acc[mb]);
         acc[mb] = M::pv(v, plo[st], acc[mb]);
       }
@@ -459,6 +551,8 @@ partition_mfma_kernel(PartitionArgs a) {
 
 // =====================================================================
 // Vector path: any kv dtype, G <= GM query heads per kv head (GM in 1, 2, 4).
+// An 8-bit cache (KV8) has 16 elements per 16-byte chunk: K words are
+// converted to the query's 16-bit pairs for v_dot2, V bytes to fp32.
 // QK: each lane dots its d-chunks of one token with the packed query
 // (v_dot2 for 16-bit, fma for fp32), then a sum across the four 16-lane rows.
 // PV: lane l owns X consecutive tokens (one 16-byte V chunk) of one d; the
@@ -472,11 +566,13 @@ template <> struct vec_elem<DT_F32> {
   static constexpr int X = 4;
 };
 
-template <int DT, int D, int BS, int GM>
+template <int DT, int D, int BS, int GM, bool KV8>
 __global__ void __launch_bounds__(kWaves * 64) PA_OCCUPANCY
 partition_vec_kernel(PartitionArgs a) {
-  constexpr int X = vec_elem<DT>::X;
-  constexpr int ESZ = 16 / X;
+  constexpr int X = KV8 ? 16 : vec_elem<DT>::X;  // cache elements per 16-byte chunk
+  constexpr int ESZ = 16 / X;                     // cache element bytes
+  constexpr int QSZ = DT == DT_F32 ? 4 : 2;       // query element bytes
+  constexpr int QW = X * QSZ / 4;                 // query words per K chunk
   constexpr int SUB = BS / 16;       // 16-token sub-tiles per page
   constexpr int KJ = D / X / 4;      // K chunks per lane per sub-tile (c = 4j + row)
   constexpr int CPS = 16 / X;        // V chunks per d-row of one sub-tile
@@ -484,7 +580,8 @@ partition_vec_kernel(PartitionArgs a) {
   constexpr int DPL = 64 / CPR;      // d distance between one lane's V chunks
   constexpr int VJ = D / DPL;        // V chunks per lane per page
   constexpr size_t PAGE = (size_t)D * BS * ESZ;
-  constexpr int PF = prefetch_for((SUB * KJ + VJ) * 4);
+  constexpr int PREGS = (SUB * KJ + VJ) * 4;
+  constexpr int PF = KV8 ? prefetch_fp8(PREGS) : prefetch_for(PREGS);
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   Unit u;
@@ -495,17 +592,21 @@ partition_vec_kernel(PartitionArgs a) {
   const int t = lane & 15, grp = lane >> 4;     // K: token, chunk row
   const int h = lane % CPR, dl = lane / CPR;    // V: token chunk, d offset
 
-  // Query d-chunks c = 4j + grp of each head, as raw 32-bit words.
-  uint32_t qw[GM][KJ][4];
+  // Query d-chunks c = 4j + grp of each head (the d of K chunk c), as raw
+  // 32-bit words: 16 bytes per chunk, or 32 for an 8-bit cache's 16-d chunks.
+  uint32_t qw[GM][KJ][QW];
 #pragma unroll
   for (int gg = 0; gg < GM; ++gg) {
     const int hh = gg < G ? gg : 0;
-    const uint8_t* qrow = (const uint8_t*)a.q + (((size_t)u.s * a.H + u.kh * G + hh) * D) * ESZ;
+    const uint8_t* qrow = (const uint8_t*)a.q + (((size_t)u.s * a.H + u.kh * G + hh) * D) * QSZ;
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
-      const u32x4 v = *(const u32x4*)(qrow + (4 * j + grp) * 16);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) qw[gg][j][w] = gg < G ? v[w] : 0u;
+      for (int q4 = 0; q4 < QW / 4; ++q4) {
+        const u32x4 v = *(const u32x4*)(qrow + (4 * j + grp) * X * QSZ + 16 * q4);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) qw[gg][j][4 * q4 + w] = gg < G ? v[w] : 0u;
+      }
     }
   }
   if (!unit_hoist<BS>(a, (int32_t*)smem, u)) return;
@@ -602,7 +703,12 @@ partition_vec_kernel(PartitionArgs a) {
         for (int j = 0; j < KJ; ++j) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            if constexpr (DT == DT_F32) {
+            if constexpr (KV8) {
+              // word w holds d 4w .. 4w+3 of the chunk: two 16-bit pairs
+              const uint32_t kw = pg.k[st][j][w];
+              dot = codec<DT>::dot2(fp8cvt<DT>::template pair<false>(kw), qw[gg][j][2 * w], dot);
+              dot = codec<DT>::dot2(fp8cvt<DT>::template pair<true>(kw), qw[gg][j][2 * w + 1], dot);
+            } else if constexpr (DT == DT_F32) {
               dot = fmaf(__uint_as_float(pg.k[st][j][w]), __uint_as_float(qw[gg][j][w]), dot);
             } else {
               dot = codec<DT>::dot2(pg.k[st][j][w], qw[gg][j][w], dot);
@@ -625,8 +731,10 @@ partition_vec_kernel(PartitionArgs a) {
       }
       lpart[gg] = lpart[gg] * alpha + ps;
       m[gg] = mn;
+      if (any_lane(alpha != 1.0f)) {  // skipping a multiply by exactly 1 is bit-identical
 #pragma unroll
-      for (int j = 0; j < VJ; ++j) acc[gg][j] *= alpha;
+        for (int j = 0; j < VJ; ++j) acc[gg][j] *= alpha;
+      }
     }
     const int nv = u.L - (tok0 + h * X);  // valid tokens among this lane's X
 #pragma unroll
@@ -645,7 +753,17 @@ partition_vec_kernel(PartitionArgs a) {
         float sum = acc[gg][j];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          if constexpr (DT == DT_F32) {
+          if constexpr (KV8) {
+            const f32x2 lo = fp8_pair_f32<false>(pg.v[j][w]), hi = fp8_pair_f32<true>(pg.v[j][w]);
+            const float v0 = e_valid(4 * w, nv) ? lo[0] : 0.0f;
+            const float v1 = e_valid(4 * w + 1, nv) ? lo[1] : 0.0f;
+            const float v2 = e_valid(4 * w + 2, nv) ? hi[0] : 0.0f;
+            const float v3 = e_valid(4 * w + 3, nv) ? hi[1] : 0.0f;
+            sum = fmaf(pw[4 * w], v0, sum);
+            sum = fmaf(pw[4 * w + 1], v1, sum);
+            sum = fmaf(pw[4 * w + 2], v2, sum);
+            sum = fmaf(pw[4 * w + 3], v3, sum);
+          } else if constexpr (DT == DT_F32) {
             const float v = e_valid(w, nv) ? __uint_as_float(pg.v[j][w]) : 0.0f;
             sum = fmaf(pw[w], v, sum);
           } else {

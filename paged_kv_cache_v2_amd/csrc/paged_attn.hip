@@ -29,7 +29,8 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-int elem_size(int32_t dt) { return dt == PA_F32 ? 4 : 2; }
+int elem_size(int32_t dt) { return dt == PA_F32 ? 4 : dt == PA_FP8_E4M3 ? 1 : 2; }
+bool is_16bit(int32_t dt) { return dt == PA_F16 || dt == PA_BF16; }
 
 using pa::PartitionArgs;
 using pa::ReduceArgs;
@@ -40,10 +41,10 @@ int d_index(int D) { return D == 64 ? 0 : D == 128 ? 1 : D == 256 ? 2 : -1; }
 int bs_index(int BS) { return BS == 16 ? 0 : BS == 32 ? 1 : -1; }
 
 // ---------------------------------------------------------------- kernel tables
-template <int DT, int D, int BS>
-constexpr partition_fn mfma_k() { return pa::partition_mfma_kernel<DT, D, BS>; }
-template <int DT, int D, int BS, int GM>
-constexpr partition_fn vec_k() { return pa::partition_vec_kernel<DT, D, BS, GM>; }
+template <int DT, int D, int BS, bool KV8 = false>
+constexpr partition_fn mfma_k() { return pa::partition_mfma_kernel<DT, D, BS, KV8>; }
+template <int DT, int D, int BS, int GM, bool KV8 = false>
+constexpr partition_fn vec_k() { return pa::partition_vec_kernel<DT, D, BS, GM, KV8>; }
 
 // [dtype 1..2 -> 0..1][D][BS]
 const partition_fn kMfma[2][3][2] = {
@@ -55,12 +56,25 @@ const partition_fn kMfma[2][3][2] = {
      {mfma_k<pa::DT_BF16, 256, 16>(), mfma_k<pa::DT_BF16, 256, 32>()}},
 };
 
-#define PA_VEC_GM(DT, D, BS) {vec_k<DT, D, BS, 1>(), vec_k<DT, D, BS, 2>(), vec_k<DT, D, BS, 4>()}
-#define PA_VEC_BS(DT, D) {PA_VEC_GM(DT, D, 16), PA_VEC_GM(DT, D, 32)}
-#define PA_VEC_D(DT) {PA_VEC_BS(DT, 64), PA_VEC_BS(DT, 128), PA_VEC_BS(DT, 256)}
+// 8-bit (E4M3) caches, [query dtype f16 / bf16][D][BS]
+const partition_fn kMfma8[2][3][2] = {
+    {{mfma_k<pa::DT_F16, 64, 16, true>(), mfma_k<pa::DT_F16, 64, 32, true>()},
+     {mfma_k<pa::DT_F16, 128, 16, true>(), mfma_k<pa::DT_F16, 128, 32, true>()},
+     {mfma_k<pa::DT_F16, 256, 16, true>(), mfma_k<pa::DT_F16, 256, 32, true>()}},
+    {{mfma_k<pa::DT_BF16, 64, 16, true>(), mfma_k<pa::DT_BF16, 64, 32, true>()},
+     {mfma_k<pa::DT_BF16, 128, 16, true>(), mfma_k<pa::DT_BF16, 128, 32, true>()},
+     {mfma_k<pa::DT_BF16, 256, 16, true>(), mfma_k<pa::DT_BF16, 256, 32, true>()}},
+};
+
+#define PA_VEC_GM(DT, D, BS, K8) \
+  {vec_k<DT, D, BS, 1, K8>(), vec_k<DT, D, BS, 2, K8>(), vec_k<DT, D, BS, 4, K8>()}
+#define PA_VEC_BS(DT, D, K8) {PA_VEC_GM(DT, D, 16, K8), PA_VEC_GM(DT, D, 32, K8)}
+#define PA_VEC_D(DT, K8) {PA_VEC_BS(DT, 64, K8), PA_VEC_BS(DT, 128, K8), PA_VEC_BS(DT, 256, K8)}
 // [dtype][D][BS][GM = 1, 2, 4]
-const partition_fn kVec[3][3][2][3] = {PA_VEC_D(pa::DT_F32), PA_VEC_D(pa::DT_F16),
-                                       PA_VEC_D(pa::DT_BF16)};
+const partition_fn kVec[3][3][2][3] = {PA_VEC_D(pa::DT_F32, false), PA_VEC_D(pa::DT_F16, false),
+                                       PA_VEC_D(pa::DT_BF16, false)};
+// 8-bit caches, [query dtype f16 / bf16][D][BS][GM]
+const partition_fn kVec8[2][3][2][3] = {PA_VEC_D(pa::DT_F16, true), PA_VEC_D(pa::DT_BF16, true)};
 #undef PA_VEC_D
 #undef PA_VEC_BS
 #undef PA_VEC_GM
@@ -132,24 +146,31 @@ int pick_span(int S, int KH, int P, int PS, int BS, int G, int D, int esz, int l
   return best;
 }
 
-// Host checks shared by the partition entry points; fills `plan`.
+// Host checks shared by the partition entry points; fills `plan`. The query
+// has dtype qdt; the caches kvdt (== qdt, or PA_FP8_E4M3 with a 16-bit query).
 int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const void* query,
                     const void* key_cache, const void* value_cache, const int32_t* block_tables,
                     const int32_t* seq_lens, int32_t S, int32_t H, int32_t KH, int32_t D,
-                    int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS, int32_t dt,
-                    Plan* plan) {
+                    int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS, int32_t qdt,
+                    int32_t kvdt, Plan* plan) {
   if (S < 0 || H < 0 || KH < 0 || D < 0 || BS < 0 || NB < 0 || MB < 0 || P < 0)
     return fail(PA_ERR_SHAPE, "negative size argument");
   if (S == 0) {
     plan->fn = nullptr;
     return PA_OK;  // nothing to do; pointers of empty tensors may be NULL
   }
-  if (dt != PA_F32 && dt != PA_F16 && dt != PA_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "unknown kv dtype %d", dt);
+  if (kvdt == PA_FP8_E4M3) {
+    if (!is_16bit(qdt))
+      return fail(PA_ERR_UNSUPPORTED, "an 8-bit cache needs an f16 or bf16 query (got %d)", qdt);
+  } else if (kvdt != PA_F32 && !is_16bit(kvdt)) {
+    return fail(PA_ERR_UNSUPPORTED, "unknown kv dtype %d", kvdt);
+  } else if (qdt != kvdt) {
+    return fail(PA_ERR_UNSUPPORTED, "query dtype %d differs from kv dtype %d", qdt, kvdt);
+  }
   if (!tmp_output || !exp_sums || !max_logits || !query || !key_cache || !value_cache ||
       !block_tables || !seq_lens)
     return fail(PA_ERR_NULL, "a required pointer is NULL");
-  const int x = 16 / elem_size(dt);
+  const int x = 16 / elem_size(kvdt);
   if (H < 1 || KH < 1 || H % KH) return fail(PA_ERR_SHAPE, "num_heads %d not a multiple of num_kv_heads %d", H, KH);
   if (D < 1 || D % x) return fail(PA_ERR_SHAPE, "head_size %d not a multiple of x = %d", D, x);
   if (BS < 1 || PS <= 0 || PS % BS)
@@ -164,11 +185,11 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
     return fail(PA_ERR_UNSUPPORTED, "partition_size / block_size > %d", pa::kWaves * 64);
   const int G = H / KH;
   partition_fn fn = nullptr;
-  if (dt != PA_F32 && G >= 4 && G <= 16) {
-    fn = kMfma[dt - 1][di][bi];
+  if (is_16bit(qdt) && G >= 4 && G <= 16) {
+    fn = kvdt == PA_FP8_E4M3 ? kMfma8[qdt - 1][di][bi] : kMfma[qdt - 1][di][bi];
   } else if (G <= 4) {
     const int gi = G == 1 ? 0 : G == 2 ? 1 : 2;
-    fn = kVec[dt][di][bi][gi];
+    fn = kvdt == PA_FP8_E4M3 ? kVec8[qdt - 1][di][bi][gi] : kVec[qdt][di][bi][gi];
   } else {
     return fail(PA_ERR_UNSUPPORTED, "group size %d not supported for this dtype", G);
   }
@@ -182,7 +203,7 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   if (lds1 > lds_limit)
     return fail(PA_ERR_UNSUPPORTED, "needs %d bytes of LDS per workgroup, device allows %d", lds1,
                 lds_limit);
-  const int span = pick_span(S, KH, P, PS, BS, G, D, elem_size(dt), lds_limit);
+  const int span = pick_span(S, KH, P, PS, BS, G, D, elem_size(kvdt), lds_limit);
   const long long grid = (long long)S * KH * ((P + span - 1) / span);
   if (grid > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many work units");
   plan->fn = fn;
@@ -196,7 +217,7 @@ int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float
                      const void* query, const void* key_cache, const void* value_cache,
                      const int32_t* block_tables, const int32_t* seq_lens, int32_t S, int32_t H,
                      int32_t KH, int32_t NB, int32_t MB, int32_t P, int32_t PS, float scale,
-                     hipStream_t stream) {
+                     float k_scale, float v_scale, hipStream_t stream) {
   PartitionArgs a;
   a.tmp_out = tmp_output;
   a.exp_sums = exp_sums;
@@ -215,7 +236,8 @@ int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float
   a.NB = NB;
   a.C = plan.span;
   a.through = P >= kThroughMinPartitions;
-  a.qk_scale = scale * pa::kLog2e;
+  a.qk_scale = scale * k_scale * pa::kLog2e;
+  a.v_scale = v_scale;
   hipLaunchKernelGGL(plan.fn, dim3(plan.grid), dim3(pa::kWaves * 64), plan.lds_bytes, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "partition launch failed: %s", hipGetErrorString(e));
@@ -269,6 +291,54 @@ int launch_reduce(reduce_fn fn, void* out, const float* tmp_output, const float*
   return PA_OK;
 }
 
+bool finite(float v) { return v == v && v - v == 0.0f; }
+
+int partition_entry(float* tmp_output, float* exp_sums, float* max_logits, const void* query,
+                    const void* key_cache, const void* value_cache, const int32_t* block_tables,
+                    const int32_t* seq_lens, int32_t S, int32_t H, int32_t KH, int32_t D,
+                    int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS, float scale,
+                    float k_scale, float v_scale, int32_t qdt, int32_t kvdt, void* stream) {
+  g_err[0] = 0;
+  if (!finite(k_scale) || !finite(v_scale))
+    return fail(PA_ERR_SHAPE, "k_scale and v_scale must be finite");
+  Plan plan;
+  int rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                           block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt,
+                           &plan);
+  if (rc != PA_OK || S == 0) return rc;
+  return launch_partition(plan, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                          block_tables, seq_lens, S, H, KH, NB, MB, P, PS, scale, k_scale,
+                          v_scale, (hipStream_t)stream);
+}
+
+int decode_entry(void* out, float* tmp_output, float* exp_sums, float* max_logits,
+                 const void* query, const void* key_cache, const void* value_cache,
+                 const int32_t* block_tables, const int32_t* seq_lens, int32_t S, int32_t H,
+                 int32_t KH, int32_t D, int32_t BS, int32_t NB, int32_t MB, int32_t P,
+                 int32_t PS, float scale, float k_scale, float v_scale, int32_t qdt,
+                 int32_t kvdt, int32_t out_dtype, void* stream) {
+  g_err[0] = 0;
+  if (!finite(k_scale) || !finite(v_scale))
+    return fail(PA_ERR_SHAPE, "k_scale and v_scale must be finite");
+  Plan plan;
+  int rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                           block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt,
+                           &plan);
+  if (rc != PA_OK || S == 0) return rc;
+  if (out_dtype != PA_F32 && out_dtype != qdt)
+    return fail(PA_ERR_UNSUPPORTED, "out dtype must be PA_F32 or the query dtype");
+  reduce_fn fn = nullptr;
+  rc = check_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, S, H, D, P, PS, out_dtype,
+                    &fn);
+  if (rc != PA_OK) return rc;
+  rc = launch_partition(plan, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                        block_tables, seq_lens, S, H, KH, NB, MB, P, PS, scale, k_scale, v_scale,
+                        (hipStream_t)stream);
+  if (rc != PA_OK) return rc;
+  return launch_reduce(fn, out, tmp_output, exp_sums, max_logits, seq_lens, S, H, D, P, PS,
+                       (hipStream_t)stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -281,17 +351,28 @@ int paged_attn_v2_partition(float* tmp_output, float* exp_sums, float* max_logit
                             int32_t max_blocks_per_seq, int32_t max_num_partitions,
                             int32_t partition_size, float scale, int32_t kv_dtype,
                             void* stream) {
-  g_err[0] = 0;
-  Plan plan;
-  int rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
-                           block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_size,
-                           block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
-                           partition_size, kv_dtype, &plan);
-  if (rc != PA_OK || num_seqs == 0) return rc;
-  return launch_partition(plan, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
-                          block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
-                          num_blocks, max_blocks_per_seq, max_num_partitions, partition_size, scale,
-                          (hipStream_t)stream);
+  if (kv_dtype == PA_FP8_E4M3) {
+    g_err[0] = 0;
+    return fail(PA_ERR_UNSUPPORTED, "8-bit caches go through paged_attn_v2_partition_fp8");
+  }
+  return partition_entry(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                         block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                         block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
+                         partition_size, scale, 1.0f, 1.0f, kv_dtype, kv_dtype, stream);
+}
+
+int paged_attn_v2_partition_fp8(float* tmp_output, float* exp_sums, float* max_logits,
+                                const void* query, const void* key_cache,
+                                const void* value_cache, const int32_t* block_tables,
+                                const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                int32_t num_blocks, int32_t max_blocks_per_seq,
+                                int32_t max_num_partitions, int32_t partition_size, float scale,
+                                float k_scale, float v_scale, int32_t q_dtype, void* stream) {
+  return partition_entry(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                         block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                         block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
+                         partition_size, scale, k_scale, v_scale, q_dtype, PA_FP8_E4M3, stream);
 }
 
 int paged_attn_v2_reduce(void* out, const float* tmp_output, const float* exp_sums,
@@ -314,26 +395,29 @@ int paged_attn_decode(void* out, float* tmp_output, float* exp_sums, float* max_
                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                       int32_t max_num_partitions, int32_t partition_size, float scale,
                       int32_t kv_dtype, int32_t out_dtype, void* stream) {
-  g_err[0] = 0;
-  Plan plan;
-  int rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
-                           block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_size,
-                           block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
-                           partition_size, kv_dtype, &plan);
-  if (rc != PA_OK || num_seqs == 0) return rc;
-  if (out_dtype != PA_F32 && out_dtype != kv_dtype)
-    return fail(PA_ERR_UNSUPPORTED, "out dtype must be PA_F32 or the kv dtype");
-  reduce_fn fn = nullptr;
-  rc = check_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, num_seqs, num_heads,
-                    head_size, max_num_partitions, partition_size, out_dtype, &fn);
-  if (rc != PA_OK || num_seqs == 0) return rc;
-  rc = launch_partition(plan, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
-                        block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
-                        num_blocks, max_blocks_per_seq, max_num_partitions, partition_size, scale,
-                        (hipStream_t)stream);
-  if (rc != PA_OK) return rc;
-  return launch_reduce(fn, out, tmp_output, exp_sums, max_logits, seq_lens, num_seqs, num_heads,
-                       head_size, max_num_partitions, partition_size, (hipStream_t)stream);
+  if (kv_dtype == PA_FP8_E4M3) {
+    g_err[0] = 0;
+    return fail(PA_ERR_UNSUPPORTED, "8-bit caches go through paged_attn_decode_fp8");
+  }
+  return decode_entry(out, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                      block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                      block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
+                      partition_size, scale, 1.0f, 1.0f, kv_dtype, kv_dtype, out_dtype, stream);
+}
+
+int paged_attn_decode_fp8(void* out, float* tmp_output, float* exp_sums, float* max_logits,
+                          const void* query, const void* key_cache, const void* value_cache,
+                          const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                          int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                          int32_t max_num_partitions, int32_t partition_size, float scale,
+                          float k_scale, float v_scale, int32_t q_dtype, int32_t out_dtype,
+                          void* stream) {
+  return decode_entry(out, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                      block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                      block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
+                      partition_size, scale, k_scale, v_scale, q_dtype, PA_FP8_E4M3, out_dtype,
+                      stream);
 }
 
 const char* paged_attn_last_error(void) { return g_err; }
@@ -347,7 +431,7 @@ int paged_attn_partition_span(int32_t num_seqs, int32_t num_heads, int32_t num_k
   const int S = num_seqs, H = num_heads, KH = num_kv_heads, D = head_size, BS = block_size,
             P = max_num_partitions, PS = partition_size, dt = kv_dtype;
   if (S < 0 || H < 1 || KH < 1 || H % KH) return fail(PA_ERR_SHAPE, "bad head counts");
-  if (dt != PA_F32 && dt != PA_F16 && dt != PA_BF16)
+  if (dt != PA_F32 && dt != PA_F16 && dt != PA_BF16 && dt != PA_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "unknown kv dtype %d", dt);
   if (d_index(D) < 0 || bs_index(BS) < 0)
     return fail(PA_ERR_UNSUPPORTED, "unsupported head_size / block_size");
@@ -360,7 +444,7 @@ int paged_attn_default_partition_size(int32_t head_size, int32_t block_size, int
                                       int32_t group) {
   if (d_index(head_size) < 0 || bs_index(block_size) < 0)
     return fail(PA_ERR_UNSUPPORTED, "unsupported head_size / block_size");
-  if (kv_dtype != PA_F32 && kv_dtype != PA_F16 && kv_dtype != PA_BF16)
+  if (kv_dtype != PA_F32 && kv_dtype != PA_F16 && kv_dtype != PA_BF16 && kv_dtype != PA_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "unknown kv dtype %d", kv_dtype);
   if (group < 1 || group > 16) return fail(PA_ERR_UNSUPPORTED, "group size %d", group);
   // Measured on MI355X over GQA (G=4, 8), MHA and 256-wide-head batches: 1024

@@ -52,7 +52,14 @@ def run_decode(dinp: Dict[str, object], PS: Optional[int] = None, P: Optional[in
     ml = torch.full((S, H, P), float("nan"), device=DEV)
     out = torch.full((S, H, D), float("nan"), device=DEV).to(out_dtype)
     args = (q, dinp["key_cache"], dinp["value_cache"], dinp["block_tables"], dinp["seq_lens"])
-    if split:
+    if dinp["key_cache"].dtype == torch.float8_e4m3fn:
+        ks, vs = dinp["k_scale"], dinp["v_scale"]
+        if split:
+            pa.paged_attn_v2_partition_fp8(tmp, es, ml, *args, dinp["scale"], ks, vs, PS)
+            pa.paged_attn_v2_reduce(out, tmp, es, ml, dinp["seq_lens"], PS)
+        else:
+            pa.paged_attn_decode_fp8(out, tmp, es, ml, *args, dinp["scale"], ks, vs, PS)
+    elif split:
         pa.paged_attn_v2_partition(tmp, es, ml, *args, dinp["scale"], PS)
         pa.paged_attn_v2_reduce(out, tmp, es, ml, dinp["seq_lens"], PS)
     else:
@@ -82,9 +89,10 @@ def check_against_oracle(inp: Dict[str, object], res: Dict[str, torch.Tensor],
     rows = list(range(S)) if seqs is None else sorted(set(int(s) for s in seqs))
     args = (inp["query"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
             inp["seq_lens"], inp["scale"])
-    ref = oracle.attention(*args, seqs=rows)
+    sc = dict(k_scale=inp.get("k_scale", 1.0), v_scale=inp.get("v_scale", 1.0))
+    ref = oracle.attention(*args, seqs=rows, **sc)
     assert_close(f"{label} out", res["out"][rows].float(), ref[rows])
-    tmp, es, ml = oracle.partition_stats(*args, res["P"], res["PS"], seqs=rows)
+    tmp, es, ml = oracle.partition_stats(*args, res["P"], res["PS"], seqs=rows, **sc)
     sl = inp["seq_lens"].tolist()
     for s in rows:
         n = -(-sl[s] // res["PS"]) if sl[s] > 0 else 0
@@ -113,4 +121,10 @@ def small_config(name: str) -> W.DecodeConfig:
         return cfg.replace(num_seqs=2, fixed_lens=(2500, 1300))
     if name == "wide_f16_d256":
         return cfg.replace(num_seqs=3, len_lo=100, len_hi=1800)
+    if name == "gqa_fp8_g4":
+        return cfg.replace(num_seqs=6, len_lo=1, len_hi=1600)
+    if name == "longctx_fp8_g8":
+        return cfg.replace(num_seqs=2, fixed_lens=(2500, 1300))
+    if name == "mha_fp8_d128":
+        return cfg.replace(num_seqs=5, len_lo=1, len_hi=1100)
     raise KeyError(name)

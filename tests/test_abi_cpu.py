@@ -136,6 +136,32 @@ def test_num_seqs_zero_is_noop_even_with_null_pointers():
                                       binding.PA_BF16, binding.PA_F32, None) == binding.PA_OK
 
 
+def part_fp8(q_dtype=binding.PA_BF16, k_scale=1.0, v_scale=1.0, **kw):
+    a = dict(BASE, **kw)
+    return pa.lib().paged_attn_v2_partition_fp8(*([FAKE] * 8), a["S"], a["H"], a["KH"], a["D"],
+                                                a["BS"], a["B"], a["MB"], a["P"], a["PS"], 0.125,
+                                                k_scale, v_scale, q_dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_dtype=binding.PA_F32), binding.PA_ERR_UNSUPPORTED),
+    (dict(q_dtype=binding.PA_FP8_E4M3), binding.PA_ERR_UNSUPPORTED),
+    (dict(k_scale=float("inf")), binding.PA_ERR_SHAPE),
+    (dict(v_scale=float("nan")), binding.PA_ERR_SHAPE),
+    (dict(D=72), binding.PA_ERR_SHAPE),                # 72 % 16 != 0 (x = 16 for 8-bit)
+    (dict(H=64, KH=2), binding.PA_ERR_UNSUPPORTED),    # G = 32
+])
+def test_fp8_partition_rejects(kw, code):
+    assert part_fp8(**kw) == code
+    assert pa.last_error() != ""
+
+
+def test_plain_calls_reject_8bit_cache():
+    assert part(dt=binding.PA_FP8_E4M3) == binding.PA_ERR_UNSUPPORTED
+    assert decode(binding.PA_F32, dt=binding.PA_FP8_E4M3) == binding.PA_ERR_UNSUPPORTED
+    assert "fp8" in pa.last_error()
+
+
 def test_decode_out_dtype_must_be_f32_or_kv():
     assert decode(binding.PA_F16) == binding.PA_ERR_UNSUPPORTED
     assert decode(binding.PA_BF16, D=96) == binding.PA_ERR_UNSUPPORTED

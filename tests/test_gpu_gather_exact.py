@@ -4,7 +4,9 @@ A single wrong token moves a long-context output by about 1/L, far below the
 floating-point tolerance, so the gather is proven exactly instead:
 
 * index-encoding selector: V stores (block mod 256, block div 256, slot,
-  kv head) in its first four dims, K is zero except a 1 at (target token,
+  kv head) in its first four dims (for an 8-bit E4M3 cache, which holds
+  integers exactly only up to 16: the hexadecimal digits of block, slot and
+  kv head in its first eight dims), K is zero except a 1 at (target token,
   head-specific dim d_h), q = c * e_{d_h} with c * scale >= 128. Every other
   token's weight underflows to exactly 0 in fp32, so out[s, h, 0:4] must equal
   the encoding of the target's (block, slot) as the oracle's gather gives it,
@@ -45,23 +47,33 @@ class Selector:
         S, H, KH, D, BS, x = (cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_size,
                               cfg.block_size, cfg.x)
         dt = W.DTYPES[cfg.dtype]
+        self.fp8 = cfg.dtype == "fp8"
         self.kc = torch.zeros(self.NB, KH, D // x, BS, x, dtype=dt, device=U.DEV)
+        # writable view of K (8-bit caches are edited byte-wise: 1.0 is 0x38)
+        self.kw = self.kc.view(torch.uint8) if self.fp8 else self.kc
+        self.one = (torch.tensor([1.0]).to(dt).view(torch.uint8)[0].item() if self.fp8 else 1.0)
         vc = torch.zeros(self.NB, KH, D, BS, dtype=torch.float32, device=U.DEV)
         b = torch.arange(self.NB, device=U.DEV, dtype=torch.float32)[:, None, None]
         o = torch.arange(BS, device=U.DEV, dtype=torch.float32)[None, None, :]
         k = torch.arange(KH, device=U.DEV, dtype=torch.float32)[None, :, None]
-        vc[:, :, 0, :] = torch.remainder(b, 256).expand(self.NB, KH, BS)
-        vc[:, :, 1, :] = torch.floor(b / 256).expand(self.NB, KH, BS)
-        vc[:, :, 2, :] = o.expand(self.NB, KH, BS)
-        vc[:, :, 3, :] = k.expand(self.NB, KH, BS)
+        for d, val in enumerate(self.encode(b, o, k)):
+            vc[:, :, d, :] = val.expand(self.NB, KH, BS)
         self.vc = vc.to(dt)
-        self.q = torch.zeros(S, H, D, dtype=dt, device=U.DEV)
+        self.q = torch.zeros(S, H, D, dtype=W.DTYPES[cfg.query_dtype], device=U.DEV)
         self.blk, self.slot = oracle.gather_indices(self.bt, self.sl, BS)
         self.start = np.concatenate([[0], np.cumsum(self.sl.numpy())])
         self.d = dict(query=self.q, key_cache=self.kc, value_cache=self.vc,
                       block_tables=self.bt.to(U.DEV), seq_lens=self.sl.to(U.DEV),
                       scale=cfg.scale_f32, partition_size=cfg.partition_size,
-                      max_num_partitions=cfg.max_num_partitions)
+                      max_num_partitions=cfg.max_num_partitions, k_scale=1.0, v_scale=1.0)
+
+    def encode(self, b, o, k):
+        """Values of V's first dims for block b, slot o, kv head k (exact in the cache dtype)."""
+        if not self.fp8:
+            return [torch.remainder(b, 256), torch.floor(b / 256), o, k]
+        hexd = lambda v, i: torch.remainder(torch.floor(v / 16 ** i), 16)
+        return [hexd(b, 0), hexd(b, 1), hexd(b, 2), hexd(b, 3), hexd(o, 0), hexd(o, 1),
+                hexd(k, 0), hexd(k, 1)]
 
     def round(self, targets: np.ndarray, dims: np.ndarray):
         """targets[s, h] = token index, dims[s, h] = d_h; runs the decode, returns results."""
@@ -75,16 +87,16 @@ class Selector:
         dd = torch.from_numpy(dims.astype(np.int64))
         idx = (b.flatten(), kh.flatten(), (dd // x).flatten(), o.flatten(), (dd % x).flatten())
         idx = tuple(t.to(U.DEV) for t in idx)
-        self.kc.index_put_(idx, torch.ones(S * H, dtype=self.kc.dtype, device=U.DEV))
+        self.kw.index_put_(idx, torch.full((S * H,), self.one, dtype=self.kw.dtype, device=U.DEV))
         self.q.zero_()
         si = torch.arange(S)[:, None].expand(S, H).flatten().to(U.DEV)
         hi = torch.arange(H)[None, :].expand(S, H).flatten().to(U.DEV)
         self.q.index_put_((si, hi, dd.flatten().to(U.DEV)),
                           torch.full((S * H,), C_Q, dtype=self.q.dtype, device=U.DEV))
         res = U.run_decode(self.d)
-        self.kc.index_put_(idx, torch.zeros(S * H, dtype=self.kc.dtype, device=U.DEV))
-        expect = torch.stack([b % 256, b // 256, o, kh], dim=-1).to(torch.float32)
-        return res, expect
+        self.kw.index_put_(idx, torch.zeros(S * H, dtype=self.kw.dtype, device=U.DEV))
+        expect = torch.stack(self.encode(b.double(), o.double(), kh.double()), dim=-1)
+        return res, expect.to(torch.float32)
 
     def random_round(self, rng):
         cfg = self.cfg
@@ -100,7 +112,7 @@ class Selector:
 
 
 def check(res, expect, label):
-    got = res["out"][:, :, :4]
+    got = res["out"][:, :, :expect.shape[-1]]
     if not torch.equal(got, expect):
         bad = (got != expect).any(-1).nonzero()[:5].tolist()
         raise AssertionError(f"{label}: gathered indices differ at (s, h) {bad}")
@@ -120,11 +132,11 @@ def test_selector_exhaustive_tiny():
 
 
 @pytest.mark.parametrize("name", ["mha_f16_d128", "gqa_bf16_g4", "longctx_bf16_g8",
-                                  "wide_f16_d256"])
+                                  "wide_f16_d256", "gqa_fp8_g4", "longctx_fp8_g8", "mha_fp8_d128"])
 def test_selector_full_shape(name):
     cfg = W.CONFIGS[name]
-    sel = Selector(cfg, seed=W.CONFIG_ORDER.index(name) + 1)
-    rng = np.random.default_rng(W.CONFIG_ORDER.index(name))
+    sel = Selector(cfg, seed=W.workload_seed(name))
+    rng = np.random.default_rng(W.workload_seed(name) - 1)
     U.note(f"T1 full {name}")
     for r in range(64):
         targets, dims = sel.random_round(rng)
@@ -161,7 +173,7 @@ def test_seq_len_one_returns_v(name):
             assert torch.equal(res["out"][s, h], v[b, h // G, :, 0])
 
 
-@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+@pytest.mark.parametrize("name", W.CONFIG_ORDER + W.FP8_ORDER)
 def test_block_relabelling_bit_identical(name):
     cfg = U.small_config(name)
     inp = W.make_inputs(cfg, seed=4, extra_blocks=3)
@@ -184,7 +196,7 @@ def test_block_relabelling_bit_identical(name):
     assert torch.equal(a["tmp"].nan_to_num(nan=3.0), b["tmp"].nan_to_num(nan=3.0))
 
 
-@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+@pytest.mark.parametrize("name", W.CONFIG_ORDER + W.FP8_ORDER)
 def test_run_to_run_bit_identical(name):
     cfg = U.small_config(name)
     inp = W.make_inputs(cfg, seed=6)

@@ -18,6 +18,7 @@ from paged_kv_cache_v2_amd import workloads as W
 from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
+ALL = W.CONFIG_ORDER + W.FP8_ORDER  # the five configurations, then their 8-bit-cache variants
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -28,7 +29,7 @@ def built():
     oracle.build(force=False)
 
 
-@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+@pytest.mark.parametrize("name", ALL)
 @pytest.mark.parametrize("seed", [11, 12])
 def test_parity_reduced(name, seed):
     cfg = U.small_config(name)
@@ -39,7 +40,7 @@ def test_parity_reduced(name, seed):
     U.check_against_oracle(inp, res, label=name)
 
 
-@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+@pytest.mark.parametrize("name", ALL)
 def test_parity_reduced_split_calls(name):
     """paged_attn_v2_partition + paged_attn_v2_reduce give what paged_attn_decode gives."""
     cfg = U.small_config(name)
@@ -60,7 +61,7 @@ def full_inputs(name):
     if name not in _FULL:
         _FULL.clear()
         cfg = W.CONFIGS[name]
-        inp = W.make_inputs(cfg, seed=W.CONFIG_ORDER.index(name) + 1)
+        inp = W.make_inputs(cfg, seed=W.workload_seed(name))
         _FULL[name] = (inp, U.to_device(inp))
     return _FULL[name]
 
@@ -75,7 +76,7 @@ def sample_seqs(inp, k=3, seed=0):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+@pytest.mark.parametrize("name", ALL)
 @pytest.mark.parametrize("ps", ["config", "default"])
 def test_parity_full_size_sampled(name, ps):
     """Full-size inputs, in the launch configurations bench.py times: the
@@ -103,13 +104,14 @@ def test_parity_full_size_sampled(name, ps):
         assert torch.isfinite(res["tmp"][s, :, :n]).all()
 
 
-@pytest.mark.parametrize("name", ["mha_f16_d128", "gqa_bf16_g4", "wide_f16_d256"])
+@pytest.mark.parametrize("name", ["mha_f16_d128", "gqa_bf16_g4", "wide_f16_d256", "gqa_fp8_g4",
+                                  "mha_fp8_d128"])
 def test_out_cast_is_rne_of_fp32(name):
     cfg = U.small_config(name)
     inp = W.make_inputs(cfg, seed=5)
     d = U.to_device(inp)
     U.note(f"cast {name}")
     f32 = U.run_decode(d)["out"]
-    low = U.run_decode(d, out_dtype=W.DTYPES[cfg.dtype])["out"]
-    assert low.dtype == W.DTYPES[cfg.dtype]
+    low = U.run_decode(d, out_dtype=W.DTYPES[cfg.query_dtype])["out"]
+    assert low.dtype == W.DTYPES[cfg.query_dtype]
     assert torch.equal(low.view(torch.int16), f32.to(low.dtype).view(torch.int16))

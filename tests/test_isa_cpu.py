@@ -75,9 +75,32 @@ def test_no_scalar_cache_writes(kernels):
 
 def test_kv_loads_are_dwordx4_or_dwordx2_streaming(kernels):
     """K/V pages are fetched with 16-byte (K, vector-path V) or 8-byte (MFMA-path V)
-    non-temporal loads."""
+    non-temporal loads; an 8-bit cache's MFMA-path V pieces are 4 bytes."""
+    seen = 0
     for k, v in kernels.items():
-        if "partition_mfma_kernelILi2ELi128ELi16" in k:
-            nt = [l for l in v if l.startswith("global_load") and l.endswith(" nt")]
+        nt = [l for l in v if l.startswith("global_load") and l.endswith(" nt")]
+        if "partition_mfma_kernelILi2ELi128ELi16ELb0" in k:
             assert any(l.startswith("global_load_dwordx4") for l in nt)
             assert any(l.startswith("global_load_dwordx2") for l in nt)
+            seen += 1
+        if "partition_mfma_kernelILi2ELi128ELi16ELb1" in k:
+            assert any(l.startswith("global_load_dwordx4") for l in nt)
+            assert any(l.startswith("global_load_dword ") for l in nt)
+            seen += 1
+        if "partition_vec_kernelILi2ELi128ELi16ELi1ELb1" in k:
+            assert any(l.startswith("global_load_dwordx4") for l in nt)
+            seen += 1
+    assert seen == 3
+
+
+def test_fp8_kernels_convert_with_gfx950_instructions(kernels):
+    """8-bit pages are widened in registers by the gfx950 conversions."""
+    for k, v in kernels.items():
+        o = set(ops(v))
+        if "partition_mfma_kernelILi2ELi128ELi16ELb1" in k:
+            assert "v_cvt_scalef32_pk_bf16_fp8" in o
+        if "partition_mfma_kernelILi1ELi128ELi16ELb1" in k:
+            assert "v_cvt_scalef32_pk_f16_fp8" in o
+        if "partition_vec_kernelILi2ELi128ELi16ELi1ELb1" in k:
+            assert "v_cvt_scalef32_pk_bf16_fp8" in o
+            assert any(x.startswith("v_cvt_pk_f32_fp8") for x in o)
