@@ -88,12 +88,14 @@ def _bind(path: str):
     lib.oracle_partition_stats.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32,
                                            I32, I32, I32, F32, I32, P, I32, I32]
     lib.oracle_attention_ex.restype = ctypes.c_int
-    lib.oracle_attention_ex.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, F32,
-                                        I32, I32, F32, F32, P, I32, I32]
+    lib.oracle_attention_ex.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
+                                        F32, I32, I32, F32, F32, P, I32, I32]
     lib.oracle_partition_stats_ex.restype = ctypes.c_int
     lib.oracle_partition_stats_ex.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32,
-                                              I32, I32, I32, F32, I32, I32, F32, F32, P, I32,
-                                              I32]
+                                              I32, I32, I32, I32, F32, I32, I32, F32, F32, P,
+                                              I32, I32]
+    lib.oracle_combine_ex.restype = None
+    lib.oracle_combine_ex.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32]
     lib.oracle_combine.restype = None
     lib.oracle_combine.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32]
     lib.oracle_gather_indices.restype = I64
@@ -149,24 +151,34 @@ def _seq_arg(seqs: Optional[Sequence[int]]):
     return _ptr(arr), arr.size, arr
 
 
+def _query_rows(q):
+    """(S, M, H, D) of a [S, H, D] (one query token) or [S, M, H, D] query."""
+    if q.ndim == 3:
+        S, H, D = q.shape
+        return S, 1, H, D
+    return q.shape
+
+
 def attention(query, key_cache, value_cache, block_tables, seq_lens, scale: float,
               seqs: Optional[Sequence[int]] = None, nthreads: Optional[int] = None,
               k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
-    """Dense softmax attention over the block-table-gathered tokens: out[S, H, D] float64.
+    """Dense softmax attention over the block-table-gathered tokens, float64.
 
-    Rows of sequences not in ``seqs`` are NaN. The query dtype and the cache
-    dtype are read off the tensors; an e4m3fn cache stands for its decoded
-    values times ``k_scale`` / ``v_scale``.
+    query [S, H, D] gives out [S, H, D]; query [S, M, H, D] (M query tokens per
+    sequence, the last M positions, causal) gives out [S, M, H, D]. Rows of
+    sequences not in ``seqs`` are NaN. The query dtype and the cache dtype are
+    read off the tensors; an e4m3fn cache stands for its decoded values times
+    ``k_scale`` / ``v_scale``.
     """
     q, kc, vc = _np(query), _np(key_cache), _np(value_cache)
     bt, sl = _np(block_tables).astype(np.int32, copy=False), _np(seq_lens).astype(np.int32, copy=False)
-    S, H, D = q.shape
+    S, M, H, D = _query_rows(q)
     KH, BS = kc.shape[1], kc.shape[3]
     MB = bt.shape[1]
-    out = np.full((S, H, D), np.nan)
+    out = np.full(q.shape, np.nan)
     sp, ns, keep = _seq_arg(seqs)
     rc = _lib().oracle_attention_ex(_ptr(out), _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl),
-                                    S, H, KH, D, BS, MB, float(np.float32(scale)),
+                                    S, M, H, KH, D, BS, MB, float(np.float32(scale)),
                                     _dtype_code(query), _dtype_code(key_cache),
                                     float(np.float32(k_scale)), float(np.float32(v_scale)),
                                     sp, ns, nthreads or default_threads())
@@ -181,20 +193,22 @@ def partition_stats(query, key_cache, value_cache, block_tables, seq_lens, scale
                     seqs: Optional[Sequence[int]] = None,
                     nthreads: Optional[int] = None, k_scale: float = 1.0,
                     v_scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Phase-1 intermediates (tmp_output[S,H,P,D], exp_sums[S,H,P], max_logits[S,H,P])."""
+    """Phase-1 intermediates: tmp_output [rows, H, P, D], exp_sums and max_logits
+    [rows, H, P], with rows = [S] or [S, M] as for ``attention``."""
     q, kc, vc = _np(query), _np(key_cache), _np(value_cache)
     bt, sl = _np(block_tables).astype(np.int32, copy=False), _np(seq_lens).astype(np.int32, copy=False)
-    S, H, D = q.shape
+    S, M, H, D = _query_rows(q)
     KH, BS = kc.shape[1], kc.shape[3]
     MB = bt.shape[1]
     P = max_num_partitions
-    tmp = np.full((S, H, P, D), np.nan)
-    es = np.full((S, H, P), np.nan)
-    ml = np.full((S, H, P), np.nan)
+    lead = q.shape[:-2]
+    tmp = np.full(lead + (H, P, D), np.nan)
+    es = np.full(lead + (H, P), np.nan)
+    ml = np.full(lead + (H, P), np.nan)
     sp, ns, keep = _seq_arg(seqs)
     rc = _lib().oracle_partition_stats_ex(
-        _ptr(tmp), _ptr(es), _ptr(ml), _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl), S, H, KH,
-        D, BS, MB, P, partition_size, float(np.float32(scale)), _dtype_code(query),
+        _ptr(tmp), _ptr(es), _ptr(ml), _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl), S, M, H,
+        KH, D, BS, MB, P, partition_size, float(np.float32(scale)), _dtype_code(query),
         _dtype_code(key_cache), float(np.float32(k_scale)), float(np.float32(v_scale)), sp, ns,
         nthreads or default_threads())
     if rc != 0:
@@ -205,15 +219,20 @@ def partition_stats(query, key_cache, value_cache, block_tables, seq_lens, scale
 
 def combine(tmp: np.ndarray, exp_sums: np.ndarray, max_logits: np.ndarray, seq_lens,
             partition_size: int) -> np.ndarray:
-    """Phase-2 log-sum-exp combine of the partition intermediates: out[S, H, D] float64."""
+    """Phase-2 log-sum-exp combine of the partition intermediates, float64:
+    tmp [S, H, P, D] gives out [S, H, D]; tmp [S, M, H, P, D] gives [S, M, H, D]."""
     tmp = np.ascontiguousarray(tmp, dtype=np.float64)
     es = np.ascontiguousarray(exp_sums, dtype=np.float64)
     ml = np.ascontiguousarray(max_logits, dtype=np.float64)
     sl = _np(seq_lens).astype(np.int32, copy=False)
-    S, H, P, D = tmp.shape
-    out = np.empty((S, H, D))
-    _lib().oracle_combine(_ptr(out), _ptr(tmp), _ptr(es), _ptr(ml), _ptr(sl), S, H, D, P,
-                          partition_size)
+    if tmp.ndim == 4:
+        S, H, P, D = tmp.shape
+        M = 1
+    else:
+        S, M, H, P, D = tmp.shape
+    out = np.empty(tmp.shape[:-2] + (D,))
+    _lib().oracle_combine_ex(_ptr(out), _ptr(tmp), _ptr(es), _ptr(ml), _ptr(sl), S, M, H, D, P,
+                             partition_size)
     return out
 
 

@@ -34,6 +34,14 @@
  * Combine mode is the reduce kernel: over the n = ceil(L/PS) used partitions,
  * M = max m_p, Z = sum exp(m_p - M) l_p, out = sum exp(m_p - M) l_p / Z * o_p.
  *
+ * Several query tokens per sequence (speculative decode / chunked prefill
+ * over the cache). [TRITON-V2] notes its gather comes from a multi-row
+ * (BLOCK_M) prefill kernel; [METAL-FA]'s forward kernel masks keys later than
+ * the query position (score -inf). Reading taken: the M query tokens
+ * q[s][m] (query layout [S, M, H, D]) are the sequence's last M positions, so
+ * token m sits at L - M + m and attends to t <= L - M + m; everything else is
+ * unchanged, per query row (outputs [S, M, H, ...]). M = 1 is the decode above.
+ *
  * Readings where the pages leave a step open:
  *  - the scale is rounded to fp32 first (the partition kernel types it fp32);
  *  - the 1e-6 clamps on the running sum are inert for finite inputs (the
@@ -137,6 +145,7 @@ typedef struct {
     const int32_t* sl;  /* [S]                     */
     int32_t S, H, KH, D, BS, MB, P, PS;
     int32_t qdtype, kvdtype;  /* query dtype; key / value cache dtype */
+    int32_t M;                /* query tokens per sequence (1: single-query decode) */
     double scale;
     double kscale, vscale;    /* cache dequantisation scales (1 for 16/32-bit caches) */
     /* outputs (any may be NULL) */
@@ -169,8 +178,9 @@ static double value_at(const problem_t* pr, int32_t b, int32_t kh, int32_t o, in
     return load_elem(pr->vc, idx, pr->kvdtype) * pr->vscale;
 }
 
-static double query_at(const problem_t* pr, int32_t s, int32_t h, int32_t d) {
-    return load_elem(pr->q, ((int64_t)s * pr->H + h) * pr->D + d, pr->qdtype);
+/* Query row r = s * M + m (query token m of sequence s), head h. */
+static double query_at(const problem_t* pr, int64_t r, int32_t h, int32_t d) {
+    return load_elem(pr->q, (r * pr->H + h) * pr->D + d, pr->qdtype);
 }
 
 /* Softmax-weighted value mix of tokens [t0, t1) given their scores.
@@ -194,23 +204,34 @@ static void softmax_mix(const problem_t* pr, int32_t s, int32_t kh, const double
     *l_out = l;
 }
 
+/* Keys query token m of a length-L sequence attends to: the M query tokens
+ * are the sequence's last M positions, token m sits at L - M + m and sees
+ * positions t <= L - M + m (the causal rule); clamped to [0, L]. M = 1 gives L. */
+static int32_t causal_len(int32_t L, int32_t M, int32_t m) {
+    int32_t e = L - M + m + 1;
+    return e < 0 ? 0 : (e > L ? L : e);
+}
+
 static void run_item(problem_t* pr, int32_t s, int32_t kh) {
-    int32_t L = pr->sl[s];
+    int32_t L0 = pr->sl[s];
     int32_t G = pr->H / pr->KH;
-    double* score = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    double* score = (double*)malloc(sizeof(double) * (size_t)(L0 > 0 ? L0 : 1));
     double* o = (double*)malloc(sizeof(double) * (size_t)pr->D);
-    for (int32_t g = 0; g < G; ++g) {
+    for (int32_t mq = 0; mq < pr->M; ++mq) {
+      int64_t r = (int64_t)s * pr->M + mq;   /* query row */
+      int32_t L = causal_len(L0, pr->M, mq); /* keys this query token sees */
+      for (int32_t g = 0; g < G; ++g) {
         int32_t h = kh * G + g; /* consecutive query heads share one kv head */
         for (int32_t t = 0; t < L; ++t) {
             int32_t b, slot;
             gather_index(pr, s, t, &b, &slot);
             double dot = 0.0;
             for (int32_t d = 0; d < pr->D; ++d)
-                dot += query_at(pr, s, h, d) * key_at(pr, b, kh, slot, d);
+                dot += query_at(pr, r, h, d) * key_at(pr, b, kh, slot, d);
             score[t] = pr->scale * dot;
         }
         if (pr->out) {
-            double* dst = pr->out + ((int64_t)s * pr->H + h) * pr->D;
+            double* dst = pr->out + (r * pr->H + h) * pr->D;
             if (L == 0) {
                 for (int32_t d = 0; d < pr->D; ++d) dst[d] = 0.0;
             } else {
@@ -220,7 +241,7 @@ static void run_item(problem_t* pr, int32_t s, int32_t kh) {
         }
         if (pr->tmp || pr->es || pr->ml) {
             for (int32_t p = 0; p < pr->P; ++p) {
-                int64_t sp = ((int64_t)s * pr->H + h) * pr->P + p;
+                int64_t sp = (r * pr->H + h) * pr->P + p;
                 int32_t t0 = p * pr->PS;
                 int32_t t1 = t0 + pr->PS < L ? t0 + pr->PS : L;
                 double m = -INFINITY, l = 0.0;
@@ -234,6 +255,7 @@ static void run_item(problem_t* pr, int32_t s, int32_t kh) {
                 if (pr->tmp) memcpy(pr->tmp + sp * pr->D, o, sizeof(double) * (size_t)pr->D);
             }
         }
+      }
     }
     free(o);
     free(score);
@@ -282,16 +304,16 @@ static int valid_dtypes(int32_t qdtype, int32_t kvdtype) {
  * Returns 0, or -1 on a shape or dtype pair the definition does not cover. */
 int oracle_attention_ex(double* out, const void* q, const void* kc, const void* vc,
                         const int32_t* block_tables, const int32_t* seq_lens,
-                        int32_t S, int32_t H, int32_t KH, int32_t D, int32_t BS, int32_t MB,
-                        float scale, int32_t qdtype, int32_t kvdtype, float k_scale,
+                        int32_t S, int32_t M, int32_t H, int32_t KH, int32_t D, int32_t BS,
+                        int32_t MB, float scale, int32_t qdtype, int32_t kvdtype, float k_scale,
                         float v_scale, const int32_t* seqs, int32_t n_seqs, int32_t nthreads) {
-    if (!valid_dtypes(qdtype, kvdtype)) return -1;
+    if (!valid_dtypes(qdtype, kvdtype) || M < 1) return -1;
     if (KH <= 0 || H % KH || D % (16 / elem_size(kvdtype))) return -1;
     problem_t pr;
     memset(&pr, 0, sizeof pr);
     pr.q = q; pr.kc = kc; pr.vc = vc; pr.bt = block_tables; pr.sl = seq_lens;
     pr.S = S; pr.H = H; pr.KH = KH; pr.D = D; pr.BS = BS; pr.MB = MB;
-    pr.qdtype = qdtype; pr.kvdtype = kvdtype;
+    pr.qdtype = qdtype; pr.kvdtype = kvdtype; pr.M = M;
     pr.scale = (double)scale;
     pr.kscale = (double)k_scale; pr.vscale = (double)v_scale;
     pr.out = out;
@@ -305,7 +327,7 @@ int oracle_attention(double* out, const void* q, const void* kc, const void* vc,
                      int32_t S, int32_t H, int32_t KH, int32_t D, int32_t BS, int32_t MB,
                      float scale, int32_t dtype, const int32_t* seqs, int32_t n_seqs,
                      int32_t nthreads) {
-    return oracle_attention_ex(out, q, kc, vc, block_tables, seq_lens, S, H, KH, D, BS, MB,
+    return oracle_attention_ex(out, q, kc, vc, block_tables, seq_lens, S, 1, H, KH, D, BS, MB,
                                scale, dtype, dtype, 1.0f, 1.0f, seqs, n_seqs, nthreads);
 }
 
@@ -313,12 +335,12 @@ int oracle_attention(double* out, const void* q, const void* kc, const void* vc,
  * sequences. Returns -1 if a length exceeds P*PS. */
 int oracle_partition_stats_ex(double* tmp, double* es, double* ml, const void* q,
                               const void* kc, const void* vc, const int32_t* block_tables,
-                              const int32_t* seq_lens, int32_t S, int32_t H, int32_t KH,
-                              int32_t D, int32_t BS, int32_t MB, int32_t P, int32_t PS,
-                              float scale, int32_t qdtype, int32_t kvdtype, float k_scale,
-                              float v_scale, const int32_t* seqs, int32_t n_seqs,
+                              const int32_t* seq_lens, int32_t S, int32_t M, int32_t H,
+                              int32_t KH, int32_t D, int32_t BS, int32_t MB, int32_t P,
+                              int32_t PS, float scale, int32_t qdtype, int32_t kvdtype,
+                              float k_scale, float v_scale, const int32_t* seqs, int32_t n_seqs,
                               int32_t nthreads) {
-    if (!valid_dtypes(qdtype, kvdtype)) return -1;
+    if (!valid_dtypes(qdtype, kvdtype) || M < 1) return -1;
     if (KH <= 0 || H % KH || D % (16 / elem_size(kvdtype)) || PS <= 0 || P < 1) return -1;
     for (int32_t s = 0; s < S; ++s)
         if (seq_lens[s] > (int64_t)P * PS) return -1;
@@ -326,7 +348,7 @@ int oracle_partition_stats_ex(double* tmp, double* es, double* ml, const void* q
     memset(&pr, 0, sizeof pr);
     pr.q = q; pr.kc = kc; pr.vc = vc; pr.bt = block_tables; pr.sl = seq_lens;
     pr.S = S; pr.H = H; pr.KH = KH; pr.D = D; pr.BS = BS; pr.MB = MB;
-    pr.qdtype = qdtype; pr.kvdtype = kvdtype;
+    pr.qdtype = qdtype; pr.kvdtype = kvdtype; pr.M = M;
     pr.P = P; pr.PS = PS;
     pr.scale = (double)scale;
     pr.kscale = (double)k_scale; pr.vscale = (double)v_scale;
@@ -340,34 +362,44 @@ int oracle_partition_stats(double* tmp, double* es, double* ml, const void* q, c
                            int32_t S, int32_t H, int32_t KH, int32_t D, int32_t BS, int32_t MB,
                            int32_t P, int32_t PS, float scale, int32_t dtype,
                            const int32_t* seqs, int32_t n_seqs, int32_t nthreads) {
-    return oracle_partition_stats_ex(tmp, es, ml, q, kc, vc, block_tables, seq_lens, S, H, KH,
-                                     D, BS, MB, P, PS, scale, dtype, dtype, 1.0f, 1.0f, seqs,
+    return oracle_partition_stats_ex(tmp, es, ml, q, kc, vc, block_tables, seq_lens, S, 1, H,
+                                     KH, D, BS, MB, P, PS, scale, dtype, dtype, 1.0f, 1.0f, seqs,
                                      n_seqs, nthreads);
 }
 
-/* Phase-2 cross-partition log-sum-exp combine, per (s, h), over the
- * n = ceil(L / PS) partitions a length-L sequence uses; n == 0 gives 0. */
-void oracle_combine(double* out, const double* tmp, const double* es, const double* ml,
-                    const int32_t* seq_lens, int32_t S, int32_t H, int32_t D, int32_t P,
-                    int32_t PS) {
+/* Phase-2 cross-partition log-sum-exp combine, per query row (s, m) and head
+ * h, over the n = ceil(len / PS) partitions its len = causal_len(L, M, m) keys
+ * use; n == 0 gives 0. Rows are [S * M, H]; M = 1 is the single-query decode. */
+void oracle_combine_ex(double* out, const double* tmp, const double* es, const double* ml,
+                       const int32_t* seq_lens, int32_t S, int32_t M, int32_t H, int32_t D,
+                       int32_t P, int32_t PS) {
     for (int32_t s = 0; s < S; ++s) {
-        int32_t n = (seq_lens[s] + PS - 1) / PS;
+      for (int32_t mq = 0; mq < M; ++mq) {
+        int64_t r = (int64_t)s * M + mq;
+        int32_t n = (causal_len(seq_lens[s], M, mq) + PS - 1) / PS;
         for (int32_t h = 0; h < H; ++h) {
-            double* dst = out + ((int64_t)s * H + h) * D;
-            int64_t base = ((int64_t)s * H + h) * P;
+            double* dst = out + (r * H + h) * D;
+            int64_t base = (r * H + h) * P;
             for (int32_t d = 0; d < D; ++d) dst[d] = 0.0;
             if (n == 0) continue;
-            double M = -INFINITY;
+            double Mx = -INFINITY;
             for (int32_t p = 0; p < n; ++p)
-                if (ml[base + p] > M) M = ml[base + p];
+                if (ml[base + p] > Mx) Mx = ml[base + p];
             double Z = 0.0;
-            for (int32_t p = 0; p < n; ++p) Z += exp(ml[base + p] - M) * es[base + p];
+            for (int32_t p = 0; p < n; ++p) Z += exp(ml[base + p] - Mx) * es[base + p];
             for (int32_t p = 0; p < n; ++p) {
-                double w = exp(ml[base + p] - M) * es[base + p] / Z;
+                double w = exp(ml[base + p] - Mx) * es[base + p] / Z;
                 for (int32_t d = 0; d < D; ++d) dst[d] += w * tmp[(base + p) * D + d];
             }
         }
+      }
     }
+}
+
+void oracle_combine(double* out, const double* tmp, const double* es, const double* ml,
+                    const int32_t* seq_lens, int32_t S, int32_t H, int32_t D, int32_t P,
+                    int32_t PS) {
+    oracle_combine_ex(out, tmp, es, ml, seq_lens, S, 1, H, D, P, PS);
 }
 
 /* The gather itself: for every (s, t < L_s) in order, the physical block and

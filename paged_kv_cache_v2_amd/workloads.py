@@ -62,6 +62,7 @@ class DecodeConfig:
     q_dtype: Optional[str] = None  # None means the cache dtype
     k_scale: float = 1.0  # 8-bit caches: a stored key byte stands for decode(byte) * k_scale
     v_scale: float = 1.0
+    num_queries: int = 1  # query tokens per sequence (the last positions; query [S, M, H, D])
 
     @property
     def query_dtype(self) -> str:
@@ -244,7 +245,9 @@ def make_inputs(cfg: DecodeConfig, seed: int, lens: Optional[Sequence[int]] = No
             vals = (vals / np.float32(cache_scale)).clamp_(-FP8_MAX, FP8_MAX)
         return vals.to(DTYPES[dtype])
 
-    out["query"] = tensor(_KEY_Q, (S, H, D), cfg.query_dtype)
+    M = cfg.num_queries
+    out["query"] = tensor(_KEY_Q, (S, H, D) if M == 1 else (S, M, H, D), cfg.query_dtype)
+    out["num_queries"] = M
     out["key_cache"] = tensor(_KEY_K, (NB, KH, D // x, BS, x), cfg.dtype, cfg.k_scale)
     out["value_cache"] = tensor(_KEY_V, (NB, KH, D, BS), cfg.dtype, cfg.v_scale)
     if device != "cpu":
@@ -287,6 +290,16 @@ def kv_bytes(inp: Dict[str, object]) -> int:
         inp["head_size"] * esz
 
 
+def causal_len(L: int, M: int, m: int) -> int:
+    """Keys query token m (of M, the sequence's last positions) sees in a
+    length-L sequence: positions t <= L - M + m, clamped to [0, L]."""
+    return max(0, min(L, L - M + m + 1))
+
+
 def qhead_tokens(inp: Dict[str, object]) -> int:
-    """Query-head x token pairs one decode step scores."""
-    return int(inp["seq_lens"].to(torch.int64).sum()) * inp["num_heads"]
+    """(query token, query head, key token) triples one step scores."""
+    M = inp.get("num_queries", 1)
+    if M == 1:
+        return int(inp["seq_lens"].to(torch.int64).sum()) * inp["num_heads"]
+    return sum(causal_len(int(L), M, m) for L in inp["seq_lens"].tolist()
+               for m in range(M)) * inp["num_heads"]

@@ -11,6 +11,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_fp8 as FP8
+from tests import test_oracle_mq as MQ
 from tests import test_oracle_pins as PINS
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "paged_decode_oracle.c")
@@ -18,7 +19,7 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "paged_decode_oracle.c")
 # (name, text in the oracle source, replacement)
 MUTANTS = [
     ("gqa_mapping_modulo", "int32_t h = kh * G + g;", "int32_t h = g * pr->KH + kh;"),
-    ("query_indexed_by_kv_head", "dot += query_at(pr, s, h, d)", "dot += query_at(pr, s, kh, d)"),
+    ("query_indexed_by_kv_head", "dot += query_at(pr, r, h, d)", "dot += query_at(pr, r, kh, d)"),
     ("key_layout_token_major",
      "int64_t idx = ((((int64_t)b * pr->KH + kh) * (pr->D / x) + d / x) * pr->BS + o) * x + d % x;",
      "int64_t idx = ((((int64_t)b * pr->KH + kh) * pr->BS + o) * (pr->D / x) + d / x) * x + d % x;"),
@@ -32,12 +33,12 @@ MUTANTS = [
      "int32_t t1 = t0 + pr->PS - 1 < L ? t0 + pr->PS - 1 : L;"),
     ("partition_not_normalised", "for (int32_t d = 0; d < pr->D; ++d) o[d] /= l;", ""),
     ("sentinel_max_zero", "double m = -INFINITY, l = 0.0;", "double m = 0.0, l = 0.0;"),
-    ("combine_drops_exp_sums", "Z += exp(ml[base + p] - M) * es[base + p];",
-     "Z += exp(ml[base + p] - M);"),
-    ("combine_weight_sign", "double w = exp(ml[base + p] - M) * es[base + p] / Z;",
-     "double w = exp(M - ml[base + p]) * es[base + p] / Z;"),
-    ("combine_floor_partitions", "int32_t n = (seq_lens[s] + PS - 1) / PS;",
-     "int32_t n = seq_lens[s] / PS;"),
+    ("combine_drops_exp_sums", "Z += exp(ml[base + p] - Mx) * es[base + p];",
+     "Z += exp(ml[base + p] - Mx);"),
+    ("combine_weight_sign", "double w = exp(ml[base + p] - Mx) * es[base + p] / Z;",
+     "double w = exp(Mx - ml[base + p]) * es[base + p] / Z;"),
+    ("combine_floor_partitions", "int32_t n = (causal_len(seq_lens[s], M, mq) + PS - 1) / PS;",
+     "int32_t n = causal_len(seq_lens[s], M, mq) / PS;"),
     ("binary16_bias", "v = ldexp((double)(1024 + f), e - 25);",
      "v = ldexp((double)(1024 + f), e - 24);"),
     ("bfloat16_subnormal", "v = ldexp((double)f, -133);", "v = ldexp((double)f, -126);"),
@@ -52,8 +53,12 @@ MUTANTS = [
      "return load_elem(pr->vc, idx, pr->kvdtype);"),
     ("fp8_key_packing_8", "int32_t x = 16 / elem_size(pr->kvdtype);",
      "int32_t x = pr->kvdtype == ORACLE_FP8_E4M3 ? 8 : 16 / elem_size(pr->kvdtype);"),
-    ("query_decoded_as_cache", "((int64_t)s * pr->H + h) * pr->D + d, pr->qdtype)",
-     "((int64_t)s * pr->H + h) * pr->D + d, pr->kvdtype)"),
+    ("causal_off_by_one", "int32_t e = L - M + m + 1;", "int32_t e = L - M + m;"),
+    ("causal_top_left", "int32_t e = L - M + m + 1;", "int32_t e = m + 1;"),
+    ("query_row_ignores_token", "int64_t r = (int64_t)s * pr->M + mq;",
+     "int64_t r = (int64_t)s * pr->M;"),
+    ("query_decoded_as_cache", "(r * pr->H + h) * pr->D + d, pr->qdtype)",
+     "(r * pr->H + h) * pr->D + d, pr->kvdtype)"),
 ]
 
 
@@ -74,6 +79,9 @@ def battery():
         "fp8_brute_force": lambda: FP8.test_fp8_brute_force_tiny("bf16", 4, 2, 16, 2),
         "fp8_library_dense": lambda: FP8.test_fp8_library_routine_dense("bf16", 8, 2, 128, 16, 0),
         "fp8_repacked": FP8.test_fp8_equals_repacked_fp32_cache,
+        "mq_prefix": lambda: MQ.test_rows_equal_single_query_on_causal_prefix(2, "bf16"),
+        "mq_library": lambda: MQ.test_library_routine_causal(3, 4),
+        "mq_brute_force": MQ.test_brute_force_tiny,
     }
     failed = []
     for name, fn in checks.items():
