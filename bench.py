@@ -109,25 +109,42 @@ def run(args) -> dict:
     dev = torch.device("cuda", 0)
     q, kc, vc = (inp[k].to(dev) for k in ("query", "key_cache", "value_cache"))
     bt, sl = inp["block_tables"].to(dev), inp["seq_lens"].to(dev)
-    S, H, D = q.shape
-    out = torch.empty(S, H, D, dtype=torch.float32, device=dev)
-    tmp, es, ml = pa.workspace(S, H, D, P, dev)
+    MQ = cfg.num_queries
+    S, H, D = q.shape[0], q.shape[-2], q.shape[-1]
+    lead = (S,) if MQ == 1 else (S, MQ)
+
+    def work(P_):
+        return (torch.empty(*lead, H, P_, D, dtype=torch.float32, device=dev),
+                torch.empty(*lead, H, P_, dtype=torch.float32, device=dev),
+                torch.empty(*lead, H, P_, dtype=torch.float32, device=dev))
+
+    out = torch.empty(*lead, H, D, dtype=torch.float32, device=dev)
+    tmp, es, ml = work(P)
     stream = torch.cuda.current_stream(dev)
 
     fp8 = cfg.dtype == "fp8"
     ks, vs = inp["k_scale"], inp["v_scale"]
 
     def partition(tmp_, es_, ml_, PS_):
-        if fp8:
+        if MQ > 1:
+            pa.paged_attn_v2_partition_mq(tmp_, es_, ml_, q, kc, vc, bt, sl, inp["scale"], PS_,
+                                          ks, vs, stream)
+        elif fp8:
             pa.paged_attn_v2_partition_fp8(tmp_, es_, ml_, q, kc, vc, bt, sl, inp["scale"], ks, vs,
                                            PS_, stream)
         else:
             pa.paged_attn_v2_partition(tmp_, es_, ml_, q, kc, vc, bt, sl, inp["scale"], PS_,
                                        stream)
 
+    def reduce(tmp_, es_, ml_, PS_):
+        if MQ > 1:
+            pa.paged_attn_v2_reduce_mq(out, tmp_, es_, ml_, sl, PS_, stream)
+        else:
+            pa.paged_attn_v2_reduce(out, tmp_, es_, ml_, sl, PS_, stream)
+
     def step():
         partition(tmp, es, ml, PS)
-        pa.paged_attn_v2_reduce(out, tmp, es, ml, sl, PS, stream)
+        reduce(tmp, es, ml, PS)
 
     for _ in range(args.warmup):
         step()
@@ -149,7 +166,7 @@ def run(args) -> dict:
         ev[i][0].record(stream)
         partition(tmp, es, ml, PS)
         ev[i][1].record(stream)
-        pa.paged_attn_v2_reduce(out, tmp, es, ml, sl, PS, stream)
+        reduce(tmp, es, ml, PS)
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     part_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
@@ -162,10 +179,13 @@ def run(args) -> dict:
     # out does not depend on the partition size beyond rounding.
     PS_t = pa.default_partition_size(D, cfg.block_size, W.DTYPES[cfg.dtype], cfg.group)
     P_t = max(1, -(-cfg.max_len // PS_t))
-    tmp_t, es_t, ml_t = pa.workspace(S, H, D, P_t, dev)
+    tmp_t, es_t, ml_t = work(P_t)
 
     def step_tuned():
-        if fp8:
+        if MQ > 1:
+            pa.paged_attn_decode_mq(out, tmp_t, es_t, ml_t, q, kc, vc, bt, sl, inp["scale"], PS_t,
+                                    ks, vs, stream=stream)
+        elif fp8:
             pa.paged_attn_decode_fp8(out, tmp_t, es_t, ml_t, q, kc, vc, bt, sl, inp["scale"], ks,
                                      vs, PS_t, stream=stream)
         else:
@@ -186,7 +206,8 @@ def run(args) -> dict:
     step_s = elapsed / K
     gbs = kvb / step_s / 1e9
     achieved = kvb / part_avg_s / 1e9
-    kernel = ("partition_mfma_kernel" if (cfg.query_dtype != "f32" and 4 <= cfg.group <= 16)
+    kernel = ("partition_mfma_kernel"
+              if (cfg.query_dtype != "f32" and (4 <= cfg.group <= 16 or MQ > 1))
               else "partition_vec_kernel")
     traffic, traffic_src = committed_traffic(args.workload, kernel)
     res = {
@@ -213,12 +234,15 @@ def run(args) -> dict:
             "total_tokens": int(inp["seq_lens"].sum()), "kv_bytes_per_step": kvb,
             "num_blocks": inp["num_blocks"],
             **({"k_scale": inp["k_scale"], "v_scale": inp["v_scale"]} if fp8 else {}),
+            **({"num_queries": MQ} if MQ > 1 else {}),
         },
         "tuned": {
-            "entry": "paged_attn_decode_fp8" if fp8 else "paged_attn_decode",
+            "entry": ("paged_attn_decode_mq" if MQ > 1 else
+                      "paged_attn_decode_fp8" if fp8 else "paged_attn_decode"),
             "partition_size": PS_t, "max_num_partitions": P_t,
-            "partition_span": pa.partition_span(S, H, cfg.num_kv_heads, D, cfg.block_size, P_t,
-                                                PS_t, W.DTYPES[cfg.dtype]),
+            "partition_span": (None if MQ > 1 else
+                               pa.partition_span(S, H, cfg.num_kv_heads, D, cfg.block_size, P_t,
+                                                 PS_t, W.DTYPES[cfg.dtype])),
             "ms_per_step": round(tuned_s * 1e3, 5), "value": round(kvb / tuned_s / 1e9, 2),
             "unit": "GB/s", "pct_of_peak_hbm": round(100.0 * kvb / tuned_s / 1e9 / PEAK_HBM_GBS, 2),
             "qheads_tokens_per_s": round(W.qhead_tokens(inp) / tuned_s, 1),
@@ -232,8 +256,9 @@ def run(args) -> dict:
             "bytes_per_launch": kvb, "traffic_source": traffic_src,
             "kernel_source_hash": source_hash(),
             "reduce_avg_us": round(red_avg_s * 1e6, 3),
-            "partition_span": pa.partition_span(S, H, cfg.num_kv_heads, D, cfg.block_size, P, PS,
-                                                W.DTYPES[cfg.dtype]),
+            "partition_span": (None if MQ > 1 else
+                               pa.partition_span(S, H, cfg.num_kv_heads, D, cfg.block_size, P,
+                                                 PS, W.DTYPES[cfg.dtype])),
         },
     }
     if args.calibrate_copy:

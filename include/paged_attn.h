@@ -170,6 +170,58 @@ PA_API int paged_attn_decode_fp8(void* out, float* tmp_output, float* exp_sums,
                                  float k_scale, float v_scale, int32_t q_dtype, int32_t out_dtype,
                                  void* stream);
 
+/*
+ * Several query tokens per sequence (speculative decoding, chunked prefill
+ * over the paged cache). The Triton PagedAttention V2 page takes its gather
+ * from a multi-row (BLOCK_M) prefill kernel; the Flash Attention Metal page's
+ * forward kernel masks keys later than the query position. Reading taken:
+ * the M query tokens of sequence s are its last M positions (their keys and
+ * values are already in the cache, seq_lens counts them), so query token m
+ * sits at L - M + m and attends to keys t <= L - M + m (none if that is
+ * negative: its output row is 0). Everything else is per (sequence, query
+ * token, head) row:
+ *
+ *   query        [S, M, H, D]        q_dtype: PA_F16 or PA_BF16
+ *   key_cache / value_cache          as above, kv_dtype == q_dtype or PA_FP8_E4M3
+ *                                    (k_scale / v_scale apply to 8-bit caches;
+ *                                    pass 1 for 16-bit ones)
+ *   tmp_output   [S, M, H, P, D] fp32, exp_sums / max_logits [S, M, H, P] fp32
+ *   out          [S, M, H, D]        out_dtype PA_F32 or q_dtype
+ *
+ * A row's partitions past its causal prefix get the sentinels (max -inf, sum
+ * 0; tmp_output unspecified). Requires (H / KH) * M <= 16 (one MFMA column
+ * per (query token, head) of a kv head); PA_ERR_UNSUPPORTED otherwise.
+ * num_queries = 1 computes exactly what the single-query calls compute.
+ */
+PA_API int paged_attn_v2_partition_mq(float* tmp_output, float* exp_sums, float* max_logits,
+                                      const void* query, const void* key_cache,
+                                      const void* value_cache, const int32_t* block_tables,
+                                      const int32_t* seq_lens, int32_t num_seqs,
+                                      int32_t num_queries, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_size,
+                                      int32_t block_size, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t max_num_partitions,
+                                      int32_t partition_size, float scale, float k_scale,
+                                      float v_scale, int32_t q_dtype, int32_t kv_dtype,
+                                      void* stream);
+
+PA_API int paged_attn_v2_reduce_mq(void* out, const float* tmp_output, const float* exp_sums,
+                                   const float* max_logits, const int32_t* seq_lens,
+                                   int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                                   int32_t head_size, int32_t max_num_partitions,
+                                   int32_t partition_size, int32_t out_dtype, void* stream);
+
+PA_API int paged_attn_decode_mq(void* out, float* tmp_output, float* exp_sums, float* max_logits,
+                                const void* query, const void* key_cache,
+                                const void* value_cache, const int32_t* block_tables,
+                                const int32_t* seq_lens, int32_t num_seqs, int32_t num_queries,
+                                int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                int32_t block_size, int32_t num_blocks,
+                                int32_t max_blocks_per_seq, int32_t max_num_partitions,
+                                int32_t partition_size, float scale, float k_scale,
+                                float v_scale, int32_t q_dtype, int32_t kv_dtype,
+                                int32_t out_dtype, void* stream);
+
 /* Text of the last nonzero return on this thread ("" if none). Owned by the
  * library; valid until the next call on the same thread. */
 PA_API const char* paged_attn_last_error(void);

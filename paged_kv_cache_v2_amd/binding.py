@@ -33,6 +33,9 @@ _SIGS = {
     "paged_attn_partition_span": [_I32] * 8,
     "paged_attn_v2_partition_fp8": [_P] * 8 + [_I32] * 9 + [_F32, _F32, _F32, _I32, _P],
     "paged_attn_decode_fp8": [_P] * 9 + [_I32] * 9 + [_F32, _F32, _F32, _I32, _I32, _P],
+    "paged_attn_v2_partition_mq": [_P] * 8 + [_I32] * 10 + [_F32, _F32, _F32, _I32, _I32, _P],
+    "paged_attn_v2_reduce_mq": [_P] * 5 + [_I32] * 7 + [_P],
+    "paged_attn_decode_mq": [_P] * 9 + [_I32] * 10 + [_F32, _F32, _F32, _I32, _I32, _I32, _P],
 }
 
 
@@ -208,6 +211,78 @@ def paged_attn_decode_fp8(out, tmp_output, exp_sums, max_logits, query, key_cach
         seq_lens.data_ptr(), S, H, KH, D, BS, B, MB, P, partition_size, float(scale),
         float(k_scale), float(v_scale), _DT[query.dtype], _DT[out.dtype], _stream(query, stream))
     _check("paged_attn_decode_fp8", rc)
+
+
+def _mq_geometry(query, key_cache, value_cache, block_tables, seq_lens):
+    """(S, M, H, KH, D, BS, B, MB) for a [S, M, H, D] query."""
+    _need(query.dim() == 4, "query [S, M, H, D] expected (M query tokens per sequence)")
+    S, M, H, D = query.shape
+    q3 = query.view(S * M, H, D)
+    cache8 = key_cache.dtype == torch.float8_e4m3fn
+    _, _, KH, _, BS, B, MB = _kv_geometry(q3[:S], key_cache, value_cache, block_tables,
+                                          seq_lens, fp8=cache8)
+    return S, M, H, KH, D, BS, B, MB
+
+
+def _mq_stats_geometry(tmp_output, exp_sums, max_logits, S, M, H, D):
+    _need(all(t.dtype == torch.float32 and t.is_cuda and t.is_contiguous()
+              for t in (tmp_output, exp_sums, max_logits)),
+          "tmp_output, exp_sums, max_logits must be contiguous fp32 device tensors")
+    _need(tmp_output.dim() == 5 and tuple(tmp_output.shape[:3]) == (S, M, H) and
+          tmp_output.shape[4] == D, "tmp_output must be [S, M, H, P, D]")
+    P = tmp_output.shape[3]
+    _need(tuple(exp_sums.shape) == (S, M, H, P) and tuple(max_logits.shape) == (S, M, H, P),
+          "exp_sums and max_logits must be [S, M, H, P]")
+    return P
+
+
+def paged_attn_v2_partition_mq(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                               block_tables, seq_lens, scale: float, partition_size: int,
+                               k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    """Phase 1 for M query tokens per sequence (the last M positions, causal)."""
+    S, M, H, KH, D, BS, B, MB = _mq_geometry(query, key_cache, value_cache, block_tables,
+                                             seq_lens)
+    P = _mq_stats_geometry(tmp_output, exp_sums, max_logits, S, M, H, D)
+    rc = lib().paged_attn_v2_partition_mq(
+        tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(), query.data_ptr(),
+        key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+        seq_lens.data_ptr(), S, M, H, KH, D, BS, B, MB, P, partition_size, float(scale),
+        float(k_scale), float(v_scale), _DT[query.dtype], _CACHE_DT[key_cache.dtype],
+        _stream(query, stream))
+    _check("paged_attn_v2_partition_mq", rc)
+
+
+def paged_attn_v2_reduce_mq(out, tmp_output, exp_sums, max_logits, seq_lens, partition_size: int,
+                            stream=None) -> None:
+    """Phase 2 for M query tokens per sequence: out [S, M, H, D]."""
+    _need(out.dim() == 4 and out.dtype in _DT and out.is_cuda and out.is_contiguous(),
+          "out must be a contiguous [S, M, H, D] f32/f16/bf16 device tensor")
+    S, M, H, D = out.shape
+    P = _mq_stats_geometry(tmp_output, exp_sums, max_logits, S, M, H, D)
+    _need(seq_lens.dtype == torch.int32 and seq_lens.is_cuda and seq_lens.shape == (S,),
+          "seq_lens must be an int32 [S] device tensor")
+    rc = lib().paged_attn_v2_reduce_mq(
+        out.data_ptr(), tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
+        seq_lens.data_ptr(), S, M, H, D, P, partition_size, _DT[out.dtype], _stream(out, stream))
+    _check("paged_attn_v2_reduce_mq", rc)
+
+
+def paged_attn_decode_mq(out, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                         block_tables, seq_lens, scale: float, partition_size: int,
+                         k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    """Phase 1 then phase 2 for M query tokens per sequence, on one stream."""
+    S, M, H, KH, D, BS, B, MB = _mq_geometry(query, key_cache, value_cache, block_tables,
+                                             seq_lens)
+    P = _mq_stats_geometry(tmp_output, exp_sums, max_logits, S, M, H, D)
+    _need(out.dim() == 4 and tuple(out.shape) == (S, M, H, D) and out.dtype in _DT and
+          out.is_cuda and out.is_contiguous(), "out must be a contiguous [S, M, H, D] tensor")
+    rc = lib().paged_attn_decode_mq(
+        out.data_ptr(), tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
+        query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+        seq_lens.data_ptr(), S, M, H, KH, D, BS, B, MB, P, partition_size, float(scale),
+        float(k_scale), float(v_scale), _DT[query.dtype], _CACHE_DT[key_cache.dtype],
+        _DT[out.dtype], _stream(query, stream))
+    _check("paged_attn_decode_mq", rc)
 
 
 def workspace(num_seqs: int, num_heads: int, head_size: int, max_num_partitions: int,

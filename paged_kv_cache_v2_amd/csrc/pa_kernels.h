@@ -157,6 +157,7 @@ struct PartitionArgs {
   const int32_t* sl;
   int S, H, KH, MB, P, PS;
   int NB;          // physical blocks; block-table entries are clamped into [0, NB)
+  int M;           // query tokens per sequence (query [S, M, H, D]; 1: single-query decode)
   int C;           // consecutive partitions per workgroup (span), 1 .. kMaxSpan
   int through;     // 1: tmp_output stores with device-scope (sc1) policy
   float qk_scale;  // scale * log2(e) (times k_scale for an 8-bit cache)
@@ -171,14 +172,15 @@ constexpr int kMaxSpan = 2;
 struct LdsLayout {
   int bt_off, m_off, l_off, acc_off, total;
 };
-__host__ __device__ inline LdsLayout lds_layout(int PS, int BS, int G, int D, int C) {
+// NC = columns of a unit (query heads x query tokens).
+__host__ __device__ inline LdsLayout lds_layout(int PS, int BS, int NC, int D, int C) {
   LdsLayout o;
   auto up16 = [](int v) { return (v + 15) & ~15; };
   o.bt_off = 0;
   o.m_off = up16(C * (PS / BS) * 4);
-  o.l_off = o.m_off + up16(C * kWaves * G * 4);
-  o.acc_off = o.l_off + up16(C * kWaves * G * 4);
-  o.total = o.acc_off + C * kWaves * G * D * 4;
+  o.l_off = o.m_off + up16(C * kWaves * NC * 4);
+  o.acc_off = o.l_off + up16(C * kWaves * NC * 4);
+  o.total = o.acc_off + C * kWaves * NC * D * 4;
   return o;
 }
 
@@ -199,44 +201,53 @@ __device__ __forceinline__ void store_row(__amdgpu_buffer_rsrc_t r, uint32_t off
     __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, 0);
 }
 
-// Slot of (partition j of the span, wavefront w, head g) in the parked state.
-__device__ __forceinline__ int slot(int j, int w, int g, int G) { return (j * kWaves + w) * G + g; }
+// Slot of (partition j of the span, wavefront w, column c) in the parked state.
+__device__ __forceinline__ int slot(int j, int w, int c, int NC) { return (j * kWaves + w) * NC + c; }
 
 // Merge the NW parked states of each of the span's ne used partitions
 // (log2-domain max m, sum l, unnormalised accumulator) and store the
-// normalised outputs. Threads walk (head, partition, d) in memory order, so
-// the rows of adjacent partitions of one head are written together.
+// normalised outputs. A unit's columns are c = m*G + g: query token m
+// (of M) and query head kh*G + g; its output rows are ((s*M + m)*H + kh*G + g)
+// of the [S*M*H, P] statistics and [S*M*H, P, D] tmp_output. Threads walk
+// (column, partition, d) in memory order, so the rows of adjacent partitions
+// of one head are written together. A column whose causal prefix ends before
+// a used partition merges to max -inf, sum 0 (the empty-partition sentinels).
 template <int D>
 __device__ __forceinline__ void merge_store(const PartitionArgs& a, const float* s_m,
                                             const float* s_l, const float* s_acc, int s, int kh,
-                                            int p0, int ne, int G) {
+                                            int p0, int ne, int G, int M) {
   constexpr int D4 = D / 4;
-  const int per_head = ne * D4;
-  // The unit's G heads x P rows of tmp_output, addressed by 32-bit offsets.
+  const int NC = G * M;
+  const int per_col = ne * D4;
+  // The unit's rows of tmp_output (query tokens x heads x P), 32-bit offsets.
   const __amdgpu_buffer_rsrc_t tmp = __builtin_amdgcn_make_buffer_rsrc(
-      a.tmp_out + ((size_t)s * a.H + kh * G) * a.P * D, (short)0, G * a.P * D * 4, kRsrcFlags);
-  for (int i = threadIdx.x; i < G * per_head; i += kWaves * 64) {
-    const int g = i / per_head, rem = i - g * per_head;
+      a.tmp_out + ((size_t)s * M * a.H + kh * G) * a.P * D, (short)0,
+      ((M - 1) * a.H + G) * a.P * D * 4, kRsrcFlags);
+  for (int i = threadIdx.x; i < NC * per_col; i += kWaves * 64) {
+    const int c = i / per_col, rem = i - c * per_col;
     const int j = rem / D4, d4 = rem - j * D4;
-    float M = kNegInf;
+    const int m = c / G, g = c - m * G;
+    float Mx = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[slot(j, w, g, G)]);
+    for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[slot(j, w, c, NC)]);
+    const float Mu = Mx == kNegInf ? 0.0f : Mx;  // a column with no keys here: all weights 0
     float Z = 0.0f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const int k = slot(j, w, g, G);
-      const float e = fast_exp2(s_m[k] - M);  // 0 for a wavefront with no tokens
+      const int k = slot(j, w, c, NC);
+      const float e = fast_exp2(s_m[k] - Mu);  // 0 for a wavefront with no tokens
       Z += e * s_l[k];
       const f32x4 v = *(const f32x4*)&s_acc[k * D + 4 * d4];
       o += e * v;
     }
     const float inv = a.v_scale / Z;
-    const size_t row = ((size_t)s * a.H + kh * G + g) * a.P + p0 + j;
-    store_row(tmp, (uint32_t)(((g * a.P + p0 + j) * D + 4 * d4) * 4), o * inv, a.through);
+    const int hrow = m * a.H + g;  // row of this column relative to the unit's first
+    const size_t row = ((size_t)s * M * a.H + kh * G + hrow) * a.P + p0 + j;
+    store_row(tmp, (uint32_t)(((hrow * a.P + p0 + j) * D + 4 * d4) * 4), o * inv, a.through);
     if (d4 == 0) {
       a.exp_sums[row] = Z;
-      a.max_logits[row] = M * kLn2;
+      a.max_logits[row] = Mx * kLn2;
     }
   }
 }
@@ -244,6 +255,7 @@ __device__ __forceinline__ void merge_store(const PartitionArgs& a, const float*
 // A work unit: sequence s, kv head kh, partitions p0 .. p0+nparts-1.
 struct Unit {
   int s, kh, p0, nparts, G, L, pg0;
+  int M, NC;       // query tokens per sequence; columns G * M
   int npages;      // used pages of the span (contiguous from its first page)
   int ne;          // used partitions of the span
   int32_t bt_val;  // this thread's entry of the span's block-table slice
@@ -262,6 +274,8 @@ __device__ __forceinline__ void unit_begin(const PartitionArgs& a, Unit& u) {
   u.p0 = (rest / a.S) * a.C;
   u.nparts = min(a.C, a.P - u.p0);
   u.G = a.H / a.KH;
+  u.M = a.M;
+  u.NC = u.G * a.M;
   const int pps = a.PS / BS;
   u.pg0 = u.p0 * pps;
   const int nspec = min(u.nparts * pps, a.MB - u.pg0);
@@ -274,10 +288,11 @@ __device__ __forceinline__ void unit_begin(const PartitionArgs& a, Unit& u) {
 // block-table slice to LDS for the whole workgroup.
 template <int BS>
 __device__ __forceinline__ bool unit_hoist(const PartitionArgs& a, int32_t* s_bt, Unit& u) {
-  if ((int)threadIdx.x < u.nparts * u.G) {
-    const int j = threadIdx.x / u.G, g = threadIdx.x % u.G;
+  if ((int)threadIdx.x < u.nparts * u.NC) {
+    const int j = threadIdx.x / u.NC, c = threadIdx.x % u.NC;
+    const int m = c / u.G, g = c - m * u.G;
     if ((u.p0 + j) * a.PS >= u.L) {
-      const size_t row = ((size_t)u.s * a.H + u.kh * u.G + g) * a.P + u.p0 + j;
+      const size_t row = (((size_t)u.s * u.M + m) * a.H + u.kh * u.G + g) * a.P + u.p0 + j;
       a.max_logits[row] = kNegInf;
       a.exp_sums[row] = 0.0f;
     }
@@ -353,25 +368,30 @@ partition_mfma_kernel(PartitionArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   Unit u;
   unit_begin<BS>(a, u);
-  const int G = u.G;
+  const int G = u.G, NC = u.NC;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane & 15, grp = lane >> 4;
+  const int g = lane & 15, grp = lane >> 4;  // g: this lane's column (and token row in a tile)
+  // Column g < NC is query head kh*G + g%G of query token g/G, which sees
+  // tokens t < lim (the causal prefix; L for single-query decode).
+  const int qtok = g < NC ? g / G : 0;
+  const int lim = min(u.L, max(0, u.L - u.M + qtok + 1));
 
-  // Q group as the QK B operand, k-step m: lane holds 8 consecutive d of head
-  // g, d = 32m + 8*grp (16-bit cache) or 16*(4*(m/2) + grp) + 8*(m%2) (8-bit).
+  // Q columns as the QK B operand, k-step m: lane holds 8 consecutive d of its
+  // column, d = 32m + 8*grp (16-bit cache) or 16*(4*(m/2) + grp) + 8*(m%2) (8-bit).
   u32x4 qb[KS];
   {
     const uint16_t* qrow =
-        (const uint16_t*)a.q + ((size_t)u.s * a.H + u.kh * G + (g < G ? g : 0)) * D;
+        (const uint16_t*)a.q +
+        (((size_t)u.s * u.M + qtok) * a.H + u.kh * G + (g < NC ? g - qtok * G : 0)) * D;
 #pragma unroll
     for (int m = 0; m < KS; ++m) {
       const int d0 = KV8 ? 16 * (4 * (m / 2) + grp) + 8 * (m % 2) : 32 * m + 8 * grp;
       u32x4 v = *(const u32x4*)(qrow + d0);
-      qb[m] = g < G ? v : u32x4{0u, 0u, 0u, 0u};
+      qb[m] = g < NC ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
   if (!unit_hoist<BS>(a, (int32_t*)smem, u)) return;
-  const LdsLayout lay = lds_layout(a.PS, BS, G, D, a.C);
+  const LdsLayout lay = lds_layout(a.PS, BS, NC, D, a.C);
   const int32_t* s_bt = (const int32_t*)(smem + lay.bt_off);
   float* s_m = (float*)(smem + lay.m_off);
   float* s_l = (float*)(smem + lay.l_off);
@@ -400,8 +420,8 @@ partition_mfma_kernel(PartitionArgs a) {
   int jcur = 0, next_edge = pps;  // next_edge: first page of partition jcur + 1
   auto park = [&]() {
     const float ls = rows_sum(lsum);
-    if (g < G) {
-      const int k = slot(jcur, wave, g, G);
+    if (g < NC) {
+      const int k = slot(jcur, wave, g, NC);
       if (grp == 0) {
         s_m[k] = m;
         s_l[k] = ls;
@@ -475,7 +495,7 @@ partition_mfma_kernel(PartitionArgs a) {
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mk = 0; mk < KS; ++mk) sc = M::qk(k_operand(pg, st, mk), qb[mk], sc);
-      const int nvalid = u.L - (tok0 + 16 * st + 4 * grp);  // row 4*grp+r valid iff r < nvalid
+      const int nvalid = lim - (tok0 + 16 * st + 4 * grp);  // row 4*grp+r valid iff r < nvalid
 #pragma unroll
       for (int r = 0; r < 4; ++r) s2[st][r] = r < nvalid ? sc[r] * a.qk_scale : kNegInf;
     }
@@ -546,7 +566,7 @@ partition_mfma_kernel(PartitionArgs a) {
   pipeline<PF>(npg, ring, fetch, process);
   while (jcur < u.ne) park();
   __syncthreads();
-  merge_store<D>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G);
+  merge_store<D>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G, u.M);
 }
 
 // =====================================================================
@@ -782,12 +802,14 @@ partition_vec_kernel(PartitionArgs a) {
   pipeline<PF>(npg, ring, fetch, process);
   while (jcur < u.ne) park();
   __syncthreads();
-  merge_store<D>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G);
+  merge_store<D>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G, 1);
 }
 
 // =====================================================================
 // Reduce: the page's phase-2 log-sum-exp combine over the n = ceil(L / PS)
-// partitions a sequence uses, for one (sequence, query head) row per WPI
+// partitions a row's keys use (L: the sequence length, or a query token's
+// causal prefix when there are several per sequence), for one (sequence,
+// query token, query head) row per WPI
 // wavefronts (WPI = 1, 2 or 4, from the partition count, so that long
 // sequences spread their rows over a whole workgroup).
 //  - First round trip: the sequence length and the first 64 partitions'
@@ -809,7 +831,8 @@ struct ReduceArgs {
   const float* max_logits;
   const int32_t* sl;
   int S, H, P, PS;
-  int WPI;  // wavefronts per (sequence, head) row: 1, 2 or 4
+  int M;    // query tokens per sequence (rows are (sequence, query token, head))
+  int WPI;  // wavefronts per row: 1, 2 or 4
 };
 
 constexpr int kReduceU = 8;  // partition rows per lane in flight
@@ -831,16 +854,19 @@ __global__ void __launch_bounds__(kWaves * 64) reduce_kernel(ReduceArgs a) {
   const int sh = blockIdx.x * (kWaves / WPI) + wave / WPI;
   const int wi = wave % WPI;
   const int sub = lane / LPR, c4 = lane % LPR;
-  const bool live = sh < a.S * a.H;
+  const bool live = sh < a.S * a.M * a.H;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (live) {
-    const int s = sh / a.H;
+    const int sm = sh / a.H;               // query row: sequence s, query token qm
+    const int s = sm / a.M, qm = sm - s * a.M;
     const float* mlr = a.max_logits + (size_t)sh * a.P;
     const float* esr = a.exp_sums + (size_t)sh * a.P;
     const float* trow = a.tmp_out + (size_t)sh * a.P * D + 4 * c4;
     // Independent loads: length and the first 64 partitions' statistics.
-    const int L = a.sl[s];
+    const int L0 = a.sl[s];
+    // keys query token qm sees: the causal prefix (L0 for single-query decode)
+    const int L = min(L0, max(0, L0 - a.M + qm + 1));
     float mi = lane < a.P ? mlr[lane] : kNegInf;
     float li = lane < a.P ? esr[lane] : 0.0f;
     const int n = L > 0 ? min((L - 1) / a.PS + 1, a.P) : 0;  // P bounds a length past P*PS

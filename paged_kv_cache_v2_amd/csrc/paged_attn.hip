@@ -129,12 +129,12 @@ constexpr int kThroughMinPartitions = 16;
 constexpr long long kSpanBytes = 512 * 1024;
 constexpr int kSpanLdsCap = 64 * 1024;
 
-int pick_span(int S, int KH, int P, int PS, int BS, int G, int D, int esz, int lds_limit) {
+int pick_span(int S, int KH, int P, int PS, int BS, int NC, int D, int esz, int lds_limit) {
   int best = 1;
   for (int c = 2; c <= pa::kMaxSpan; c *= 2) {
     const long long grid = (long long)S * KH * ((P + c - 1) / c);
     const long long bytes = (long long)c * PS * D * esz * 2;
-    const int lds = pa::lds_layout(PS, BS, G, D, c).total;
+    const int lds = pa::lds_layout(PS, BS, NC, D, c).total;
     if (c * (PS / BS) > pa::kWaves * 64 || lds > kSpanLdsCap || lds > lds_limit) break;
     if (PA_SPAN > 0) {
       if (c > PA_SPAN) break;
@@ -152,9 +152,10 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
                     const void* key_cache, const void* value_cache, const int32_t* block_tables,
                     const int32_t* seq_lens, int32_t S, int32_t H, int32_t KH, int32_t D,
                     int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS, int32_t qdt,
-                    int32_t kvdt, Plan* plan) {
+                    int32_t kvdt, int32_t M, Plan* plan) {
   if (S < 0 || H < 0 || KH < 0 || D < 0 || BS < 0 || NB < 0 || MB < 0 || P < 0)
     return fail(PA_ERR_SHAPE, "negative size argument");
+  if (M < 1) return fail(PA_ERR_SHAPE, "num_queries must be >= 1");
   if (S == 0) {
     plan->fn = nullptr;
     return PA_OK;  // nothing to do; pointers of empty tensors may be NULL
@@ -185,7 +186,14 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
     return fail(PA_ERR_UNSUPPORTED, "partition_size / block_size > %d", pa::kWaves * 64);
   const int G = H / KH;
   partition_fn fn = nullptr;
-  if (is_16bit(qdt) && G >= 4 && G <= 16) {
+  if (M > 1) {
+    // several query tokens: the MFMA path, one column per (query token, head)
+    if (!is_16bit(qdt) || (long long)G * M > 16)
+      return fail(PA_ERR_UNSUPPORTED,
+                  "several query tokens need an f16/bf16 query and group * num_queries <= 16 "
+                  "(got %d x %d)", G, M);
+    fn = kvdt == PA_FP8_E4M3 ? kMfma8[qdt - 1][di][bi] : kMfma[qdt - 1][di][bi];
+  } else if (is_16bit(qdt) && G >= 4 && G <= 16) {
     fn = kvdt == PA_FP8_E4M3 ? kMfma8[qdt - 1][di][bi] : kMfma[qdt - 1][di][bi];
   } else if (G <= 4) {
     const int gi = G == 1 ? 0 : G == 2 ? 1 : 2;
@@ -196,18 +204,19 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
       !aligned16(tmp_output))
     return fail(PA_ERR_ALIGN, "query, key_cache, value_cache and tmp_output must be 16-byte aligned");
-  if ((long long)G * P * D * 4 > 0x7fffffffLL)
-    return fail(PA_ERR_UNSUPPORTED, "tmp_output rows of one kv head exceed 2 GiB");
+  if (((long long)(M - 1) * H + G) * P * D * 4 > 0x7fffffffLL)
+    return fail(PA_ERR_UNSUPPORTED, "tmp_output rows of one (sequence, kv head) exceed 2 GiB");
+  const int NC = G * M;  // columns of a work unit
   const int lds_limit = max_lds_per_block();
-  const int lds1 = pa::lds_layout(PS, BS, G, D, 1).total;
+  const int lds1 = pa::lds_layout(PS, BS, NC, D, 1).total;
   if (lds1 > lds_limit)
     return fail(PA_ERR_UNSUPPORTED, "needs %d bytes of LDS per workgroup, device allows %d", lds1,
                 lds_limit);
-  const int span = pick_span(S, KH, P, PS, BS, G, D, elem_size(kvdt), lds_limit);
+  const int span = pick_span(S, KH, P, PS, BS, NC, D, elem_size(kvdt), lds_limit);
   const long long grid = (long long)S * KH * ((P + span - 1) / span);
   if (grid > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many work units");
   plan->fn = fn;
-  plan->lds_bytes = pa::lds_layout(PS, BS, G, D, span).total;
+  plan->lds_bytes = pa::lds_layout(PS, BS, NC, D, span).total;
   plan->grid = (int)grid;
   plan->span = span;
   return PA_OK;
@@ -217,7 +226,7 @@ int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float
                      const void* query, const void* key_cache, const void* value_cache,
                      const int32_t* block_tables, const int32_t* seq_lens, int32_t S, int32_t H,
                      int32_t KH, int32_t NB, int32_t MB, int32_t P, int32_t PS, float scale,
-                     float k_scale, float v_scale, hipStream_t stream) {
+                     float k_scale, float v_scale, int32_t M, hipStream_t stream) {
   PartitionArgs a;
   a.tmp_out = tmp_output;
   a.exp_sums = exp_sums;
@@ -234,6 +243,7 @@ int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float
   a.P = P;
   a.PS = PS;
   a.NB = NB;
+  a.M = M;
   a.C = plan.span;
   a.through = P >= kThroughMinPartitions;
   a.qk_scale = scale * k_scale * pa::kLog2e;
@@ -245,9 +255,10 @@ int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float
 }
 
 int check_reduce(void* out, const float* tmp_output, const float* exp_sums,
-                 const float* max_logits, const int32_t* seq_lens, int32_t S, int32_t H,
-                 int32_t D, int32_t P, int32_t PS, int32_t odt, reduce_fn* fn) {
+                 const float* max_logits, const int32_t* seq_lens, int32_t S, int32_t M,
+                 int32_t H, int32_t D, int32_t P, int32_t PS, int32_t odt, reduce_fn* fn) {
   if (S < 0 || H < 0 || D < 0 || P < 0) return fail(PA_ERR_SHAPE, "negative size argument");
+  if (M < 1) return fail(PA_ERR_SHAPE, "num_queries must be >= 1");
   if (S == 0) {
     *fn = nullptr;
     return PA_OK;
@@ -263,14 +274,14 @@ int check_reduce(void* out, const float* tmp_output, const float* exp_sums,
   if (di < 0) return fail(PA_ERR_UNSUPPORTED, "head_size %d not in {64, 128, 256}", D);
   if (!aligned16(out) || !aligned16(tmp_output))
     return fail(PA_ERR_ALIGN, "out and tmp_output must be 16-byte aligned");
-  if ((long long)S * H > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many rows");
+  if ((long long)S * M * H > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many rows");
   *fn = kReduce[odt][di];
   return PA_OK;
 }
 
 int launch_reduce(reduce_fn fn, void* out, const float* tmp_output, const float* exp_sums,
-                  const float* max_logits, const int32_t* seq_lens, int32_t S, int32_t H,
-                  int32_t D, int32_t P, int32_t PS, hipStream_t stream) {
+                  const float* max_logits, const int32_t* seq_lens, int32_t S, int32_t M,
+                  int32_t H, int32_t D, int32_t P, int32_t PS, hipStream_t stream) {
   ReduceArgs a;
   a.out = out;
   a.tmp_out = tmp_output;
@@ -281,8 +292,9 @@ int launch_reduce(reduce_fn fn, void* out, const float* tmp_output, const float*
   a.H = H;
   a.P = P;
   a.PS = PS;
+  a.M = M;
   a.WPI = pa::reduce_waves_per_row(P, D);
-  const long long rows = (long long)S * H;
+  const long long rows = (long long)S * M * H;
   const int rows_per_block = pa::kWaves / a.WPI;
   hipLaunchKernelGGL(fn, dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
                      dim3(pa::kWaves * 64), 0, stream, a);
@@ -295,27 +307,28 @@ bool finite(float v) { return v == v && v - v == 0.0f; }
 
 int partition_entry(float* tmp_output, float* exp_sums, float* max_logits, const void* query,
                     const void* key_cache, const void* value_cache, const int32_t* block_tables,
-                    const int32_t* seq_lens, int32_t S, int32_t H, int32_t KH, int32_t D,
-                    int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS, float scale,
-                    float k_scale, float v_scale, int32_t qdt, int32_t kvdt, void* stream) {
+                    const int32_t* seq_lens, int32_t S, int32_t M, int32_t H, int32_t KH,
+                    int32_t D, int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS,
+                    float scale, float k_scale, float v_scale, int32_t qdt, int32_t kvdt,
+                    void* stream) {
   g_err[0] = 0;
   if (!finite(k_scale) || !finite(v_scale))
     return fail(PA_ERR_SHAPE, "k_scale and v_scale must be finite");
   Plan plan;
   int rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                            block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt,
-                           &plan);
+                           M, &plan);
   if (rc != PA_OK || S == 0) return rc;
   return launch_partition(plan, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                           block_tables, seq_lens, S, H, KH, NB, MB, P, PS, scale, k_scale,
-                          v_scale, (hipStream_t)stream);
+                          v_scale, M, (hipStream_t)stream);
 }
 
 int decode_entry(void* out, float* tmp_output, float* exp_sums, float* max_logits,
                  const void* query, const void* key_cache, const void* value_cache,
-                 const int32_t* block_tables, const int32_t* seq_lens, int32_t S, int32_t H,
-                 int32_t KH, int32_t D, int32_t BS, int32_t NB, int32_t MB, int32_t P,
-                 int32_t PS, float scale, float k_scale, float v_scale, int32_t qdt,
+                 const int32_t* block_tables, const int32_t* seq_lens, int32_t S, int32_t M,
+                 int32_t H, int32_t KH, int32_t D, int32_t BS, int32_t NB, int32_t MB,
+                 int32_t P, int32_t PS, float scale, float k_scale, float v_scale, int32_t qdt,
                  int32_t kvdt, int32_t out_dtype, void* stream) {
   g_err[0] = 0;
   if (!finite(k_scale) || !finite(v_scale))
@@ -323,19 +336,19 @@ int decode_entry(void* out, float* tmp_output, float* exp_sums, float* max_logit
   Plan plan;
   int rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                            block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt,
-                           &plan);
+                           M, &plan);
   if (rc != PA_OK || S == 0) return rc;
   if (out_dtype != PA_F32 && out_dtype != qdt)
     return fail(PA_ERR_UNSUPPORTED, "out dtype must be PA_F32 or the query dtype");
   reduce_fn fn = nullptr;
-  rc = check_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, S, H, D, P, PS, out_dtype,
-                    &fn);
+  rc = check_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, S, M, H, D, P, PS,
+                    out_dtype, &fn);
   if (rc != PA_OK) return rc;
   rc = launch_partition(plan, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                         block_tables, seq_lens, S, H, KH, NB, MB, P, PS, scale, k_scale, v_scale,
-                        (hipStream_t)stream);
+                        M, (hipStream_t)stream);
   if (rc != PA_OK) return rc;
-  return launch_reduce(fn, out, tmp_output, exp_sums, max_logits, seq_lens, S, H, D, P, PS,
+  return launch_reduce(fn, out, tmp_output, exp_sums, max_logits, seq_lens, S, M, H, D, P, PS,
                        (hipStream_t)stream);
 }
 
@@ -356,7 +369,7 @@ int paged_attn_v2_partition(float* tmp_output, float* exp_sums, float* max_logit
     return fail(PA_ERR_UNSUPPORTED, "8-bit caches go through paged_attn_v2_partition_fp8");
   }
   return partition_entry(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
-                         block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                         block_tables, seq_lens, num_seqs, 1, num_heads, num_kv_heads, head_size,
                          block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
                          partition_size, scale, 1.0f, 1.0f, kv_dtype, kv_dtype, stream);
 }
@@ -370,7 +383,7 @@ int paged_attn_v2_partition_fp8(float* tmp_output, float* exp_sums, float* max_l
                                 int32_t max_num_partitions, int32_t partition_size, float scale,
                                 float k_scale, float v_scale, int32_t q_dtype, void* stream) {
   return partition_entry(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
-                         block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                         block_tables, seq_lens, num_seqs, 1, num_heads, num_kv_heads, head_size,
                          block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
                          partition_size, scale, k_scale, v_scale, q_dtype, PA_FP8_E4M3, stream);
 }
@@ -381,11 +394,12 @@ int paged_attn_v2_reduce(void* out, const float* tmp_output, const float* exp_su
                          int32_t partition_size, int32_t out_dtype, void* stream) {
   g_err[0] = 0;
   reduce_fn fn = nullptr;
-  int rc = check_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, num_seqs, num_heads,
+  int rc = check_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, num_seqs, 1, num_heads,
                         head_size, max_num_partitions, partition_size, out_dtype, &fn);
   if (rc != PA_OK || num_seqs == 0) return rc;
-  return launch_reduce(fn, out, tmp_output, exp_sums, max_logits, seq_lens, num_seqs, num_heads,
-                       head_size, max_num_partitions, partition_size, (hipStream_t)stream);
+  return launch_reduce(fn, out, tmp_output, exp_sums, max_logits, seq_lens, num_seqs, 1,
+                       num_heads, head_size, max_num_partitions, partition_size,
+                       (hipStream_t)stream);
 }
 
 int paged_attn_decode(void* out, float* tmp_output, float* exp_sums, float* max_logits,
@@ -400,7 +414,7 @@ int paged_attn_decode(void* out, float* tmp_output, float* exp_sums, float* max_
     return fail(PA_ERR_UNSUPPORTED, "8-bit caches go through paged_attn_decode_fp8");
   }
   return decode_entry(out, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
-                      block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                      block_tables, seq_lens, num_seqs, 1, num_heads, num_kv_heads, head_size,
                       block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
                       partition_size, scale, 1.0f, 1.0f, kv_dtype, kv_dtype, out_dtype, stream);
 }
@@ -414,9 +428,55 @@ int paged_attn_decode_fp8(void* out, float* tmp_output, float* exp_sums, float* 
                           float k_scale, float v_scale, int32_t q_dtype, int32_t out_dtype,
                           void* stream) {
   return decode_entry(out, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
-                      block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_size,
+                      block_tables, seq_lens, num_seqs, 1, num_heads, num_kv_heads, head_size,
                       block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
                       partition_size, scale, k_scale, v_scale, q_dtype, PA_FP8_E4M3, out_dtype,
+                      stream);
+}
+
+int paged_attn_v2_partition_mq(float* tmp_output, float* exp_sums, float* max_logits,
+                               const void* query, const void* key_cache, const void* value_cache,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t max_num_partitions, int32_t partition_size, float scale,
+                               float k_scale, float v_scale, int32_t q_dtype, int32_t kv_dtype,
+                               void* stream) {
+  return partition_entry(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                         block_tables, seq_lens, num_seqs, num_queries, num_heads, num_kv_heads,
+                         head_size, block_size, num_blocks, max_blocks_per_seq,
+                         max_num_partitions, partition_size, scale, k_scale, v_scale, q_dtype,
+                         kv_dtype, stream);
+}
+
+int paged_attn_v2_reduce_mq(void* out, const float* tmp_output, const float* exp_sums,
+                            const float* max_logits, const int32_t* seq_lens, int32_t num_seqs,
+                            int32_t num_queries, int32_t num_heads, int32_t head_size,
+                            int32_t max_num_partitions, int32_t partition_size,
+                            int32_t out_dtype, void* stream) {
+  g_err[0] = 0;
+  reduce_fn fn = nullptr;
+  int rc = check_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, num_seqs, num_queries,
+                        num_heads, head_size, max_num_partitions, partition_size, out_dtype, &fn);
+  if (rc != PA_OK || num_seqs == 0) return rc;
+  return launch_reduce(fn, out, tmp_output, exp_sums, max_logits, seq_lens, num_seqs,
+                       num_queries, num_heads, head_size, max_num_partitions, partition_size,
+                       (hipStream_t)stream);
+}
+
+int paged_attn_decode_mq(void* out, float* tmp_output, float* exp_sums, float* max_logits,
+                         const void* query, const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                         int32_t num_queries, int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_size, int32_t block_size, int32_t num_blocks,
+                         int32_t max_blocks_per_seq, int32_t max_num_partitions,
+                         int32_t partition_size, float scale, float k_scale, float v_scale,
+                         int32_t q_dtype, int32_t kv_dtype, int32_t out_dtype, void* stream) {
+  return decode_entry(out, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                      block_tables, seq_lens, num_seqs, num_queries, num_heads, num_kv_heads,
+                      head_size, block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
+                      partition_size, scale, k_scale, v_scale, q_dtype, kv_dtype, out_dtype,
                       stream);
 }
 

@@ -137,13 +137,26 @@ FP8_CONFIGS: Dict[str, DecodeConfig] = {
 FP8_ORDER = ["gqa_fp8_g4", "longctx_fp8_g8", "mha_fp8_d128"]
 CONFIGS.update(FP8_CONFIGS)
 
+# Several query tokens per sequence (speculative decoding: the last M positions
+# of each sequence query the cache causally): the GQA workload with 4 tokens
+# (4 heads x 4 tokens fill one 16-column tile) and the long-context one with 2.
+MQ_CONFIGS: Dict[str, DecodeConfig] = {
+    "gqa_bf16_g4_m4": CONFIGS["gqa_bf16_g4"].replace(name="gqa_bf16_g4_m4", num_queries=4),
+    "longctx_bf16_g8_m2": CONFIGS["longctx_bf16_g8"].replace(name="longctx_bf16_g8_m2",
+                                                            num_queries=2),
+}
+MQ_ORDER = ["gqa_bf16_g4_m4", "longctx_bf16_g8_m2"]
+CONFIGS.update(MQ_CONFIGS)
+
 
 def workload_seed(name: str) -> int:
     """Seed of a named workload's reported runs: its index in its list, plus 1
-    (the 8-bit workloads from 101)."""
+    (the 8-bit workloads from 101, the multi-token ones from 201)."""
     if name in CONFIG_ORDER:
         return CONFIG_ORDER.index(name) + 1
-    return FP8_ORDER.index(name) + 101
+    if name in FP8_ORDER:
+        return FP8_ORDER.index(name) + 101
+    return MQ_ORDER.index(name) + 201
 
 
 def _workers() -> int:

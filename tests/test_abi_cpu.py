@@ -156,6 +156,24 @@ def test_fp8_partition_rejects(kw, code):
     assert pa.last_error() != ""
 
 
+def part_mq(M=2, q_dtype=binding.PA_BF16, kv_dtype=binding.PA_BF16, **kw):
+    a = dict(BASE, **kw)
+    return pa.lib().paged_attn_v2_partition_mq(*([FAKE] * 8), a["S"], M, a["H"], a["KH"], a["D"],
+                                               a["BS"], a["B"], a["MB"], a["P"], a["PS"], 0.125,
+                                               1.0, 1.0, q_dtype, kv_dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=0), binding.PA_ERR_SHAPE),
+    (dict(M=5), binding.PA_ERR_UNSUPPORTED),                   # G=4 x 5 > 16 columns
+    (dict(q_dtype=binding.PA_F32, kv_dtype=binding.PA_F32), binding.PA_ERR_UNSUPPORTED),
+    (dict(q_dtype=binding.PA_F16, kv_dtype=binding.PA_BF16), binding.PA_ERR_UNSUPPORTED),
+])
+def test_multi_token_rejects(kw, code):
+    assert part_mq(**kw) == code
+    assert pa.last_error() != ""
+
+
 def test_plain_calls_reject_8bit_cache():
     assert part(dt=binding.PA_FP8_E4M3) == binding.PA_ERR_UNSUPPORTED
     assert decode(binding.PA_F32, dt=binding.PA_FP8_E4M3) == binding.PA_ERR_UNSUPPORTED

@@ -1,0 +1,141 @@
+"""Several query tokens per sequence (the last M positions, causal) through the C ABI.
+
+Every output row and every partition intermediate is compared with the
+oracle's multi-token mode (which is pinned to the single-query oracle on each
+row's causal prefix): several (group, M) mixes that fill one MFMA column tile
+(G * M <= 16), 8-bit caches, lengths shorter than M, equal to M and at block /
+partition edges, the two-call and one-call forms, and M = 1 against the
+single-query entry points bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_v2_amd as pa
+from paged_kv_cache_v2_amd import workloads as W
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    pa.ensure_built()
+    oracle.build(force=False)
+
+
+def run_mq(d, PS, P, split=False, out_dtype=torch.float32):
+    q = d["query"]
+    S, M, H, D = q.shape
+    tmp = torch.full((S, M, H, P, D), float("nan"), device=U.DEV)
+    es = torch.full((S, M, H, P), float("nan"), device=U.DEV)
+    ml = torch.full((S, M, H, P), float("nan"), device=U.DEV)
+    out = torch.full((S, M, H, D), float("nan"), device=U.DEV).to(out_dtype)
+    args = (q, d["key_cache"], d["value_cache"], d["block_tables"], d["seq_lens"], d["scale"], PS)
+    sc = dict(k_scale=d.get("k_scale", 1.0), v_scale=d.get("v_scale", 1.0))
+    if split:
+        pa.paged_attn_v2_partition_mq(tmp, es, ml, *args, **sc)
+        pa.paged_attn_v2_reduce_mq(out, tmp, es, ml, d["seq_lens"], PS)
+    else:
+        pa.paged_attn_decode_mq(out, tmp, es, ml, *args, **sc)
+    torch.cuda.synchronize()
+    return dict(out=out.cpu(), tmp=tmp.cpu(), es=es.cpu(), ml=ml.cpu())
+
+
+def check(inp, res, PS, P, label):
+    a = (inp["query"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
+         inp["seq_lens"], inp["scale"])
+    sc = dict(k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+    ref = oracle.attention(*a, **sc)
+    U.assert_close(f"{label} out", res["out"].float(), ref)
+    tmp, es, ml = oracle.partition_stats(*a, P, PS, **sc)
+    M = inp["query"].shape[1]
+    for s, L in enumerate(inp["seq_lens"].tolist()):
+        for m in range(M):
+            n = -(-W.causal_len(L, M, m) // PS)
+            if n:
+                U.assert_close(f"{label} ml s={s} m={m}", res["ml"][s, m, :, :n], ml[s, m, :, :n])
+                U.assert_close(f"{label} es s={s} m={m}", res["es"][s, m, :, :n], es[s, m, :, :n])
+                U.assert_close(f"{label} tmp s={s} m={m}", res["tmp"][s, m, :, :n],
+                               tmp[s, m, :, :n])
+            assert torch.all(res["ml"][s, m, :, n:] == -math.inf), (label, s, m)
+            assert torch.all(res["es"][s, m, :, n:] == 0), (label, s, m)
+
+
+def mq_geom(dtype, H, KH, D, BS, PS, M, lens, q_dtype=None, **kw):
+    return W.DecodeConfig(f"mq_{dtype}", num_seqs=len(lens), num_heads=H, num_kv_heads=KH,
+                          head_size=D, block_size=BS, partition_size=PS, dtype=dtype,
+                          q_dtype=q_dtype, len_lo=0, len_hi=max(max(lens), 1), num_queries=M,
+                          **kw)
+
+
+# dtype, H, KH, D, BS, PS, M
+CASES = [
+    ("bf16", 32, 8, 128, 16, 64, 4),    # G=4 x M=4: a full column tile
+    ("bf16", 64, 8, 128, 16, 64, 2),    # G=8 x M=2
+    ("f16", 8, 8, 128, 16, 64, 8),      # G=1 x M=8
+    ("bf16", 16, 8, 64, 32, 64, 3),     # G=2 x M=3 (6 columns), D=64, BS=32
+    ("f16", 16, 2, 256, 16, 128, 2),    # G=8 x M=2, D=256
+    ("fp8", 32, 8, 128, 16, 64, 4),     # 8-bit cache, G=4 x M=4
+    ("fp8", 8, 4, 256, 32, 64, 5),      # 8-bit cache, G=2 x M=5, D=256, BS=32
+]
+
+
+@pytest.mark.parametrize("c", CASES, ids=lambda c: "_".join(map(str, c)))
+@pytest.mark.parametrize("split", [False, True], ids=["decode", "split"])
+def test_multi_token_parity(c, split):
+    dtype, H, KH, D, BS, PS, M = c
+    lens = [0, 1, M - 1, M, M + 1, BS, PS - 1, PS, PS + M - 1, 2 * PS + 3, 3 * PS]
+    kw = dict(q_dtype="bf16" if H // KH != 1 else "f16", k_scale=0.03, v_scale=0.045) \
+        if dtype == "fp8" else {}
+    cfg = mq_geom(dtype, H, KH, D, BS, PS, M, lens, **kw)
+    inp = W.make_inputs(cfg, seed=51, lens=lens, extra_blocks=3)
+    W.poison_unused(inp)
+    P = cfg.max_num_partitions
+    U.note(f"multi-token {c} split={split}")
+    res = run_mq(U.to_device(inp), PS, P, split=split)
+    check(inp, res, PS, P, f"mq {c}")
+    assert torch.all(res["out"][0] == 0)  # a sequence with no keys
+
+
+@pytest.mark.parametrize("name", ["gqa_bf16_g4", "longctx_bf16_g8"])
+def test_multi_token_reduced_workload(name):
+    """The GQA / long-context shapes with 4 (resp. 2) draft tokens per sequence."""
+    M = 4 if name == "gqa_bf16_g4" else 2
+    cfg = U.small_config(name).replace(num_queries=M)
+    inp = W.make_inputs(cfg, seed=13)
+    W.poison_unused(inp)
+    U.note(f"multi-token reduced {name} M={M}")
+    P = cfg.max_num_partitions
+    res = run_mq(U.to_device(inp), cfg.partition_size, P)
+    check(inp, res, cfg.partition_size, P, f"mq {name}")
+
+
+@pytest.mark.parametrize("name", ["gqa_bf16_g4", "mha_f16_d128", "gqa_fp8_g4"])
+def test_one_query_token_matches_single_query_calls(name):
+    cfg = U.small_config(name)
+    inp = W.make_inputs(cfg, seed=17)
+    d = U.to_device(inp)
+    U.note(f"mq M=1 vs single {name}")
+    single = U.run_decode(d)
+    d4 = dict(d, query=d["query"][:, None].contiguous())
+    if cfg.group > 16 or cfg.query_dtype == "f32":
+        pytest.skip("not an MFMA-path shape")
+    res = run_mq(d4, cfg.partition_size, single["P"])
+    # the single-query calls use the vector path for G < 4; the MFMA path then
+    # differs in rounding only, so compare at tolerance, bitwise where both are MFMA
+    if cfg.group >= 4:
+        assert torch.equal(res["out"][:, 0], single["out"])
+        assert torch.equal(res["es"][:, 0], single["es"])
+    else:
+        U.assert_close("M=1 vs vector path", res["out"][:, 0], single["out"].double().numpy())
+
+
+def test_multi_token_rejects_wide_columns():
+    cfg = mq_geom("bf16", 32, 4, 128, 16, 64, 3, [10, 20])   # G=8 x M=3 = 24 columns
+    d = U.to_device(W.make_inputs(cfg, seed=1, lens=[10, 20]))
+    with pytest.raises(RuntimeError):
+        run_mq(d, 64, 1)
