@@ -96,6 +96,11 @@ def _bind(path: str):
                                               I32, I32]
     lib.oracle_combine_ex.restype = None
     lib.oracle_combine_ex.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32]
+    lib.oracle_attention_lse.restype = ctypes.c_int
+    lib.oracle_attention_lse.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
+                                         F32, I32, I32, F32, F32, P, I32, I32]
+    lib.oracle_merge_states.restype = None
+    lib.oracle_merge_states.argtypes = [P, P, P, P, P, P, I64, I32]
     lib.oracle_combine.restype = None
     lib.oracle_combine.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32]
     lib.oracle_gather_indices.restype = I64
@@ -186,6 +191,45 @@ def attention(query, key_cache, value_cache, block_tables, seq_lens, scale: floa
         raise ValueError("oracle_attention: unsupported shape")
     del keep
     return out
+
+
+def attention_lse(query, key_cache, value_cache, block_tables, seq_lens, scale: float,
+                  seqs: Optional[Sequence[int]] = None, nthreads: Optional[int] = None,
+                  k_scale: float = 1.0, v_scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
+    """``attention`` plus the log-sum-exp of each row's scores: (out, lse), lse
+    shaped like out without its last dim (-inf for a row with no keys)."""
+    q, kc, vc = _np(query), _np(key_cache), _np(value_cache)
+    bt, sl = _np(block_tables).astype(np.int32, copy=False), _np(seq_lens).astype(np.int32, copy=False)
+    S, M, H, D = _query_rows(q)
+    KH, BS = kc.shape[1], kc.shape[3]
+    MB = bt.shape[1]
+    out = np.full(q.shape, np.nan)
+    lse = np.full(q.shape[:-1], np.nan)
+    sp, ns, keep = _seq_arg(seqs)
+    rc = _lib().oracle_attention_lse(_ptr(out), _ptr(lse), _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt),
+                                     _ptr(sl), S, M, H, KH, D, BS, MB, float(np.float32(scale)),
+                                     _dtype_code(query), _dtype_code(key_cache),
+                                     float(np.float32(k_scale)), float(np.float32(v_scale)),
+                                     sp, ns, nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_attention_lse: unsupported shape")
+    del keep
+    return out, lse
+
+
+def merge_states(a, lse_a, b, lse_b) -> Tuple[np.ndarray, np.ndarray]:
+    """Merge two attention results over disjoint key sets: (out, out_lse), float64.
+    a, b: [..., D]; lse_a, lse_b: [...]."""
+    a = np.ascontiguousarray(np.asarray(a, np.float64))
+    b = np.ascontiguousarray(np.asarray(b, np.float64))
+    la = np.ascontiguousarray(np.asarray(lse_a, np.float64))
+    lb = np.ascontiguousarray(np.asarray(lse_b, np.float64))
+    assert a.shape == b.shape and la.shape == lb.shape == a.shape[:-1]
+    out = np.empty_like(a)
+    lse = np.empty_like(la)
+    _lib().oracle_merge_states(_ptr(out), _ptr(lse), _ptr(a), _ptr(la), _ptr(b), _ptr(lb),
+                               la.size, a.shape[-1])
+    return out, lse
 
 
 def partition_stats(query, key_cache, value_cache, block_tables, seq_lens, scale: float,

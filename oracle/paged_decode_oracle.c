@@ -59,6 +59,13 @@
  * stand for decode(byte) * k_scale and decode(byte) * v_scale (scales are
  * fp32 scalars, applied in double); the query keeps its own 16-bit dtype and
  * the cache packing factor is x = 16 / 1 = 16. Everything else is unchanged.
+ *
+ * Log-sum-exp output and merge. [METAL-FA]'s forward kernel stores, per query
+ * row, the log-sum-exp of its scores, m + log(l) (its clamp of l is inert once
+ * a row has a key). Reading taken: lse = log(sum_t exp(s_t)) over the scores
+ * defined above, -inf for a row with no keys. Two results of the same rows
+ * over disjoint key sets merge by the [TRITON-V2] reduce's combine, each
+ * side's (m, l) folded into its lse (oracle_merge_states).
  */
 #include <math.h>
 #include <pthread.h>
@@ -153,6 +160,7 @@ typedef struct {
     double* tmp;        /* [S, H, P, D]  partition outputs    */
     double* es;         /* [S, H, P]     partition exp sums   */
     double* ml;         /* [S, H, P]     partition max logits */
+    double* lse;        /* [S, H]        log-sum-exp of the scores (with out) */
     /* work list */
     const int32_t* seqs;
     int32_t n_seqs;
@@ -234,9 +242,11 @@ static void run_item(problem_t* pr, int32_t s, int32_t kh) {
             double* dst = pr->out + (r * pr->H + h) * pr->D;
             if (L == 0) {
                 for (int32_t d = 0; d < pr->D; ++d) dst[d] = 0.0;
+                if (pr->lse) pr->lse[r * pr->H + h] = -INFINITY;
             } else {
                 double m, l;
                 softmax_mix(pr, s, kh, score, 0, L, &m, &l, dst);
+                if (pr->lse) pr->lse[r * pr->H + h] = m + log(l);
             }
         }
         if (pr->tmp || pr->es || pr->ml) {
@@ -319,6 +329,52 @@ int oracle_attention_ex(double* out, const void* q, const void* kc, const void* 
     pr.out = out;
     run_all(&pr, seqs, n_seqs, nthreads);
     return 0;
+}
+
+/* oracle_attention_ex plus the log-sum-exp of every row's scores,
+ * lse = m + log(l) = log(sum_t exp(s_t)); -inf for a row with no keys (the
+ * Flash Attention Metal forward kernel stores the same quantity per row; its
+ * clamp of l is inert when there is at least one key, since l >= 1 then). */
+int oracle_attention_lse(double* out, double* lse, const void* q, const void* kc,
+                         const void* vc, const int32_t* block_tables, const int32_t* seq_lens,
+                         int32_t S, int32_t M, int32_t H, int32_t KH, int32_t D, int32_t BS,
+                         int32_t MB, float scale, int32_t qdtype, int32_t kvdtype,
+                         float k_scale, float v_scale, const int32_t* seqs, int32_t n_seqs,
+                         int32_t nthreads) {
+    if (!valid_dtypes(qdtype, kvdtype) || M < 1) return -1;
+    if (KH <= 0 || H % KH || D % (16 / elem_size(kvdtype))) return -1;
+    problem_t pr;
+    memset(&pr, 0, sizeof pr);
+    pr.q = q; pr.kc = kc; pr.vc = vc; pr.bt = block_tables; pr.sl = seq_lens;
+    pr.S = S; pr.H = H; pr.KH = KH; pr.D = D; pr.BS = BS; pr.MB = MB;
+    pr.qdtype = qdtype; pr.kvdtype = kvdtype; pr.M = M;
+    pr.scale = (double)scale;
+    pr.kscale = (double)k_scale; pr.vscale = (double)v_scale;
+    pr.out = out; pr.lse = lse;
+    run_all(&pr, seqs, n_seqs, nthreads);
+    return 0;
+}
+
+/* Merge two attention results of the same query rows over disjoint key sets
+ * (rows x D values and their log-sum-exps): with Mx = max(lse_a, lse_b),
+ * w = exp(lse - Mx), out = (w_a a + w_b b) / (w_a + w_b) and
+ * out_lse = Mx + log(w_a + w_b); both -inf (no keys on either side) gives
+ * out = 0, out_lse = -inf. This is the reduce's log-sum-exp combine for two
+ * "partitions" whose weights are already folded into their lse. */
+void oracle_merge_states(double* out, double* out_lse, const double* a, const double* lse_a,
+                         const double* b, const double* lse_b, int64_t rows, int32_t D) {
+    for (int64_t r = 0; r < rows; ++r) {
+        double mx = lse_a[r] > lse_b[r] ? lse_a[r] : lse_b[r];
+        if (mx == -INFINITY) {
+            for (int32_t d = 0; d < D; ++d) out[r * D + d] = 0.0;
+            out_lse[r] = -INFINITY;
+            continue;
+        }
+        double wa = exp(lse_a[r] - mx), wb = exp(lse_b[r] - mx);
+        for (int32_t d = 0; d < D; ++d)
+            out[r * D + d] = (wa * a[r * D + d] + wb * b[r * D + d]) / (wa + wb);
+        out_lse[r] = mx + log(wa + wb);
+    }
 }
 
 /* Same, one dtype for query and caches, no cache scales. */

@@ -11,6 +11,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_fp8 as FP8
+from tests import test_oracle_lse as LSE
 from tests import test_oracle_mq as MQ
 from tests import test_oracle_pins as PINS
 
@@ -59,6 +60,16 @@ MUTANTS = [
      "int64_t r = (int64_t)s * pr->M;"),
     ("query_decoded_as_cache", "(r * pr->H + h) * pr->D + d, pr->qdtype)",
      "(r * pr->H + h) * pr->D + d, pr->kvdtype)"),
+    ("lse_drops_max", "pr->lse[r * pr->H + h] = m + log(l);", "pr->lse[r * pr->H + h] = log(l);"),
+    ("lse_empty_zero", "pr->lse[r * pr->H + h] = -INFINITY;", "pr->lse[r * pr->H + h] = 0.0;"),
+    ("merge_weight_sign", "double wa = exp(lse_a[r] - mx), wb = exp(lse_b[r] - mx);",
+     "double wa = exp(mx - lse_a[r]), wb = exp(mx - lse_b[r]);"),
+    ("merge_swapped_weights", "(wa * a[r * D + d] + wb * b[r * D + d]) / (wa + wb);",
+     "(wb * a[r * D + d] + wa * b[r * D + d]) / (wa + wb);"),
+    ("merge_unnormalised", "(wa * a[r * D + d] + wb * b[r * D + d]) / (wa + wb);",
+     "(wa * a[r * D + d] + wb * b[r * D + d]);"),
+    ("merge_lse_drops_max", "out_lse[r] = mx + log(wa + wb);", "out_lse[r] = log(wa + wb);"),
+    ("merge_empty_lse_zero", "out_lse[r] = -INFINITY;", "out_lse[r] = 0.0;"),
 ]
 
 
@@ -82,6 +93,10 @@ def battery():
         "mq_prefix": lambda: MQ.test_rows_equal_single_query_on_causal_prefix(2, "bf16"),
         "mq_library": lambda: MQ.test_library_routine_causal(3, 4),
         "mq_brute_force": MQ.test_brute_force_tiny,
+        "lse_library": lambda: LSE.test_lse_matches_library_logsumexp("bf16", 1),
+        "lse_merge_split": lambda: LSE.test_merge_of_disjoint_splits_is_full_attention("bf16", 4),
+        "lse_merge_closed_form": LSE.test_merge_two_single_keys_closed_form,
+        "lse_merge_identities": LSE.test_merge_infinite_identities_and_symmetry,
     }
     failed = []
     for name, fn in checks.items():
