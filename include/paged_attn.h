@@ -62,7 +62,7 @@ enum {
   PA_ERR_UNSUPPORTED = -3, /* D not in {64,128,256}, BS not in {16,32}, G outside the
                               built range, PS / BS > 256, unknown dtype, or out_dtype
                               neither PA_F32 nor kv_dtype                              */
-  PA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned                  */
+  PA_ERR_ALIGN = -4,       /* a pointer lacks its alignment (16 bytes; lse arrays 4)  */
   PA_ERR_HIP = -5          /* the HIP runtime rejected a launch                        */
 };
 
@@ -221,6 +221,72 @@ PA_API int paged_attn_decode_mq(void* out, float* tmp_output, float* exp_sums, f
                                 int32_t partition_size, float scale, float k_scale,
                                 float v_scale, int32_t q_dtype, int32_t kv_dtype,
                                 int32_t out_dtype, void* stream);
+
+/*
+ * Row log-sum-exp export. The Flash Attention Metal page's forward kernel
+ * stores, next to each normalised output row, the log-sum-exp of the row's
+ * scores, m + log(l). Here, for each (sequence, query token, head) row,
+ *
+ *   lse[row] = M + ln Z,   M = max_p m_p,  Z = sum_p exp(m_p - M) l_p
+ *
+ * over the row's used partitions, i.e. ln sum_t exp(s_t) over the row's
+ * keys (natural log, fp32); -inf for a row with no keys. (out, lse) is the
+ * state paged_attn_merge_states combines.
+ *
+ *   lse   float [S, M, H] (M = num_queries; M = 1 for single-query decode),
+ *         4-byte aligned, caller-owned; NULL -> PA_ERR_NULL
+ *
+ * paged_attn_v2_reduce_lse is paged_attn_v2_reduce_mq plus lse (out is the
+ * same bits); paged_attn_decode_lse is paged_attn_decode_mq plus lse (any
+ * query / cache dtype pair the other decode calls accept, k_scale / v_scale
+ * as for paged_attn_decode_mq). Other arguments and errors as there.
+ */
+PA_API int paged_attn_v2_reduce_lse(void* out, float* lse, const float* tmp_output,
+                                    const float* exp_sums, const float* max_logits,
+                                    const int32_t* seq_lens, int32_t num_seqs,
+                                    int32_t num_queries, int32_t num_heads, int32_t head_size,
+                                    int32_t max_num_partitions, int32_t partition_size,
+                                    int32_t out_dtype, void* stream);
+
+PA_API int paged_attn_decode_lse(void* out, float* lse, float* tmp_output, float* exp_sums,
+                                 float* max_logits, const void* query, const void* key_cache,
+                                 const void* value_cache, const int32_t* block_tables,
+                                 const int32_t* seq_lens, int32_t num_seqs, int32_t num_queries,
+                                 int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                 int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t max_num_partitions,
+                                 int32_t partition_size, float scale, float k_scale,
+                                 float v_scale, int32_t q_dtype, int32_t kv_dtype,
+                                 int32_t out_dtype, void* stream);
+
+/*
+ * Merge two attention states of the same rows computed over disjoint key sets
+ * (a shared prefix and a per-request suffix, or two shards of one long
+ * sequence) into the state over their union: the Triton PagedAttention V2
+ * page's reduce combine for two parts, each part's (max, exp-sum) pair folded
+ * into its lse. Per row, with Mx = max(lse_a, lse_b) and w = exp(lse - Mx):
+ *
+ *   out     = (w_a a + w_b b) / (w_a + w_b)
+ *   out_lse = Mx + ln(w_a + w_b)
+ *
+ * both lse -inf (no keys on either side) -> out = 0, out_lse = -inf; one side
+ * -inf -> the other side's row. fp32 arithmetic, one rounding to `dtype` at
+ * the end.
+ *
+ *   a, b, out          [num_rows, head_size] of `dtype` (PA_F32, PA_F16 or
+ *                      PA_BF16), 16-byte aligned
+ *   lse_a, lse_b       float [num_rows], finite or -inf (a NaN or +inf lse
+ *                      gives NaN rows), 4-byte aligned
+ *   out_lse            float [num_rows], or NULL to skip it
+ *
+ * out may be the same pointer as a or b, and out_lse as lse_a or lse_b
+ * (in-place merge); partially overlapping buffers are not allowed.
+ * head_size in {64, 128, 256}. num_rows == 0 is a no-op. Errors: PA_ERR_SHAPE,
+ * PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_UNSUPPORTED, PA_ERR_HIP (launch).
+ */
+PA_API int paged_attn_merge_states(void* out, float* out_lse, const void* a, const float* lse_a,
+                                   const void* b, const float* lse_b, int64_t num_rows,
+                                   int32_t head_size, int32_t dtype, void* stream);
 
 /* Text of the last nonzero return on this thread ("" if none). Owned by the
  * library; valid until the next call on the same thread. */

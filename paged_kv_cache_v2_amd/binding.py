@@ -22,7 +22,7 @@ _CACHE_DT = {**_DT, torch.float8_e4m3fn: PA_FP8_E4M3}
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpaged_attn.so")
 _LIB = None
 
-_P, _I32, _F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+_P, _I32, _I64, _F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 _SIGS = {
     "paged_attn_v2_partition": [_P, _P, _P, _P, _P, _P, _P, _P] + [_I32] * 9 + [_F32, _I32, _P],
     "paged_attn_v2_reduce": [_P, _P, _P, _P, _P] + [_I32] * 6 + [_P],
@@ -36,6 +36,9 @@ _SIGS = {
     "paged_attn_v2_partition_mq": [_P] * 8 + [_I32] * 10 + [_F32, _F32, _F32, _I32, _I32, _P],
     "paged_attn_v2_reduce_mq": [_P] * 5 + [_I32] * 7 + [_P],
     "paged_attn_decode_mq": [_P] * 9 + [_I32] * 10 + [_F32, _F32, _F32, _I32, _I32, _I32, _P],
+    "paged_attn_v2_reduce_lse": [_P] * 6 + [_I32] * 7 + [_P],
+    "paged_attn_decode_lse": [_P] * 10 + [_I32] * 10 + [_F32, _F32, _F32, _I32, _I32, _I32, _P],
+    "paged_attn_merge_states": [_P] * 6 + [_I64, _I32, _I32, _P],
 }
 
 
@@ -283,6 +286,81 @@ def paged_attn_decode_mq(out, tmp_output, exp_sums, max_logits, query, key_cache
         float(k_scale), float(v_scale), _DT[query.dtype], _CACHE_DT[key_cache.dtype],
         _DT[out.dtype], _stream(query, stream))
     _check("paged_attn_decode_mq", rc)
+
+
+def _rows4(t, name):
+    """A [S, H, ...] single-query tensor as its [S, 1, H, ...] view (M = 1); 4-D+ as is."""
+    return t.unsqueeze(1) if t.dim() == {"query": 3, "out": 3, "tmp": 4, "stats": 3}[name] else t
+
+
+def _lse_arg(lse, out4):
+    _need(lse.dtype == torch.float32 and lse.is_cuda and lse.is_contiguous() and
+          lse.numel() == out4.shape[0] * out4.shape[1] * out4.shape[2],
+          "lse must be a contiguous fp32 device tensor shaped like out without its last dim")
+    return lse.data_ptr()
+
+
+def paged_attn_v2_reduce_lse(out, lse, tmp_output, exp_sums, max_logits, seq_lens,
+                             partition_size: int, stream=None) -> None:
+    """Phase 2 plus each row's log-sum-exp: lse[...] = ln sum_t exp(s_t) (-inf: no keys).
+    Single-query ([S, H, D] out, [S, H, P, D] stats) or M-token ([S, M, H, D]) shapes."""
+    _need(out.dim() in (3, 4) and out.dtype in _DT and out.is_cuda and out.is_contiguous(),
+          "out must be a contiguous [S, (M,) H, D] f32/f16/bf16 device tensor")
+    o4 = _rows4(out, "out")
+    t4, e4, m4 = _rows4(tmp_output, "tmp"), _rows4(exp_sums, "stats"), _rows4(max_logits, "stats")
+    S, M, H, D = o4.shape
+    P = _mq_stats_geometry(t4, e4, m4, S, M, H, D)
+    _need(seq_lens.dtype == torch.int32 and seq_lens.is_cuda and seq_lens.shape == (S,),
+          "seq_lens must be an int32 [S] device tensor")
+    rc = lib().paged_attn_v2_reduce_lse(
+        out.data_ptr(), _lse_arg(lse, o4), tmp_output.data_ptr(), exp_sums.data_ptr(),
+        max_logits.data_ptr(), seq_lens.data_ptr(), S, M, H, D, P, partition_size,
+        _DT[out.dtype], _stream(out, stream))
+    _check("paged_attn_v2_reduce_lse", rc)
+
+
+def paged_attn_decode_lse(out, lse, tmp_output, exp_sums, max_logits, query, key_cache,
+                          value_cache, block_tables, seq_lens, scale: float, partition_size: int,
+                          k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    """Decode (any supported query / cache dtype pair, one or M query tokens) that also
+    writes each row's log-sum-exp into lse (shaped like out without its last dim)."""
+    _need(query.dim() in (3, 4), "query [S, H, D] or [S, M, H, D] expected")
+    q4 = _rows4(query, "query")
+    S, M, H, KH, D, BS, B, MB = _mq_geometry(q4, key_cache, value_cache, block_tables, seq_lens)
+    o4 = _rows4(out, "out") if out.dim() == query.dim() else out
+    t4, e4, m4 = _rows4(tmp_output, "tmp"), _rows4(exp_sums, "stats"), _rows4(max_logits, "stats")
+    P = _mq_stats_geometry(t4, e4, m4, S, M, H, D)
+    _need(out.dim() == query.dim() and tuple(o4.shape) == (S, M, H, D) and out.dtype in _DT and
+          out.is_cuda and out.is_contiguous(), "out must be a contiguous tensor shaped like query")
+    rc = lib().paged_attn_decode_lse(
+        out.data_ptr(), _lse_arg(lse, o4), tmp_output.data_ptr(), exp_sums.data_ptr(),
+        max_logits.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), seq_lens.data_ptr(), S, M, H, KH, D, BS, B, MB, P,
+        partition_size, float(scale), float(k_scale), float(v_scale), _DT[query.dtype],
+        _CACHE_DT[key_cache.dtype], _DT[out.dtype], _stream(query, stream))
+    _check("paged_attn_decode_lse", rc)
+
+
+def paged_attn_merge_states(out, out_lse, a, lse_a, b, lse_b, stream=None) -> None:
+    """Merge two attention states over disjoint key sets (rows [..., D] plus their
+    log-sum-exps [...]) into out / out_lse (out_lse may be None; out may be a or b)."""
+    _need(a.dtype in _DT and b.dtype == a.dtype and out.dtype == a.dtype,
+          "a, b and out must share one dtype (f32, f16 or bf16)")
+    _need(a.dim() >= 1 and tuple(b.shape) == tuple(a.shape) and tuple(out.shape) == tuple(a.shape),
+          "a, b and out must have one shape [..., D]")
+    lse_shape = tuple(a.shape[:-1])
+    lses = [lse_a, lse_b] + ([out_lse] if out_lse is not None else [])
+    _need(all(t.dtype == torch.float32 and tuple(t.shape) == lse_shape for t in lses),
+          "lse tensors must be fp32 and shaped like a without its last dim")
+    for t in [out, a, b] + lses:
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    D = a.shape[-1]
+    rows = a.numel() // D if D else 0
+    rc = lib().paged_attn_merge_states(
+        out.data_ptr(), out_lse.data_ptr() if out_lse is not None else None, a.data_ptr(),
+        lse_a.data_ptr(), b.data_ptr(), lse_b.data_ptr(), rows, D, _DT[a.dtype],
+        _stream(a, stream))
+    _check("paged_attn_merge_states", rc)
 
 
 def workspace(num_seqs: int, num_heads: int, head_size: int, max_num_partitions: int,

@@ -833,6 +833,7 @@ struct ReduceArgs {
   int S, H, P, PS;
   int M;    // query tokens per sequence (rows are (sequence, query token, head))
   int WPI;  // wavefronts per row: 1, 2 or 4
+  float* lse;  // optional [rows]: log-sum-exp of each row's scores (NULL: not written)
 };
 
 constexpr int kReduceU = 8;  // partition rows per lane in flight
@@ -857,6 +858,7 @@ __global__ void __launch_bounds__(kWaves * 64) reduce_kernel(ReduceArgs a) {
   const bool live = sh < a.S * a.M * a.H;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float lse = kNegInf;  // row log-sum-exp, natural units; -inf when the row has no keys
   if (live) {
     const int sm = sh / a.H;               // query row: sequence s, query token qm
     const int s = sm / a.M, qm = sm - s * a.M;
@@ -881,6 +883,8 @@ __global__ void __launch_bounds__(kWaves * 64) reduce_kernel(ReduceArgs a) {
       float Z = lane < n ? fast_exp2((mi - M) * kLog2e) * li : 0.0f;
       for (int i = lane + 64; i < n; i += 64) Z += fast_exp2((mlr[i] - M) * kLog2e) * esr[i];
       Z = wave_sum(Z);
+      // Z >= 1 (the partition holding the row's max contributes its l >= 1)
+      lse = M + __builtin_amdgcn_logf(Z) * kLn2;
       for (int base = 0; base < n; base += 64) {
         // Weight of partition base + lane.
         float wl;
@@ -921,6 +925,7 @@ __global__ void __launch_bounds__(kWaves * 64) reduce_kernel(ReduceArgs a) {
       for (int w = 1; w < WPI; ++w) acc += s_part[wave + w][c4];
     }
   }
+  if (a.lse && live && wi == 0 && lane == 0) a.lse[sh] = lse;
   if (live && wi == 0 && sub == 0) {
     const size_t o = (size_t)sh * D + 4 * c4;
     if constexpr (ODT == DT_F32) {
@@ -930,6 +935,63 @@ __global__ void __launch_bounds__(kWaves * 64) reduce_kernel(ReduceArgs a) {
       *(u32x2*)((uint16_t*)a.out + o) = u32x2{Cd::pack(acc[0], acc[1]), Cd::pack(acc[2], acc[3])};
     }
   }
+}
+
+// ---------------------------------------------------------------- merge states
+// Two attention results of the same rows over disjoint key sets, each with its
+// rows' log-sum-exps, merge into one: with Mx = max(la, lb), w = e^(l - Mx),
+// out = (wa a + wb b) / (wa + wb), out_lse = Mx + ln(wa + wb); both -inf gives
+// out = 0, out_lse = -inf. This is the V2 reduce's combine for two parts whose
+// (max, exp-sum) pairs are already folded into one number each.
+//
+// Streaming and HBM-bound: each lane moves one 16-byte chunk of a, b and out;
+// a row's D values take TPR = D * esize / 16 lanes (4..64, a power of two),
+// so a row never straddles a wavefront. Every lane of a row reads the row's
+// two lse words (cache broadcasts) and the row's first lane writes out_lse;
+// within a wavefront all loads are issued before the dependent stores, so out
+// may be a or b and out_lse may be lse_a or lse_b (exactly, not offset).
+struct MergeArgs {
+  void* out;
+  float* out_lse;  // NULL: not written
+  const void* a;
+  const float* lse_a;
+  const void* b;
+  const float* lse_b;
+  long long chunks;  // rows * TPR
+  int tpr_shift;     // log2(TPR)
+};
+
+template <int DT>
+__global__ void __launch_bounds__(256) merge_states_kernel(MergeArgs g) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= g.chunks) return;
+  const long long r = i >> g.tpr_shift;
+  const float la = g.lse_a[r], lb = g.lse_b[r];
+  const float mx = fmaxf(la, lb);
+  const u32x4 va = ((const u32x4*)g.a)[i];
+  const u32x4 vb = ((const u32x4*)g.b)[i];
+  float pa = 0.0f, pb = 0.0f, ol = kNegInf;
+  if (mx != kNegInf) {
+    const float wa = fast_exp2((la - mx) * kLog2e), wb = fast_exp2((lb - mx) * kLog2e);
+    const float inv = 1.0f / (wa + wb);  // wa + wb in [1, 2]
+    pa = wa * inv;
+    pb = wb * inv;
+    ol = mx + __builtin_amdgcn_logf(wa + wb) * kLn2;
+  }
+  u32x4 vo;
+  if constexpr (DT == DT_F32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      vo[e] = __float_as_uint(pa * __uint_as_float(va[e]) + pb * __uint_as_float(vb[e]));
+  } else {
+    using Cd = codec<DT>;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      vo[e] = Cd::pack(pa * Cd::lo(va[e]) + pb * Cd::lo(vb[e]),
+                       pa * Cd::hi(va[e]) + pb * Cd::hi(vb[e]));
+  }
+  ((u32x4*)g.out)[i] = vo;
+  if (g.out_lse && (i & ((1 << g.tpr_shift) - 1)) == 0) g.out_lse[r] = ol;
 }
 
 }  // namespace pa

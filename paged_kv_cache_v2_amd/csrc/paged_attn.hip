@@ -28,14 +28,17 @@ int fail(int code, const char* fmt, ...) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 int elem_size(int32_t dt) { return dt == PA_F32 ? 4 : dt == PA_FP8_E4M3 ? 1 : 2; }
 bool is_16bit(int32_t dt) { return dt == PA_F16 || dt == PA_BF16; }
 
 using pa::PartitionArgs;
 using pa::ReduceArgs;
+using pa::MergeArgs;
 typedef void (*partition_fn)(PartitionArgs);
 typedef void (*reduce_fn)(ReduceArgs);
+typedef void (*merge_fn)(MergeArgs);
 
 int d_index(int D) { return D == 64 ? 0 : D == 128 ? 1 : D == 256 ? 2 : -1; }
 int bs_index(int BS) { return BS == 16 ? 0 : BS == 32 ? 1 : -1; }
@@ -88,6 +91,11 @@ const reduce_fn kReduce[3][3] = {
     {pa::reduce_kernel<64, pa::DT_BF16>, pa::reduce_kernel<128, pa::DT_BF16>,
      pa::reduce_kernel<256, pa::DT_BF16>},
 };
+
+// [dtype]
+const merge_fn kMerge[3] = {pa::merge_states_kernel<pa::DT_F32>,
+                            pa::merge_states_kernel<pa::DT_F16>,
+                            pa::merge_states_kernel<pa::DT_BF16>};
 
 // Per-device limit on dynamic LDS per workgroup (read once per device).
 int max_lds_per_block() {
@@ -279,11 +287,13 @@ int check_reduce(void* out, const float* tmp_output, const float* exp_sums,
   return PA_OK;
 }
 
-int launch_reduce(reduce_fn fn, void* out, const float* tmp_output, const float* exp_sums,
-                  const float* max_logits, const int32_t* seq_lens, int32_t S, int32_t M,
-                  int32_t H, int32_t D, int32_t P, int32_t PS, hipStream_t stream) {
+int launch_reduce(reduce_fn fn, void* out, float* lse, const float* tmp_output,
+                  const float* exp_sums, const float* max_logits, const int32_t* seq_lens,
+                  int32_t S, int32_t M, int32_t H, int32_t D, int32_t P, int32_t PS,
+                  hipStream_t stream) {
   ReduceArgs a;
   a.out = out;
+  a.lse = lse;
   a.tmp_out = tmp_output;
   a.exp_sums = exp_sums;
   a.max_logits = max_logits;
@@ -324,7 +334,7 @@ int partition_entry(float* tmp_output, float* exp_sums, float* max_logits, const
                           v_scale, M, (hipStream_t)stream);
 }
 
-int decode_entry(void* out, float* tmp_output, float* exp_sums, float* max_logits,
+int decode_entry(void* out, float* lse, float* tmp_output, float* exp_sums, float* max_logits,
                  const void* query, const void* key_cache, const void* value_cache,
                  const int32_t* block_tables, const int32_t* seq_lens, int32_t S, int32_t M,
                  int32_t H, int32_t KH, int32_t D, int32_t BS, int32_t NB, int32_t MB,
@@ -348,8 +358,20 @@ int decode_entry(void* out, float* tmp_output, float* exp_sums, float* max_logit
                         block_tables, seq_lens, S, H, KH, NB, MB, P, PS, scale, k_scale, v_scale,
                         M, (hipStream_t)stream);
   if (rc != PA_OK) return rc;
-  return launch_reduce(fn, out, tmp_output, exp_sums, max_logits, seq_lens, S, M, H, D, P, PS,
-                       (hipStream_t)stream);
+  return launch_reduce(fn, out, lse, tmp_output, exp_sums, max_logits, seq_lens, S, M, H, D, P,
+                       PS, (hipStream_t)stream);
+}
+
+int reduce_entry(void* out, float* lse, const float* tmp_output, const float* exp_sums,
+                 const float* max_logits, const int32_t* seq_lens, int32_t S, int32_t M,
+                 int32_t H, int32_t D, int32_t P, int32_t PS, int32_t out_dtype, void* stream) {
+  g_err[0] = 0;
+  reduce_fn fn = nullptr;
+  int rc = check_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, S, M, H, D, P, PS,
+                        out_dtype, &fn);
+  if (rc != PA_OK || S == 0) return rc;
+  return launch_reduce(fn, out, lse, tmp_output, exp_sums, max_logits, seq_lens, S, M, H, D, P,
+                       PS, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -392,14 +414,9 @@ int paged_attn_v2_reduce(void* out, const float* tmp_output, const float* exp_su
                          const float* max_logits, const int32_t* seq_lens, int32_t num_seqs,
                          int32_t num_heads, int32_t head_size, int32_t max_num_partitions,
                          int32_t partition_size, int32_t out_dtype, void* stream) {
-  g_err[0] = 0;
-  reduce_fn fn = nullptr;
-  int rc = check_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, num_seqs, 1, num_heads,
-                        head_size, max_num_partitions, partition_size, out_dtype, &fn);
-  if (rc != PA_OK || num_seqs == 0) return rc;
-  return launch_reduce(fn, out, tmp_output, exp_sums, max_logits, seq_lens, num_seqs, 1,
-                       num_heads, head_size, max_num_partitions, partition_size,
-                       (hipStream_t)stream);
+  return reduce_entry(out, nullptr, tmp_output, exp_sums, max_logits, seq_lens, num_seqs, 1,
+                      num_heads, head_size, max_num_partitions, partition_size, out_dtype,
+                      stream);
 }
 
 int paged_attn_decode(void* out, float* tmp_output, float* exp_sums, float* max_logits,
@@ -413,7 +430,8 @@ int paged_attn_decode(void* out, float* tmp_output, float* exp_sums, float* max_
     g_err[0] = 0;
     return fail(PA_ERR_UNSUPPORTED, "8-bit caches go through paged_attn_decode_fp8");
   }
-  return decode_entry(out, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+  return decode_entry(out, nullptr, tmp_output, exp_sums, max_logits, query, key_cache,
+                      value_cache,
                       block_tables, seq_lens, num_seqs, 1, num_heads, num_kv_heads, head_size,
                       block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
                       partition_size, scale, 1.0f, 1.0f, kv_dtype, kv_dtype, out_dtype, stream);
@@ -427,7 +445,8 @@ int paged_attn_decode_fp8(void* out, float* tmp_output, float* exp_sums, float* 
                           int32_t max_num_partitions, int32_t partition_size, float scale,
                           float k_scale, float v_scale, int32_t q_dtype, int32_t out_dtype,
                           void* stream) {
-  return decode_entry(out, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+  return decode_entry(out, nullptr, tmp_output, exp_sums, max_logits, query, key_cache,
+                      value_cache,
                       block_tables, seq_lens, num_seqs, 1, num_heads, num_kv_heads, head_size,
                       block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
                       partition_size, scale, k_scale, v_scale, q_dtype, PA_FP8_E4M3, out_dtype,
@@ -455,14 +474,9 @@ int paged_attn_v2_reduce_mq(void* out, const float* tmp_output, const float* exp
                             int32_t num_queries, int32_t num_heads, int32_t head_size,
                             int32_t max_num_partitions, int32_t partition_size,
                             int32_t out_dtype, void* stream) {
-  g_err[0] = 0;
-  reduce_fn fn = nullptr;
-  int rc = check_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, num_seqs, num_queries,
-                        num_heads, head_size, max_num_partitions, partition_size, out_dtype, &fn);
-  if (rc != PA_OK || num_seqs == 0) return rc;
-  return launch_reduce(fn, out, tmp_output, exp_sums, max_logits, seq_lens, num_seqs,
-                       num_queries, num_heads, head_size, max_num_partitions, partition_size,
-                       (hipStream_t)stream);
+  return reduce_entry(out, nullptr, tmp_output, exp_sums, max_logits, seq_lens, num_seqs,
+                      num_queries, num_heads, head_size, max_num_partitions, partition_size,
+                      out_dtype, stream);
 }
 
 int paged_attn_decode_mq(void* out, float* tmp_output, float* exp_sums, float* max_logits,
@@ -473,11 +487,83 @@ int paged_attn_decode_mq(void* out, float* tmp_output, float* exp_sums, float* m
                          int32_t max_blocks_per_seq, int32_t max_num_partitions,
                          int32_t partition_size, float scale, float k_scale, float v_scale,
                          int32_t q_dtype, int32_t kv_dtype, int32_t out_dtype, void* stream) {
-  return decode_entry(out, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+  return decode_entry(out, nullptr, tmp_output, exp_sums, max_logits, query, key_cache,
+                      value_cache,
                       block_tables, seq_lens, num_seqs, num_queries, num_heads, num_kv_heads,
                       head_size, block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
                       partition_size, scale, k_scale, v_scale, q_dtype, kv_dtype, out_dtype,
                       stream);
+}
+
+int paged_attn_v2_reduce_lse(void* out, float* lse, const float* tmp_output,
+                             const float* exp_sums, const float* max_logits,
+                             const int32_t* seq_lens, int32_t num_seqs, int32_t num_queries,
+                             int32_t num_heads, int32_t head_size, int32_t max_num_partitions,
+                             int32_t partition_size, int32_t out_dtype, void* stream) {
+  if (num_seqs > 0 && (!lse || !aligned4(lse))) {
+    g_err[0] = 0;
+    return fail(lse ? PA_ERR_ALIGN : PA_ERR_NULL, "lse must be a non-NULL, 4-byte aligned float*");
+  }
+  return reduce_entry(out, lse, tmp_output, exp_sums, max_logits, seq_lens, num_seqs,
+                      num_queries, num_heads, head_size, max_num_partitions, partition_size,
+                      out_dtype, stream);
+}
+
+int paged_attn_decode_lse(void* out, float* lse, float* tmp_output, float* exp_sums,
+                          float* max_logits, const void* query, const void* key_cache,
+                          const void* value_cache, const int32_t* block_tables,
+                          const int32_t* seq_lens, int32_t num_seqs, int32_t num_queries,
+                          int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                          int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                          int32_t max_num_partitions, int32_t partition_size, float scale,
+                          float k_scale, float v_scale, int32_t q_dtype, int32_t kv_dtype,
+                          int32_t out_dtype, void* stream) {
+  if (num_seqs > 0 && (!lse || !aligned4(lse))) {
+    g_err[0] = 0;
+    return fail(lse ? PA_ERR_ALIGN : PA_ERR_NULL, "lse must be a non-NULL, 4-byte aligned float*");
+  }
+  return decode_entry(out, lse, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                      block_tables, seq_lens, num_seqs, num_queries, num_heads, num_kv_heads,
+                      head_size, block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
+                      partition_size, scale, k_scale, v_scale, q_dtype, kv_dtype, out_dtype,
+                      stream);
+}
+
+int paged_attn_merge_states(void* out, float* out_lse, const void* a, const float* lse_a,
+                            const void* b, const float* lse_b, int64_t num_rows,
+                            int32_t head_size, int32_t dtype, void* stream) {
+  g_err[0] = 0;
+  if (num_rows < 0 || head_size < 0) return fail(PA_ERR_SHAPE, "negative size argument");
+  if (num_rows == 0) return PA_OK;
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "merge dtype %d not in {PA_F32, PA_F16, PA_BF16}", dtype);
+  if (!out || !a || !lse_a || !b || !lse_b) return fail(PA_ERR_NULL, "a required pointer is NULL");
+  if (d_index(head_size) < 0)
+    return fail(PA_ERR_UNSUPPORTED, "head_size %d not in {64, 128, 256}", head_size);
+  if (!aligned16(out) || !aligned16(a) || !aligned16(b))
+    return fail(PA_ERR_ALIGN, "out, a and b must be 16-byte aligned");
+  if (!aligned4(lse_a) || !aligned4(lse_b) || (out_lse && !aligned4(out_lse)))
+    return fail(PA_ERR_ALIGN, "lse arrays must be 4-byte aligned");
+  const int tpr = head_size * elem_size(dtype) / 16;  // 8..64 lanes per row
+  int shift = 0;
+  while ((1 << shift) < tpr) ++shift;
+  const long long chunks = (long long)num_rows * tpr;
+  const long long blocks = (chunks + 255) / 256;
+  if (num_rows > (1LL << 40) || blocks > 0x7fffffffLL)
+    return fail(PA_ERR_UNSUPPORTED, "too many rows");
+  MergeArgs g;
+  g.out = out;
+  g.out_lse = out_lse;
+  g.a = a;
+  g.lse_a = lse_a;
+  g.b = b;
+  g.lse_b = lse_b;
+  g.chunks = chunks;
+  g.tpr_shift = shift;
+  hipLaunchKernelGGL(kMerge[dtype], dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, g);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
 }
 
 const char* paged_attn_last_error(void) { return g_err; }

@@ -223,3 +223,56 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(binding, "LIB_PATH", "/nonexistent/libpaged_attn.so")
     with pytest.raises(RuntimeError, match="not built"):
         binding.lib()
+
+
+def reduce_lse(lse=FAKE, ptrs=None, S=2, M=1):
+    ptrs = ptrs or [FAKE] * 5
+    return pa.lib().paged_attn_v2_reduce_lse(ptrs[0], lse, *ptrs[1:], S, M, 8, 128, 4, 512,
+                                             binding.PA_F32, None)
+
+
+def test_reduce_lse_rejects():
+    assert reduce_lse(lse=None) == binding.PA_ERR_NULL
+    assert reduce_lse(lse=FAKE + 2) == binding.PA_ERR_ALIGN
+    assert reduce_lse(M=0) == binding.PA_ERR_SHAPE
+    ptrs = [FAKE] * 5
+    ptrs[1] = None
+    assert reduce_lse(ptrs=ptrs) == binding.PA_ERR_NULL
+    assert reduce_lse(lse=None, ptrs=[None] * 5, S=0) == binding.PA_OK
+
+
+def test_decode_lse_rejects():
+    lib = pa.lib()
+    args = lambda lse, M=1, qdt=binding.PA_BF16, kvdt=binding.PA_BF16: (
+        FAKE, lse, *([FAKE] * 8), 2, M, 8, 2, 128, 16, 64, 8, 1, 512, 0.125, 1.0, 1.0, qdt, kvdt,
+        binding.PA_F32, None)
+    assert lib.paged_attn_decode_lse(*args(None)) == binding.PA_ERR_NULL
+    assert lib.paged_attn_decode_lse(*args(FAKE + 1)) == binding.PA_ERR_ALIGN
+    assert lib.paged_attn_decode_lse(*args(FAKE, M=5)) == binding.PA_ERR_UNSUPPORTED
+    assert lib.paged_attn_decode_lse(*args(FAKE, qdt=binding.PA_F32)) == binding.PA_ERR_UNSUPPORTED
+
+
+def merge(ptrs=None, rows=4, D=128, dt=binding.PA_BF16):
+    ptrs = ptrs or [FAKE] * 6
+    return pa.lib().paged_attn_merge_states(*ptrs, rows, D, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=-1), binding.PA_ERR_SHAPE),
+    (dict(D=-64), binding.PA_ERR_SHAPE),
+    (dict(D=96), binding.PA_ERR_UNSUPPORTED),
+    (dict(dt=binding.PA_FP8_E4M3), binding.PA_ERR_UNSUPPORTED),
+    (dict(ptrs=[FAKE, FAKE, None, FAKE, FAKE, FAKE]), binding.PA_ERR_NULL),
+    (dict(ptrs=[FAKE, FAKE, FAKE, FAKE, FAKE, None]), binding.PA_ERR_NULL),
+    (dict(ptrs=[FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE]), binding.PA_ERR_ALIGN),
+    (dict(ptrs=[FAKE, FAKE, FAKE, FAKE + 2, FAKE, FAKE]), binding.PA_ERR_ALIGN),
+    (dict(ptrs=[FAKE, FAKE + 1, FAKE, FAKE, FAKE, FAKE]), binding.PA_ERR_ALIGN),
+])
+def test_merge_states_rejects(kw, code):
+    assert merge(**kw) == code
+    assert pa.last_error() != ""
+
+
+def test_merge_states_zero_rows_is_noop():
+    assert merge(ptrs=[None] * 6, rows=0) == binding.PA_OK
+    assert pa.last_error() == ""
