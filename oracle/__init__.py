@@ -99,6 +99,13 @@ def _bind(path: str):
     lib.oracle_attention_lse.restype = ctypes.c_int
     lib.oracle_attention_lse.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
                                          F32, I32, I32, F32, F32, P, I32, I32]
+    lib.oracle_attention_full.restype = ctypes.c_int
+    lib.oracle_attention_full.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
+                                          F32, I32, I32, F32, F32, P, P, I32, I32]
+    lib.oracle_partition_stats_full.restype = ctypes.c_int
+    lib.oracle_partition_stats_full.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32,
+                                                I32, I32, I32, I32, F32, I32, I32, F32, F32, P, P,
+                                                I32, I32]
     lib.oracle_merge_states.restype = None
     lib.oracle_merge_states.argtypes = [P, P, P, P, P, P, I64, I32]
     lib.oracle_combine.restype = None
@@ -164,38 +171,19 @@ def _query_rows(q):
     return q.shape
 
 
-def attention(query, key_cache, value_cache, block_tables, seq_lens, scale: float,
-              seqs: Optional[Sequence[int]] = None, nthreads: Optional[int] = None,
-              k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
-    """Dense softmax attention over the block-table-gathered tokens, float64.
-
-    query [S, H, D] gives out [S, H, D]; query [S, M, H, D] (M query tokens per
-    sequence, the last M positions, causal) gives out [S, M, H, D]. Rows of
-    sequences not in ``seqs`` are NaN. The query dtype and the cache dtype are
-    read off the tensors; an e4m3fn cache stands for its decoded values times
-    ``k_scale`` / ``v_scale``.
-    """
-    q, kc, vc = _np(query), _np(key_cache), _np(value_cache)
-    bt, sl = _np(block_tables).astype(np.int32, copy=False), _np(seq_lens).astype(np.int32, copy=False)
-    S, M, H, D = _query_rows(q)
-    KH, BS = kc.shape[1], kc.shape[3]
-    MB = bt.shape[1]
-    out = np.full(q.shape, np.nan)
-    sp, ns, keep = _seq_arg(seqs)
-    rc = _lib().oracle_attention_ex(_ptr(out), _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl),
-                                    S, M, H, KH, D, BS, MB, float(np.float32(scale)),
-                                    _dtype_code(query), _dtype_code(key_cache),
-                                    float(np.float32(k_scale)), float(np.float32(v_scale)),
-                                    sp, ns, nthreads or default_threads())
-    if rc != 0:
-        raise ValueError("oracle_attention: unsupported shape")
-    del keep
-    return out
+def _slopes(alibi_slopes, H):
+    """(pointer or None, keep-alive array) of fp32 ALiBi slopes [H]."""
+    if alibi_slopes is None:
+        return None, None
+    a = np.ascontiguousarray(_np(alibi_slopes), dtype=np.float32)
+    assert a.shape == (H,), "alibi_slopes must be [num_heads]"
+    return _ptr(a), a
 
 
 def attention_lse(query, key_cache, value_cache, block_tables, seq_lens, scale: float,
                   seqs: Optional[Sequence[int]] = None, nthreads: Optional[int] = None,
-                  k_scale: float = 1.0, v_scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
+                  k_scale: float = 1.0, v_scale: float = 1.0,
+                  alibi_slopes=None) -> Tuple[np.ndarray, np.ndarray]:
     """``attention`` plus the log-sum-exp of each row's scores: (out, lse), lse
     shaped like out without its last dim (-inf for a row with no keys)."""
     q, kc, vc = _np(query), _np(key_cache), _np(value_cache)
@@ -206,15 +194,33 @@ def attention_lse(query, key_cache, value_cache, block_tables, seq_lens, scale: 
     out = np.full(q.shape, np.nan)
     lse = np.full(q.shape[:-1], np.nan)
     sp, ns, keep = _seq_arg(seqs)
-    rc = _lib().oracle_attention_lse(_ptr(out), _ptr(lse), _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt),
-                                     _ptr(sl), S, M, H, KH, D, BS, MB, float(np.float32(scale)),
-                                     _dtype_code(query), _dtype_code(key_cache),
-                                     float(np.float32(k_scale)), float(np.float32(v_scale)),
-                                     sp, ns, nthreads or default_threads())
+    ap, akeep = _slopes(alibi_slopes, H)
+    rc = _lib().oracle_attention_full(_ptr(out), _ptr(lse), _ptr(q), _ptr(kc), _ptr(vc),
+                                      _ptr(bt), _ptr(sl), S, M, H, KH, D, BS, MB,
+                                      float(np.float32(scale)), _dtype_code(query),
+                                      _dtype_code(key_cache), float(np.float32(k_scale)),
+                                      float(np.float32(v_scale)), ap, sp, ns,
+                                      nthreads or default_threads())
     if rc != 0:
-        raise ValueError("oracle_attention_lse: unsupported shape")
-    del keep
+        raise ValueError("oracle_attention: unsupported shape")
+    del keep, akeep
     return out, lse
+
+
+def attention(query, key_cache, value_cache, block_tables, seq_lens, scale: float,
+              seqs: Optional[Sequence[int]] = None, nthreads: Optional[int] = None,
+              k_scale: float = 1.0, v_scale: float = 1.0, alibi_slopes=None) -> np.ndarray:
+    """Dense softmax attention over the block-table-gathered tokens, float64.
+
+    query [S, H, D] gives out [S, H, D]; query [S, M, H, D] (M query tokens per
+    sequence, the last M positions, causal) gives out [S, M, H, D]. Rows of
+    sequences not in ``seqs`` are NaN. The query dtype and the cache dtype are
+    read off the tensors; an e4m3fn cache stands for its decoded values times
+    ``k_scale`` / ``v_scale``. ``alibi_slopes`` [H] adds slope * (key position
+    - query position) to each score.
+    """
+    return attention_lse(query, key_cache, value_cache, block_tables, seq_lens, scale, seqs,
+                         nthreads, k_scale, v_scale, alibi_slopes)[0]
 
 
 def merge_states(a, lse_a, b, lse_b) -> Tuple[np.ndarray, np.ndarray]:
@@ -236,7 +242,8 @@ def partition_stats(query, key_cache, value_cache, block_tables, seq_lens, scale
                     max_num_partitions: int, partition_size: int,
                     seqs: Optional[Sequence[int]] = None,
                     nthreads: Optional[int] = None, k_scale: float = 1.0,
-                    v_scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                    v_scale: float = 1.0,
+                    alibi_slopes=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Phase-1 intermediates: tmp_output [rows, H, P, D], exp_sums and max_logits
     [rows, H, P], with rows = [S] or [S, M] as for ``attention``."""
     q, kc, vc = _np(query), _np(key_cache), _np(value_cache)
@@ -250,14 +257,15 @@ def partition_stats(query, key_cache, value_cache, block_tables, seq_lens, scale
     es = np.full(lead + (H, P), np.nan)
     ml = np.full(lead + (H, P), np.nan)
     sp, ns, keep = _seq_arg(seqs)
-    rc = _lib().oracle_partition_stats_ex(
+    ap, akeep = _slopes(alibi_slopes, H)
+    rc = _lib().oracle_partition_stats_full(
         _ptr(tmp), _ptr(es), _ptr(ml), _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl), S, M, H,
         KH, D, BS, MB, P, partition_size, float(np.float32(scale)), _dtype_code(query),
-        _dtype_code(key_cache), float(np.float32(k_scale)), float(np.float32(v_scale)), sp, ns,
-        nthreads or default_threads())
+        _dtype_code(key_cache), float(np.float32(k_scale)), float(np.float32(v_scale)), ap, sp,
+        ns, nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_partition_stats: unsupported shape or length > P*PS")
-    del keep
+    del keep, akeep
     return tmp, es, ml
 
 

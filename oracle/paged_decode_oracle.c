@@ -60,6 +60,16 @@
  * fp32 scalars, applied in double); the query keeps its own 16-bit dtype and
  * the cache packing factor is x = 16 / 1 = 16. Everything else is unchanged.
  *
+ * ALiBi. The Triton PagedAttention V2 page's launcher accepts per-head
+ * "alibi_slopes" and never uses them; the pages give no formula. Reading
+ * taken: the published ALiBi definition (Press, Smith and Lewis, "Train
+ * Short, Test Long: Attention with Linear Biases", ICLR 2022): a query at
+ * position i adds slope_h * (j - i) to its score for the key at position j
+ * (0 at its own position, more negative further back), after the scaling of
+ * the dot product; the slopes are the caller's fp32 [H] values. The query
+ * position is L - 1 for single-query decode and L - M + m for query token m
+ * of M.
+ *
  * Log-sum-exp output and merge. [METAL-FA]'s forward kernel stores, per query
  * row, the log-sum-exp of its scores, m + log(l) (its clamp of l is inert once
  * a row has a key). Reading taken: lse = log(sum_t exp(s_t)) over the scores
@@ -155,6 +165,7 @@ typedef struct {
     int32_t M;                /* query tokens per sequence (1: single-query decode) */
     double scale;
     double kscale, vscale;    /* cache dequantisation scales (1 for 16/32-bit caches) */
+    const float* alibi;       /* [H] ALiBi slopes, or NULL (no position bias) */
     /* outputs (any may be NULL) */
     double* out;        /* [S, H, D]     dense attention      */
     double* tmp;        /* [S, H, P, D]  partition outputs    */
@@ -237,6 +248,8 @@ static void run_item(problem_t* pr, int32_t s, int32_t kh) {
             for (int32_t d = 0; d < pr->D; ++d)
                 dot += query_at(pr, r, h, d) * key_at(pr, b, kh, slot, d);
             score[t] = pr->scale * dot;
+            if (pr->alibi) /* the query sits at position L0 - M + mq */
+                score[t] += (double)pr->alibi[h] * (double)(t - (L0 - pr->M + mq));
         }
         if (pr->out) {
             double* dst = pr->out + (r * pr->H + h) * pr->D;
@@ -308,15 +321,22 @@ static int valid_dtypes(int32_t qdtype, int32_t kvdtype) {
     return kvdtype == qdtype;
 }
 
-/* Dense attention over the gathered tokens. out[S,H,D]: only rows of the
- * listed sequences are written (seqs == NULL means all). The query is
- * decoded as qdtype, the caches as kvdtype scaled by k_scale / v_scale.
- * Returns 0, or -1 on a shape or dtype pair the definition does not cover. */
-int oracle_attention_ex(double* out, const void* q, const void* kc, const void* vc,
-                        const int32_t* block_tables, const int32_t* seq_lens,
-                        int32_t S, int32_t M, int32_t H, int32_t KH, int32_t D, int32_t BS,
-                        int32_t MB, float scale, int32_t qdtype, int32_t kvdtype, float k_scale,
-                        float v_scale, const int32_t* seqs, int32_t n_seqs, int32_t nthreads) {
+/* Dense attention over the gathered tokens, the most general form: query
+ * [S, M, H, D] rows (M = 1: single-query decode), caches decoded as kvdtype
+ * and scaled by k_scale / v_scale, optional ALiBi slopes [H] (NULL: none).
+ * out [S, M, H, D] and lse [S, M, H] (either may be NULL): only rows of the
+ * listed sequences are written (seqs == NULL means all). lse is the
+ * log-sum-exp of each row's scores, m + log(l) = log(sum_t exp(s_t)), -inf
+ * for a row with no keys (the Flash Attention Metal forward kernel stores the
+ * same quantity per row; its clamp of l is inert when there is at least one
+ * key, since l >= 1 then). Returns 0, or -1 on a shape or dtype pair the
+ * definition does not cover. */
+int oracle_attention_full(double* out, double* lse, const void* q, const void* kc,
+                          const void* vc, const int32_t* block_tables, const int32_t* seq_lens,
+                          int32_t S, int32_t M, int32_t H, int32_t KH, int32_t D, int32_t BS,
+                          int32_t MB, float scale, int32_t qdtype, int32_t kvdtype,
+                          float k_scale, float v_scale, const float* alibi_slopes,
+                          const int32_t* seqs, int32_t n_seqs, int32_t nthreads) {
     if (!valid_dtypes(qdtype, kvdtype) || M < 1) return -1;
     if (KH <= 0 || H % KH || D % (16 / elem_size(kvdtype))) return -1;
     problem_t pr;
@@ -326,33 +346,33 @@ int oracle_attention_ex(double* out, const void* q, const void* kc, const void* 
     pr.qdtype = qdtype; pr.kvdtype = kvdtype; pr.M = M;
     pr.scale = (double)scale;
     pr.kscale = (double)k_scale; pr.vscale = (double)v_scale;
-    pr.out = out;
+    pr.alibi = alibi_slopes;
+    pr.out = out; pr.lse = lse;
     run_all(&pr, seqs, n_seqs, nthreads);
     return 0;
 }
 
-/* oracle_attention_ex plus the log-sum-exp of every row's scores,
- * lse = m + log(l) = log(sum_t exp(s_t)); -inf for a row with no keys (the
- * Flash Attention Metal forward kernel stores the same quantity per row; its
- * clamp of l is inert when there is at least one key, since l >= 1 then). */
+/* oracle_attention_full without lse or ALiBi. */
+int oracle_attention_ex(double* out, const void* q, const void* kc, const void* vc,
+                        const int32_t* block_tables, const int32_t* seq_lens,
+                        int32_t S, int32_t M, int32_t H, int32_t KH, int32_t D, int32_t BS,
+                        int32_t MB, float scale, int32_t qdtype, int32_t kvdtype, float k_scale,
+                        float v_scale, const int32_t* seqs, int32_t n_seqs, int32_t nthreads) {
+    return oracle_attention_full(out, NULL, q, kc, vc, block_tables, seq_lens, S, M, H, KH, D,
+                                 BS, MB, scale, qdtype, kvdtype, k_scale, v_scale, NULL, seqs,
+                                 n_seqs, nthreads);
+}
+
+/* oracle_attention_full without ALiBi. */
 int oracle_attention_lse(double* out, double* lse, const void* q, const void* kc,
                          const void* vc, const int32_t* block_tables, const int32_t* seq_lens,
                          int32_t S, int32_t M, int32_t H, int32_t KH, int32_t D, int32_t BS,
                          int32_t MB, float scale, int32_t qdtype, int32_t kvdtype,
                          float k_scale, float v_scale, const int32_t* seqs, int32_t n_seqs,
                          int32_t nthreads) {
-    if (!valid_dtypes(qdtype, kvdtype) || M < 1) return -1;
-    if (KH <= 0 || H % KH || D % (16 / elem_size(kvdtype))) return -1;
-    problem_t pr;
-    memset(&pr, 0, sizeof pr);
-    pr.q = q; pr.kc = kc; pr.vc = vc; pr.bt = block_tables; pr.sl = seq_lens;
-    pr.S = S; pr.H = H; pr.KH = KH; pr.D = D; pr.BS = BS; pr.MB = MB;
-    pr.qdtype = qdtype; pr.kvdtype = kvdtype; pr.M = M;
-    pr.scale = (double)scale;
-    pr.kscale = (double)k_scale; pr.vscale = (double)v_scale;
-    pr.out = out; pr.lse = lse;
-    run_all(&pr, seqs, n_seqs, nthreads);
-    return 0;
+    return oracle_attention_full(out, lse, q, kc, vc, block_tables, seq_lens, S, M, H, KH, D,
+                                 BS, MB, scale, qdtype, kvdtype, k_scale, v_scale, NULL, seqs,
+                                 n_seqs, nthreads);
 }
 
 /* Merge two attention results of the same query rows over disjoint key sets
@@ -387,15 +407,16 @@ int oracle_attention(double* out, const void* q, const void* kc, const void* vc,
                                scale, dtype, dtype, 1.0f, 1.0f, seqs, n_seqs, nthreads);
 }
 
-/* Phase-1 intermediates: tmp[S,H,P,D], es[S,H,P], ml[S,H,P] for the listed
- * sequences. Returns -1 if a length exceeds P*PS. */
-int oracle_partition_stats_ex(double* tmp, double* es, double* ml, const void* q,
-                              const void* kc, const void* vc, const int32_t* block_tables,
-                              const int32_t* seq_lens, int32_t S, int32_t M, int32_t H,
-                              int32_t KH, int32_t D, int32_t BS, int32_t MB, int32_t P,
-                              int32_t PS, float scale, int32_t qdtype, int32_t kvdtype,
-                              float k_scale, float v_scale, const int32_t* seqs, int32_t n_seqs,
-                              int32_t nthreads) {
+/* Phase-1 intermediates: tmp[S,M,H,P,D], es[S,M,H,P], ml[S,M,H,P] for the
+ * listed sequences (ALiBi slopes [H] or NULL). Returns -1 if a length
+ * exceeds P*PS. */
+int oracle_partition_stats_full(double* tmp, double* es, double* ml, const void* q,
+                                const void* kc, const void* vc, const int32_t* block_tables,
+                                const int32_t* seq_lens, int32_t S, int32_t M, int32_t H,
+                                int32_t KH, int32_t D, int32_t BS, int32_t MB, int32_t P,
+                                int32_t PS, float scale, int32_t qdtype, int32_t kvdtype,
+                                float k_scale, float v_scale, const float* alibi_slopes,
+                                const int32_t* seqs, int32_t n_seqs, int32_t nthreads) {
     if (!valid_dtypes(qdtype, kvdtype) || M < 1) return -1;
     if (KH <= 0 || H % KH || D % (16 / elem_size(kvdtype)) || PS <= 0 || P < 1) return -1;
     for (int32_t s = 0; s < S; ++s)
@@ -408,9 +429,23 @@ int oracle_partition_stats_ex(double* tmp, double* es, double* ml, const void* q
     pr.P = P; pr.PS = PS;
     pr.scale = (double)scale;
     pr.kscale = (double)k_scale; pr.vscale = (double)v_scale;
+    pr.alibi = alibi_slopes;
     pr.tmp = tmp; pr.es = es; pr.ml = ml;
     run_all(&pr, seqs, n_seqs, nthreads);
     return 0;
+}
+
+/* oracle_partition_stats_full without ALiBi. */
+int oracle_partition_stats_ex(double* tmp, double* es, double* ml, const void* q,
+                              const void* kc, const void* vc, const int32_t* block_tables,
+                              const int32_t* seq_lens, int32_t S, int32_t M, int32_t H,
+                              int32_t KH, int32_t D, int32_t BS, int32_t MB, int32_t P,
+                              int32_t PS, float scale, int32_t qdtype, int32_t kvdtype,
+                              float k_scale, float v_scale, const int32_t* seqs, int32_t n_seqs,
+                              int32_t nthreads) {
+    return oracle_partition_stats_full(tmp, es, ml, q, kc, vc, block_tables, seq_lens, S, M, H,
+                                       KH, D, BS, MB, P, PS, scale, qdtype, kvdtype, k_scale,
+                                       v_scale, NULL, seqs, n_seqs, nthreads);
 }
 
 int oracle_partition_stats(double* tmp, double* es, double* ml, const void* q, const void* kc,

@@ -10,6 +10,7 @@ import tempfile
 import pytest
 
 import oracle
+from tests import test_oracle_alibi as ALIBI
 from tests import test_oracle_fp8 as FP8
 from tests import test_oracle_lse as LSE
 from tests import test_oracle_mq as MQ
@@ -70,6 +71,20 @@ MUTANTS = [
      "(wa * a[r * D + d] + wb * b[r * D + d]);"),
     ("merge_lse_drops_max", "out_lse[r] = mx + log(wa + wb);", "out_lse[r] = log(wa + wb);"),
     ("merge_empty_lse_zero", "out_lse[r] = -INFINITY;", "out_lse[r] = 0.0;"),
+    ("alibi_sign", "(double)pr->alibi[h] * (double)(t - (L0 - pr->M + mq));",
+     "(double)pr->alibi[h] * (double)((L0 - pr->M + mq) - t);"),
+    ("alibi_slope_by_kv_head", "(double)pr->alibi[h] * (double)(t - (L0 - pr->M + mq));",
+     "(double)pr->alibi[kh] * (double)(t - (L0 - pr->M + mq));"),
+    ("alibi_absolute_position", "(double)pr->alibi[h] * (double)(t - (L0 - pr->M + mq));",
+     "(double)pr->alibi[h] * (double)t;"),
+    ("alibi_query_at_sequence_end", "(double)pr->alibi[h] * (double)(t - (L0 - pr->M + mq));",
+     "(double)pr->alibi[h] * (double)(t - (L0 - 1));"),
+    ("alibi_before_scale",
+     "score[t] = pr->scale * dot;\n            if (pr->alibi) /* the query sits at position "
+     "L0 - M + mq */\n                score[t] += (double)pr->alibi[h] * (double)(t - (L0 - "
+     "pr->M + mq));",
+     "score[t] = dot;\n            if (pr->alibi) score[t] += (double)pr->alibi[h] * "
+     "(double)(t - (L0 - pr->M + mq));\n            score[t] *= pr->scale;"),
 ]
 
 
@@ -97,6 +112,9 @@ def battery():
         "lse_merge_split": lambda: LSE.test_merge_of_disjoint_splits_is_full_attention("bf16", 4),
         "lse_merge_closed_form": LSE.test_merge_two_single_keys_closed_form,
         "lse_merge_identities": LSE.test_merge_infinite_identities_and_symmetry,
+        "alibi_library": lambda: ALIBI.test_library_route("bf16", 3, 4),
+        "alibi_closed_form": lambda: ALIBI.test_zero_query_closed_form(0.5),
+        "alibi_steep": ALIBI.test_steep_slope_selects_the_query_position,
     }
     failed = []
     for name, fn in checks.items():
