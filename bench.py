@@ -22,6 +22,11 @@ Prints ONE JSON line:
                current kernel source (else null).
   cpu_baseline = the fp64 oracle (partition stats + combine) timed on this
                host's cores over a bounded sample of the same workload.
+  merge_states = paged_attn_merge_states timed with HIP events: on the
+               batch's own rows (two query-dtype states of every (sequence,
+               query token, head) row, as a cascade merges them) and on a
+               2^20-row stream that shows the kernel's bandwidth; bytes are
+               2 inputs + 1 output row plus 3 lse words per row.
 
 Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -90,6 +95,39 @@ def cpu_baseline(inp, W, min_seconds: float):
         "sample": (f"whole workload ({inp['num_seqs']} sequences, "
                    f"{int(inp['seq_lens'].sum())} tokens) x {runs} run(s), fp64 partition "
                    f"stats + combine, {per_run:.2f} s per run"),
+    }
+
+
+def merge_bench(pa, torch, dev, stream, rows: int, D: int, dtype, K: int) -> dict:
+    """Average duration and algorithmic GB/s of paged_attn_merge_states."""
+    def one(R):
+        g = torch.Generator(device=dev).manual_seed(R)
+        a = torch.randn(R, D, device=dev, generator=g).to(dtype)
+        b = torch.randn(R, D, device=dev, generator=g).to(dtype)
+        la = torch.randn(R, device=dev, generator=g)
+        lb = torch.randn(R, device=dev, generator=g)
+        out, lse = torch.empty_like(a), torch.empty_like(la)
+        for _ in range(3):
+            pa.paged_attn_merge_states(out, lse, a, la, b, lb, stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        ev[0].record(stream)
+        for i in range(K):
+            pa.paged_attn_merge_states(out, lse, a, la, b, lb, stream)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        avg_s = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(K)) / K / 1e3
+        nbytes = R * (3 * D * a.element_size() + 3 * 4)
+        return nbytes, avg_s
+
+    nb, t = one(rows)
+    nb_s, t_s = one(1 << 20)
+    return {
+        "dtype": str(dtype).replace("torch.", ""), "head_size": D,
+        "rows": rows, "bytes_per_launch": nb, "avg_us": round(t * 1e6, 3),
+        "achieved": round(nb / t / 1e9, 2), "frac": round(nb / t / 1e9 / PEAK_HBM_GBS, 4),
+        "stream_rows": 1 << 20, "stream_bytes_per_launch": nb_s,
+        "stream_avg_us": round(t_s * 1e6, 3), "stream_achieved": round(nb_s / t_s / 1e9, 2),
+        "stream_frac": round(nb_s / t_s / 1e9 / PEAK_HBM_GBS, 4), "unit": "GB/s",
     }
 
 
@@ -261,6 +299,8 @@ def run(args) -> dict:
                                                  PS, W.DTYPES[cfg.dtype])),
         },
     }
+    res["merge_states"] = merge_bench(pa, torch, dev, stream, S * MQ * H, D,
+                                      W.DTYPES[cfg.query_dtype], K)
     if args.calibrate_copy:
         n = 1 << 28  # 1 GiB of fp32: FETCH_SIZE / WRITE_SIZE calibration for the counters
         a = torch.ones(n, device=dev)
@@ -288,7 +328,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU mode; see the sharding notes in DESIGN.md)",
+              "(the path has no multi-GPU mode)",
               file=sys.stderr)
         return 2
     res = run(args)

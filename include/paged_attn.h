@@ -260,6 +260,52 @@ PA_API int paged_attn_decode_lse(void* out, float* lse, float* tmp_output, float
                                  int32_t out_dtype, void* stream);
 
 /*
+ * The general form of the two phases: any query / cache dtype pair the other
+ * calls accept, one or several query tokens per sequence, optional row
+ * log-sum-exp, optional ALiBi position bias.
+ *
+ * ALiBi. The Triton PagedAttention V2 page's launcher takes per-head
+ * alibi_slopes and never reads them; the pages give no formula. Reading
+ * taken: the published ALiBi definition (Press, Smith and Lewis, "Train
+ * Short, Test Long", ICLR 2022): the score of the key at position t for a
+ * query at position i gains slope_h * (t - i) after the scaling of the dot
+ * product, i = L - 1 for single-query decode and L - M + m for query token m
+ * of M (so the bias is 0 at the query's own position and negative before
+ * it). max_logits and lse include the bias.
+ *
+ *   alibi_slopes  float [num_heads] (query heads), 4-byte aligned, device
+ *                 memory read by the partition kernels; NULL: no bias (the
+ *                 same kernels and bits as the other calls)
+ *   lse           as for paged_attn_decode_lse, or NULL to skip it
+ *
+ * Other arguments, layouts and errors as for paged_attn_v2_partition_mq /
+ * paged_attn_decode_mq (query [S, M, H, D]; M = 1 is single-query decode with
+ * query [S, H, D]).
+ */
+PA_API int paged_attn_v2_partition_ex(float* tmp_output, float* exp_sums, float* max_logits,
+                                      const void* query, const void* key_cache,
+                                      const void* value_cache, const int32_t* block_tables,
+                                      const int32_t* seq_lens, int32_t num_seqs,
+                                      int32_t num_queries, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_size,
+                                      int32_t block_size, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t max_num_partitions,
+                                      int32_t partition_size, float scale, float k_scale,
+                                      float v_scale, const float* alibi_slopes,
+                                      int32_t q_dtype, int32_t kv_dtype, void* stream);
+
+PA_API int paged_attn_decode_ex(void* out, float* lse, float* tmp_output, float* exp_sums,
+                                float* max_logits, const void* query, const void* key_cache,
+                                const void* value_cache, const int32_t* block_tables,
+                                const int32_t* seq_lens, int32_t num_seqs, int32_t num_queries,
+                                int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                int32_t block_size, int32_t num_blocks,
+                                int32_t max_blocks_per_seq, int32_t max_num_partitions,
+                                int32_t partition_size, float scale, float k_scale,
+                                float v_scale, const float* alibi_slopes, int32_t q_dtype,
+                                int32_t kv_dtype, int32_t out_dtype, void* stream);
+
+/*
  * Merge two attention states of the same rows computed over disjoint key sets
  * (a shared prefix and a per-request suffix, or two shards of one long
  * sequence) into the state over their union: the Triton PagedAttention V2

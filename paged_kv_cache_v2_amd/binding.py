@@ -39,6 +39,9 @@ _SIGS = {
     "paged_attn_v2_reduce_lse": [_P] * 6 + [_I32] * 7 + [_P],
     "paged_attn_decode_lse": [_P] * 10 + [_I32] * 10 + [_F32, _F32, _F32, _I32, _I32, _I32, _P],
     "paged_attn_merge_states": [_P] * 6 + [_I64, _I32, _I32, _P],
+    "paged_attn_v2_partition_ex": [_P] * 8 + [_I32] * 10 + [_F32, _F32, _F32, _P, _I32, _I32, _P],
+    "paged_attn_decode_ex": [_P] * 10 + [_I32] * 10 + [_F32, _F32, _F32, _P, _I32, _I32, _I32,
+                                                        _P],
 }
 
 
@@ -339,6 +342,60 @@ def paged_attn_decode_lse(out, lse, tmp_output, exp_sums, max_logits, query, key
         partition_size, float(scale), float(k_scale), float(v_scale), _DT[query.dtype],
         _CACHE_DT[key_cache.dtype], _DT[out.dtype], _stream(query, stream))
     _check("paged_attn_decode_lse", rc)
+
+
+def _slopes_arg(alibi_slopes, H):
+    if alibi_slopes is None:
+        return None
+    _need(alibi_slopes.dtype == torch.float32 and alibi_slopes.is_cuda and
+          alibi_slopes.is_contiguous() and tuple(alibi_slopes.shape) == (H,),
+          "alibi_slopes must be a contiguous fp32 [num_heads] device tensor")
+    return alibi_slopes.data_ptr()
+
+
+def paged_attn_v2_partition_ex(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                               block_tables, seq_lens, scale: float, partition_size: int,
+                               k_scale: float = 1.0, v_scale: float = 1.0, alibi_slopes=None,
+                               stream=None) -> None:
+    """Phase 1, general form: [S, H, D] or [S, M, H, D] query, any supported cache
+    dtype, optional ALiBi slopes [H] (slope * (key position - query position))."""
+    _need(query.dim() in (3, 4), "query [S, H, D] or [S, M, H, D] expected")
+    q4 = _rows4(query, "query")
+    S, M, H, KH, D, BS, B, MB = _mq_geometry(q4, key_cache, value_cache, block_tables, seq_lens)
+    t4, e4, m4 = _rows4(tmp_output, "tmp"), _rows4(exp_sums, "stats"), _rows4(max_logits, "stats")
+    P = _mq_stats_geometry(t4, e4, m4, S, M, H, D)
+    rc = lib().paged_attn_v2_partition_ex(
+        tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(), query.data_ptr(),
+        key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+        seq_lens.data_ptr(), S, M, H, KH, D, BS, B, MB, P, partition_size, float(scale),
+        float(k_scale), float(v_scale), _slopes_arg(alibi_slopes, H), _DT[query.dtype],
+        _CACHE_DT[key_cache.dtype], _stream(query, stream))
+    _check("paged_attn_v2_partition_ex", rc)
+
+
+def paged_attn_decode_ex(out, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                         block_tables, seq_lens, scale: float, partition_size: int,
+                         k_scale: float = 1.0, v_scale: float = 1.0, alibi_slopes=None,
+                         lse=None, stream=None) -> None:
+    """Both phases, general form (see paged_attn_v2_partition_ex); lse (shaped like
+    out without its last dim) receives each row's log-sum-exp when given."""
+    _need(query.dim() in (3, 4), "query [S, H, D] or [S, M, H, D] expected")
+    q4 = _rows4(query, "query")
+    S, M, H, KH, D, BS, B, MB = _mq_geometry(q4, key_cache, value_cache, block_tables, seq_lens)
+    t4, e4, m4 = _rows4(tmp_output, "tmp"), _rows4(exp_sums, "stats"), _rows4(max_logits, "stats")
+    P = _mq_stats_geometry(t4, e4, m4, S, M, H, D)
+    _need(out.dim() == query.dim() and tuple(out.shape) == tuple(query.shape) and
+          out.dtype in _DT and out.is_cuda and out.is_contiguous(),
+          "out must be a contiguous tensor shaped like query")
+    lse_ptr = _lse_arg(lse, _rows4(out, "out")) if lse is not None else None
+    rc = lib().paged_attn_decode_ex(
+        out.data_ptr(), lse_ptr, tmp_output.data_ptr(), exp_sums.data_ptr(),
+        max_logits.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), seq_lens.data_ptr(), S, M, H, KH, D, BS, B, MB, P,
+        partition_size, float(scale), float(k_scale), float(v_scale),
+        _slopes_arg(alibi_slopes, H), _DT[query.dtype], _CACHE_DT[key_cache.dtype],
+        _DT[out.dtype], _stream(query, stream))
+    _check("paged_attn_decode_ex", rc)
 
 
 def paged_attn_merge_states(out, out_lse, a, lse_a, b, lse_b, stream=None) -> None:

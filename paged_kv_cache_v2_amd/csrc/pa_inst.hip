@@ -1,0 +1,59 @@
+// Instantiations of the partition kernels, one family per compilation:
+//   PA_FAMILY 0: MFMA, 16-bit caches     1: MFMA, 8-bit caches
+//             2: vector, 16/32-bit       3: vector, 8-bit caches
+//   PA_AL     0: no position bias        1: ALiBi
+// The build compiles this file once per (family, ALiBi) pair in parallel.
+#include <hip/hip_runtime.h>
+
+#include "pa_tables.h"
+
+#if !defined(PA_FAMILY) || !defined(PA_AL)
+#error "PA_FAMILY and PA_AL must be defined"
+#endif
+
+#define PA_CAT2(a, b) a##b
+#define PA_CAT(a, b) PA_CAT2(a, b)
+#if PA_AL
+#define PA_TABLE(name) PA_CAT(name, _al1)
+#else
+#define PA_TABLE(name) PA_CAT(name, _al0)
+#endif
+
+namespace pa {
+
+constexpr bool kAL = PA_AL != 0;
+
+#if PA_FAMILY == 0 || PA_FAMILY == 1
+constexpr bool kKV8 = PA_FAMILY == 1;
+#define PA_MFMA_D(DT)                                                                           \
+  {{partition_mfma_kernel<DT, 64, 16, kKV8, kAL>, partition_mfma_kernel<DT, 64, 32, kKV8, kAL>}, \
+   {partition_mfma_kernel<DT, 128, 16, kKV8, kAL>,                                              \
+    partition_mfma_kernel<DT, 128, 32, kKV8, kAL>},                                             \
+   {partition_mfma_kernel<DT, 256, 16, kKV8, kAL>,                                              \
+    partition_mfma_kernel<DT, 256, 32, kKV8, kAL>}}
+#if PA_FAMILY == 0
+const partition_fn PA_TABLE(kMfma)[2][3][2] = {PA_MFMA_D(DT_F16), PA_MFMA_D(DT_BF16)};
+#else
+const partition_fn PA_TABLE(kMfma8)[2][3][2] = {PA_MFMA_D(DT_F16), PA_MFMA_D(DT_BF16)};
+#endif
+#undef PA_MFMA_D
+
+#else
+constexpr bool kKV8 = PA_FAMILY == 3;
+#define PA_VEC_GM(DT, D, BS)                                                       \
+  {partition_vec_kernel<DT, D, BS, 1, kKV8, kAL>, partition_vec_kernel<DT, D, BS, 2, kKV8, kAL>, \
+   partition_vec_kernel<DT, D, BS, 4, kKV8, kAL>}
+#define PA_VEC_BS(DT, D) {PA_VEC_GM(DT, D, 16), PA_VEC_GM(DT, D, 32)}
+#define PA_VEC_D(DT) {PA_VEC_BS(DT, 64), PA_VEC_BS(DT, 128), PA_VEC_BS(DT, 256)}
+#if PA_FAMILY == 2
+const partition_fn PA_TABLE(kVec)[3][3][2][3] = {PA_VEC_D(DT_F32), PA_VEC_D(DT_F16),
+                                                 PA_VEC_D(DT_BF16)};
+#else
+const partition_fn PA_TABLE(kVec8)[2][3][2][3] = {PA_VEC_D(DT_F16), PA_VEC_D(DT_BF16)};
+#endif
+#undef PA_VEC_D
+#undef PA_VEC_BS
+#undef PA_VEC_GM
+#endif
+
+}  // namespace pa

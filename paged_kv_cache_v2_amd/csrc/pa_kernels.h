@@ -162,7 +162,17 @@ struct PartitionArgs {
   int through;     // 1: tmp_output stores with device-scope (sc1) policy
   float qk_scale;  // scale * log2(e) (times k_scale for an 8-bit cache)
   float v_scale;   // 1, or v_scale for an 8-bit cache (applied once, at the merge)
+  const float* alibi;  // [H] ALiBi slopes (read by the AL kernels only)
 };
+
+// ALiBi: a query at position i adds slope_h * (j - i) to its scaled score for
+// the key at position j (Press, Smith and Lewis, "Train Short, Test Long",
+// ICLR 2022; the page's launcher only names the slopes). The bias is split as
+// slope * (j - T0) + slope * (T0 - i), T0 the first key of j's partition: the
+// first part enters each score (at most slope * PS in magnitude, so fp32
+// keeps the scores' absolute precision however far the partition lies from
+// the query); the second is the same for the whole partition, cancels in its
+// exp sum and normalised output, and is added to its max logit at the store.
 
 constexpr int kMaxSpan = 2;
 
@@ -212,10 +222,10 @@ __device__ __forceinline__ int slot(int j, int w, int c, int NC) { return (j * k
 // (column, partition, d) in memory order, so the rows of adjacent partitions
 // of one head are written together. A column whose causal prefix ends before
 // a used partition merges to max -inf, sum 0 (the empty-partition sentinels).
-template <int D>
+template <int D, bool AL>
 __device__ __forceinline__ void merge_store(const PartitionArgs& a, const float* s_m,
                                             const float* s_l, const float* s_acc, int s, int kh,
-                                            int p0, int ne, int G, int M) {
+                                            int p0, int ne, int G, int M, int L) {
   constexpr int D4 = D / 4;
   const int NC = G * M;
   const int per_col = ne * D4;
@@ -246,8 +256,13 @@ __device__ __forceinline__ void merge_store(const PartitionArgs& a, const float*
     const size_t row = ((size_t)s * M * a.H + kh * G + hrow) * a.P + p0 + j;
     store_row(tmp, (uint32_t)(((hrow * a.P + p0 + j) * D + 4 * d4) * 4), o * inv, a.through);
     if (d4 == 0) {
+      float mx = Mx;
+      if constexpr (AL) {  // the partition's share of the ALiBi bias (see PartitionArgs)
+        const float slope2 = a.alibi[kh * G + g] * kLog2e;
+        mx += slope2 * (float)((p0 + j) * a.PS - (L - M + m));
+      }
       a.exp_sums[row] = Z;
-      a.max_logits[row] = Mx * kLn2;
+      a.max_logits[row] = mx * kLn2;
     }
   }
 }
@@ -346,12 +361,15 @@ constexpr int prefetch_fp8(int page_regs) { return page_regs <= 16 ? PA_PREFETCH
 // pages carry twice the arithmetic per byte of a 16-bit cache's, so latency
 // hiding needs more resident wavefronts (D = 128, BS = 16: 4 per SIMD
 // measured ~10 % faster than 3 and ~25 % faster than 2). Larger pages need
-// more registers; the budget shrinks so that nothing spills.
-constexpr int fp8_waves(int D, int BS) { return D * BS <= 2048 ? 4 : D <= 128 ? 3 : 2; }
+// more registers; the budget shrinks so that nothing spills (the ALiBi
+// variant's two extra per-lane values tip the smallest page over 4).
+constexpr int fp8_waves(int D, int BS, bool AL) {
+  return D * BS <= 2048 && !AL ? 4 : D <= 128 ? 3 : 2;
+}
 
-template <int DT, int D, int BS, bool KV8>
+template <int DT, int D, int BS, bool KV8, bool AL>
 __global__ void __launch_bounds__(kWaves * 64)
-__attribute__((amdgpu_waves_per_eu(KV8 ? fp8_waves(D, BS) : (PA_MIN_WAVES > 0 ? PA_MIN_WAVES : 1))))
+__attribute__((amdgpu_waves_per_eu(KV8 ? fp8_waves(D, BS, AL) : (PA_MIN_WAVES > 0 ? PA_MIN_WAVES : 1))))
 partition_mfma_kernel(PartitionArgs a) {
   constexpr int SUB = BS / 16;  // 16-token sub-tiles per page
   constexpr int KS = D / 32;    // QK k-steps (32 d each) per sub-tile
@@ -375,6 +393,8 @@ partition_mfma_kernel(PartitionArgs a) {
   // tokens t < lim (the causal prefix; L for single-query decode).
   const int qtok = g < NC ? g / G : 0;
   const int lim = min(u.L, max(0, u.L - u.M + qtok + 1));
+  // ALiBi slope of this lane's column, log2 units.
+  const float slope2 = AL && g < NC ? a.alibi[u.kh * G + g - qtok * G] * kLog2e : 0.0f;
 
   // Q columns as the QK B operand, k-step m: lane holds 8 consecutive d of its
   // column, d = 32m + 8*grp (16-bit cache) or 16*(4*(m/2) + grp) + 8*(m%2) (8-bit).
@@ -496,8 +516,15 @@ partition_mfma_kernel(PartitionArgs a) {
 #pragma unroll
       for (int mk = 0; mk < KS; ++mk) sc = M::qk(k_operand(pg, st, mk), qb[mk], sc);
       const int nvalid = lim - (tok0 + 16 * st + 4 * grp);  // row 4*grp+r valid iff r < nvalid
+      if constexpr (AL) {  // position relative to the page's partition start
+        const float base = slope2 * (float)(tok0 + 16 * st + 4 * grp - (u.p0 + jcur) * a.PS);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s2[st][r] = r < nvalid ? sc[r] * a.qk_scale : kNegInf;
+        for (int r = 0; r < 4; ++r)
+          s2[st][r] = r < nvalid ? fmaf(sc[r], a.qk_scale, fmaf(slope2, (float)r, base)) : kNegInf;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s2[st][r] = r < nvalid ? sc[r] * a.qk_scale : kNegInf;
+      }
     }
     float mt = kNegInf;
 #pragma unroll
@@ -566,7 +593,7 @@ partition_mfma_kernel(PartitionArgs a) {
   pipeline<PF>(npg, ring, fetch, process);
   while (jcur < u.ne) park();
   __syncthreads();
-  merge_store<D>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G, u.M);
+  merge_store<D, AL>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G, u.M, u.L);
 }
 
 // =====================================================================
@@ -586,7 +613,7 @@ template <> struct vec_elem<DT_F32> {
   static constexpr int X = 4;
 };
 
-template <int DT, int D, int BS, int GM, bool KV8>
+template <int DT, int D, int BS, int GM, bool KV8, bool AL>
 __global__ void __launch_bounds__(kWaves * 64) PA_OCCUPANCY
 partition_vec_kernel(PartitionArgs a) {
   constexpr int X = KV8 ? 16 : vec_elem<DT>::X;  // cache elements per 16-byte chunk
@@ -629,6 +656,10 @@ partition_vec_kernel(PartitionArgs a) {
       }
     }
   }
+  // ALiBi slopes of the lane's heads, log2 units.
+  float slope2[GM];
+#pragma unroll
+  for (int gg = 0; gg < GM; ++gg) slope2[gg] = AL && gg < G ? a.alibi[u.kh * G + gg] * kLog2e : 0.0f;
   if (!unit_hoist<BS>(a, (int32_t*)smem, u)) return;
   const LdsLayout lay = lds_layout(a.PS, BS, G, D, a.C);
   const int32_t* s_bt = (const int32_t*)(smem + lay.bt_off);
@@ -736,7 +767,12 @@ partition_vec_kernel(PartitionArgs a) {
           }
         }
         dot = rows_sum(dot);
-        s2[st] = tok0 + 16 * st + t < u.L ? dot * a.qk_scale : kNegInf;
+        const int tk = tok0 + 16 * st + t;  // this lane's token
+        if constexpr (AL)  // position relative to the page's partition start
+          s2[st] = tk < u.L ? fmaf(dot, a.qk_scale, slope2[gg] * (float)(tk - (u.p0 + jcur) * a.PS))
+                            : kNegInf;
+        else
+          s2[st] = tk < u.L ? dot * a.qk_scale : kNegInf;
         mt = fmaxf(mt, s2[st]);
       }
       mt = row16_max(mt);
@@ -802,7 +838,7 @@ partition_vec_kernel(PartitionArgs a) {
   pipeline<PF>(npg, ring, fetch, process);
   while (jcur < u.ne) park();
   __syncthreads();
-  merge_store<D>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G, 1);
+  merge_store<D, AL>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G, 1, u.L);
 }
 
 // =====================================================================

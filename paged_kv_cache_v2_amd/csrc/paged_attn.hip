@@ -14,6 +14,7 @@
 
 #include "paged_attn.h"
 #include "pa_kernels.h"
+#include "pa_tables.h"
 
 namespace {
 
@@ -36,7 +37,7 @@ bool is_16bit(int32_t dt) { return dt == PA_F16 || dt == PA_BF16; }
 using pa::PartitionArgs;
 using pa::ReduceArgs;
 using pa::MergeArgs;
-typedef void (*partition_fn)(PartitionArgs);
+using pa::partition_fn;
 typedef void (*reduce_fn)(ReduceArgs);
 typedef void (*merge_fn)(MergeArgs);
 
@@ -44,43 +45,12 @@ int d_index(int D) { return D == 64 ? 0 : D == 128 ? 1 : D == 256 ? 2 : -1; }
 int bs_index(int BS) { return BS == 16 ? 0 : BS == 32 ? 1 : -1; }
 
 // ---------------------------------------------------------------- kernel tables
-template <int DT, int D, int BS, bool KV8 = false>
-constexpr partition_fn mfma_k() { return pa::partition_mfma_kernel<DT, D, BS, KV8>; }
-template <int DT, int D, int BS, int GM, bool KV8 = false>
-constexpr partition_fn vec_k() { return pa::partition_vec_kernel<DT, D, BS, GM, KV8>; }
-
-// [dtype 1..2 -> 0..1][D][BS]
-const partition_fn kMfma[2][3][2] = {
-    {{mfma_k<pa::DT_F16, 64, 16>(), mfma_k<pa::DT_F16, 64, 32>()},
-     {mfma_k<pa::DT_F16, 128, 16>(), mfma_k<pa::DT_F16, 128, 32>()},
-     {mfma_k<pa::DT_F16, 256, 16>(), mfma_k<pa::DT_F16, 256, 32>()}},
-    {{mfma_k<pa::DT_BF16, 64, 16>(), mfma_k<pa::DT_BF16, 64, 32>()},
-     {mfma_k<pa::DT_BF16, 128, 16>(), mfma_k<pa::DT_BF16, 128, 32>()},
-     {mfma_k<pa::DT_BF16, 256, 16>(), mfma_k<pa::DT_BF16, 256, 32>()}},
-};
-
-// 8-bit (E4M3) caches, [query dtype f16 / bf16][D][BS]
-const partition_fn kMfma8[2][3][2] = {
-    {{mfma_k<pa::DT_F16, 64, 16, true>(), mfma_k<pa::DT_F16, 64, 32, true>()},
-     {mfma_k<pa::DT_F16, 128, 16, true>(), mfma_k<pa::DT_F16, 128, 32, true>()},
-     {mfma_k<pa::DT_F16, 256, 16, true>(), mfma_k<pa::DT_F16, 256, 32, true>()}},
-    {{mfma_k<pa::DT_BF16, 64, 16, true>(), mfma_k<pa::DT_BF16, 64, 32, true>()},
-     {mfma_k<pa::DT_BF16, 128, 16, true>(), mfma_k<pa::DT_BF16, 128, 32, true>()},
-     {mfma_k<pa::DT_BF16, 256, 16, true>(), mfma_k<pa::DT_BF16, 256, 32, true>()}},
-};
-
-#define PA_VEC_GM(DT, D, BS, K8) \
-  {vec_k<DT, D, BS, 1, K8>(), vec_k<DT, D, BS, 2, K8>(), vec_k<DT, D, BS, 4, K8>()}
-#define PA_VEC_BS(DT, D, K8) {PA_VEC_GM(DT, D, 16, K8), PA_VEC_GM(DT, D, 32, K8)}
-#define PA_VEC_D(DT, K8) {PA_VEC_BS(DT, 64, K8), PA_VEC_BS(DT, 128, K8), PA_VEC_BS(DT, 256, K8)}
-// [dtype][D][BS][GM = 1, 2, 4]
-const partition_fn kVec[3][3][2][3] = {PA_VEC_D(pa::DT_F32, false), PA_VEC_D(pa::DT_F16, false),
-                                       PA_VEC_D(pa::DT_BF16, false)};
-// 8-bit caches, [query dtype f16 / bf16][D][BS][GM]
-const partition_fn kVec8[2][3][2][3] = {PA_VEC_D(pa::DT_F16, true), PA_VEC_D(pa::DT_BF16, true)};
-#undef PA_VEC_D
-#undef PA_VEC_BS
-#undef PA_VEC_GM
+// Partition kernels: the tables of pa_tables.h, defined in the instantiation
+// units; [ALiBi off / on] here.
+const pa::partition_fn (*const kMfma[2])[3][2] = {pa::kMfma_al0, pa::kMfma_al1};
+const pa::partition_fn (*const kMfma8[2])[3][2] = {pa::kMfma8_al0, pa::kMfma8_al1};
+const pa::partition_fn (*const kVec[2])[3][2][3] = {pa::kVec_al0, pa::kVec_al1};
+const pa::partition_fn (*const kVec8[2])[3][2][3] = {pa::kVec8_al0, pa::kVec8_al1};
 
 // [out dtype][D]
 const reduce_fn kReduce[3][3] = {
@@ -160,7 +130,7 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
                     const void* key_cache, const void* value_cache, const int32_t* block_tables,
                     const int32_t* seq_lens, int32_t S, int32_t H, int32_t KH, int32_t D,
                     int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS, int32_t qdt,
-                    int32_t kvdt, int32_t M, Plan* plan) {
+                    int32_t kvdt, int32_t M, const float* alibi, Plan* plan) {
   if (S < 0 || H < 0 || KH < 0 || D < 0 || BS < 0 || NB < 0 || MB < 0 || P < 0)
     return fail(PA_ERR_SHAPE, "negative size argument");
   if (M < 1) return fail(PA_ERR_SHAPE, "num_queries must be >= 1");
@@ -193,6 +163,8 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   if (PS / BS > pa::kWaves * 64)
     return fail(PA_ERR_UNSUPPORTED, "partition_size / block_size > %d", pa::kWaves * 64);
   const int G = H / KH;
+  const int al = alibi ? 1 : 0;
+  if (alibi && !aligned4(alibi)) return fail(PA_ERR_ALIGN, "alibi_slopes must be 4-byte aligned");
   partition_fn fn = nullptr;
   if (M > 1) {
     // several query tokens: the MFMA path, one column per (query token, head)
@@ -200,12 +172,12 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
       return fail(PA_ERR_UNSUPPORTED,
                   "several query tokens need an f16/bf16 query and group * num_queries <= 16 "
                   "(got %d x %d)", G, M);
-    fn = kvdt == PA_FP8_E4M3 ? kMfma8[qdt - 1][di][bi] : kMfma[qdt - 1][di][bi];
+    fn = kvdt == PA_FP8_E4M3 ? kMfma8[al][qdt - 1][di][bi] : kMfma[al][qdt - 1][di][bi];
   } else if (is_16bit(qdt) && G >= 4 && G <= 16) {
-    fn = kvdt == PA_FP8_E4M3 ? kMfma8[qdt - 1][di][bi] : kMfma[qdt - 1][di][bi];
+    fn = kvdt == PA_FP8_E4M3 ? kMfma8[al][qdt - 1][di][bi] : kMfma[al][qdt - 1][di][bi];
   } else if (G <= 4) {
     const int gi = G == 1 ? 0 : G == 2 ? 1 : 2;
-    fn = kvdt == PA_FP8_E4M3 ? kVec8[qdt - 1][di][bi][gi] : kVec[qdt][di][bi][gi];
+    fn = kvdt == PA_FP8_E4M3 ? kVec8[al][qdt - 1][di][bi][gi] : kVec[al][qdt][di][bi][gi];
   } else {
     return fail(PA_ERR_UNSUPPORTED, "group size %d not supported for this dtype", G);
   }
@@ -234,7 +206,8 @@ int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float
                      const void* query, const void* key_cache, const void* value_cache,
                      const int32_t* block_tables, const int32_t* seq_lens, int32_t S, int32_t H,
                      int32_t KH, int32_t NB, int32_t MB, int32_t P, int32_t PS, float scale,
-                     float k_scale, float v_scale, int32_t M, hipStream_t stream) {
+                     float k_scale, float v_scale, int32_t M, const float* alibi,
+                     hipStream_t stream) {
   PartitionArgs a;
   a.tmp_out = tmp_output;
   a.exp_sums = exp_sums;
@@ -256,6 +229,7 @@ int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float
   a.through = P >= kThroughMinPartitions;
   a.qk_scale = scale * k_scale * pa::kLog2e;
   a.v_scale = v_scale;
+  a.alibi = alibi;
   hipLaunchKernelGGL(plan.fn, dim3(plan.grid), dim3(pa::kWaves * 64), plan.lds_bytes, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "partition launch failed: %s", hipGetErrorString(e));
@@ -320,18 +294,18 @@ int partition_entry(float* tmp_output, float* exp_sums, float* max_logits, const
                     const int32_t* seq_lens, int32_t S, int32_t M, int32_t H, int32_t KH,
                     int32_t D, int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS,
                     float scale, float k_scale, float v_scale, int32_t qdt, int32_t kvdt,
-                    void* stream) {
+                    void* stream, const float* alibi = nullptr) {
   g_err[0] = 0;
   if (!finite(k_scale) || !finite(v_scale))
     return fail(PA_ERR_SHAPE, "k_scale and v_scale must be finite");
   Plan plan;
   int rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                            block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt,
-                           M, &plan);
+                           M, alibi, &plan);
   if (rc != PA_OK || S == 0) return rc;
   return launch_partition(plan, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                           block_tables, seq_lens, S, H, KH, NB, MB, P, PS, scale, k_scale,
-                          v_scale, M, (hipStream_t)stream);
+                          v_scale, M, alibi, (hipStream_t)stream);
 }
 
 int decode_entry(void* out, float* lse, float* tmp_output, float* exp_sums, float* max_logits,
@@ -339,14 +313,15 @@ int decode_entry(void* out, float* lse, float* tmp_output, float* exp_sums, floa
                  const int32_t* block_tables, const int32_t* seq_lens, int32_t S, int32_t M,
                  int32_t H, int32_t KH, int32_t D, int32_t BS, int32_t NB, int32_t MB,
                  int32_t P, int32_t PS, float scale, float k_scale, float v_scale, int32_t qdt,
-                 int32_t kvdt, int32_t out_dtype, void* stream) {
+                 int32_t kvdt, int32_t out_dtype, void* stream, const float* alibi = nullptr) {
   g_err[0] = 0;
   if (!finite(k_scale) || !finite(v_scale))
     return fail(PA_ERR_SHAPE, "k_scale and v_scale must be finite");
+  if (S > 0 && lse && !aligned4(lse)) return fail(PA_ERR_ALIGN, "lse must be 4-byte aligned");
   Plan plan;
   int rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                            block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt,
-                           M, &plan);
+                           M, alibi, &plan);
   if (rc != PA_OK || S == 0) return rc;
   if (out_dtype != PA_F32 && out_dtype != qdt)
     return fail(PA_ERR_UNSUPPORTED, "out dtype must be PA_F32 or the query dtype");
@@ -356,7 +331,7 @@ int decode_entry(void* out, float* lse, float* tmp_output, float* exp_sums, floa
   if (rc != PA_OK) return rc;
   rc = launch_partition(plan, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                         block_tables, seq_lens, S, H, KH, NB, MB, P, PS, scale, k_scale, v_scale,
-                        M, (hipStream_t)stream);
+                        M, alibi, (hipStream_t)stream);
   if (rc != PA_OK) return rc;
   return launch_reduce(fn, out, lse, tmp_output, exp_sums, max_logits, seq_lens, S, M, H, D, P,
                        PS, (hipStream_t)stream);
@@ -527,6 +502,38 @@ int paged_attn_decode_lse(void* out, float* lse, float* tmp_output, float* exp_s
                       head_size, block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
                       partition_size, scale, k_scale, v_scale, q_dtype, kv_dtype, out_dtype,
                       stream);
+}
+
+int paged_attn_v2_partition_ex(float* tmp_output, float* exp_sums, float* max_logits,
+                               const void* query, const void* key_cache, const void* value_cache,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t max_num_partitions, int32_t partition_size, float scale,
+                               float k_scale, float v_scale, const float* alibi_slopes,
+                               int32_t q_dtype, int32_t kv_dtype, void* stream) {
+  return partition_entry(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                         block_tables, seq_lens, num_seqs, num_queries, num_heads, num_kv_heads,
+                         head_size, block_size, num_blocks, max_blocks_per_seq,
+                         max_num_partitions, partition_size, scale, k_scale, v_scale, q_dtype,
+                         kv_dtype, stream, alibi_slopes);
+}
+
+int paged_attn_decode_ex(void* out, float* lse, float* tmp_output, float* exp_sums,
+                         float* max_logits, const void* query, const void* key_cache,
+                         const void* value_cache, const int32_t* block_tables,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t num_queries,
+                         int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                         int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                         int32_t max_num_partitions, int32_t partition_size, float scale,
+                         float k_scale, float v_scale, const float* alibi_slopes,
+                         int32_t q_dtype, int32_t kv_dtype, int32_t out_dtype, void* stream) {
+  return decode_entry(out, lse, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                      block_tables, seq_lens, num_seqs, num_queries, num_heads, num_kv_heads,
+                      head_size, block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
+                      partition_size, scale, k_scale, v_scale, q_dtype, kv_dtype, out_dtype,
+                      stream, alibi_slopes);
 }
 
 int paged_attn_merge_states(void* out, float* out_lse, const void* a, const float* lse_a,

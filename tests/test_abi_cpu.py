@@ -276,3 +276,18 @@ def test_merge_states_rejects(kw, code):
 def test_merge_states_zero_rows_is_noop():
     assert merge(ptrs=[None] * 6, rows=0) == binding.PA_OK
     assert pa.last_error() == ""
+
+
+def test_ex_entries_reject_misaligned_alibi_and_lse():
+    lib = pa.lib()
+    part_args = lambda al: (*([FAKE] * 8), 2, 1, 8, 2, 128, 16, 64, 8, 1, 512, 0.125, 1.0, 1.0,
+                            al, binding.PA_BF16, binding.PA_BF16, None)
+    assert lib.paged_attn_v2_partition_ex(*part_args(FAKE + 2)) == binding.PA_ERR_ALIGN
+    assert "alibi" in pa.last_error()
+    dec_args = lambda lse, al: (FAKE, lse, *([FAKE] * 8), 2, 1, 8, 2, 128, 16, 64, 8, 1, 512,
+                                0.125, 1.0, 1.0, al, binding.PA_BF16, binding.PA_BF16,
+                                binding.PA_F32, None)
+    assert lib.paged_attn_decode_ex(*dec_args(FAKE + 1, None)) == binding.PA_ERR_ALIGN
+    assert lib.paged_attn_decode_ex(*dec_args(None, FAKE + 1)) == binding.PA_ERR_ALIGN
+    assert lib.paged_attn_decode_ex(*dec_args(None, None)[:10], 2, 5, *dec_args(None, None)[12:]) \
+        == binding.PA_ERR_UNSUPPORTED  # G=4 x M=5 > 16 columns
