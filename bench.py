@@ -83,7 +83,8 @@ def cpu_baseline(inp, W, min_seconds: float):
     while runs == 0 or t_total < min_seconds:
         t0 = time.perf_counter()
         tmp, es, ml = oracle.partition_stats(*args, P, PS, nthreads=threads,
-                                             k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+                                             k_scale=inp["k_scale"], v_scale=inp["v_scale"],
+                                             alibi_slopes=inp.get("alibi_slopes"))
         oracle.combine(tmp, es, ml, inp["seq_lens"], PS)
         t_total += time.perf_counter() - t0
         runs += 1
@@ -109,13 +110,15 @@ def merge_bench(pa, torch, dev, stream, rows: int, D: int, dtype, K: int) -> dic
         out, lse = torch.empty_like(a), torch.empty_like(la)
         for _ in range(3):
             pa.paged_attn_merge_states(out, lse, a, la, b, lb, stream)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        # K back-to-back launches between two events: a small merge takes a few
+        # microseconds, less than an event pair between every launch would add
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record(stream)
         for i in range(K):
             pa.paged_attn_merge_states(out, lse, a, la, b, lb, stream)
-            ev[i + 1].record(stream)
+        ev[1].record(stream)
         torch.cuda.synchronize()
-        avg_s = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(K)) / K / 1e3
+        avg_s = ev[0].elapsed_time(ev[1]) / K / 1e3
         nbytes = R * (3 * D * a.element_size() + 3 * 4)
         return nbytes, avg_s
 
@@ -162,9 +165,13 @@ def run(args) -> dict:
 
     fp8 = cfg.dtype == "fp8"
     ks, vs = inp["k_scale"], inp["v_scale"]
+    al = inp["alibi_slopes"].to(dev) if cfg.alibi else None
 
     def partition(tmp_, es_, ml_, PS_):
-        if MQ > 1:
+        if al is not None:
+            pa.paged_attn_v2_partition_ex(tmp_, es_, ml_, q, kc, vc, bt, sl, inp["scale"], PS_,
+                                          ks, vs, al, stream)
+        elif MQ > 1:
             pa.paged_attn_v2_partition_mq(tmp_, es_, ml_, q, kc, vc, bt, sl, inp["scale"], PS_,
                                           ks, vs, stream)
         elif fp8:
@@ -220,7 +227,10 @@ def run(args) -> dict:
     tmp_t, es_t, ml_t = work(P_t)
 
     def step_tuned():
-        if MQ > 1:
+        if al is not None:
+            pa.paged_attn_decode_ex(out, tmp_t, es_t, ml_t, q, kc, vc, bt, sl, inp["scale"], PS_t,
+                                    ks, vs, al, stream=stream)
+        elif MQ > 1:
             pa.paged_attn_decode_mq(out, tmp_t, es_t, ml_t, q, kc, vc, bt, sl, inp["scale"], PS_t,
                                     ks, vs, stream=stream)
         elif fp8:
@@ -273,9 +283,11 @@ def run(args) -> dict:
             "num_blocks": inp["num_blocks"],
             **({"k_scale": inp["k_scale"], "v_scale": inp["v_scale"]} if fp8 else {}),
             **({"num_queries": MQ} if MQ > 1 else {}),
+            **({"alibi": "slopes 2^(-8(h+1)/H)"} if al is not None else {}),
         },
         "tuned": {
-            "entry": ("paged_attn_decode_mq" if MQ > 1 else
+            "entry": ("paged_attn_decode_ex" if al is not None else
+                      "paged_attn_decode_mq" if MQ > 1 else
                       "paged_attn_decode_fp8" if fp8 else "paged_attn_decode"),
             "partition_size": PS_t, "max_num_partitions": P_t,
             "partition_span": (None if MQ > 1 else

@@ -63,6 +63,7 @@ class DecodeConfig:
     k_scale: float = 1.0  # 8-bit caches: a stored key byte stands for decode(byte) * k_scale
     v_scale: float = 1.0
     num_queries: int = 1  # query tokens per sequence (the last positions; query [S, M, H, D])
+    alibi: bool = False  # per-head ALiBi slopes (alibi_slopes) come with the inputs
 
     @property
     def query_dtype(self) -> str:
@@ -148,14 +149,38 @@ MQ_CONFIGS: Dict[str, DecodeConfig] = {
 MQ_ORDER = ["gqa_bf16_g4_m4", "longctx_bf16_g8_m2"]
 CONFIGS.update(MQ_CONFIGS)
 
+# ALiBi position bias: the MHA workload (the head structure of the published
+# ALiBi models) and the GQA one, with the ALiBi paper's slopes.
+ALIBI_CONFIGS: Dict[str, DecodeConfig] = {
+    "mha_f16_d128_alibi": CONFIGS["mha_f16_d128"].replace(name="mha_f16_d128_alibi", alibi=True),
+    "gqa_bf16_g4_alibi": CONFIGS["gqa_bf16_g4"].replace(name="gqa_bf16_g4_alibi", alibi=True),
+}
+ALIBI_ORDER = ["mha_f16_d128_alibi", "gqa_bf16_g4_alibi"]
+CONFIGS.update(ALIBI_CONFIGS)
+
+
+def alibi_slopes(num_heads: int) -> torch.Tensor:
+    """The ALiBi paper's head slopes (Press, Smith and Lewis, ICLR 2022): for a
+    power-of-two head count H, the geometric sequence 2^(-8 (h + 1) / H);
+    otherwise the slopes of the next lower power of two followed by every
+    other slope of the next higher one."""
+    def pow2(n):
+        return [2.0 ** (-8.0 * (h + 1) / n) for h in range(n)]
+    p = 1 << (num_heads.bit_length() - 1)
+    sl = pow2(p) if p == num_heads else pow2(p) + pow2(2 * p)[0::2][:num_heads - p]
+    return torch.tensor(sl, dtype=torch.float32)
+
 
 def workload_seed(name: str) -> int:
     """Seed of a named workload's reported runs: its index in its list, plus 1
-    (the 8-bit workloads from 101, the multi-token ones from 201)."""
+    (the 8-bit workloads from 101, the multi-token ones from 201, the ALiBi
+    ones from 301)."""
     if name in CONFIG_ORDER:
         return CONFIG_ORDER.index(name) + 1
     if name in FP8_ORDER:
         return FP8_ORDER.index(name) + 101
+    if name in ALIBI_ORDER:
+        return ALIBI_ORDER.index(name) + 301
     return MQ_ORDER.index(name) + 201
 
 
@@ -263,6 +288,7 @@ def make_inputs(cfg: DecodeConfig, seed: int, lens: Optional[Sequence[int]] = No
     out["num_queries"] = M
     out["key_cache"] = tensor(_KEY_K, (NB, KH, D // x, BS, x), cfg.dtype, cfg.k_scale)
     out["value_cache"] = tensor(_KEY_V, (NB, KH, D, BS), cfg.dtype, cfg.v_scale)
+    out["alibi_slopes"] = alibi_slopes(H) if cfg.alibi else None
     if device != "cpu":
         for k in ("query", "key_cache", "value_cache", "block_tables", "seq_lens"):
             out[k] = out[k].to(device)
