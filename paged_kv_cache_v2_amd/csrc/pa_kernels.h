@@ -163,6 +163,7 @@ struct PartitionArgs {
   float qk_scale;  // scale * log2(e) (times k_scale for an 8-bit cache)
   float v_scale;   // 1, or v_scale for an 8-bit cache (applied once, at the merge)
   const float* alibi;  // [H] ALiBi slopes (read by the AL kernels only)
+  int lpt;             // 1: workgroups take units largest first (see lpt_pair)
 };
 
 // ALiBi: a query at position i adds slope_h * (j - i) to its scaled score for
@@ -276,17 +277,108 @@ struct Unit {
   int32_t bt_val;  // this thread's entry of the span's block-table slice
 };
 
+// Pages of span ch (partitions ch*C .. ch*C + C - 1) of a length-L sequence.
+template <int BS>
+__device__ __forceinline__ int span_pages(const PartitionArgs& a, int L, int ch) {
+  const int cap = min(a.C, a.P - ch * a.C) * a.PS;
+  const int n = min(max(L - ch * a.C * a.PS, 0), cap);
+  return (n + BS - 1) / BS;
+}
+
+// LDS bytes lpt_pair needs (host and device).
+__host__ __device__ inline int lpt_lds_bytes(int S, int P, int PS, int BS, int C) {
+  const int pmax = C * PS / BS, pairs = S * ((P + C - 1) / C);
+  return ((4 * (pmax + 1) + 15) & ~15) + ((2 * pairs + 15) & ~15) + 16;
+}
+
+// Largest-first work order. With ragged lengths the units (sequence, span)
+// range from empty to full; dispatched in index order, the last workgroups of
+// a launch are a random mix of sizes and a few long ones finish alone. Here
+// every workgroup ranks all (sequence, span) pairs by their page count,
+// descending (a counting sort; ties keep index order), and takes the pair of
+// its own rank, so full spans run first, partial ones by size after them and
+// empty ones (sentinel writes only) last. The order depends only on the
+// lengths, so every workgroup derives the same one; each unit is still
+// computed exactly as before, so results do not depend on the order.
+// Uses LDS from `smem` (lpt_lds_bytes) before the unit's own use of it.
+template <int BS>
+__device__ __forceinline__ int lpt_pair(const PartitionArgs& a, uint8_t* smem) {
+  const int pmax = a.C * a.PS / BS;
+  const int pairs = a.S * ((a.P + a.C - 1) / a.C);
+  int* hist = (int*)smem;  // [pmax + 1] pairs per page count
+  uint16_t* keys = (uint16_t*)(smem + ((4 * (pmax + 1) + 15) & ~15));  // [pairs] page counts
+  int* res = (int*)((uint8_t*)keys + ((2 * pairs + 15) & ~15));
+  for (int k = threadIdx.x; k <= pmax; k += kWaves * 64) hist[k] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < pairs; i += kWaves * 64) {  // pair i = span ch of sequence s
+    const int ch = i / a.S, s = i - ch * a.S;
+    const int key = span_pages<BS>(a, a.sl[s], ch);
+    keys[i] = (uint16_t)key;
+    atomicAdd(&hist[key], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int r = blockIdx.x / a.KH;  // this workgroup's rank among the pairs
+    if (lane == 0) res[0] = r;         // (index order if the search below finds nothing)
+    // Page counts in descending order d = pmax - k; lane owns d in [lane*W, lane*W + W).
+    const int W = (pmax + 64) / 64;
+    int sum = 0;
+    for (int e = 0; e < W; ++e) {
+      const int d = lane * W + e;
+      if (d <= pmax) sum += hist[pmax - d];
+    }
+    int incl = sum;  // inclusive scan over lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    const int excl = incl - sum;
+    const uint64_t own = __builtin_amdgcn_ballot_w64(r >= excl && r < incl);
+    const int owner = own ? __builtin_ctzll(own) : 0;
+    int key = -1, j = 0;
+    if (lane == owner && own) {
+      int before = excl;
+      for (int e = 0; e < W && lane * W + e <= pmax; ++e) {
+        const int k = pmax - (lane * W + e);
+        if (r < before + hist[k]) {
+          key = k;
+          j = r - before;
+          break;
+        }
+        before += hist[k];
+      }
+    }
+    key = __builtin_amdgcn_readlane(key, owner);
+    j = __builtin_amdgcn_readlane(j, owner);
+    // The j-th pair (in index order) whose page count is key.
+    for (int base = 0; base < pairs; base += 64) {
+      const int i = base + lane;
+      const bool m = i < pairs && keys[i] == key;
+      const uint64_t mb = __builtin_amdgcn_ballot_w64(m);
+      const int c = __builtin_popcountll(mb);
+      if (j < c) {
+        if (m && __builtin_popcountll(mb & ((1ull << lane) - 1)) == j) res[0] = i;
+        break;
+      }
+      j -= c;
+    }
+  }
+  __syncthreads();
+  return min(max(res[0], 0), pairs - 1);
+}
+
 // Decode the unit and issue its first loads together: the sequence length and
 // the block-table slice of the whole span (clamped to the row, so always in
 // bounds; entries past the sequence's last block are loaded but never used).
 // Nothing here waits on the length, so the loads overlap.
 template <int BS>
-__device__ __forceinline__ void unit_begin(const PartitionArgs& a, Unit& u) {
-  const int unit = blockIdx.x;
-  u.kh = unit % a.KH;
-  const int rest = unit / a.KH;
-  u.s = rest % a.S;
-  u.p0 = (rest / a.S) * a.C;
+__device__ __forceinline__ void unit_begin(const PartitionArgs& a, Unit& u, uint8_t* smem) {
+  u.kh = blockIdx.x % a.KH;
+  const int pair = a.lpt ? lpt_pair<BS>(a, smem) : (int)(blockIdx.x / a.KH);
+  u.s = pair % a.S;
+  u.p0 = (pair / a.S) * a.C;
   u.nparts = min(a.C, a.P - u.p0);
   u.G = a.H / a.KH;
   u.M = a.M;
@@ -385,7 +477,7 @@ partition_mfma_kernel(PartitionArgs a) {
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   Unit u;
-  unit_begin<BS>(a, u);
+  unit_begin<BS>(a, u, smem);
   const int G = u.G, NC = u.NC;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane & 15, grp = lane >> 4;  // g: this lane's column (and token row in a tile)
@@ -632,7 +724,7 @@ partition_vec_kernel(PartitionArgs a) {
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   Unit u;
-  unit_begin<BS>(a, u);
+  unit_begin<BS>(a, u, smem);
   const int G = u.G;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

@@ -86,6 +86,7 @@ struct Plan {
   int lds_bytes;
   int grid;
   int span;
+  int lpt;  // largest-first unit order
 };
 
 #ifndef PA_SPAN
@@ -105,6 +106,18 @@ constexpr long long kMinGrid = 2048;
 // many partitions (measured; see store_row in pa_kernels.h).
 constexpr int kThroughMinPartitions = 16;
 constexpr long long kSpanBytes = 512 * 1024;
+#ifndef PA_LPT
+#define PA_LPT 1  // 0: units in index order (measurement builds)
+#endif
+// Largest-first unit order (lpt_pair in pa_kernels.h) while every workgroup's
+// ranking stays cheap: at most this many (sequence, span) pairs. Measured on
+// the ragged batches (index order -> largest first): 8-bit GQA 102.7 -> 90.8 µs,
+// 8-bit MHA 105.7 -> 102.1, 16-bit MHA (vector kernel) 212.0 -> 207.9; but
+// 16-bit GQA (MFMA kernel, two workgroups per CU, so the ranking's extra
+// round trip is poorly hidden) 186.8 -> 192.1, and uniform lengths lose
+// ~1 % (nothing to reorder). So it is taken for 8-bit caches and the vector
+// kernel only.
+constexpr int kLptMaxPairs = 4096;
 constexpr int kSpanLdsCap = 64 * 1024;
 
 int pick_span(int S, int KH, int P, int PS, int BS, int NC, int D, int esz, int lds_limit) {
@@ -166,6 +179,7 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   const int al = alibi ? 1 : 0;
   if (alibi && !aligned4(alibi)) return fail(PA_ERR_ALIGN, "alibi_slopes must be 4-byte aligned");
   partition_fn fn = nullptr;
+  bool vec = false;
   if (M > 1) {
     // several query tokens: the MFMA path, one column per (query token, head)
     if (!is_16bit(qdt) || (long long)G * M > 16)
@@ -178,6 +192,7 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   } else if (G <= 4) {
     const int gi = G == 1 ? 0 : G == 2 ? 1 : 2;
     fn = kvdt == PA_FP8_E4M3 ? kVec8[al][qdt - 1][di][bi][gi] : kVec[al][qdt][di][bi][gi];
+    vec = true;
   } else {
     return fail(PA_ERR_UNSUPPORTED, "group size %d not supported for this dtype", G);
   }
@@ -197,6 +212,13 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   if (grid > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many work units");
   plan->fn = fn;
   plan->lds_bytes = pa::lds_layout(PS, BS, NC, D, span).total;
+  const long long pairs = (long long)S * ((P + span - 1) / span);
+  plan->lpt = PA_LPT && pairs <= kLptMaxPairs && (vec || kvdt == PA_FP8_E4M3 || PA_LPT == 2);
+  if (plan->lpt) {
+    const int ord = pa::lpt_lds_bytes(S, P, PS, BS, span);
+    if (ord > lds_limit) plan->lpt = 0;
+    else plan->lds_bytes = plan->lds_bytes > ord ? plan->lds_bytes : ord;
+  }
   plan->grid = (int)grid;
   plan->span = span;
   return PA_OK;
@@ -230,6 +252,7 @@ int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float
   a.qk_scale = scale * k_scale * pa::kLog2e;
   a.v_scale = v_scale;
   a.alibi = alibi;
+  a.lpt = plan.lpt;
   hipLaunchKernelGGL(plan.fn, dim3(plan.grid), dim3(pa::kWaves * 64), plan.lds_bytes, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "partition launch failed: %s", hipGetErrorString(e));
