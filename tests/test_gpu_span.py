@@ -47,7 +47,16 @@ SPAN_CASES = [
     ("bf16", 16, 8, 64, 32, 64, 4, 256),    # vector G=2, D=64, BS=32
     ("f32", 8, 8, 64, 16, 64, 4, 128),      # vector fp32
     ("f16", 16, 16, 256, 32, 64, 4, 64),    # vector D=256, BS=32
+    ("fp8", 32, 8, 128, 16, 64, 5, 104),    # MFMA, 8-bit cache, odd P (largest-first order)
+    ("fp8", 16, 16, 128, 16, 64, 5, 104),   # vector, 8-bit cache, odd P (largest-first order)
 ]
+
+
+def case_config(name, dtype, H, KH, D, BS, PS, P, S):
+    fp8 = dict(q_dtype="bf16", k_scale=0.015, v_scale=0.02) if dtype == "fp8" else {}
+    return W.DecodeConfig(name, num_seqs=S, num_heads=H, num_kv_heads=KH, head_size=D,
+                          block_size=BS, partition_size=PS, dtype=dtype, len_lo=0,
+                          len_hi=P * PS, **fp8)
 
 
 @pytest.mark.parametrize("c", SPAN_CASES, ids=lambda c: "_".join(map(str, c)))
@@ -56,9 +65,7 @@ def test_two_partition_span(c, split):
     dtype, H, KH, D, BS, PS, P, S = c
     span = pa.partition_span(S, H, KH, D, BS, P, PS, W.DTYPES[dtype])
     assert span == 2, f"plan chose span {span}; the case no longer exercises two-partition spans"
-    cfg = W.DecodeConfig(f"span_{dtype}", num_seqs=S, num_heads=H, num_kv_heads=KH, head_size=D,
-                         block_size=BS, partition_size=PS, dtype=dtype, len_lo=0,
-                         len_hi=P * PS)
+    cfg = case_config(f"span_{dtype}", dtype, H, KH, D, BS, PS, P, S)
     lens = span_lens(S, BS, PS, P, seed=S + P)
     inp = W.make_inputs(cfg, seed=41, lens=lens, extra_blocks=3)
     W.poison_unused(inp)
@@ -118,3 +125,24 @@ def test_span_results_match_single_partition_workgroups():
     for s in range(4):
         assert torch.equal(small["tmp"][s, :, :n[s]], big["tmp"][s, :, :n[s]]), s
     assert torch.equal(small["out"], big["out"][:4])
+
+
+# More (sequence, span) pairs than the largest-first ranking takes (4096): the
+# vector and 8-bit kernels fall back to index order. Short ragged sequences
+# keep the oracle quick.
+@pytest.mark.parametrize("dtype,H,KH", [("f16", 8, 8), ("fp8", 16, 4)], ids=["vec_f16", "mfma_fp8"])
+def test_many_pairs_index_order(dtype, H, KH):
+    S, D, BS, PS, P = 4200, 64, 16, 32, 2
+    assert S * P > 4096
+    cfg = case_config(f"pairs_{dtype}", dtype, H, KH, D, BS, PS, P, S)
+    lens = np.random.default_rng(9).integers(0, P * PS + 1, size=S).tolist()
+    inp = W.make_inputs(cfg, seed=49, lens=lens)
+    W.poison_unused(inp)
+    U.note(f"many pairs {dtype} S={S}")
+    res = U.run_decode(U.to_device(inp), split=True)
+    U.check_against_oracle(inp, res, seqs=list(range(0, S, 7)), label=f"pairs {dtype}")
+    # every sequence: sentinels exactly past its partitions, finite statistics before
+    for s_, L in enumerate(lens):
+        n = -(-L // PS)
+        assert torch.all(res["ml"][s_, :, n:] == -np.inf) and torch.all(res["es"][s_, :, n:] == 0)
+        assert torch.isfinite(res["ml"][s_, :, :n]).all() and torch.all(res["es"][s_, :, :n] >= 1)
