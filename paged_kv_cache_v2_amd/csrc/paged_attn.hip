@@ -107,7 +107,7 @@ constexpr long long kMinGrid = 2048;
 constexpr int kThroughMinPartitions = 16;
 constexpr long long kSpanBytes = 512 * 1024;
 #ifndef PA_LPT
-#define PA_LPT 1  // 0: units in index order (measurement builds)
+#define PA_LPT 1  // measurement builds: 0 index order everywhere, 2 largest-first everywhere
 #endif
 // Largest-first unit order (lpt_pair in pa_kernels.h) while every workgroup's
 // ranking stays cheap: at most this many (sequence, span) pairs. Measured on
