@@ -173,14 +173,14 @@ def alibi_slopes(num_heads: int) -> torch.Tensor:
 
 def workload_seed(name: str) -> int:
     """Seed of a named workload's reported runs: its index in its list, plus 1
-    (the 8-bit workloads from 101, the multi-token ones from 201, the ALiBi
-    ones from 301)."""
+    (the 8-bit workloads from 101, the multi-token ones from 201); an ALiBi
+    workload reuses its base workload's seed (the same inputs plus slopes)."""
     if name in CONFIG_ORDER:
         return CONFIG_ORDER.index(name) + 1
     if name in FP8_ORDER:
         return FP8_ORDER.index(name) + 101
     if name in ALIBI_ORDER:
-        return ALIBI_ORDER.index(name) + 301
+        return workload_seed(name[:-len("_alibi")])
     return MQ_ORDER.index(name) + 201
 
 
