@@ -21,7 +21,13 @@ Prints ONE JSON line:
                rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the
                current kernel source (else null).
   cpu_baseline = the fp64 oracle (partition stats + combine) timed on this
-               host's cores over a bounded sample of the same workload.
+               host's cores over the same workload: one warm run, then the
+               median of at least three timed runs (at least 10 s in all).
+  flushed    = the same two calls timed one by one with their own event
+               pairs after a 512 MiB scratch write (evicts the Infinity
+               Cache): median and p10 / p90 over 100 calls.
+  copy_context = a 1 GiB device-to-device copy's bandwidth (context for the
+               8 TB/s peak).
   merge_states = paged_attn_merge_states timed with HIP events: on the
                batch's own rows (two query-dtype states of every (sequence,
                query token, head) row, as a cascade merges them) and on a
@@ -79,23 +85,26 @@ def cpu_baseline(inp, W, min_seconds: float):
     args = (inp["query"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
             inp["seq_lens"], inp["scale"])
     P, PS = inp["max_num_partitions"], inp["partition_size"]
-    runs, t_total = 0, 0.0
-    while runs == 0 or t_total < min_seconds:
+
+    def one():
         t0 = time.perf_counter()
         tmp, es, ml = oracle.partition_stats(*args, P, PS, nthreads=threads,
                                              k_scale=inp["k_scale"], v_scale=inp["v_scale"],
                                              alibi_slopes=inp.get("alibi_slopes"))
         oracle.combine(tmp, es, ml, inp["seq_lens"], PS)
-        t_total += time.perf_counter() - t0
-        runs += 1
-        del tmp, es, ml
-    per_run = t_total / runs
+        return time.perf_counter() - t0
+
+    one()  # warm run (page-in, thread start)
+    times = []
+    while len(times) < 3 or sum(times) < min_seconds:
+        times.append(one())
+    per_run = sorted(times)[len(times) // 2]
     return {
         "value": round(W.kv_bytes(inp) / per_run / 1e9, 4), "unit": "GB/s", "cores": threads,
         "kind": "oracle",
         "sample": (f"whole workload ({inp['num_seqs']} sequences, "
-                   f"{int(inp['seq_lens'].sum())} tokens) x {runs} run(s), fp64 partition "
-                   f"stats + combine, {per_run:.2f} s per run"),
+                   f"{int(inp['seq_lens'].sum())} tokens), fp64 partition stats + combine: "
+                   f"1 warm run, median of {len(times)} timed runs, {per_run:.2f} s per run"),
     }
 
 
@@ -132,6 +141,57 @@ def merge_bench(pa, torch, dev, stream, rows: int, D: int, dtype, K: int) -> dic
         "stream_avg_us": round(t_s * 1e6, 3), "stream_achieved": round(nb_s / t_s / 1e9, 2),
         "stream_frac": round(nb_s / t_s / 1e9 / PEAK_HBM_GBS, 4), "unit": "GB/s",
     }
+
+
+def flushed_calls(torch, dev, stream, partition, reduce, tmp, es, ml, PS, kvb, n) -> dict:
+    """Each call timed by its own event pairs (partition, reduce) after a
+    512 MiB scratch write that evicts the 256 MB Infinity Cache (outside the
+    events): median and p10 / p90 of the step and of each kernel."""
+    scratch = torch.empty(1 << 27, dtype=torch.float32, device=dev)  # 512 MiB
+    steps, parts, reds = [], [], []
+    for i in range(n + 10):
+        scratch.fill_(float(i))
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        partition(tmp, es, ml, PS)
+        e[1].record(stream)
+        reduce(tmp, es, ml, PS)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        if i >= 10:  # 10 warm-up calls
+            parts.append(e[0].elapsed_time(e[1]) * 1e3)
+            reds.append(e[1].elapsed_time(e[2]) * 1e3)
+            steps.append(e[0].elapsed_time(e[2]) * 1e3)
+    del scratch
+
+    def q(v, f):
+        v = sorted(v)
+        return round(v[min(len(v) - 1, int(f * len(v)))], 3)
+
+    med = q(steps, 0.5)
+    return {"calls": n, "step_median_us": med, "step_p10_us": q(steps, 0.1),
+            "step_p90_us": q(steps, 0.9), "partition_median_us": q(parts, 0.5),
+            "reduce_median_us": q(reds, 0.5), "value": round(kvb / med / 1e3, 2), "unit": "GB/s",
+            "pct_of_peak_hbm": round(100.0 * kvb / med / 1e3 / PEAK_HBM_GBS, 2)}
+
+
+def copy_bandwidth(torch, dev, stream) -> dict:
+    """A 1 GiB device-to-device copy (torch copy_): read + write bytes / time."""
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 10 / 1e3
+    del a, b
+    return {"bytes": 2 * 4 * n, "us": round(t * 1e6, 2), "value": round(2 * 4 * n / t / 1e9, 1),
+            "unit": "GB/s", "pct_of_peak_hbm": round(100.0 * 2 * 4 * n / t / 1e9 / PEAK_HBM_GBS, 2)}
 
 
 def run(args) -> dict:
@@ -313,6 +373,9 @@ def run(args) -> dict:
     }
     res["merge_states"] = merge_bench(pa, torch, dev, stream, S * MQ * H, D,
                                       W.DTYPES[cfg.query_dtype], K)
+    res["flushed"] = flushed_calls(torch, dev, stream, partition, reduce, tmp, es, ml, PS, kvb,
+                                   args.flushed_calls)
+    res["copy_context"] = copy_bandwidth(torch, dev, stream)
     if args.calibrate_copy:
         n = 1 << 28  # 1 GiB of fp32: FETCH_SIZE / WRITE_SIZE calibration for the counters
         a = torch.ones(n, device=dev)
@@ -335,6 +398,8 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
+    ap.add_argument("--flushed-calls", type=int, default=100,
+                    help="calls timed one by one after an Infinity Cache flush")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
