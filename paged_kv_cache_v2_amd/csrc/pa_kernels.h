@@ -436,8 +436,28 @@ template <bool KV8, int SUB, int D> struct MfmaPage {
 };
 template <int SUB, int D> struct MfmaPage<true, SUB, D> {
   u32x4 k[SUB][D / 64];  // 8-bit K: one 16-byte load per two k-steps
-  uint32_t v[SUB][D / 16];  // 8-bit V: 4 tokens x 1 byte per d-block
+  u32x4 v[SUB][D / 64];  // 8-bit V: 16 tokens of one d per 16-byte load (see v_words)
 };
+
+// 8-bit V operands. The PV A operand of d-block mb wants, in lane (g, r)
+// (g = lane % 16, r = lane / 16), tokens 4r .. 4r+3 of d-row 16 mb + g: four
+// bytes. Loading those directly takes one 4-byte load per d-block; instead
+// lane (g, r) loads all 16 tokens of d-row 16 (4q + r) + g with one 16-byte
+// load (words w0..w3 = tokens 0-3 .. 12-15), and a 4 x 4 transpose across
+// the four 16-lane rows (gfx950's v_permlane32_swap then v_permlane16_swap:
+// the former swaps the upper half of its first operand with the lower half of
+// its second, the latter the odd rows of the first with the even rows of the
+// second) leaves in lane (g, r) word r of each of d-blocks 4q .. 4q+3.
+__device__ __forceinline__ void v_words(u32x4 w, uint32_t (&out)[4]) {
+  const auto a02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+  const auto a13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+  const auto b01 = __builtin_amdgcn_permlane16_swap(a02[0], a13[0], false, false);
+  const auto b23 = __builtin_amdgcn_permlane16_swap(a02[1], a13[1], false, false);
+  out[0] = b01[0];
+  out[1] = b01[1];
+  out[2] = b23[0];
+  out[3] = b23[1];
+}
 
 // Pages in flight for an 8-bit cache page of `page_regs` VGPRs. An 8-bit page
 // carries twice the arithmetic per byte of a 16-bit one, so occupancy matters
@@ -516,8 +536,9 @@ partition_mfma_kernel(PartitionArgs a) {
   const uint8_t* vbase = (const uint8_t*)a.vc + head_off;
   // K: chunk c = 4j + grp of token g at (c*BS + g)*16 bytes (+ st*256).
   const uint32_t k_lane = (uint32_t)(grp * BS + g) * 16;
-  // V: d-row 16*mb + g, tokens 16*st + 4*grp .. +3.
-  const uint32_t v_lane = (uint32_t)(g * BS + 4 * grp) * ESZ;
+  // V: d-row 16*mb + g, tokens 16*st + 4*grp .. +3 (16-bit); 8-bit: d-row
+  // 16*(4q + grp) + g, tokens 16*st .. +15 (v_words).
+  const uint32_t v_lane = KV8 ? (uint32_t)(16 * grp + g) * BS : (uint32_t)(g * BS + 4 * grp) * ESZ;
 
   const int npg = u.npages > wave ? (u.npages - wave + kWaves - 1) / kWaves : 0;
 
@@ -567,10 +588,11 @@ partition_mfma_kernel(PartitionArgs a) {
     for (int mb = 0; mb < VB; ++mb) {
 #pragma unroll
       for (int st = 0; st < SUB; ++st) {
-        if constexpr (KV8)
-          pg.v[st][mb] = stream_load<uint32_t>(vp + mb * 16 * BS + st * 16);
-        else
+        if constexpr (KV8) {
+          if (mb % 4 == 0) pg.v[st][mb / 4] = stream_load<u32x4>(vp + mb * 16 * BS + st * 16);
+        } else {
           pg.v[st][mb] = stream_load<u32x2>(vp + mb * 16 * BS * 2 + st * 32);
+        }
       }
     }
   };
@@ -587,7 +609,7 @@ partition_mfma_kernel(PartitionArgs a) {
       return pg.k[st][mk];
     }
   };
-  using VWord = typename std::remove_reference<decltype(Page::v[0][0])>::type;
+  using VWord = typename std::conditional<KV8, uint32_t, u32x2>::type;
   auto v_operand = [&](VWord w) -> u32x2 {
     if constexpr (KV8) {
       using F = fp8cvt<DT>;
@@ -654,8 +676,18 @@ partition_mfma_kernel(PartitionArgs a) {
     VWord vw[SUB][VB];
 #pragma unroll
     for (int st = 0; st < SUB; ++st) {
+      if constexpr (KV8) {
 #pragma unroll
-      for (int mb = 0; mb < VB; ++mb) vw[st][mb] = pg.v[st][mb];
+        for (int q = 0; q < VB / 4; ++q) {
+          uint32_t w[4];
+          v_words(pg.v[st][q], w);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) vw[st][4 * q + j] = w[j];
+        }
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < VB; ++mb) vw[st][mb] = pg.v[st][mb];
+      }
     }
     if (tok0 + BS > u.L) {
 #pragma unroll

@@ -76,8 +76,9 @@ def test_no_scalar_cache_writes(kernels):
 
 
 def test_kv_loads_are_dwordx4_or_dwordx2_streaming(kernels):
-    """K/V pages are fetched with 16-byte (K, vector-path V) or 8-byte (MFMA-path V)
-    non-temporal loads; an 8-bit cache's MFMA-path V pieces are 4 bytes."""
+    """K/V pages are fetched with 16-byte (K, vector-path V, 8-bit MFMA-path V) or
+    8-byte (16-bit MFMA-path V) non-temporal loads; the 8-bit MFMA path then
+    transposes its V words across lane rows with the gfx950 permlane swaps."""
     seen = 0
     for k, v in kernels.items():
         nt = [l for l in v if l.startswith("global_load") and l.endswith(" nt")]
@@ -87,7 +88,8 @@ def test_kv_loads_are_dwordx4_or_dwordx2_streaming(kernels):
             seen += 1
         if "partition_mfma_kernelILi2ELi128ELi16ELb1" in k:
             assert any(l.startswith("global_load_dwordx4") for l in nt)
-            assert any(l.startswith("global_load_dword ") for l in nt)
+            assert not any(l.startswith(("global_load_dword ", "global_load_dwordx2")) for l in nt)
+            assert {"v_permlane32_swap_b32_e32", "v_permlane16_swap_b32_e32"} <= set(ops(v))
             seen += 1
         if "partition_vec_kernelILi2ELi128ELi16ELi1ELb1" in k:
             assert any(l.startswith("global_load_dwordx4") for l in nt)
