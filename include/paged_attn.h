@@ -28,9 +28,11 @@
  *    that are never read and may hold anything (e.g. -1). Cache slots that no
  *    sequence reads (unreferenced blocks, tail slots of a last block) never
  *    influence any result, whatever they hold (NaN included).
- *  - Outputs must not alias inputs. Calls on one stream are ordered; the
- *    functions keep no state between calls and are safe to call from several
- *    threads on different streams.
+ *  - Outputs must not alias inputs (paged_attn_merge_states states its
+ *    in-place exception). Calls on one stream are ordered; the functions keep
+ *    no state between calls and are safe to call from several threads on
+ *    different streams. No call allocates, fills memory or waits, so calls
+ *    may be captured into a HIP graph and replayed.
  */
 #ifndef PAGED_ATTN_H
 #define PAGED_ATTN_H
