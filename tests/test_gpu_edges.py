@@ -146,3 +146,26 @@ def test_many_empty_partitions():
     U.note("many empty partitions")
     res = U.run_decode(U.to_device(inp), PS=64, P=40)
     U.check_against_oracle(inp, res, label="P=40")
+
+
+# The largest partition the launchers accept: PS / BS = 256 pages, one page per
+# thread of the block-table hoist (and one partition per workgroup), on each
+# kernel family; lengths around one and two full partitions.
+@pytest.mark.parametrize("dtype,H,KH,D,BS,extra", [
+    ("bf16", 32, 8, 128, 16, {}),                                          # MFMA
+    ("f16", 16, 16, 128, 32, {}),                                          # vector, BS=32
+    ("fp8", 32, 8, 128, 16, dict(q_dtype="bf16", k_scale=0.02, v_scale=0.03)),  # 8-bit MFMA
+    ("fp8", 8, 8, 64, 16, dict(q_dtype="f16", k_scale=0.02, v_scale=0.03)),     # 8-bit vector
+], ids=["mfma_bf16", "vec_f16_bs32", "mfma_fp8", "vec_fp8"])
+def test_max_pages_per_partition(dtype, H, KH, D, BS, extra):
+    PS = 256 * BS
+    lens = [0, 1, PS - 1, PS, PS + 1, 2 * PS]
+    cfg = W.DecodeConfig(f"maxps_{dtype}", num_seqs=len(lens), num_heads=H, num_kv_heads=KH,
+                         head_size=D, block_size=BS, partition_size=PS, dtype=dtype, len_lo=0,
+                         len_hi=2 * PS, **extra)
+    inp = W.make_inputs(cfg, seed=37, lens=lens, extra_blocks=2)
+    W.poison_unused(inp)
+    assert pa.partition_span(len(lens), H, KH, D, BS, 2, PS, W.DTYPES[dtype]) == 1
+    U.note(f"max pages per partition {dtype} PS={PS}")
+    res = U.run_decode(U.to_device(inp))
+    U.check_against_oracle(inp, res, label=f"max PS {dtype}")
