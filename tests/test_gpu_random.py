@@ -1,0 +1,111 @@
+"""Seeded random configurations through the general entry point.
+
+Each case draws a geometry (dtype pair, head counts, head size, block and
+partition size, batch, lengths with empty and partial partitions, query
+tokens, ALiBi on or off, output dtype) within what the launchers accept and
+runs paged_attn_decode_ex; the output, the row log-sum-exp and every
+partition intermediate are compared with the oracle. Sizes stay small so the
+oracle finishes in well under a second per case.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_v2_amd as pa
+from paged_kv_cache_v2_amd import workloads as W
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 40
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    pa.ensure_built()
+    oracle.build(force=False)
+
+
+def draw(i):
+    rng = np.random.default_rng(1000 + i)
+    kv = rng.choice(["f32", "f16", "bf16", "fp8"], p=[0.15, 0.3, 0.3, 0.25])
+    q = kv if kv != "fp8" else str(rng.choice(["f16", "bf16"]))
+    D = int(rng.choice([64, 128, 256]))
+    BS = int(rng.choice([16, 32]))
+    PS = BS * int(rng.choice([1, 2, 3, 4, 8]))
+    KH = int(rng.choice([1, 2, 4]))
+    if q == "f32":
+        G = int(rng.choice([1, 2, 3, 4]))
+        M = 1
+    else:
+        G = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
+        M = 1 if rng.random() < 0.6 else int(rng.integers(2, max(3, 16 // G + 1)))
+        if G * M > 16:
+            M = 1
+    S = int(rng.integers(1, 7))
+    P = int(rng.integers(1, 6))
+    lens = rng.integers(0, P * PS + 1, size=S)
+    lens[rng.integers(0, S)] = P * PS  # one full sequence
+    extra = dict(q_dtype=q, k_scale=float(rng.uniform(0.01, 0.05)),
+                 v_scale=float(rng.uniform(0.01, 0.05))) if kv == "fp8" else {}
+    cfg = W.DecodeConfig(f"rand{i}", num_seqs=S, num_heads=G * KH, num_kv_heads=KH, head_size=D,
+                         block_size=BS, partition_size=PS, dtype=kv, len_lo=0, len_hi=P * PS,
+                         num_queries=M, **extra)
+    alibi = rng.random() < 0.4
+    out16 = q != "f32" and rng.random() < 0.3
+    return cfg, [int(x) for x in lens], alibi, out16
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_config(i):
+    cfg, lens, alibi, out16 = draw(i)
+    inp = W.make_inputs(cfg, seed=2000 + i, lens=lens, extra_blocks=2)
+    W.poison_unused(inp)
+    d = U.to_device(inp)
+    q = d["query"]
+    lead = tuple(q.shape[:-1])
+    P, PS, D = cfg.max_num_partitions, cfg.partition_size, cfg.head_size
+    slopes = W.alibi_slopes(cfg.num_heads) if alibi else None
+    tmp = torch.full(lead + (P, D), float("nan"), device=U.DEV)
+    es = torch.full(lead + (P,), float("nan"), device=U.DEV)
+    ml = torch.full(lead + (P,), float("nan"), device=U.DEV)
+    out = torch.full(q.shape, float("nan"), device=U.DEV)
+    lse = torch.full(lead, float("nan"), device=U.DEV)
+    U.note(f"random case {i}: {cfg} lens={lens} alibi={alibi}")
+    pa.paged_attn_decode_ex(out, tmp, es, ml, q, d["key_cache"], d["value_cache"],
+                            d["block_tables"], d["seq_lens"], d["scale"], PS,
+                            k_scale=inp["k_scale"], v_scale=inp["v_scale"],
+                            alibi_slopes=slopes.to(U.DEV) if alibi else None, lse=lse)
+    if out16:  # the same call with a 16-bit output is the RNE cast of the fp32 one
+        o16 = torch.empty(q.shape, dtype=q.dtype, device=U.DEV)
+        pa.paged_attn_decode_ex(o16, tmp, es, ml, q, d["key_cache"], d["value_cache"],
+                                d["block_tables"], d["seq_lens"], d["scale"], PS,
+                                k_scale=inp["k_scale"], v_scale=inp["v_scale"],
+                                alibi_slopes=slopes.to(U.DEV) if alibi else None)
+    torch.cuda.synchronize()
+    a = (inp["query"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
+         inp["seq_lens"], inp["scale"])
+    sc = dict(k_scale=inp["k_scale"], v_scale=inp["v_scale"], alibi_slopes=slopes)
+    ref, ref_lse = oracle.attention_lse(*a, **sc)
+    U.assert_close(f"case {i} out", out.cpu(), ref)
+    got_lse = lse.cpu().double().numpy()
+    assert np.array_equal(np.isneginf(got_lse), np.isneginf(ref_lse)), f"case {i} lse -inf"
+    fin = ~np.isneginf(ref_lse)
+    U.assert_close(f"case {i} lse", got_lse[fin], ref_lse[fin])
+    rtmp, res_, rml = oracle.partition_stats(*a, P, PS, **sc)
+    M = cfg.num_queries
+    gt, ge, gm = tmp.cpu(), es.cpu(), ml.cpu()
+    for s, L in enumerate(lens):
+        for m in range(M):
+            n = -(-W.causal_len(L, M, m) // PS)
+            idx = (s, m) if M > 1 else (s,)
+            if n:
+                U.assert_close(f"case {i} ml {s},{m}", gm[idx][:, :n], rml[idx][:, :n])
+                U.assert_close(f"case {i} es {s},{m}", ge[idx][:, :n], res_[idx][:, :n])
+                U.assert_close(f"case {i} tmp {s},{m}", gt[idx][:, :n], rtmp[idx][:, :n])
+            assert torch.all(gm[idx][:, n:] == -math.inf) and torch.all(ge[idx][:, n:] == 0)
+    if out16:
+        assert torch.equal(out.to(q.dtype).cpu().view(torch.int16), o16.cpu().view(torch.int16))
