@@ -191,8 +191,11 @@ PA_API int paged_attn_decode_fp8(void* out, float* tmp_output, float* exp_sums,
  *   out          [S, M, H, D]        out_dtype PA_F32 or q_dtype
  *
  * A row's partitions past its causal prefix get the sentinels (max -inf, sum
- * 0; tmp_output unspecified). Requires (H / KH) * M <= 16 (one MFMA column
- * per (query token, head) of a kv head); PA_ERR_UNSUPPORTED otherwise.
+ * 0; tmp_output unspecified). Requires H / KH <= 16 (PA_ERR_UNSUPPORTED
+ * otherwise). Phase 1 computes one MFMA column per (query token, head) of a
+ * kv head, 16 columns per pass over the pages: when (H / KH) * M > 16 the
+ * tokens run in consecutive passes of 16 / (H / KH) tokens, each reading the
+ * K/V pages again (results are the same as in one pass).
  * num_queries = 1 computes exactly what the single-query calls compute.
  */
 PA_API int paged_attn_v2_partition_mq(float* tmp_output, float* exp_sums, float* max_logits,

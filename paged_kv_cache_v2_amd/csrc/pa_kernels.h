@@ -157,7 +157,8 @@ struct PartitionArgs {
   const int32_t* sl;
   int S, H, KH, MB, P, PS;
   int NB;          // physical blocks; block-table entries are clamped into [0, NB)
-  int M;           // query tokens per sequence (query [S, M, H, D]; 1: single-query decode)
+  int M;           // query tokens of this launch: m0 .. m0 + M - 1 (1: single-query decode)
+  int Mq, m0;      // query tokens per sequence in the tensors (query [S, Mq, H, D]), first one here
   int C;           // consecutive partitions per workgroup (span), 1 .. kMaxSpan
   int through;     // 1: tmp_output stores with device-scope (sc1) policy
   float qk_scale;  // scale * log2(e) (times k_scale for an 8-bit cache)
@@ -230,10 +231,10 @@ __device__ __forceinline__ void merge_store(const PartitionArgs& a, const float*
   constexpr int D4 = D / 4;
   const int NC = G * M;
   const int per_col = ne * D4;
+  const size_t row0 = ((size_t)s * a.Mq + a.m0) * a.H + kh * G;  // the unit's first row
   // The unit's rows of tmp_output (query tokens x heads x P), 32-bit offsets.
   const __amdgpu_buffer_rsrc_t tmp = __builtin_amdgcn_make_buffer_rsrc(
-      a.tmp_out + ((size_t)s * M * a.H + kh * G) * a.P * D, (short)0,
-      ((M - 1) * a.H + G) * a.P * D * 4, kRsrcFlags);
+      a.tmp_out + row0 * a.P * D, (short)0, ((M - 1) * a.H + G) * a.P * D * 4, kRsrcFlags);
   for (int i = threadIdx.x; i < NC * per_col; i += kWaves * 64) {
     const int c = i / per_col, rem = i - c * per_col;
     const int j = rem / D4, d4 = rem - j * D4;
@@ -254,13 +255,13 @@ __device__ __forceinline__ void merge_store(const PartitionArgs& a, const float*
     }
     const float inv = a.v_scale / Z;
     const int hrow = m * a.H + g;  // row of this column relative to the unit's first
-    const size_t row = ((size_t)s * M * a.H + kh * G + hrow) * a.P + p0 + j;
+    const size_t row = (row0 + hrow) * a.P + p0 + j;
     store_row(tmp, (uint32_t)(((hrow * a.P + p0 + j) * D + 4 * d4) * 4), o * inv, a.through);
     if (d4 == 0) {
       float mx = Mx;
       if constexpr (AL) {  // the partition's share of the ALiBi bias (see PartitionArgs)
         const float slope2 = a.alibi[kh * G + g] * kLog2e;
-        mx += slope2 * (float)((p0 + j) * a.PS - (L - M + m));
+        mx += slope2 * (float)((p0 + j) * a.PS - (L - a.Mq + a.m0 + m));
       }
       a.exp_sums[row] = Z;
       a.max_logits[row] = mx * kLn2;
@@ -399,7 +400,8 @@ __device__ __forceinline__ bool unit_hoist(const PartitionArgs& a, int32_t* s_bt
     const int j = threadIdx.x / u.NC, c = threadIdx.x % u.NC;
     const int m = c / u.G, g = c - m * u.G;
     if ((u.p0 + j) * a.PS >= u.L) {
-      const size_t row = (((size_t)u.s * u.M + m) * a.H + u.kh * u.G + g) * a.P + u.p0 + j;
+      const size_t row =
+          (((size_t)u.s * a.Mq + a.m0 + m) * a.H + u.kh * u.G + g) * a.P + u.p0 + j;
       a.max_logits[row] = kNegInf;
       a.exp_sums[row] = 0.0f;
     }
@@ -501,10 +503,10 @@ partition_mfma_kernel(PartitionArgs a) {
   const int G = u.G, NC = u.NC;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane & 15, grp = lane >> 4;  // g: this lane's column (and token row in a tile)
-  // Column g < NC is query head kh*G + g%G of query token g/G, which sees
-  // tokens t < lim (the causal prefix; L for single-query decode).
+  // Column g < NC is query head kh*G + g%G of query token m0 + g/G, which
+  // sees tokens t < lim (the causal prefix; L for single-query decode).
   const int qtok = g < NC ? g / G : 0;
-  const int lim = min(u.L, max(0, u.L - u.M + qtok + 1));
+  const int lim = min(u.L, max(0, u.L - a.Mq + a.m0 + qtok + 1));
   // ALiBi slope of this lane's column, log2 units.
   const float slope2 = AL && g < NC ? a.alibi[u.kh * G + g - qtok * G] * kLog2e : 0.0f;
 
@@ -514,7 +516,7 @@ partition_mfma_kernel(PartitionArgs a) {
   {
     const uint16_t* qrow =
         (const uint16_t*)a.q +
-        (((size_t)u.s * u.M + qtok) * a.H + u.kh * G + (g < NC ? g - qtok * G : 0)) * D;
+        (((size_t)u.s * a.Mq + a.m0 + qtok) * a.H + u.kh * G + (g < NC ? g - qtok * G : 0)) * D;
 #pragma unroll
     for (int m = 0; m < KS; ++m) {
       const int d0 = KV8 ? 16 * (4 * (m / 2) + grp) + 8 * (m % 2) : 32 * m + 8 * grp;

@@ -143,7 +143,7 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
                     const void* key_cache, const void* value_cache, const int32_t* block_tables,
                     const int32_t* seq_lens, int32_t S, int32_t H, int32_t KH, int32_t D,
                     int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS, int32_t qdt,
-                    int32_t kvdt, int32_t M, const float* alibi, Plan* plan) {
+                    int32_t kvdt, int32_t M, int32_t Mc, const float* alibi, Plan* plan) {
   if (S < 0 || H < 0 || KH < 0 || D < 0 || BS < 0 || NB < 0 || MB < 0 || P < 0)
     return fail(PA_ERR_SHAPE, "negative size argument");
   if (M < 1) return fail(PA_ERR_SHAPE, "num_queries must be >= 1");
@@ -181,11 +181,11 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   partition_fn fn = nullptr;
   bool vec = false;
   if (M > 1) {
-    // several query tokens: the MFMA path, one column per (query token, head)
-    if (!is_16bit(qdt) || (long long)G * M > 16)
+    // several query tokens: the MFMA path, one column per (query token, head),
+    // at most 16 columns per launch (query_chunk)
+    if (!is_16bit(qdt) || G > 16)
       return fail(PA_ERR_UNSUPPORTED,
-                  "several query tokens need an f16/bf16 query and group * num_queries <= 16 "
-                  "(got %d x %d)", G, M);
+                  "several query tokens need an f16/bf16 query and group <= 16 (got group %d)", G);
     fn = kvdt == PA_FP8_E4M3 ? kMfma8[al][qdt - 1][di][bi] : kMfma[al][qdt - 1][di][bi];
   } else if (is_16bit(qdt) && G >= 4 && G <= 16) {
     fn = kvdt == PA_FP8_E4M3 ? kMfma8[al][qdt - 1][di][bi] : kMfma[al][qdt - 1][di][bi];
@@ -199,9 +199,9 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
       !aligned16(tmp_output))
     return fail(PA_ERR_ALIGN, "query, key_cache, value_cache and tmp_output must be 16-byte aligned");
-  if (((long long)(M - 1) * H + G) * P * D * 4 > 0x7fffffffLL)
+  if (((long long)(Mc - 1) * H + G) * P * D * 4 > 0x7fffffffLL)
     return fail(PA_ERR_UNSUPPORTED, "tmp_output rows of one (sequence, kv head) exceed 2 GiB");
-  const int NC = G * M;  // columns of a work unit
+  const int NC = G * Mc;  // columns of a work unit
   const int lds_limit = max_lds_per_block();
   const int lds1 = pa::lds_layout(PS, BS, NC, D, 1).total;
   if (lds1 > lds_limit)
@@ -224,12 +224,20 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   return PA_OK;
 }
 
+// Query tokens per partition launch: one MFMA column per (query token, head),
+// 16 columns; M tokens beyond that run as several launches over the same
+// pages (each reads K/V once).
+int query_chunk(int G, int M) {
+  const int per = G >= 1 && G <= 16 ? 16 / G : 1;  // (G > 16 is rejected by check_partition)
+  return M > 1 ? (per < M ? per : M) : 1;
+}
+
 int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float* max_logits,
                      const void* query, const void* key_cache, const void* value_cache,
                      const int32_t* block_tables, const int32_t* seq_lens, int32_t S, int32_t H,
                      int32_t KH, int32_t NB, int32_t MB, int32_t P, int32_t PS, float scale,
-                     float k_scale, float v_scale, int32_t M, const float* alibi,
-                     hipStream_t stream) {
+                     float k_scale, float v_scale, int32_t Mc, int32_t Mq, int32_t m0,
+                     const float* alibi, hipStream_t stream) {
   PartitionArgs a;
   a.tmp_out = tmp_output;
   a.exp_sums = exp_sums;
@@ -246,7 +254,9 @@ int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float
   a.P = P;
   a.PS = PS;
   a.NB = NB;
-  a.M = M;
+  a.M = Mc;
+  a.Mq = Mq;
+  a.m0 = m0;
   a.C = plan.span;
   a.through = P >= kThroughMinPartitions;
   a.qk_scale = scale * k_scale * pa::kLog2e;
@@ -312,6 +322,46 @@ int launch_reduce(reduce_fn fn, void* out, float* lse, const float* tmp_output,
 
 bool finite(float v) { return v == v && v - v == 0.0f; }
 
+// Plans for the query-token chunks of a phase-1 call: `full` for chunks of mc
+// tokens, `last` for a shorter final one (all validated before any launch).
+int plan_partitions(float* tmp_output, float* exp_sums, float* max_logits, const void* query,
+                    const void* key_cache, const void* value_cache, const int32_t* block_tables,
+                    const int32_t* seq_lens, int32_t S, int32_t H, int32_t KH, int32_t D,
+                    int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS, int32_t qdt,
+                    int32_t kvdt, int32_t M, const float* alibi, Plan* full, Plan* last,
+                    int* mc) {
+  const int G = KH > 0 && H >= KH ? H / KH : 1;  // (validated by check_partition)
+  *mc = M > 0 ? query_chunk(G, M) : 1;
+  int rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                           block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt, M,
+                           *mc, alibi, full);
+  if (rc != PA_OK || S == 0) return rc;
+  *last = *full;
+  if (M % *mc)
+    rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                         block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt, M,
+                         M % *mc, alibi, last);
+  return rc;
+}
+
+int launch_partitions(const Plan& full, const Plan& last, int mc, float* tmp_output,
+                      float* exp_sums, float* max_logits, const void* query,
+                      const void* key_cache, const void* value_cache,
+                      const int32_t* block_tables, const int32_t* seq_lens, int32_t S,
+                      int32_t H, int32_t KH, int32_t NB, int32_t MB, int32_t P, int32_t PS,
+                      float scale, float k_scale, float v_scale, int32_t M, const float* alibi,
+                      hipStream_t stream) {
+  for (int m0 = 0; m0 < M; m0 += mc) {
+    const int n = M - m0 < mc ? M - m0 : mc;
+    const int rc = launch_partition(n == mc ? full : last, tmp_output, exp_sums, max_logits,
+                                    query, key_cache, value_cache, block_tables, seq_lens, S, H,
+                                    KH, NB, MB, P, PS, scale, k_scale, v_scale, n, M, m0, alibi,
+                                    stream);
+    if (rc != PA_OK) return rc;
+  }
+  return PA_OK;
+}
+
 int partition_entry(float* tmp_output, float* exp_sums, float* max_logits, const void* query,
                     const void* key_cache, const void* value_cache, const int32_t* block_tables,
                     const int32_t* seq_lens, int32_t S, int32_t M, int32_t H, int32_t KH,
@@ -321,14 +371,15 @@ int partition_entry(float* tmp_output, float* exp_sums, float* max_logits, const
   g_err[0] = 0;
   if (!finite(k_scale) || !finite(v_scale))
     return fail(PA_ERR_SHAPE, "k_scale and v_scale must be finite");
-  Plan plan;
-  int rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
-                           block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt,
-                           M, alibi, &plan);
+  Plan full, last;
+  int mc = 1;
+  int rc = plan_partitions(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                           block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt, M,
+                           alibi, &full, &last, &mc);
   if (rc != PA_OK || S == 0) return rc;
-  return launch_partition(plan, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
-                          block_tables, seq_lens, S, H, KH, NB, MB, P, PS, scale, k_scale,
-                          v_scale, M, alibi, (hipStream_t)stream);
+  return launch_partitions(full, last, mc, tmp_output, exp_sums, max_logits, query, key_cache,
+                           value_cache, block_tables, seq_lens, S, H, KH, NB, MB, P, PS, scale,
+                           k_scale, v_scale, M, alibi, (hipStream_t)stream);
 }
 
 int decode_entry(void* out, float* lse, float* tmp_output, float* exp_sums, float* max_logits,
@@ -341,10 +392,11 @@ int decode_entry(void* out, float* lse, float* tmp_output, float* exp_sums, floa
   if (!finite(k_scale) || !finite(v_scale))
     return fail(PA_ERR_SHAPE, "k_scale and v_scale must be finite");
   if (S > 0 && lse && !aligned4(lse)) return fail(PA_ERR_ALIGN, "lse must be 4-byte aligned");
-  Plan plan;
-  int rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
-                           block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt,
-                           M, alibi, &plan);
+  Plan full, last;
+  int mc = 1;
+  int rc = plan_partitions(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                           block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt, M,
+                           alibi, &full, &last, &mc);
   if (rc != PA_OK || S == 0) return rc;
   if (out_dtype != PA_F32 && out_dtype != qdt)
     return fail(PA_ERR_UNSUPPORTED, "out dtype must be PA_F32 or the query dtype");
@@ -352,9 +404,9 @@ int decode_entry(void* out, float* lse, float* tmp_output, float* exp_sums, floa
   rc = check_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, S, M, H, D, P, PS,
                     out_dtype, &fn);
   if (rc != PA_OK) return rc;
-  rc = launch_partition(plan, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
-                        block_tables, seq_lens, S, H, KH, NB, MB, P, PS, scale, k_scale, v_scale,
-                        M, alibi, (hipStream_t)stream);
+  rc = launch_partitions(full, last, mc, tmp_output, exp_sums, max_logits, query, key_cache,
+                         value_cache, block_tables, seq_lens, S, H, KH, NB, MB, P, PS, scale,
+                         k_scale, v_scale, M, alibi, (hipStream_t)stream);
   if (rc != PA_OK) return rc;
   return launch_reduce(fn, out, lse, tmp_output, exp_sums, max_logits, seq_lens, S, M, H, D, P,
                        PS, (hipStream_t)stream);

@@ -165,7 +165,7 @@ def part_mq(M=2, q_dtype=binding.PA_BF16, kv_dtype=binding.PA_BF16, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(M=0), binding.PA_ERR_SHAPE),
-    (dict(M=5), binding.PA_ERR_UNSUPPORTED),                   # G=4 x 5 > 16 columns
+    (dict(M=2, H=64, KH=2), binding.PA_ERR_UNSUPPORTED),       # group 32 > 16 columns
     (dict(q_dtype=binding.PA_F32, kv_dtype=binding.PA_F32), binding.PA_ERR_UNSUPPORTED),
     (dict(q_dtype=binding.PA_F16, kv_dtype=binding.PA_BF16), binding.PA_ERR_UNSUPPORTED),
 ])
@@ -248,7 +248,8 @@ def test_decode_lse_rejects():
         binding.PA_F32, None)
     assert lib.paged_attn_decode_lse(*args(None)) == binding.PA_ERR_NULL
     assert lib.paged_attn_decode_lse(*args(FAKE + 1)) == binding.PA_ERR_ALIGN
-    assert lib.paged_attn_decode_lse(*args(FAKE, M=5)) == binding.PA_ERR_UNSUPPORTED
+    assert lib.paged_attn_decode_lse(*args(FAKE, M=2, qdt=binding.PA_F32, kvdt=binding.PA_F32)) \
+        == binding.PA_ERR_UNSUPPORTED  # several query tokens need a 16-bit query
     assert lib.paged_attn_decode_lse(*args(FAKE, qdt=binding.PA_F32)) == binding.PA_ERR_UNSUPPORTED
 
 
@@ -289,5 +290,6 @@ def test_ex_entries_reject_misaligned_alibi_and_lse():
                                 binding.PA_F32, None)
     assert lib.paged_attn_decode_ex(*dec_args(FAKE + 1, None)) == binding.PA_ERR_ALIGN
     assert lib.paged_attn_decode_ex(*dec_args(None, FAKE + 1)) == binding.PA_ERR_ALIGN
-    assert lib.paged_attn_decode_ex(*dec_args(None, None)[:10], 2, 5, *dec_args(None, None)[12:]) \
-        == binding.PA_ERR_UNSUPPORTED  # G=4 x M=5 > 16 columns
+    assert lib.paged_attn_decode_ex(*dec_args(None, None)[:10], 2, 2, 64, 2,
+                                    *dec_args(None, None)[14:]) \
+        == binding.PA_ERR_UNSUPPORTED  # two query tokens, group 32 > 16

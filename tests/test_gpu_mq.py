@@ -3,9 +3,10 @@
 Every output row and every partition intermediate is compared with the
 oracle's multi-token mode (which is pinned to the single-query oracle on each
 row's causal prefix): several (group, M) mixes that fill one MFMA column tile
-(G * M <= 16), 8-bit caches, lengths shorter than M, equal to M and at block /
-partition edges, the two-call and one-call forms, and M = 1 against the
-single-query entry points bit for bit.
+(G * M <= 16) and wider windows that run in several passes, 8-bit caches,
+lengths shorter than M, equal to M and at block / partition edges, the
+two-call and one-call forms, and M = 1 against the single-query entry points
+bit for bit.
 """
 import math
 
@@ -81,6 +82,11 @@ CASES = [
     ("f16", 16, 2, 256, 16, 128, 2),    # G=8 x M=2, D=256
     ("fp8", 32, 8, 128, 16, 64, 4),     # 8-bit cache, G=4 x M=4
     ("fp8", 8, 4, 256, 32, 64, 5),      # 8-bit cache, G=2 x M=5, D=256, BS=32
+    # more than 16 columns: the tokens run in several passes over the pages
+    ("bf16", 64, 8, 128, 16, 64, 4),    # G=8 x M=4: two passes of 2 tokens
+    ("f16", 32, 8, 128, 16, 64, 7),     # G=4 x M=7: passes of 4 and 3 tokens
+    ("bf16", 16, 1, 64, 32, 64, 3),     # G=16 x M=3: three passes of 1 token
+    ("fp8", 32, 8, 128, 16, 64, 6),     # 8-bit cache, G=4 x M=6: passes of 4 and 2
 ]
 
 
@@ -134,8 +140,8 @@ def test_one_query_token_matches_single_query_calls(name):
         U.assert_close("M=1 vs vector path", res["out"][:, 0], single["out"].double().numpy())
 
 
-def test_multi_token_rejects_wide_columns():
-    cfg = mq_geom("bf16", 32, 4, 128, 16, 64, 3, [10, 20])   # G=8 x M=3 = 24 columns
+def test_multi_token_rejects_group_over_16():
+    cfg = mq_geom("bf16", 64, 2, 128, 16, 64, 2, [10, 20])   # G=32: no MFMA column layout
     d = U.to_device(W.make_inputs(cfg, seed=1, lens=[10, 20]))
     with pytest.raises(RuntimeError):
         run_mq(d, 64, 1)

@@ -42,9 +42,8 @@ def draw(i):
         M = 1
     else:
         G = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
-        M = 1 if rng.random() < 0.6 else int(rng.integers(2, max(3, 16 // G + 1)))
-        if G * M > 16:
-            M = 1
+        # up to 16 columns per pass; wider windows run in several passes
+        M = 1 if rng.random() < 0.6 else int(rng.integers(2, max(3, 16 // G + 1) + 3))
     S = int(rng.integers(1, 7))
     P = int(rng.integers(1, 6))
     lens = rng.integers(0, P * PS + 1, size=S)
