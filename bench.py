@@ -315,7 +315,7 @@ def run(args) -> dict:
     gbs = kvb / step_s / 1e9
     achieved = kvb / part_avg_s / 1e9
     kernel = ("partition_mfma_kernel"
-              if (cfg.query_dtype != "f32" and (4 <= cfg.group <= 16 or MQ > 1))
+              if (cfg.query_dtype != "f32" and (cfg.group >= 4 or MQ > 1))
               else "partition_vec_kernel")
     traffic, traffic_src = committed_traffic(args.workload, kernel)
     res = {
@@ -373,8 +373,9 @@ def run(args) -> dict:
     }
     res["merge_states"] = merge_bench(pa, torch, dev, stream, S * MQ * H, D,
                                       W.DTYPES[cfg.query_dtype], K)
-    res["flushed"] = flushed_calls(torch, dev, stream, partition, reduce, tmp, es, ml, PS, kvb,
-                                   args.flushed_calls)
+    if args.flushed_calls > 0:
+        res["flushed"] = flushed_calls(torch, dev, stream, partition, reduce, tmp, es, ml, PS,
+                                       kvb, args.flushed_calls)
     res["copy_context"] = copy_bandwidth(torch, dev, stream)
     if args.calibrate_copy:
         n = 1 << 28  # 1 GiB of fp32: FETCH_SIZE / WRITE_SIZE calibration for the counters

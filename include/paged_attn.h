@@ -61,8 +61,8 @@ enum {
   PA_ERR_NULL = -1,        /* a required pointer is NULL                              */
   PA_ERR_SHAPE = -2,       /* negative size, H % KH, D % x, PS <= 0 or PS % BS, P < 1,
                               MB < 1, B < 1                                            */
-  PA_ERR_UNSUPPORTED = -3, /* D not in {64,128,256}, BS not in {16,32}, G outside the
-                              built range, PS / BS > 256, unknown dtype, or out_dtype
+  PA_ERR_UNSUPPORTED = -3, /* D not in {64,128,256}, BS not in {16,32}, G > 4 with
+                              fp32 data, PS / BS > 256, unknown dtype, or out_dtype
                               neither PA_F32 nor kv_dtype                              */
   PA_ERR_ALIGN = -4,       /* a pointer lacks its alignment (16 bytes; lse arrays 4)  */
   PA_ERR_HIP = -5          /* the HIP runtime rejected a launch                        */
@@ -89,7 +89,9 @@ enum {
  *   seq_lens     [S]     int32
  *   scale        multiplies q.k (applied after the dot product)
  *   kv_dtype     PA_F32, PA_F16 or PA_BF16
- * num_seqs == 0 is a successful no-op.
+ * num_seqs == 0 is a successful no-op. Any G with 16-bit data; G <= 4 with
+ * fp32. (With G > 32, or G > 16 at D = 256, the heads of a kv head are
+ * computed in several launches over the same pages, each reading them again.)
  */
 PA_API int paged_attn_v2_partition(float* tmp_output, float* exp_sums, float* max_logits,
                                    const void* query, const void* key_cache, const void* value_cache,
@@ -191,11 +193,11 @@ PA_API int paged_attn_decode_fp8(void* out, float* tmp_output, float* exp_sums,
  *   out          [S, M, H, D]        out_dtype PA_F32 or q_dtype
  *
  * A row's partitions past its causal prefix get the sentinels (max -inf, sum
- * 0; tmp_output unspecified). Requires H / KH <= 16 (PA_ERR_UNSUPPORTED
- * otherwise). Phase 1 computes one MFMA column per (query token, head) of a
- * kv head, 16 columns per pass over the pages: when (H / KH) * M > 16 the
- * tokens run in consecutive passes of 16 / (H / KH) tokens, each reading the
- * K/V pages again (results are the same as in one pass).
+ * 0; tmp_output unspecified). Phase 1 computes one MFMA column per (query
+ * token, head) of a kv head, up to 32 columns per pass over the pages (16 at
+ * D = 256): when (H / KH) * M is larger, consecutive passes take the next
+ * columns (token-major), each reading the K/V pages again (results are the
+ * same as in one pass).
  * num_queries = 1 computes exactly what the single-query calls compute.
  */
 PA_API int paged_attn_v2_partition_mq(float* tmp_output, float* exp_sums, float* max_logits,

@@ -157,8 +157,11 @@ struct PartitionArgs {
   const int32_t* sl;
   int S, H, KH, MB, P, PS;
   int NB;          // physical blocks; block-table entries are clamped into [0, NB)
-  int M;           // query tokens of this launch: m0 .. m0 + M - 1 (1: single-query decode)
-  int Mq, m0;      // query tokens per sequence in the tensors (query [S, Mq, H, D]), first one here
+  // Columns: a unit's Mq * G (query token m, query head kh*G + h) pairs, column
+  // m*G + h; one launch covers columns c0 .. c0 + NC - 1 (NC = G, c0 = 0 for
+  // single-query decode).
+  int Mq;          // query tokens per sequence in the tensors (query [S, Mq, H, D])
+  int NC, c0;      // columns of this launch, first one
   int C;           // consecutive partitions per workgroup (span), 1 .. kMaxSpan
   int through;     // 1: tmp_output stores with device-scope (sc1) policy
   float qk_scale;  // scale * log2(e) (times k_scale for an 8-bit cache)
@@ -218,27 +221,28 @@ __device__ __forceinline__ int slot(int j, int w, int c, int NC) { return (j * k
 
 // Merge the NW parked states of each of the span's ne used partitions
 // (log2-domain max m, sum l, unnormalised accumulator) and store the
-// normalised outputs. A unit's columns are c = m*G + g: query token m
-// (of M) and query head kh*G + g; its output rows are ((s*M + m)*H + kh*G + g)
-// of the [S*M*H, P] statistics and [S*M*H, P, D] tmp_output. Threads walk
-// (column, partition, d) in memory order, so the rows of adjacent partitions
-// of one head are written together. A column whose causal prefix ends before
-// a used partition merges to max -inf, sum 0 (the empty-partition sentinels).
+// normalised outputs. Local column c of the launch is column a.c0 + c = m*G + h
+// of the unit: query token m (of Mq) and query head kh*G + h; its output rows
+// are ((s*Mq + m)*H + kh*G + h) of the [S*Mq*H, P] statistics and
+// [S*Mq*H, P, D] tmp_output. Threads walk (column, partition, d) in memory
+// order, so the rows of adjacent partitions of one head are written together.
+// A column whose causal prefix ends before a used partition merges to max
+// -inf, sum 0 (the empty-partition sentinels).
 template <int D, bool AL>
 __device__ __forceinline__ void merge_store(const PartitionArgs& a, const float* s_m,
                                             const float* s_l, const float* s_acc, int s, int kh,
-                                            int p0, int ne, int G, int M, int L) {
+                                            int p0, int ne, int G, int NC, int L) {
   constexpr int D4 = D / 4;
-  const int NC = G * M;
   const int per_col = ne * D4;
-  const size_t row0 = ((size_t)s * a.Mq + a.m0) * a.H + kh * G;  // the unit's first row
-  // The unit's rows of tmp_output (query tokens x heads x P), 32-bit offsets.
+  const int mf = a.c0 / G, ml = (a.c0 + NC - 1) / G;  // first and last query token here
+  const size_t row0 = ((size_t)s * a.Mq + mf) * a.H + kh * G;  // row of (mf, head kh*G)
+  // The launch's rows of tmp_output (query tokens mf..ml x heads x P), 32-bit offsets.
   const __amdgpu_buffer_rsrc_t tmp = __builtin_amdgcn_make_buffer_rsrc(
-      a.tmp_out + row0 * a.P * D, (short)0, ((M - 1) * a.H + G) * a.P * D * 4, kRsrcFlags);
+      a.tmp_out + row0 * a.P * D, (short)0, ((ml - mf) * a.H + G) * a.P * D * 4, kRsrcFlags);
   for (int i = threadIdx.x; i < NC * per_col; i += kWaves * 64) {
     const int c = i / per_col, rem = i - c * per_col;
     const int j = rem / D4, d4 = rem - j * D4;
-    const int m = c / G, g = c - m * G;
+    const int m = (a.c0 + c) / G, h = a.c0 + c - m * G;
     float Mx = kNegInf;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[slot(j, w, c, NC)]);
@@ -254,14 +258,14 @@ __device__ __forceinline__ void merge_store(const PartitionArgs& a, const float*
       o += e * v;
     }
     const float inv = a.v_scale / Z;
-    const int hrow = m * a.H + g;  // row of this column relative to the unit's first
+    const int hrow = (m - mf) * a.H + h;  // row of this column relative to row0
     const size_t row = (row0 + hrow) * a.P + p0 + j;
     store_row(tmp, (uint32_t)(((hrow * a.P + p0 + j) * D + 4 * d4) * 4), o * inv, a.through);
     if (d4 == 0) {
       float mx = Mx;
       if constexpr (AL) {  // the partition's share of the ALiBi bias (see PartitionArgs)
-        const float slope2 = a.alibi[kh * G + g] * kLog2e;
-        mx += slope2 * (float)((p0 + j) * a.PS - (L - a.Mq + a.m0 + m));
+        const float slope2 = a.alibi[kh * G + h] * kLog2e;
+        mx += slope2 * (float)((p0 + j) * a.PS - (L - a.Mq + m));
       }
       a.exp_sums[row] = Z;
       a.max_logits[row] = mx * kLn2;
@@ -272,7 +276,7 @@ __device__ __forceinline__ void merge_store(const PartitionArgs& a, const float*
 // A work unit: sequence s, kv head kh, partitions p0 .. p0+nparts-1.
 struct Unit {
   int s, kh, p0, nparts, G, L, pg0;
-  int M, NC;       // query tokens per sequence; columns G * M
+  int NC;          // columns of this launch
   int npages;      // used pages of the span (contiguous from its first page)
   int ne;          // used partitions of the span
   int32_t bt_val;  // this thread's entry of the span's block-table slice
@@ -382,8 +386,7 @@ __device__ __forceinline__ void unit_begin(const PartitionArgs& a, Unit& u, uint
   u.p0 = (pair / a.S) * a.C;
   u.nparts = min(a.C, a.P - u.p0);
   u.G = a.H / a.KH;
-  u.M = a.M;
-  u.NC = u.G * a.M;
+  u.NC = a.NC;
   const int pps = a.PS / BS;
   u.pg0 = u.p0 * pps;
   const int nspec = min(u.nparts * pps, a.MB - u.pg0);
@@ -397,11 +400,11 @@ __device__ __forceinline__ void unit_begin(const PartitionArgs& a, Unit& u, uint
 template <int BS>
 __device__ __forceinline__ bool unit_hoist(const PartitionArgs& a, int32_t* s_bt, Unit& u) {
   if ((int)threadIdx.x < u.nparts * u.NC) {
-    const int j = threadIdx.x / u.NC, c = threadIdx.x % u.NC;
-    const int m = c / u.G, g = c - m * u.G;
+    const int j = threadIdx.x / u.NC, c = a.c0 + threadIdx.x % u.NC;
+    const int m = c / u.G, h = c - m * u.G;
     if ((u.p0 + j) * a.PS >= u.L) {
       const size_t row =
-          (((size_t)u.s * a.Mq + a.m0 + m) * a.H + u.kh * u.G + g) * a.P + u.p0 + j;
+          (((size_t)u.s * a.Mq + m) * a.H + u.kh * u.G + h) * a.P + u.p0 + j;
       a.max_logits[row] = kNegInf;
       a.exp_sums[row] = 0.0f;
     }
@@ -417,11 +420,13 @@ __device__ __forceinline__ bool unit_hoist(const PartitionArgs& a, int32_t* s_bt
 }
 
 // =====================================================================
-// MFMA path: 16-bit query, G in [4, 16] query heads per kv head; the cache is
-// 16-bit (KV8 = false) or OCP E4M3 bytes converted to the query's type in
-// registers (KV8 = true).
-// QK^T per 16-token sub-tile: D/32 MFMA 16x16x32, token rows x head columns
-// (heads >= G are zero-padded). The fp32 C tile (lane l: tokens 4*(l/16)+r,
+// MFMA path: 16-bit query, columns (query token, query head) of a kv head in
+// CT tiles of 16 (a launch covers up to 16*CT of them); the cache is 16-bit
+// (KV8 = false) or OCP E4M3 bytes converted to the query's type in registers
+// (KV8 = true). The column tiles share every K and V operand: CT = 2 reads the
+// pages once for up to 32 columns.
+// QK^T per 16-token sub-tile and column tile: D/32 MFMA 16x16x32, token rows x
+// columns (columns past the launch's are zero-padded). The fp32 C tile (lane l: tokens 4*(l/16)+r,
 // head l%16) is exactly the B operand layout of a 16x16x16 MFMA with tokens as
 // k, so P feeds PV without any data movement. V is read as 4 tokens of one d
 // (8 bytes, or 4 bytes for an 8-bit cache) that form the matching A operand.
@@ -480,11 +485,17 @@ constexpr int prefetch_fp8(int page_regs) { return page_regs <= 16 ? PA_PREFETCH
 constexpr int fp8_waves(int D, int BS, bool AL) {
   return D * BS <= 2048 && !AL ? 4 : D <= 128 ? 3 : 2;
 }
+// Register budget (wavefronts per SIMD) of the MFMA kernel: two column tiles
+// hold two accumulators and two query operands, which only fit at 2.
+constexpr int mfma_waves(int D, int BS, bool KV8, bool AL, int CT) {
+  return CT > 1 ? 2 : KV8 ? fp8_waves(D, BS, AL) : (PA_MIN_WAVES > 0 ? PA_MIN_WAVES : 1);
+}
 
-template <int DT, int D, int BS, bool KV8, bool AL>
+template <int DT, int D, int BS, bool KV8, bool AL, int CT>
 __global__ void __launch_bounds__(kWaves * 64)
-__attribute__((amdgpu_waves_per_eu(KV8 ? fp8_waves(D, BS, AL) : (PA_MIN_WAVES > 0 ? PA_MIN_WAVES : 1))))
+__attribute__((amdgpu_waves_per_eu(mfma_waves(D, BS, KV8, AL, CT))))
 partition_mfma_kernel(PartitionArgs a) {
+  static_assert(CT == 1 || CT == 2, "one or two column tiles");
   constexpr int SUB = BS / 16;  // 16-token sub-tiles per page
   constexpr int KS = D / 32;    // QK k-steps (32 d each) per sub-tile
   constexpr int KL = KV8 ? D / 64 : D / 32;  // K 16-byte loads per lane per sub-tile
@@ -502,26 +513,31 @@ partition_mfma_kernel(PartitionArgs a) {
   unit_begin<BS>(a, u, smem);
   const int G = u.G, NC = u.NC;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane & 15, grp = lane >> 4;  // g: this lane's column (and token row in a tile)
-  // Column g < NC is query head kh*G + g%G of query token m0 + g/G, which
-  // sees tokens t < lim (the causal prefix; L for single-query decode).
-  const int qtok = g < NC ? g / G : 0;
-  const int lim = min(u.L, max(0, u.L - a.Mq + a.m0 + qtok + 1));
-  // ALiBi slope of this lane's column, log2 units.
-  const float slope2 = AL && g < NC ? a.alibi[u.kh * G + g - qtok * G] * kLog2e : 0.0f;
-
-  // Q columns as the QK B operand, k-step m: lane holds 8 consecutive d of its
-  // column, d = 32m + 8*grp (16-bit cache) or 16*(4*(m/2) + grp) + 8*(m%2) (8-bit).
-  u32x4 qb[KS];
-  {
-    const uint16_t* qrow =
-        (const uint16_t*)a.q +
-        (((size_t)u.s * a.Mq + a.m0 + qtok) * a.H + u.kh * G + (g < NC ? g - qtok * G : 0)) * D;
+  const int g = lane & 15, grp = lane >> 4;  // g: this lane's column in a tile (and token row)
+  // Column 16t + g of the launch (tile t) is column a.c0 + 16t + g = qm*G + h
+  // of the unit: query head kh*G + h of query token qm, which sees tokens
+  // t < lim (the causal prefix; L for single-query decode). Padding columns
+  // (>= NC) take the launch's first column with a zero query, so their
+  // running max stays put like a live column's.
+  int lim[CT];
+  float slope2[CT];  // ALiBi slope of the column, log2 units
+  u32x4 qb[CT][KS];  // Q columns as the QK B operand
 #pragma unroll
-    for (int m = 0; m < KS; ++m) {
-      const int d0 = KV8 ? 16 * (4 * (m / 2) + grp) + 8 * (m % 2) : 32 * m + 8 * grp;
+  for (int t = 0; t < CT; ++t) {
+    const bool live = 16 * t + g < NC;
+    const int c = a.c0 + (live ? 16 * t + g : 0);
+    const int qm = c / G, h = c - qm * G;
+    lim[t] = min(u.L, max(0, u.L - a.Mq + qm + 1));
+    slope2[t] = AL && live ? a.alibi[u.kh * G + h] * kLog2e : 0.0f;
+    // k-step mk: lane holds 8 consecutive d of its column, d = 32mk + 8*grp
+    // (16-bit cache) or 16*(4*(mk/2) + grp) + 8*(mk%2) (8-bit).
+    const uint16_t* qrow =
+        (const uint16_t*)a.q + (((size_t)u.s * a.Mq + qm) * a.H + u.kh * G + h) * D;
+#pragma unroll
+    for (int mk = 0; mk < KS; ++mk) {
+      const int d0 = KV8 ? 16 * (4 * (mk / 2) + grp) + 8 * (mk % 2) : 32 * mk + 8 * grp;
       u32x4 v = *(const u32x4*)(qrow + d0);
-      qb[m] = g < NC ? v : u32x4{0u, 0u, 0u, 0u};
+      qb[t][mk] = live ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
   if (!unit_hoist<BS>(a, (int32_t*)smem, u)) return;
@@ -544,34 +560,42 @@ partition_mfma_kernel(PartitionArgs a) {
 
   const int npg = u.npages > wave ? (u.npages - wave + kWaves - 1) / kWaves : 0;
 
-  float m = kNegInf;  // running max (log2 domain), uniform over a head column
-  float lsum = 0.0f;  // this lane's share of the running exp sum
-  f32x4 acc[VB];
+  float m[CT];     // running max (log2 domain), uniform over a column
+  float lsum[CT];  // this lane's share of the running exp sum
+  f32x4 acc[CT][VB];
 #pragma unroll
-  for (int i = 0; i < VB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < CT; ++t) {
+    m[t] = kNegInf;
+    lsum[t] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VB; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // Park this wavefront's state of partition jcur of the span in LDS and
   // start the next partition empty (wavefront-uniform control flow).
   int jcur = 0, next_edge = pps;  // next_edge: first page of partition jcur + 1
   auto park = [&]() {
-    const float ls = rows_sum(lsum);
-    if (g < NC) {
-      const int k = slot(jcur, wave, g, NC);
-      if (grp == 0) {
-        s_m[k] = m;
-        s_l[k] = ls;
-      }
-      float* dst = s_acc + k * D + 4 * grp;
 #pragma unroll
-      for (int mb = 0; mb < VB; ++mb) {
+    for (int t = 0; t < CT; ++t) {
+      const float ls = rows_sum(lsum[t]);
+      if (16 * t + g < NC) {
+        const int k = slot(jcur, wave, 16 * t + g, NC);
+        if (grp == 0) {
+          s_m[k] = m[t];
+          s_l[k] = ls;
+        }
+        float* dst = s_acc + k * D + 4 * grp;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[16 * mb + r] = acc[mb][r];
+        for (int mb = 0; mb < VB; ++mb) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[16 * mb + r] = acc[t][mb][r];
+        }
       }
+      m[t] = kNegInf;
+      lsum[t] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < VB; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    m = kNegInf;
-    lsum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < VB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     ++jcur;
     next_edge += pps;
   };
@@ -625,52 +649,66 @@ partition_mfma_kernel(PartitionArgs a) {
     const int page = wave + i * kWaves;  // page of the span
     while (page >= next_edge) park();
     const int tok0 = (u.pg0 + page) * BS;  // first token of the page
-    float s2[SUB][4];
+    float s2[CT][SUB][4];
 #pragma unroll
     for (int st = 0; st < SUB; ++st) {
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 sc[CT];
 #pragma unroll
-      for (int mk = 0; mk < KS; ++mk) sc = M::qk(k_operand(pg, st, mk), qb[mk], sc);
-      const int nvalid = lim - (tok0 + 16 * st + 4 * grp);  // row 4*grp+r valid iff r < nvalid
-      if constexpr (AL) {  // position relative to the page's partition start
-        const float base = slope2 * (float)(tok0 + 16 * st + 4 * grp - (u.p0 + jcur) * a.PS);
+      for (int t = 0; t < CT; ++t) sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          s2[st][r] = r < nvalid ? fmaf(sc[r], a.qk_scale, fmaf(slope2, (float)r, base)) : kNegInf;
-      } else {
+      for (int mk = 0; mk < KS; ++mk) {
+        const u32x4 ko = k_operand(pg, st, mk);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s2[st][r] = r < nvalid ? sc[r] * a.qk_scale : kNegInf;
+        for (int t = 0; t < CT; ++t) sc[t] = M::qk(ko, qb[t][mk], sc[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < CT; ++t) {
+        const int nvalid = lim[t] - (tok0 + 16 * st + 4 * grp);  // row 4*grp+r valid iff r < nvalid
+        if constexpr (AL) {  // position relative to the page's partition start
+          const float base =
+              slope2[t] * (float)(tok0 + 16 * st + 4 * grp - (u.p0 + jcur) * a.PS);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            s2[t][st][r] = r < nvalid ? fmaf(sc[t][r], a.qk_scale, fmaf(slope2[t], (float)r, base))
+                                      : kNegInf;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s2[t][st][r] = r < nvalid ? sc[t][r] * a.qk_scale : kNegInf;
+        }
       }
     }
-    float mt = kNegInf;
+    u32x2 phi[CT][SUB], plo[CT][SUB];
 #pragma unroll
-    for (int st = 0; st < SUB; ++st)
-      mt = fmaxf(mt, fmaxf(fmaxf(s2[st][0], s2[st][1]), fmaxf(s2[st][2], s2[st][3])));
-    mt = rows_max(mt);
-    const float mn = fmaxf(m, mt);
-    const float mu = mn == kNegInf ? 0.0f : mn;
-    const float alpha = fast_exp2(m - mu);
-    m = mn;
-    u32x2 phi[SUB], plo[SUB];
-    float psum = 0.0f;
+    for (int t = 0; t < CT; ++t) {
+      float mt = kNegInf;
 #pragma unroll
-    for (int st = 0; st < SUB; ++st) {
-      float pr[4];
+      for (int st = 0; st < SUB; ++st)
+        mt = fmaxf(mt, fmaxf(fmaxf(s2[t][st][0], s2[t][st][1]), fmaxf(s2[t][st][2], s2[t][st][3])));
+      mt = rows_max(mt);
+      const float mn = fmaxf(m[t], mt);
+      const float mu = mn == kNegInf ? 0.0f : mn;
+      const float alpha = fast_exp2(m[t] - mu);
+      m[t] = mn;
+      float psum = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(s2[st][r] - mu);
-      psum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-      const uint32_t h01 = C::pack(pr[0], pr[1]), h23 = C::pack(pr[2], pr[3]);
-      phi[st] = u32x2{h01, h23};
-      plo[st] = u32x2{C::pack(pr[0] - C::lo(h01), pr[1] - C::hi(h01)),
-                      C::pack(pr[2] - C::lo(h23), pr[3] - C::hi(h23))};
-    }
-    lsum = lsum * alpha + psum;
-    // Rescale the accumulator only if some head's running max moved: alpha is
-    // exactly 1 otherwise, so skipping is bit-identical and saves 4*VB
-    // multiplies on most pages.
-    if (any_lane(alpha != 1.0f)) {
+      for (int st = 0; st < SUB; ++st) {
+        float pr[4];
 #pragma unroll
-      for (int mb = 0; mb < VB; ++mb) acc[mb] *= alpha;
+        for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(s2[t][st][r] - mu);
+        psum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        const uint32_t h01 = C::pack(pr[0], pr[1]), h23 = C::pack(pr[2], pr[3]);
+        phi[t][st] = u32x2{h01, h23};
+        plo[t][st] = u32x2{C::pack(pr[0] - C::lo(h01), pr[1] - C::hi(h01)),
+                           C::pack(pr[2] - C::lo(h23), pr[3] - C::hi(h23))};
+      }
+      lsum[t] = lsum[t] * alpha + psum;
+      // Rescale the accumulator only if some column's running max moved: alpha
+      // is exactly 1 otherwise, so skipping is bit-identical and saves 4*VB
+      // multiplies on most pages.
+      if (any_lane(alpha != 1.0f)) {
+#pragma unroll
+        for (int mb = 0; mb < VB; ++mb) acc[t][mb] *= alpha;
+      }
     }
     // V tail slots past the sequence end are zeroed (selected, never multiplied
     // by a zero weight: they may hold NaN). Only the last page of a sequence is
@@ -709,8 +747,11 @@ partition_mfma_kernel(PartitionArgs a) {
 #pragma unroll
       for (int st = 0; st < SUB; ++st) {
         const u32x2 v = v_operand(vw[st][mb]);
-        acc[mb] = M::pv(v, phi[st], acc[mb]);
-        acc[mb] = M::pv(v, plo[st], acc[mb]);
+#pragma unroll
+        for (int t = 0; t < CT; ++t) {
+          acc[t][mb] = M::pv(v, phi[t][st], acc[t][mb]);
+          acc[t][mb] = M::pv(v, plo[t][st], acc[t][mb]);
+        }
       }
     }
   };
@@ -719,7 +760,7 @@ partition_mfma_kernel(PartitionArgs a) {
   pipeline<PF>(npg, ring, fetch, process);
   while (jcur < u.ne) park();
   __syncthreads();
-  merge_store<D, AL>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G, u.M, u.L);
+  merge_store<D, AL>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G, NC, u.L);
 }
 
 // =====================================================================
@@ -964,7 +1005,7 @@ partition_vec_kernel(PartitionArgs a) {
   pipeline<PF>(npg, ring, fetch, process);
   while (jcur < u.ne) park();
   __syncthreads();
-  merge_store<D, AL>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G, 1, u.L);
+  merge_store<D, AL>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G, G, u.L);
 }
 
 // =====================================================================

@@ -7,6 +7,7 @@
 // reduce kernel, launched back to back on one stream by its host launcher.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -46,9 +47,11 @@ int bs_index(int BS) { return BS == 16 ? 0 : BS == 32 ? 1 : -1; }
 
 // ---------------------------------------------------------------- kernel tables
 // Partition kernels: the tables of pa_tables.h, defined in the instantiation
-// units; [ALiBi off / on] here.
-const pa::partition_fn (*const kMfma[2])[3][2] = {pa::kMfma_al0, pa::kMfma_al1};
-const pa::partition_fn (*const kMfma8[2])[3][2] = {pa::kMfma8_al0, pa::kMfma8_al1};
+// units; [ALiBi off / on] here, and for the MFMA kernels [column tiles 1 / 2].
+const pa::partition_fn (*const kMfma[2][2])[3][2] = {{pa::kMfma_al0, pa::kMfmaW_al0},
+                                                     {pa::kMfma_al1, pa::kMfmaW_al1}};
+const pa::partition_fn (*const kMfma8[2][2])[3][2] = {{pa::kMfma8_al0, pa::kMfma8W_al0},
+                                                      {pa::kMfma8_al1, pa::kMfma8W_al1}};
 const pa::partition_fn (*const kVec[2])[3][2][3] = {pa::kVec_al0, pa::kVec_al1};
 const pa::partition_fn (*const kVec8[2])[3][2][3] = {pa::kVec8_al0, pa::kVec8_al1};
 
@@ -137,13 +140,29 @@ int pick_span(int S, int KH, int P, int PS, int BS, int NC, int D, int esz, int 
   return best;
 }
 
-// Host checks shared by the partition entry points; fills `plan`. The query
-// has dtype qdt; the caches kvdt (== qdt, or PA_FP8_E4M3 with a 16-bit query).
+// Columns per partition launch. A (sequence, kv head) unit has M*G columns
+// (query token, query head); the MFMA kernel takes up to 16 per column tile
+// and one or two tiles (two for head sizes up to 128, where both tiles'
+// accumulators fit the register budget), so wider units run as several
+// launches over the same pages. The vector kernel (a single query token, at
+// most 4 heads) takes all G in one launch.
+#ifndef PA_MAX_TILES
+#define PA_MAX_TILES 2  // measurement builds: 1 keeps every launch to one column tile
+#endif
+int launch_columns(int G, int M, int D) {
+  const int width = PA_MAX_TILES > 1 && D <= 128 ? 32 : 16;
+  const long long total = (long long)G * M;
+  return total < width ? (int)total : width;
+}
+
+// Host checks shared by the partition entry points; fills `plan` for a launch
+// of NC columns. The query has dtype qdt; the caches kvdt (== qdt, or
+// PA_FP8_E4M3 with a 16-bit query).
 int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const void* query,
                     const void* key_cache, const void* value_cache, const int32_t* block_tables,
                     const int32_t* seq_lens, int32_t S, int32_t H, int32_t KH, int32_t D,
                     int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS, int32_t qdt,
-                    int32_t kvdt, int32_t M, int32_t Mc, const float* alibi, Plan* plan) {
+                    int32_t kvdt, int32_t M, int32_t NC, const float* alibi, Plan* plan) {
   if (S < 0 || H < 0 || KH < 0 || D < 0 || BS < 0 || NB < 0 || MB < 0 || P < 0)
     return fail(PA_ERR_SHAPE, "negative size argument");
   if (M < 1) return fail(PA_ERR_SHAPE, "num_queries must be >= 1");
@@ -180,15 +199,15 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   if (alibi && !aligned4(alibi)) return fail(PA_ERR_ALIGN, "alibi_slopes must be 4-byte aligned");
   partition_fn fn = nullptr;
   bool vec = false;
-  if (M > 1) {
-    // several query tokens: the MFMA path, one column per (query token, head),
-    // at most 16 columns per launch (query_chunk)
-    if (!is_16bit(qdt) || G > 16)
-      return fail(PA_ERR_UNSUPPORTED,
-                  "several query tokens need an f16/bf16 query and group <= 16 (got group %d)", G);
-    fn = kvdt == PA_FP8_E4M3 ? kMfma8[al][qdt - 1][di][bi] : kMfma[al][qdt - 1][di][bi];
-  } else if (is_16bit(qdt) && G >= 4 && G <= 16) {
-    fn = kvdt == PA_FP8_E4M3 ? kMfma8[al][qdt - 1][di][bi] : kMfma[al][qdt - 1][di][bi];
+  if (M > 1 || (is_16bit(qdt) && G >= 4)) {
+    // the MFMA path: one column per (query token, head), launch_columns of
+    // them per launch in one or two column tiles
+    if (!is_16bit(qdt))
+      return fail(PA_ERR_UNSUPPORTED, "several query tokens need an f16/bf16 query");
+    const int ct = NC > 16 ? 1 : 0;
+    if (NC < 1 || NC > 32 || (ct && di > 1))
+      return fail(PA_ERR_UNSUPPORTED, "bad column count %d for head size %d", NC, D);
+    fn = kvdt == PA_FP8_E4M3 ? kMfma8[al][ct][qdt - 1][di][bi] : kMfma[al][ct][qdt - 1][di][bi];
   } else if (G <= 4) {
     const int gi = G == 1 ? 0 : G == 2 ? 1 : 2;
     fn = kvdt == PA_FP8_E4M3 ? kVec8[al][qdt - 1][di][bi][gi] : kVec[al][qdt][di][bi][gi];
@@ -199,9 +218,11 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
       !aligned16(tmp_output))
     return fail(PA_ERR_ALIGN, "query, key_cache, value_cache and tmp_output must be 16-byte aligned");
-  if (((long long)(Mc - 1) * H + G) * P * D * 4 > 0x7fffffffLL)
-    return fail(PA_ERR_UNSUPPORTED, "tmp_output rows of one (sequence, kv head) exceed 2 GiB");
-  const int NC = G * Mc;  // columns of a work unit
+  // A launch's columns span at most this many query tokens; its tmp_output
+  // rows are addressed with 32-bit byte offsets.
+  const long long toks = std::min<long long>(M, (NC + G - 2) / G + 1);
+  if (((toks - 1) * H + G) * P * D * 4 > 0x7fffffffLL)
+    return fail(PA_ERR_UNSUPPORTED, "tmp_output rows of one launch's units exceed 2 GiB");
   const int lds_limit = max_lds_per_block();
   const int lds1 = pa::lds_layout(PS, BS, NC, D, 1).total;
   if (lds1 > lds_limit)
@@ -224,19 +245,11 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   return PA_OK;
 }
 
-// Query tokens per partition launch: one MFMA column per (query token, head),
-// 16 columns; M tokens beyond that run as several launches over the same
-// pages (each reads K/V once).
-int query_chunk(int G, int M) {
-  const int per = G >= 1 && G <= 16 ? 16 / G : 1;  // (G > 16 is rejected by check_partition)
-  return M > 1 ? (per < M ? per : M) : 1;
-}
-
 int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float* max_logits,
                      const void* query, const void* key_cache, const void* value_cache,
                      const int32_t* block_tables, const int32_t* seq_lens, int32_t S, int32_t H,
                      int32_t KH, int32_t NB, int32_t MB, int32_t P, int32_t PS, float scale,
-                     float k_scale, float v_scale, int32_t Mc, int32_t Mq, int32_t m0,
+                     float k_scale, float v_scale, int32_t NC, int32_t Mq, int32_t c0,
                      const float* alibi, hipStream_t stream) {
   PartitionArgs a;
   a.tmp_out = tmp_output;
@@ -254,9 +267,9 @@ int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float
   a.P = P;
   a.PS = PS;
   a.NB = NB;
-  a.M = Mc;
   a.Mq = Mq;
-  a.m0 = m0;
+  a.NC = NC;
+  a.c0 = c0;
   a.C = plan.span;
   a.through = P >= kThroughMinPartitions;
   a.qk_scale = scale * k_scale * pa::kLog2e;
@@ -322,40 +335,43 @@ int launch_reduce(reduce_fn fn, void* out, float* lse, const float* tmp_output,
 
 bool finite(float v) { return v == v && v - v == 0.0f; }
 
-// Plans for the query-token chunks of a phase-1 call: `full` for chunks of mc
-// tokens, `last` for a shorter final one (all validated before any launch).
+// Plans for the column launches of a phase-1 call: `full` for launches of nc
+// columns, `last` for a narrower final one (all validated before any launch).
 int plan_partitions(float* tmp_output, float* exp_sums, float* max_logits, const void* query,
                     const void* key_cache, const void* value_cache, const int32_t* block_tables,
                     const int32_t* seq_lens, int32_t S, int32_t H, int32_t KH, int32_t D,
                     int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS, int32_t qdt,
                     int32_t kvdt, int32_t M, const float* alibi, Plan* full, Plan* last,
-                    int* mc) {
-  const int G = KH > 0 && H >= KH ? H / KH : 1;  // (validated by check_partition)
-  *mc = M > 0 ? query_chunk(G, M) : 1;
+                    int* nc) {
+  const int G = KH > 0 && H >= KH && H % KH == 0 ? H / KH : 1;  // (validated by check_partition)
+  const long long total = (long long)G * (M > 0 ? M : 1);
+  *nc = launch_columns(G, M > 0 ? M : 1, D);
   int rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                            block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt, M,
-                           *mc, alibi, full);
+                           *nc, alibi, full);
   if (rc != PA_OK || S == 0) return rc;
+  if (total > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many query columns");
   *last = *full;
-  if (M % *mc)
+  if (total % *nc)
     rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                          block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt, M,
-                         M % *mc, alibi, last);
+                         (int)(total % *nc), alibi, last);
   return rc;
 }
 
-int launch_partitions(const Plan& full, const Plan& last, int mc, float* tmp_output,
+int launch_partitions(const Plan& full, const Plan& last, int nc, float* tmp_output,
                       float* exp_sums, float* max_logits, const void* query,
                       const void* key_cache, const void* value_cache,
                       const int32_t* block_tables, const int32_t* seq_lens, int32_t S,
                       int32_t H, int32_t KH, int32_t NB, int32_t MB, int32_t P, int32_t PS,
                       float scale, float k_scale, float v_scale, int32_t M, const float* alibi,
                       hipStream_t stream) {
-  for (int m0 = 0; m0 < M; m0 += mc) {
-    const int n = M - m0 < mc ? M - m0 : mc;
-    const int rc = launch_partition(n == mc ? full : last, tmp_output, exp_sums, max_logits,
+  const int total = H / KH * M;  // (bounded by plan_partitions)
+  for (int c0 = 0; c0 < total; c0 += nc) {
+    const int n = total - c0 < nc ? total - c0 : nc;
+    const int rc = launch_partition(n == nc ? full : last, tmp_output, exp_sums, max_logits,
                                     query, key_cache, value_cache, block_tables, seq_lens, S, H,
-                                    KH, NB, MB, P, PS, scale, k_scale, v_scale, n, M, m0, alibi,
+                                    KH, NB, MB, P, PS, scale, k_scale, v_scale, n, M, c0, alibi,
                                     stream);
     if (rc != PA_OK) return rc;
   }
@@ -372,12 +388,12 @@ int partition_entry(float* tmp_output, float* exp_sums, float* max_logits, const
   if (!finite(k_scale) || !finite(v_scale))
     return fail(PA_ERR_SHAPE, "k_scale and v_scale must be finite");
   Plan full, last;
-  int mc = 1;
+  int nc = 1;
   int rc = plan_partitions(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                            block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt, M,
-                           alibi, &full, &last, &mc);
+                           alibi, &full, &last, &nc);
   if (rc != PA_OK || S == 0) return rc;
-  return launch_partitions(full, last, mc, tmp_output, exp_sums, max_logits, query, key_cache,
+  return launch_partitions(full, last, nc, tmp_output, exp_sums, max_logits, query, key_cache,
                            value_cache, block_tables, seq_lens, S, H, KH, NB, MB, P, PS, scale,
                            k_scale, v_scale, M, alibi, (hipStream_t)stream);
 }
@@ -393,10 +409,10 @@ int decode_entry(void* out, float* lse, float* tmp_output, float* exp_sums, floa
     return fail(PA_ERR_SHAPE, "k_scale and v_scale must be finite");
   if (S > 0 && lse && !aligned4(lse)) return fail(PA_ERR_ALIGN, "lse must be 4-byte aligned");
   Plan full, last;
-  int mc = 1;
+  int nc = 1;
   int rc = plan_partitions(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                            block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt, M,
-                           alibi, &full, &last, &mc);
+                           alibi, &full, &last, &nc);
   if (rc != PA_OK || S == 0) return rc;
   if (out_dtype != PA_F32 && out_dtype != qdt)
     return fail(PA_ERR_UNSUPPORTED, "out dtype must be PA_F32 or the query dtype");
@@ -404,7 +420,7 @@ int decode_entry(void* out, float* lse, float* tmp_output, float* exp_sums, floa
   rc = check_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, S, M, H, D, P, PS,
                     out_dtype, &fn);
   if (rc != PA_OK) return rc;
-  rc = launch_partitions(full, last, mc, tmp_output, exp_sums, max_logits, query, key_cache,
+  rc = launch_partitions(full, last, nc, tmp_output, exp_sums, max_logits, query, key_cache,
                          value_cache, block_tables, seq_lens, S, H, KH, NB, MB, P, PS, scale,
                          k_scale, v_scale, M, alibi, (hipStream_t)stream);
   if (rc != PA_OK) return rc;
@@ -665,7 +681,8 @@ int paged_attn_partition_span(int32_t num_seqs, int32_t num_heads, int32_t num_k
     return fail(PA_ERR_UNSUPPORTED, "unsupported head_size / block_size");
   if (PS <= 0 || PS % BS || PS / BS > pa::kWaves * 64 || P < 1)
     return fail(PA_ERR_SHAPE, "bad partition size / count");
-  return pick_span(S, KH, P, PS, BS, H / KH, D, elem_size(dt), max_lds_per_block());
+  return pick_span(S, KH, P, PS, BS, launch_columns(H / KH, 1, D), D, elem_size(dt),
+                   max_lds_per_block());
 }
 
 int paged_attn_default_partition_size(int32_t head_size, int32_t block_size, int32_t kv_dtype,
@@ -674,7 +691,7 @@ int paged_attn_default_partition_size(int32_t head_size, int32_t block_size, int
     return fail(PA_ERR_UNSUPPORTED, "unsupported head_size / block_size");
   if (kv_dtype != PA_F32 && kv_dtype != PA_F16 && kv_dtype != PA_BF16 && kv_dtype != PA_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "unknown kv dtype %d", kv_dtype);
-  if (group < 1 || group > 16) return fail(PA_ERR_UNSUPPORTED, "group size %d", group);
+  if (group < 1) return fail(PA_ERR_UNSUPPORTED, "group size %d", group);
   // Measured on MI355X over GQA (G=4, 8), MHA and 256-wide-head batches: with
   // 16-bit caches 1024 tokens per partition is never slower than 512 (GQA
   // -5 %, long context -2 %, others within 1 %): half the per-partition output

@@ -140,13 +140,16 @@ CONFIGS.update(FP8_CONFIGS)
 
 # Several query tokens per sequence (speculative decoding: the last M positions
 # of each sequence query the cache causally): the GQA workload with 4 tokens
-# (4 heads x 4 tokens fill one 16-column tile) and the long-context one with 2.
+# (4 heads x 4 tokens fill one 16-column tile) and the long-context one with 2
+# (16 columns) and 4 (8 heads x 4 tokens: 32 columns, two tiles).
 MQ_CONFIGS: Dict[str, DecodeConfig] = {
     "gqa_bf16_g4_m4": CONFIGS["gqa_bf16_g4"].replace(name="gqa_bf16_g4_m4", num_queries=4),
     "longctx_bf16_g8_m2": CONFIGS["longctx_bf16_g8"].replace(name="longctx_bf16_g8_m2",
                                                             num_queries=2),
+    "longctx_bf16_g8_m4": CONFIGS["longctx_bf16_g8"].replace(name="longctx_bf16_g8_m4",
+                                                            num_queries=4),
 }
-MQ_ORDER = ["gqa_bf16_g4_m4", "longctx_bf16_g8_m2"]
+MQ_ORDER = ["gqa_bf16_g4_m4", "longctx_bf16_g8_m2", "longctx_bf16_g8_m4"]
 CONFIGS.update(MQ_CONFIGS)
 
 # ALiBi position bias: the MHA workload (the head structure of the published

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 def test_abi_version_and_default_partition_size():
     assert pa.abi_version() == 1
     for D, BS, dt, G in [(128, 16, torch.bfloat16, 4), (256, 32, torch.float16, 1),
-                         (64, 16, torch.float32, 1)]:
+                         (64, 16, torch.float32, 1), (128, 16, torch.bfloat16, 32)]:
         ps = pa.default_partition_size(D, BS, dt, G)
         assert ps > 0 and ps % BS == 0
     with pytest.raises(RuntimeError):
@@ -63,6 +63,9 @@ def test_partition_span_plan():
     assert pa.partition_span(32, 16, 16, 256, 32, 16, 512, f16) == 1   # 1 MiB span too long
     assert pa.partition_span(2, 4, 4, 64, 16, 2, 64, f32) == 1         # small grid
     assert pa.partition_span(128, 8, 8, 64, 16, 4, 64, f32) == 2
+    # 32 query heads per kv head: two column tiles, whose parked state for two
+    # partitions would exceed the LDS cap
+    assert pa.partition_span(128, 64, 2, 128, 16, 8, 512, bf) == 1
     with pytest.raises(RuntimeError):
         pa.partition_span(2, 4, 3, 64, 16, 2, 64, f32)                  # H % KH
     with pytest.raises(RuntimeError):
@@ -104,8 +107,8 @@ def reduce(ptrs=None, S=2, H=8, D=128, P=1, PS=512, odt=binding.PA_F32):
     (dict(D=512), binding.PA_ERR_UNSUPPORTED),
     (dict(BS=8, PS=512), binding.PA_ERR_UNSUPPORTED),
     (dict(dt=7), binding.PA_ERR_UNSUPPORTED),
-    (dict(H=64, KH=2), binding.PA_ERR_UNSUPPORTED),    # G = 32
     (dict(H=16, KH=2, dt=binding.PA_F32), binding.PA_ERR_UNSUPPORTED),  # fp32, G = 8
+    (dict(H=64, KH=2, dt=binding.PA_F32), binding.PA_ERR_UNSUPPORTED),  # fp32, G = 32
     (dict(PS=16 * 512), binding.PA_ERR_UNSUPPORTED),   # PS / BS > 256
 ])
 def test_partition_rejects(kw, code):
@@ -149,7 +152,7 @@ def part_fp8(q_dtype=binding.PA_BF16, k_scale=1.0, v_scale=1.0, **kw):
     (dict(k_scale=float("inf")), binding.PA_ERR_SHAPE),
     (dict(v_scale=float("nan")), binding.PA_ERR_SHAPE),
     (dict(D=72), binding.PA_ERR_SHAPE),                # 72 % 16 != 0 (x = 16 for 8-bit)
-    (dict(H=64, KH=2), binding.PA_ERR_UNSUPPORTED),    # G = 32
+    (dict(D=96), binding.PA_ERR_UNSUPPORTED),          # head size, also with an 8-bit cache
 ])
 def test_fp8_partition_rejects(kw, code):
     assert part_fp8(**kw) == code
@@ -165,7 +168,7 @@ def part_mq(M=2, q_dtype=binding.PA_BF16, kv_dtype=binding.PA_BF16, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(M=0), binding.PA_ERR_SHAPE),
-    (dict(M=2, H=64, KH=2), binding.PA_ERR_UNSUPPORTED),       # group 32 > 16 columns
+    (dict(M=2, H=64, KH=2, D=96), binding.PA_ERR_UNSUPPORTED),  # group 32, unknown head size
     (dict(q_dtype=binding.PA_F32, kv_dtype=binding.PA_F32), binding.PA_ERR_UNSUPPORTED),
     (dict(q_dtype=binding.PA_F16, kv_dtype=binding.PA_BF16), binding.PA_ERR_UNSUPPORTED),
 ])
@@ -290,6 +293,6 @@ def test_ex_entries_reject_misaligned_alibi_and_lse():
                                 binding.PA_F32, None)
     assert lib.paged_attn_decode_ex(*dec_args(FAKE + 1, None)) == binding.PA_ERR_ALIGN
     assert lib.paged_attn_decode_ex(*dec_args(None, FAKE + 1)) == binding.PA_ERR_ALIGN
-    assert lib.paged_attn_decode_ex(*dec_args(None, None)[:10], 2, 2, 64, 2,
-                                    *dec_args(None, None)[14:]) \
-        == binding.PA_ERR_UNSUPPORTED  # two query tokens, group 32 > 16
+    assert lib.paged_attn_decode_ex(*dec_args(None, None)[:10], 2, 2, 64, 2, 96,
+                                    *dec_args(None, None)[15:]) \
+        == binding.PA_ERR_UNSUPPORTED  # two query tokens, group 32, unknown head size

@@ -3,10 +3,11 @@
 Every output row and every partition intermediate is compared with the
 oracle's multi-token mode (which is pinned to the single-query oracle on each
 row's causal prefix): several (group, M) mixes that fill one MFMA column tile
-(G * M <= 16) and wider windows that run in several passes, 8-bit caches,
-lengths shorter than M, equal to M and at block / partition edges, the
-two-call and one-call forms, and M = 1 against the single-query entry points
-bit for bit.
+(G * M <= 16), two column tiles (17 to 32 columns, head sizes up to 128) and
+wider windows that run in several launches over the pages (one of them ending
+part-way through a token's heads), 8-bit caches, lengths shorter than M, equal
+to M and at block / partition edges, the two-call and one-call forms, and
+M = 1 against the single-query entry points bit for bit.
 """
 import math
 
@@ -82,11 +83,16 @@ CASES = [
     ("f16", 16, 2, 256, 16, 128, 2),    # G=8 x M=2, D=256
     ("fp8", 32, 8, 128, 16, 64, 4),     # 8-bit cache, G=4 x M=4
     ("fp8", 8, 4, 256, 32, 64, 5),      # 8-bit cache, G=2 x M=5, D=256, BS=32
-    # more than 16 columns: the tokens run in several passes over the pages
-    ("bf16", 64, 8, 128, 16, 64, 4),    # G=8 x M=4: two passes of 2 tokens
-    ("f16", 32, 8, 128, 16, 64, 7),     # G=4 x M=7: passes of 4 and 3 tokens
-    ("bf16", 16, 1, 64, 32, 64, 3),     # G=16 x M=3: three passes of 1 token
-    ("fp8", 32, 8, 128, 16, 64, 6),     # 8-bit cache, G=4 x M=6: passes of 4 and 2
+    # 17 to 32 columns, head size <= 128: one launch with two column tiles
+    ("bf16", 64, 8, 128, 16, 64, 4),    # G=8 x M=4: 32 columns
+    ("f16", 32, 8, 128, 16, 64, 7),     # G=4 x M=7: 28 columns
+    ("bf16", 40, 8, 64, 16, 64, 5),     # G=5 x M=5: 25 columns, D=64
+    ("fp8", 32, 8, 128, 16, 64, 6),     # 8-bit cache, G=4 x M=6: 24 columns
+    # wider: several launches over the pages
+    ("bf16", 16, 1, 64, 32, 64, 3),     # G=16 x M=3: launches of 32 and 16 columns
+    ("bf16", 48, 8, 128, 16, 64, 6),    # G=6 x M=6: 32 + 4, token 5's heads split
+    ("f16", 32, 2, 256, 16, 128, 3),    # G=16 x M=3, D=256: three 16-column launches
+    ("fp8", 64, 2, 128, 32, 64, 2),     # 8-bit cache, G=32 x M=2: two 32-column launches
 ]
 
 
@@ -140,8 +146,8 @@ def test_one_query_token_matches_single_query_calls(name):
         U.assert_close("M=1 vs vector path", res["out"][:, 0], single["out"].double().numpy())
 
 
-def test_multi_token_rejects_group_over_16():
-    cfg = mq_geom("bf16", 64, 2, 128, 16, 64, 2, [10, 20])   # G=32: no MFMA column layout
+def test_multi_token_rejects_fp32_query():
+    cfg = mq_geom("f32", 8, 2, 64, 16, 64, 2, [10, 20])   # the MFMA path needs a 16-bit query
     d = U.to_device(W.make_inputs(cfg, seed=1, lens=[10, 20]))
     with pytest.raises(RuntimeError):
         run_mq(d, 64, 1)

@@ -5,7 +5,9 @@ partition size, batch, lengths with empty and partial partitions, query
 tokens, ALiBi on or off, output dtype) within what the launchers accept and
 runs paged_attn_decode_ex; the output, the row log-sum-exp and every
 partition intermediate are compared with the oracle. Sizes stay small so the
-oracle finishes in well under a second per case.
+oracle finishes in well under a second per case. The cases from N_NARROW on
+draw 16-bit queries with more than 16 (query token, head) columns per kv
+head: two MFMA column tiles, or several launches over the pages.
 """
 import math
 
@@ -20,7 +22,8 @@ from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 40
+N_NARROW = 40
+N_CASES = 56
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -31,7 +34,9 @@ def built():
 
 def draw(i):
     rng = np.random.default_rng(1000 + i)
-    kv = rng.choice(["f32", "f16", "bf16", "fp8"], p=[0.15, 0.3, 0.3, 0.25])
+    wide = i >= N_NARROW
+    kv = rng.choice(["f32", "f16", "bf16", "fp8"], p=[0, 0.35, 0.35, 0.3] if wide else
+                    [0.15, 0.3, 0.3, 0.25])
     q = kv if kv != "fp8" else str(rng.choice(["f16", "bf16"]))
     D = int(rng.choice([64, 128, 256]))
     BS = int(rng.choice([16, 32]))
@@ -40,6 +45,9 @@ def draw(i):
     if q == "f32":
         G = int(rng.choice([1, 2, 3, 4]))
         M = 1
+    elif wide:  # 17 .. ~50 columns per kv head
+        G = int(rng.choice([2, 3, 5, 6, 8, 12, 17, 24, 32]))
+        M = int(rng.integers(max(1, 17 // G + (17 % G > 0)), max(2, 48 // G) + 1))
     else:
         G = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
         # up to 16 columns per pass; wider windows run in several passes

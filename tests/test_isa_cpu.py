@@ -94,7 +94,7 @@ def test_kv_loads_are_dwordx4_or_dwordx2_streaming(kernels):
         if "partition_vec_kernelILi2ELi128ELi16ELi1ELb1" in k:
             assert any(l.startswith("global_load_dwordx4") for l in nt)
             seen += 1
-    assert seen == 6  # each with ALiBi off and on
+    assert seen == 10  # each with ALiBi off and on; the MFMA ones with one and two column tiles
 
 
 def test_fp8_kernels_convert_with_gfx950_instructions(kernels):
