@@ -74,6 +74,13 @@ namespace pa {
 #ifndef PA_PIN_PREFETCH
 #define PA_PIN_PREFETCH 1    // scheduling barrier between prefetch issue and compute
 #endif
+// MFMA path: the P high part and residual in one 16x16x32 PV MFMA (1: with
+// 16-bit caches; 2: also 8-bit ones, whose 4-wavefront budget then spills a
+// few registers; 0: two 16x16x16 MFMAs everywhere). Measured: neutral to
+// 0.7 % faster on the 16-bit workloads, neutral on 8-bit ones.
+#ifndef PA_PV32
+#define PA_PV32 1
+#endif
 #ifndef PA_NT_LOADS
 #define PA_NT_LOADS 1        // K/V loads carry the non-temporal (streaming) hint
 #endif
@@ -430,8 +437,9 @@ __device__ __forceinline__ bool unit_hoist(const PartitionArgs& a, int32_t* s_bt
 // head l%16) is exactly the B operand layout of a 16x16x16 MFMA with tokens as
 // k, so P feeds PV without any data movement. V is read as 4 tokens of one d
 // (8 bytes, or 4 bytes for an 8-bit cache) that form the matching A operand.
-// P is split into a 16-bit high part and a 16-bit residual (two PV MFMAs) so
-// the probabilities keep ~16 bits of mantissa instead of bf16's 8.
+// P is split into a 16-bit high part and a 16-bit residual so the
+// probabilities keep ~16 bits of mantissa instead of bf16's 8; both enter one
+// 16x16x32 PV MFMA (16-bit caches) or two 16x16x16 ones (8-bit caches).
 // K k-steps: a 16-bit cache chunk is 8 d of one token (one k-step per 16-byte
 // load); an 8-bit chunk is 16 d (two k-steps per load: its low and high 8 d).
 // The query B operand follows the same d assignment, so the contraction over
@@ -482,8 +490,11 @@ constexpr int prefetch_fp8(int page_regs) { return page_regs <= 16 ? PA_PREFETCH
 // measured ~10 % faster than 3 and ~25 % faster than 2). Larger pages need
 // more registers; the budget shrinks so that nothing spills (the ALiBi
 // variant's two extra per-lane values tip the smallest page over 4).
+#ifndef PA_FP8_WAVES
+#define PA_FP8_WAVES 0  // measurement builds: >0 overrides the budget below
+#endif
 constexpr int fp8_waves(int D, int BS, bool AL) {
-  return D * BS <= 2048 && !AL ? 4 : D <= 128 ? 3 : 2;
+  return PA_FP8_WAVES > 0 ? PA_FP8_WAVES : D * BS <= 2048 && !AL ? 4 : D <= 128 ? 3 : 2;
 }
 // Register budget (wavefronts per SIMD) of the MFMA kernel: two column tiles
 // hold two accumulators and two query operands, which only fit at 2.
@@ -742,15 +753,39 @@ partition_mfma_kernel(PartitionArgs a) {
         }
       }
     }
+    if constexpr (PA_PV32 == 2 || (PA_PV32 == 1 && !KV8)) {
+      // One 16x16x32 MFMA per d-block and sub-tile: lane row grp holds k-slots
+      // 8grp .. 8grp+7 = (its 4 tokens' P high parts, the same tokens'
+      // residuals) in B and its 4 V values twice in A, so the contraction is
+      // sum_t v_t * (hi_t + lo_t), both parts in one instruction.
+      u32x4 pp[CT][SUB];
 #pragma unroll
-    for (int mb = 0; mb < VB; ++mb) {
+      for (int t = 0; t < CT; ++t) {
 #pragma unroll
-      for (int st = 0; st < SUB; ++st) {
-        const u32x2 v = v_operand(vw[st][mb]);
+        for (int st = 0; st < SUB; ++st)
+          pp[t][st] = u32x4{phi[t][st][0], phi[t][st][1], plo[t][st][0], plo[t][st][1]};
+      }
 #pragma unroll
-        for (int t = 0; t < CT; ++t) {
-          acc[t][mb] = M::pv(v, phi[t][st], acc[t][mb]);
-          acc[t][mb] = M::pv(v, plo[t][st], acc[t][mb]);
+      for (int mb = 0; mb < VB; ++mb) {
+#pragma unroll
+        for (int st = 0; st < SUB; ++st) {
+          const u32x2 v = v_operand(vw[st][mb]);
+          const u32x4 vv = {v[0], v[1], v[0], v[1]};
+#pragma unroll
+          for (int t = 0; t < CT; ++t) acc[t][mb] = M::qk(vv, pp[t][st], acc[t][mb]);
+        }
+      }
+    } else {  // two 16x16x16 MFMAs (high part, then residual)
+#pragma unroll
+      for (int mb = 0; mb < VB; ++mb) {
+#pragma unroll
+        for (int st = 0; st < SUB; ++st) {
+          const u32x2 v = v_operand(vw[st][mb]);
+#pragma unroll
+          for (int t = 0; t < CT; ++t) {
+            acc[t][mb] = M::pv(v, phi[t][st], acc[t][mb]);
+            acc[t][mb] = M::pv(v, plo[t][st], acc[t][mb]);
+          }
         }
       }
     }
