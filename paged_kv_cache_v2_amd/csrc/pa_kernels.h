@@ -210,7 +210,8 @@ __host__ __device__ inline LdsLayout lds_layout(int PS, int BS, int NC, int D, i
 // Interleaved with the streaming K/V reads, written-back tmp lines cost
 // several times their size in read bandwidth. Device-scope (sc1) stores
 // measured up to ~6 % faster where each row has many partitions (64: long
-// context, 16: 256-wide heads) and up to ~2.5 % slower where it has few (4-8:
+// context, 16: 256-wide heads, or 16 columns per unit: 4x the rows) and up
+// to ~2.5 % slower where it has few (4-8 partitions of 4 single-query heads:
 // ragged GQA batches), so the host picks the policy per launch (`through`).
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer resource: 32-bit format, no swizzle
 constexpr int kStoreThrough = 16;       // buffer-instruction cache policy: sc1

@@ -12,6 +12,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <utility>
+#include <vector>
 
 #include "paged_attn.h"
 #include "pa_kernels.h"
@@ -84,6 +87,22 @@ int max_lds_per_block() {
   return v;
 }
 
+// LDS of one CU (if unknown, that of two workgroups at the fallback limit).
+int max_lds_per_cu() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 2 * 65536;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess ||
+        v < 1)
+      v = 2 * 65536;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 struct Plan {
   partition_fn fn;
   int lds_bytes;
@@ -105,9 +124,15 @@ struct Plan {
 // spans measured ~6 % slower). The span's block-table slice must fit the
 // 256-thread hoist and its parked state the LDS.
 constexpr long long kMinGrid = 2048;
-// tmp_output store policy: device-scope stores when rows have at least this
-// many partitions (measured; see store_row in pa_kernels.h).
+// tmp_output store policy: device-scope stores when rows have at least
+// kThroughMinPartitions partitions, or a unit writes at least
+// kThroughMinColumns rows per partition (see store_row in pa_kernels.h).
+// Measured on the 16-column GQA window (4 heads x 4 query tokens, 8 or 4
+// partitions): 230.5 -> 225.5 us at PS=512, 218.3 -> 214.4 at PS=1024; the
+// 4-column single-query GQA batch stays on the default policy (equal at
+// PS=512, 2.5 % slower at PS=1024 with device-scope stores).
 constexpr int kThroughMinPartitions = 16;
+constexpr int kThroughMinColumns = 16;
 constexpr long long kSpanBytes = 512 * 1024;
 #ifndef PA_LPT
 #define PA_LPT 1  // measurement builds: 0 index order everywhere, 2 largest-first everywhere
@@ -121,15 +146,20 @@ constexpr long long kSpanBytes = 512 * 1024;
 // ~1 % (nothing to reorder). So it is taken for 8-bit caches and the vector
 // kernel only.
 constexpr int kLptMaxPairs = 4096;
-constexpr int kSpanLdsCap = 64 * 1024;
+// Upper bound on the LDS of a span's parked state (see span_lds_cap): 80 KiB
+// is two workgroups per CU, what the 16-bit MFMA kernel's registers allow at
+// head size 128. It admits two-partition spans for 16-column units there (66
+// KiB; measured against one-partition units: GQA with 4 query tokens 225.3 ->
+// 220.6 us, long context with 2 tokens 192.8 -> 185.5 us).
+constexpr int kSpanLdsCap = 80 * 1024;
 
-int pick_span(int S, int KH, int P, int PS, int BS, int NC, int D, int esz, int lds_limit) {
+int pick_span(int S, int KH, int P, int PS, int BS, int NC, int D, int esz, int lds_cap) {
   int best = 1;
   for (int c = 2; c <= pa::kMaxSpan; c *= 2) {
     const long long grid = (long long)S * KH * ((P + c - 1) / c);
     const long long bytes = (long long)c * PS * D * esz * 2;
     const int lds = pa::lds_layout(PS, BS, NC, D, c).total;
-    if (c * (PS / BS) > pa::kWaves * 64 || lds > kSpanLdsCap || lds > lds_limit) break;
+    if (c * (PS / BS) > pa::kWaves * 64 || lds > lds_cap) break;
     if (PA_SPAN > 0) {
       if (c > PA_SPAN) break;
     } else if (grid < kMinGrid || bytes > kSpanBytes) {
@@ -153,6 +183,62 @@ int launch_columns(int G, int M, int D) {
   const int width = PA_MAX_TILES > 1 && D <= 128 ? 32 : 16;
   const long long total = (long long)G * M;
   return total < width ? (int)total : width;
+}
+
+// The partition kernel for a launch of NC columns (query dtype qdt, cache
+// kvdt, group G, M query tokens, ALiBi flag al); *vec: the vector kernel.
+int select_kernel(int qdt, int kvdt, int M, int G, int NC, int D, int BS, int al,
+                  partition_fn* fn, bool* vec) {
+  const int di = d_index(D), bi = bs_index(BS);
+  if (di < 0 || bi < 0) return fail(PA_ERR_UNSUPPORTED, "unsupported head_size / block_size");
+  *vec = false;
+  if (M > 1 || (is_16bit(qdt) && G >= 4)) {
+    // the MFMA path: one column per (query token, head), launch_columns of
+    // them per launch in one or two column tiles
+    if (!is_16bit(qdt))
+      return fail(PA_ERR_UNSUPPORTED, "several query tokens need an f16/bf16 query");
+    const int ct = NC > 16 ? 1 : 0;
+    if (NC < 1 || NC > 32 || (ct && di > 1))
+      return fail(PA_ERR_UNSUPPORTED, "bad column count %d for head size %d", NC, D);
+    *fn = kvdt == PA_FP8_E4M3 ? kMfma8[al][ct][qdt - 1][di][bi] : kMfma[al][ct][qdt - 1][di][bi];
+  } else if (G <= 4) {
+    const int gi = G == 1 ? 0 : G == 2 ? 1 : 2;
+    *fn = kvdt == PA_FP8_E4M3 ? kVec8[al][qdt - 1][di][bi][gi] : kVec[al][qdt][di][bi][gi];
+    *vec = true;
+  } else {
+    return fail(PA_ERR_UNSUPPORTED, "group size %d not supported for this dtype", G);
+  }
+  return PA_OK;
+}
+
+// Workgroups of `fn` that one CU holds by its register use (the HIP runtime's
+// occupancy calculator, without LDS; cached per kernel). 2 if unknown.
+int wgs_per_cu(partition_fn fn) {
+  static std::mutex mu;
+  static std::vector<std::pair<partition_fn, int>> seen;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto& e : seen)
+      if (e.first == fn) return e.second;
+  }
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)fn, pa::kWaves * 64, 0) !=
+          hipSuccess ||
+      n < 1) {
+    (void)hipGetLastError();
+    n = 2;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  seen.emplace_back(fn, n);
+  return n;
+}
+
+// LDS a span's parked state may take: the CU's LDS shared by the workgroups
+// the kernel's registers allow (a longer span must not cost occupancy), at
+// most kSpanLdsCap and the per-workgroup limit.
+int span_lds_cap(partition_fn fn, int lds_limit) {
+  const int per_wg = max_lds_per_cu() / wgs_per_cu(fn);
+  return std::min(std::min(per_wg, kSpanLdsCap), lds_limit);
 }
 
 // Host checks shared by the partition entry points; fills `plan` for a launch
@@ -199,22 +285,8 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   if (alibi && !aligned4(alibi)) return fail(PA_ERR_ALIGN, "alibi_slopes must be 4-byte aligned");
   partition_fn fn = nullptr;
   bool vec = false;
-  if (M > 1 || (is_16bit(qdt) && G >= 4)) {
-    // the MFMA path: one column per (query token, head), launch_columns of
-    // them per launch in one or two column tiles
-    if (!is_16bit(qdt))
-      return fail(PA_ERR_UNSUPPORTED, "several query tokens need an f16/bf16 query");
-    const int ct = NC > 16 ? 1 : 0;
-    if (NC < 1 || NC > 32 || (ct && di > 1))
-      return fail(PA_ERR_UNSUPPORTED, "bad column count %d for head size %d", NC, D);
-    fn = kvdt == PA_FP8_E4M3 ? kMfma8[al][ct][qdt - 1][di][bi] : kMfma[al][ct][qdt - 1][di][bi];
-  } else if (G <= 4) {
-    const int gi = G == 1 ? 0 : G == 2 ? 1 : 2;
-    fn = kvdt == PA_FP8_E4M3 ? kVec8[al][qdt - 1][di][bi][gi] : kVec[al][qdt][di][bi][gi];
-    vec = true;
-  } else {
-    return fail(PA_ERR_UNSUPPORTED, "group size %d not supported for this dtype", G);
-  }
+  const int rc = select_kernel(qdt, kvdt, M, G, NC, D, BS, al, &fn, &vec);
+  if (rc != PA_OK) return rc;
   if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
       !aligned16(tmp_output))
     return fail(PA_ERR_ALIGN, "query, key_cache, value_cache and tmp_output must be 16-byte aligned");
@@ -228,7 +300,7 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   if (lds1 > lds_limit)
     return fail(PA_ERR_UNSUPPORTED, "needs %d bytes of LDS per workgroup, device allows %d", lds1,
                 lds_limit);
-  const int span = pick_span(S, KH, P, PS, BS, NC, D, elem_size(kvdt), lds_limit);
+  const int span = pick_span(S, KH, P, PS, BS, NC, D, elem_size(kvdt), span_lds_cap(fn, lds_limit));
   const long long grid = (long long)S * KH * ((P + span - 1) / span);
   if (grid > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many work units");
   plan->fn = fn;
@@ -271,7 +343,7 @@ int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float
   a.NC = NC;
   a.c0 = c0;
   a.C = plan.span;
-  a.through = P >= kThroughMinPartitions;
+  a.through = P >= kThroughMinPartitions || NC >= kThroughMinColumns;
   a.qk_scale = scale * k_scale * pa::kLog2e;
   a.v_scale = v_scale;
   a.alibi = alibi;
@@ -681,8 +753,14 @@ int paged_attn_partition_span(int32_t num_seqs, int32_t num_heads, int32_t num_k
     return fail(PA_ERR_UNSUPPORTED, "unsupported head_size / block_size");
   if (PS <= 0 || PS % BS || PS / BS > pa::kWaves * 64 || P < 1)
     return fail(PA_ERR_SHAPE, "bad partition size / count");
-  return pick_span(S, KH, P, PS, BS, launch_columns(H / KH, 1, D), D, elem_size(dt),
-                   max_lds_per_block());
+  const int G = H / KH, NC = launch_columns(G, 1, D);
+  partition_fn fn = nullptr;
+  bool vec = false;
+  const int qdt = dt == PA_FP8_E4M3 ? PA_BF16 : dt;  // (an 8-bit cache's f16 query: same plan)
+  const int rc = select_kernel(qdt, dt, 1, G, NC, D, BS, 0, &fn, &vec);
+  if (rc != PA_OK) return rc;
+  const int lds_limit = max_lds_per_block();
+  return pick_span(S, KH, P, PS, BS, NC, D, elem_size(dt), span_lds_cap(fn, lds_limit));
 }
 
 int paged_attn_default_partition_size(int32_t head_size, int32_t block_size, int32_t kv_dtype,

@@ -126,6 +126,23 @@ def test_multi_token_reduced_workload(name):
     check(inp, res, cfg.partition_size, P, f"mq {name}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_multi_token_two_partition_spans(dtype):
+    """4 heads x 4 tokens (16 columns) over enough units that the host takes
+    two-partition spans (66 KiB of parked state per workgroup at head size 128)."""
+    S, PS, P, M = 64, 64, 8, 4
+    rng = np.random.default_rng(5)
+    lens = [int(x) for x in rng.integers(0, P * PS + 1, size=S)]
+    lens[:4] = [0, 3, PS + 1, P * PS]
+    kw = dict(q_dtype="bf16", k_scale=0.03, v_scale=0.045) if dtype == "fp8" else {}
+    cfg = mq_geom(dtype, 32, 8, 128, 16, PS, M, lens, **kw)
+    inp = W.make_inputs(cfg, seed=52, lens=lens, extra_blocks=3)
+    W.poison_unused(inp)
+    U.note(f"multi-token spans {dtype}")
+    res = run_mq(U.to_device(inp), PS, P)
+    check(inp, res, PS, P, f"mq spans {dtype}")
+
+
 @pytest.mark.parametrize("name", ["gqa_bf16_g4", "mha_f16_d128", "gqa_fp8_g4"])
 def test_one_query_token_matches_single_query_calls(name):
     cfg = U.small_config(name)

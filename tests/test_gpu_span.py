@@ -43,6 +43,7 @@ SPAN_CASES = [
     ("bf16", 32, 8, 128, 16, 64, 5, 104),   # MFMA G=4, odd P: last span has one partition
     ("bf16", 32, 8, 128, 16, 48, 6, 96),    # MFMA G=4, 3 pages per partition
     ("bf16", 64, 8, 128, 16, 64, 8, 64),    # MFMA G=8
+    ("bf16", 32, 2, 128, 16, 64, 8, 256),   # MFMA G=16: 66 KiB of parked state per span
     ("f16", 32, 32, 128, 16, 64, 8, 32),    # vector G=1
     ("bf16", 16, 8, 64, 32, 64, 4, 256),    # vector G=2, D=64, BS=32
     ("f32", 8, 8, 64, 16, 64, 4, 128),      # vector fp32
@@ -96,6 +97,17 @@ def test_reduce_row_spread(c):
     res = U.run_decode(U.to_device(inp), split=True)
     assert res["P"] == P
     U.check_against_oracle(inp, res, label=f"reduce {c[:7]}")
+
+
+def test_span_plan_keeps_occupancy():
+    """A two-partition span's parked state may take the LDS that the kernel's
+    register-limited occupancy leaves: 66 KiB for 16 columns at head size 128
+    fits the 16-bit MFMA kernel (two workgroups per CU) but not the 8-bit one
+    (four per CU), which keeps one partition per workgroup there."""
+    args = (256, 32, 2, 128, 16, 8, 512)  # G = 16: one full column tile
+    assert pa.partition_span(*args, torch.bfloat16) == 2
+    assert pa.partition_span(*args, torch.float8_e4m3fn) == 1
+    assert pa.partition_span(256, 32, 8, 128, 16, 8, 512, torch.float8_e4m3fn) == 2  # G = 4
 
 
 def test_span_results_match_single_partition_workgroups():
