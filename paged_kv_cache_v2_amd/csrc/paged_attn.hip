@@ -770,14 +770,13 @@ int paged_attn_default_partition_size(int32_t head_size, int32_t block_size, int
   if (kv_dtype != PA_F32 && kv_dtype != PA_F16 && kv_dtype != PA_BF16 && kv_dtype != PA_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "unknown kv dtype %d", kv_dtype);
   if (group < 1) return fail(PA_ERR_UNSUPPORTED, "group size %d", group);
-  // Measured on MI355X over GQA (G=4, 8), MHA and 256-wide-head batches: with
-  // 16-bit caches 1024 tokens per partition is never slower than 512 (GQA
-  // -5 %, long context -2 %, others within 1 %): half the per-partition output
-  // bytes, while the grids stay large; 2048 loses on MHA and wide heads (fewer
-  // workgroups). 8-bit caches move half the bytes per token, so their
-  // partitions are already short work units: 512 (1024 measured 3-9 % slower
-  // on the GQA and MHA batches).
-  return kv_dtype == PA_FP8_E4M3 ? 512 : 1024;
+  // Measured on MI355X, step time (partition + reduce) against 1024-token
+  // partitions: 2048 is faster on the long-context (-2.7 %), MHA (-1.3 %),
+  // 256-wide-head (-1.2 %) and 4-token GQA (-2 %) batches and 0.7 % slower on
+  // the ragged GQA batch (shorter units balance its tail better); half the
+  // partition outputs to write and reduce. With 8-bit caches (half the bytes
+  // per token) 2048 against 512: GQA -8 %, long context -7 %, MHA equal.
+  return 2048;
 }
 
 }  // extern "C"
