@@ -173,14 +173,18 @@ int pick_span(int S, int KH, int P, int PS, int BS, int NC, int D, int esz, int 
 // Columns per partition launch. A (sequence, kv head) unit has M*G columns
 // (query token, query head); the MFMA kernel takes up to 16 per column tile
 // and one or two tiles (two for head sizes up to 128, where both tiles'
-// accumulators fit the register budget), so wider units run as several
-// launches over the same pages. The vector kernel (a single query token, at
-// most 4 heads) takes all G in one launch.
+// accumulators fit the register budget, and where the device's per-workgroup
+// LDS holds their parked state), so wider units run as several launches over
+// the same pages. The vector kernel (a single query token, at most 4 heads)
+// takes all G in one launch.
 #ifndef PA_MAX_TILES
 #define PA_MAX_TILES 2  // measurement builds: 1 keeps every launch to one column tile
 #endif
-int launch_columns(int G, int M, int D) {
-  const int width = PA_MAX_TILES > 1 && D <= 128 ? 32 : 16;
+int launch_columns(int G, int M, int D, int PS, int BS) {
+  bool two = PA_MAX_TILES > 1 && D <= 128;
+  if (two && BS > 0 && PS > 0 && PS / BS <= pa::kWaves * 64)  // (else rejected later)
+    two = pa::lds_layout(PS, BS, 32, D, 1).total <= max_lds_per_block();
+  const int width = two ? 32 : 16;
   const long long total = (long long)G * M;
   return total < width ? (int)total : width;
 }
@@ -417,7 +421,7 @@ int plan_partitions(float* tmp_output, float* exp_sums, float* max_logits, const
                     int* nc) {
   const int G = KH > 0 && H >= KH && H % KH == 0 ? H / KH : 1;  // (validated by check_partition)
   const long long total = (long long)G * (M > 0 ? M : 1);
-  *nc = launch_columns(G, M > 0 ? M : 1, D);
+  *nc = launch_columns(G, M > 0 ? M : 1, D, PS, BS);
   int rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                            block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt, M,
                            *nc, alibi, full);
@@ -753,7 +757,7 @@ int paged_attn_partition_span(int32_t num_seqs, int32_t num_heads, int32_t num_k
     return fail(PA_ERR_UNSUPPORTED, "unsupported head_size / block_size");
   if (PS <= 0 || PS % BS || PS / BS > pa::kWaves * 64 || P < 1)
     return fail(PA_ERR_SHAPE, "bad partition size / count");
-  const int G = H / KH, NC = launch_columns(G, 1, D);
+  const int G = H / KH, NC = launch_columns(G, 1, D, PS, BS);
   partition_fn fn = nullptr;
   bool vec = false;
   const int qdt = dt == PA_FP8_E4M3 ? PA_BF16 : dt;  // (an 8-bit cache's f16 query: same plan)

@@ -296,3 +296,19 @@ def test_ex_entries_reject_misaligned_alibi_and_lse():
     assert lib.paged_attn_decode_ex(*dec_args(None, None)[:10], 2, 2, 64, 2, 96,
                                     *dec_args(None, None)[15:]) \
         == binding.PA_ERR_UNSUPPORTED  # two query tokens, group 32, unknown head size
+
+
+def test_size_limits_are_rejected_before_launch():
+    """Shapes whose 32-bit offsets or launch grids would overflow fail on the host."""
+    # one launch's tmp_output rows past 2 GiB (32-bit buffer offsets): G * P * D * 4 bytes
+    assert part(H=8, KH=2, D=256, P=600_000) == binding.PA_ERR_UNSUPPORTED
+    assert "2 GiB" in pa.last_error()
+    # more than 2^31 - 1 workgroups
+    assert part(S=1 << 21, H=1, KH=1, D=64, P=2048) == binding.PA_ERR_UNSUPPORTED
+    assert "work units" in pa.last_error()
+    # more than 2^31 - 1 (query token, head) columns per kv head
+    assert part_mq(M=1 << 30) == binding.PA_ERR_UNSUPPORTED
+    assert "columns" in pa.last_error()
+    # more than 2^31 - 1 reduce rows
+    assert reduce(S=1 << 20, H=4096) == binding.PA_ERR_UNSUPPORTED
+    assert "rows" in pa.last_error()
