@@ -99,6 +99,17 @@ def _stream(t: torch.Tensor, stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _device(t: torch.Tensor):
+    """Make the tensors' device current for the call (the library launches on the
+    current device, on a stream of that device)."""
+    return torch.cuda.device(t.device)
+
+
+def _one_device(*tensors) -> None:
+    _need(len({t.device for t in tensors if t is not None}) == 1,
+          "all tensors of a call must be on one device")
+
+
 def _need(cond: bool, msg: str) -> None:
     if not cond:
         raise ValueError(msg)
@@ -148,11 +159,14 @@ def paged_attn_v2_partition(tmp_output, exp_sums, max_logits, query, key_cache, 
     """Phase 1: per-partition attention into tmp_output / exp_sums / max_logits."""
     S, H, KH, D, BS, B, MB = _kv_geometry(query, key_cache, value_cache, block_tables, seq_lens)
     P = _stats_geometry(tmp_output, exp_sums, max_logits, S, H, D)
-    rc = lib().paged_attn_v2_partition(
-        tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(), query.data_ptr(),
-        key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
-        seq_lens.data_ptr(), S, H, KH, D, BS, B, MB, P, partition_size, float(scale),
-        _DT[query.dtype], _stream(query, stream))
+    _one_device(tmp_output, exp_sums, max_logits, query, key_cache, value_cache, block_tables,
+                seq_lens)
+    with _device(query):
+        rc = lib().paged_attn_v2_partition(
+            tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(), query.data_ptr(),
+            key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+            seq_lens.data_ptr(), S, H, KH, D, BS, B, MB, P, partition_size, float(scale),
+            _DT[query.dtype], _stream(query, stream))
     _check("paged_attn_v2_partition", rc)
 
 
@@ -165,9 +179,11 @@ def paged_attn_v2_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, partit
     P = _stats_geometry(tmp_output, exp_sums, max_logits, S, H, D)
     _need(seq_lens.dtype == torch.int32 and seq_lens.is_cuda and seq_lens.shape == (S,),
           "seq_lens must be an int32 [S] device tensor")
-    rc = lib().paged_attn_v2_reduce(
-        out.data_ptr(), tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
-        seq_lens.data_ptr(), S, H, D, P, partition_size, _DT[out.dtype], _stream(out, stream))
+    _one_device(out, tmp_output, exp_sums, max_logits, seq_lens)
+    with _device(out):
+        rc = lib().paged_attn_v2_reduce(
+            out.data_ptr(), tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
+            seq_lens.data_ptr(), S, H, D, P, partition_size, _DT[out.dtype], _stream(out, stream))
     _check("paged_attn_v2_reduce", rc)
 
 
@@ -179,11 +195,14 @@ def paged_attn_decode(out, tmp_output, exp_sums, max_logits, query, key_cache, v
     P = _stats_geometry(tmp_output, exp_sums, max_logits, S, H, D)
     _need(out.dim() == 3 and tuple(out.shape) == (S, H, D) and out.dtype in _DT and out.is_cuda
           and out.is_contiguous(), "out must be a contiguous [S, H, D] device tensor")
-    rc = lib().paged_attn_decode(
-        out.data_ptr(), tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
-        query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
-        seq_lens.data_ptr(), S, H, KH, D, BS, B, MB, P, partition_size, float(scale),
-        _DT[query.dtype], _DT[out.dtype], _stream(query, stream))
+    _one_device(out, tmp_output, exp_sums, max_logits, query, key_cache, value_cache, block_tables,
+                seq_lens)
+    with _device(query):
+        rc = lib().paged_attn_decode(
+            out.data_ptr(), tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
+            query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+            seq_lens.data_ptr(), S, H, KH, D, BS, B, MB, P, partition_size, float(scale),
+            _DT[query.dtype], _DT[out.dtype], _stream(query, stream))
     _check("paged_attn_decode", rc)
 
 
@@ -194,11 +213,14 @@ def paged_attn_v2_partition_fp8(tmp_output, exp_sums, max_logits, query, key_cac
     S, H, KH, D, BS, B, MB = _kv_geometry(query, key_cache, value_cache, block_tables, seq_lens,
                                           fp8=True)
     P = _stats_geometry(tmp_output, exp_sums, max_logits, S, H, D)
-    rc = lib().paged_attn_v2_partition_fp8(
-        tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(), query.data_ptr(),
-        key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
-        seq_lens.data_ptr(), S, H, KH, D, BS, B, MB, P, partition_size, float(scale),
-        float(k_scale), float(v_scale), _DT[query.dtype], _stream(query, stream))
+    _one_device(tmp_output, exp_sums, max_logits, query, key_cache, value_cache, block_tables,
+                seq_lens)
+    with _device(query):
+        rc = lib().paged_attn_v2_partition_fp8(
+            tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(), query.data_ptr(),
+            key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+            seq_lens.data_ptr(), S, H, KH, D, BS, B, MB, P, partition_size, float(scale),
+            float(k_scale), float(v_scale), _DT[query.dtype], _stream(query, stream))
     _check("paged_attn_v2_partition_fp8", rc)
 
 
@@ -211,11 +233,15 @@ def paged_attn_decode_fp8(out, tmp_output, exp_sums, max_logits, query, key_cach
     P = _stats_geometry(tmp_output, exp_sums, max_logits, S, H, D)
     _need(out.dim() == 3 and tuple(out.shape) == (S, H, D) and out.dtype in _DT and out.is_cuda
           and out.is_contiguous(), "out must be a contiguous [S, H, D] device tensor")
-    rc = lib().paged_attn_decode_fp8(
-        out.data_ptr(), tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
-        query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
-        seq_lens.data_ptr(), S, H, KH, D, BS, B, MB, P, partition_size, float(scale),
-        float(k_scale), float(v_scale), _DT[query.dtype], _DT[out.dtype], _stream(query, stream))
+    _one_device(out, tmp_output, exp_sums, max_logits, query, key_cache, value_cache, block_tables,
+                seq_lens)
+    with _device(query):
+        rc = lib().paged_attn_decode_fp8(
+            out.data_ptr(), tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
+            query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+            seq_lens.data_ptr(), S, H, KH, D, BS, B, MB, P, partition_size, float(scale),
+            float(k_scale), float(v_scale), _DT[query.dtype], _DT[out.dtype],
+            _stream(query, stream))
     _check("paged_attn_decode_fp8", rc)
 
 
@@ -249,12 +275,15 @@ def paged_attn_v2_partition_mq(tmp_output, exp_sums, max_logits, query, key_cach
     S, M, H, KH, D, BS, B, MB = _mq_geometry(query, key_cache, value_cache, block_tables,
                                              seq_lens)
     P = _mq_stats_geometry(tmp_output, exp_sums, max_logits, S, M, H, D)
-    rc = lib().paged_attn_v2_partition_mq(
-        tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(), query.data_ptr(),
-        key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
-        seq_lens.data_ptr(), S, M, H, KH, D, BS, B, MB, P, partition_size, float(scale),
-        float(k_scale), float(v_scale), _DT[query.dtype], _CACHE_DT[key_cache.dtype],
-        _stream(query, stream))
+    _one_device(tmp_output, exp_sums, max_logits, query, key_cache, value_cache, block_tables,
+                seq_lens)
+    with _device(query):
+        rc = lib().paged_attn_v2_partition_mq(
+            tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(), query.data_ptr(),
+            key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+            seq_lens.data_ptr(), S, M, H, KH, D, BS, B, MB, P, partition_size, float(scale),
+            float(k_scale), float(v_scale), _DT[query.dtype], _CACHE_DT[key_cache.dtype],
+            _stream(query, stream))
     _check("paged_attn_v2_partition_mq", rc)
 
 
@@ -267,9 +296,12 @@ def paged_attn_v2_reduce_mq(out, tmp_output, exp_sums, max_logits, seq_lens, par
     P = _mq_stats_geometry(tmp_output, exp_sums, max_logits, S, M, H, D)
     _need(seq_lens.dtype == torch.int32 and seq_lens.is_cuda and seq_lens.shape == (S,),
           "seq_lens must be an int32 [S] device tensor")
-    rc = lib().paged_attn_v2_reduce_mq(
-        out.data_ptr(), tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
-        seq_lens.data_ptr(), S, M, H, D, P, partition_size, _DT[out.dtype], _stream(out, stream))
+    _one_device(out, tmp_output, exp_sums, max_logits, seq_lens)
+    with _device(out):
+        rc = lib().paged_attn_v2_reduce_mq(
+            out.data_ptr(), tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
+            seq_lens.data_ptr(), S, M, H, D, P, partition_size, _DT[out.dtype],
+            _stream(out, stream))
     _check("paged_attn_v2_reduce_mq", rc)
 
 
@@ -282,12 +314,15 @@ def paged_attn_decode_mq(out, tmp_output, exp_sums, max_logits, query, key_cache
     P = _mq_stats_geometry(tmp_output, exp_sums, max_logits, S, M, H, D)
     _need(out.dim() == 4 and tuple(out.shape) == (S, M, H, D) and out.dtype in _DT and
           out.is_cuda and out.is_contiguous(), "out must be a contiguous [S, M, H, D] tensor")
-    rc = lib().paged_attn_decode_mq(
-        out.data_ptr(), tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
-        query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
-        seq_lens.data_ptr(), S, M, H, KH, D, BS, B, MB, P, partition_size, float(scale),
-        float(k_scale), float(v_scale), _DT[query.dtype], _CACHE_DT[key_cache.dtype],
-        _DT[out.dtype], _stream(query, stream))
+    _one_device(out, tmp_output, exp_sums, max_logits, query, key_cache, value_cache, block_tables,
+                seq_lens)
+    with _device(query):
+        rc = lib().paged_attn_decode_mq(
+            out.data_ptr(), tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
+            query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+            seq_lens.data_ptr(), S, M, H, KH, D, BS, B, MB, P, partition_size, float(scale),
+            float(k_scale), float(v_scale), _DT[query.dtype], _CACHE_DT[key_cache.dtype],
+            _DT[out.dtype], _stream(query, stream))
     _check("paged_attn_decode_mq", rc)
 
 
@@ -315,10 +350,12 @@ def paged_attn_v2_reduce_lse(out, lse, tmp_output, exp_sums, max_logits, seq_len
     P = _mq_stats_geometry(t4, e4, m4, S, M, H, D)
     _need(seq_lens.dtype == torch.int32 and seq_lens.is_cuda and seq_lens.shape == (S,),
           "seq_lens must be an int32 [S] device tensor")
-    rc = lib().paged_attn_v2_reduce_lse(
-        out.data_ptr(), _lse_arg(lse, o4), tmp_output.data_ptr(), exp_sums.data_ptr(),
-        max_logits.data_ptr(), seq_lens.data_ptr(), S, M, H, D, P, partition_size,
-        _DT[out.dtype], _stream(out, stream))
+    _one_device(out, lse, tmp_output, exp_sums, max_logits, seq_lens)
+    with _device(out):
+        rc = lib().paged_attn_v2_reduce_lse(
+            out.data_ptr(), _lse_arg(lse, o4), tmp_output.data_ptr(), exp_sums.data_ptr(),
+            max_logits.data_ptr(), seq_lens.data_ptr(), S, M, H, D, P, partition_size,
+            _DT[out.dtype], _stream(out, stream))
     _check("paged_attn_v2_reduce_lse", rc)
 
 
@@ -335,12 +372,15 @@ def paged_attn_decode_lse(out, lse, tmp_output, exp_sums, max_logits, query, key
     P = _mq_stats_geometry(t4, e4, m4, S, M, H, D)
     _need(out.dim() == query.dim() and tuple(o4.shape) == (S, M, H, D) and out.dtype in _DT and
           out.is_cuda and out.is_contiguous(), "out must be a contiguous tensor shaped like query")
-    rc = lib().paged_attn_decode_lse(
-        out.data_ptr(), _lse_arg(lse, o4), tmp_output.data_ptr(), exp_sums.data_ptr(),
-        max_logits.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-        block_tables.data_ptr(), seq_lens.data_ptr(), S, M, H, KH, D, BS, B, MB, P,
-        partition_size, float(scale), float(k_scale), float(v_scale), _DT[query.dtype],
-        _CACHE_DT[key_cache.dtype], _DT[out.dtype], _stream(query, stream))
+    _one_device(out, lse, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                block_tables, seq_lens)
+    with _device(query):
+        rc = lib().paged_attn_decode_lse(
+            out.data_ptr(), _lse_arg(lse, o4), tmp_output.data_ptr(), exp_sums.data_ptr(),
+            max_logits.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+            block_tables.data_ptr(), seq_lens.data_ptr(), S, M, H, KH, D, BS, B, MB, P,
+            partition_size, float(scale), float(k_scale), float(v_scale), _DT[query.dtype],
+            _CACHE_DT[key_cache.dtype], _DT[out.dtype], _stream(query, stream))
     _check("paged_attn_decode_lse", rc)
 
 
@@ -364,12 +404,15 @@ def paged_attn_v2_partition_ex(tmp_output, exp_sums, max_logits, query, key_cach
     S, M, H, KH, D, BS, B, MB = _mq_geometry(q4, key_cache, value_cache, block_tables, seq_lens)
     t4, e4, m4 = _rows4(tmp_output, "tmp"), _rows4(exp_sums, "stats"), _rows4(max_logits, "stats")
     P = _mq_stats_geometry(t4, e4, m4, S, M, H, D)
-    rc = lib().paged_attn_v2_partition_ex(
-        tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(), query.data_ptr(),
-        key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
-        seq_lens.data_ptr(), S, M, H, KH, D, BS, B, MB, P, partition_size, float(scale),
-        float(k_scale), float(v_scale), _slopes_arg(alibi_slopes, H), _DT[query.dtype],
-        _CACHE_DT[key_cache.dtype], _stream(query, stream))
+    _one_device(tmp_output, exp_sums, max_logits, query, key_cache, value_cache, block_tables,
+                seq_lens, alibi_slopes)
+    with _device(query):
+        rc = lib().paged_attn_v2_partition_ex(
+            tmp_output.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(), query.data_ptr(),
+            key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+            seq_lens.data_ptr(), S, M, H, KH, D, BS, B, MB, P, partition_size, float(scale),
+            float(k_scale), float(v_scale), _slopes_arg(alibi_slopes, H), _DT[query.dtype],
+            _CACHE_DT[key_cache.dtype], _stream(query, stream))
     _check("paged_attn_v2_partition_ex", rc)
 
 
@@ -388,13 +431,16 @@ def paged_attn_decode_ex(out, tmp_output, exp_sums, max_logits, query, key_cache
           out.dtype in _DT and out.is_cuda and out.is_contiguous(),
           "out must be a contiguous tensor shaped like query")
     lse_ptr = _lse_arg(lse, _rows4(out, "out")) if lse is not None else None
-    rc = lib().paged_attn_decode_ex(
-        out.data_ptr(), lse_ptr, tmp_output.data_ptr(), exp_sums.data_ptr(),
-        max_logits.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-        block_tables.data_ptr(), seq_lens.data_ptr(), S, M, H, KH, D, BS, B, MB, P,
-        partition_size, float(scale), float(k_scale), float(v_scale),
-        _slopes_arg(alibi_slopes, H), _DT[query.dtype], _CACHE_DT[key_cache.dtype],
-        _DT[out.dtype], _stream(query, stream))
+    _one_device(out, lse, tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                block_tables, seq_lens, alibi_slopes)
+    with _device(query):
+        rc = lib().paged_attn_decode_ex(
+            out.data_ptr(), lse_ptr, tmp_output.data_ptr(), exp_sums.data_ptr(),
+            max_logits.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+            block_tables.data_ptr(), seq_lens.data_ptr(), S, M, H, KH, D, BS, B, MB, P,
+            partition_size, float(scale), float(k_scale), float(v_scale),
+            _slopes_arg(alibi_slopes, H), _DT[query.dtype], _CACHE_DT[key_cache.dtype],
+            _DT[out.dtype], _stream(query, stream))
     _check("paged_attn_decode_ex", rc)
 
 
@@ -413,10 +459,12 @@ def paged_attn_merge_states(out, out_lse, a, lse_a, b, lse_b, stream=None) -> No
         _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
     D = a.shape[-1]
     rows = a.numel() // D if D else 0
-    rc = lib().paged_attn_merge_states(
-        out.data_ptr(), out_lse.data_ptr() if out_lse is not None else None, a.data_ptr(),
-        lse_a.data_ptr(), b.data_ptr(), lse_b.data_ptr(), rows, D, _DT[a.dtype],
-        _stream(a, stream))
+    _one_device(out, out_lse, a, lse_a, b, lse_b)
+    with _device(a):
+        rc = lib().paged_attn_merge_states(
+            out.data_ptr(), out_lse.data_ptr() if out_lse is not None else None, a.data_ptr(),
+            lse_a.data_ptr(), b.data_ptr(), lse_b.data_ptr(), rows, D, _DT[a.dtype],
+            _stream(a, stream))
     _check("paged_attn_merge_states", rc)
 
 
