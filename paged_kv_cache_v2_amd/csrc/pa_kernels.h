@@ -71,6 +71,9 @@ namespace pa {
 #else
 #define PA_OCCUPANCY
 #endif
+#ifndef PA_STEADY
+#define PA_STEADY 1          // pipeline: branch-free steady-state rounds before the guarded drain
+#endif
 #ifndef PA_PIN_PREFETCH
 #define PA_PIN_PREFETCH 1    // scheduling barrier between prefetch issue and compute
 #endif
@@ -105,7 +108,23 @@ __device__ __forceinline__ void pipeline(int n, Buf (&buf)[PF + 1], Fetch&& fetc
 #pragma unroll
   for (int b = 0; b < PF; ++b)
     if (b < n) fetch(b, buf[b]);
-  for (int t0 = 0; t0 < n; t0 += NB) {
+  int t0 = 0;
+#if PA_STEADY
+  // Steady state: every fetch of the round is in range, so none sits under a
+  // branch (a conditional fetch joins its registers with the old contents,
+  // and the copies that join needs wait for the loads just issued).
+  for (; PF > 0 && t0 + NB + PF <= n; t0 += NB) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      fetch(t0 + b + PF, buf[(b + PF) % NB]);
+#if PA_PIN_PREFETCH
+      __builtin_amdgcn_sched_barrier(0);
+#endif
+      process(t0 + b, buf[b]);
+    }
+  }
+#endif
+  for (; t0 < n; t0 += NB) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int t = t0 + b;
