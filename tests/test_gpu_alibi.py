@@ -149,11 +149,13 @@ def test_zero_slopes_give_the_plain_bits(label):
     assert torch.equal(a["tmp"][valid].view(torch.int32), b["tmp"][valid].view(torch.int32))
 
 
-def test_alibi_full_size_mha_sampled():
+@pytest.mark.parametrize("name", ["mha_f16_d128", "gqa_bf16_g4"])
+def test_alibi_full_size_sampled(name):
     """The full-size MHA f16 batch (64 sequences, 32 heads, head size 128,
-    lengths 512..2048) with the paper's slopes, at its configured partition
-    size; sampled sequences against the oracle, properties everywhere."""
-    name = "mha_f16_d128"
+    lengths 512..2048; the vector kernel) and GQA bf16 batch (128 sequences,
+    32 / 8 heads, lengths 1..4096; the MFMA kernel) with the paper's slopes,
+    at their configured partition size; sampled sequences against the oracle,
+    properties everywhere."""
     cfg = W.CONFIGS[name]
     inp = W.make_inputs(cfg, seed=W.workload_seed(name))
     d = U.to_device(inp)

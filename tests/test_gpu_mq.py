@@ -168,3 +168,45 @@ def test_multi_token_rejects_fp32_query():
     d = U.to_device(W.make_inputs(cfg, seed=1, lens=[10, 20]))
     with pytest.raises(RuntimeError):
         run_mq(d, 64, 1)
+
+
+_FULL = {}
+
+
+@pytest.mark.parametrize("name", W.MQ_ORDER)
+@pytest.mark.parametrize("ps", ["config", "default"])
+def test_multi_token_full_size_sampled(name, ps):
+    """The multi-token workloads at full size, in the launch configurations
+    bench.py times (the configured partition size through the two calls, the
+    recommended one through paged_attn_decode_mq): sampled sequences against
+    the oracle, properties at every row."""
+    cfg = W.CONFIGS[name]
+    if name not in _FULL:
+        _FULL.clear()
+        inp = W.make_inputs(cfg, seed=W.workload_seed(name))
+        _FULL[name] = (inp, U.to_device(inp))
+    inp, d = _FULL[name]
+    sl = inp["seq_lens"].numpy()
+    S, M = len(sl), cfg.num_queries
+    # the longest and shortest sequence and one more (one if all lengths are equal)
+    seqs = sorted({int(np.argmax(sl)), int(np.argmin(sl)), 1 % S}) if sl.min() < sl.max() else [0]
+    if ps == "config":
+        PS, P = cfg.partition_size, cfg.max_num_partitions
+    else:
+        PS = pa.default_partition_size(cfg.head_size, cfg.block_size, W.DTYPES[cfg.dtype],
+                                       cfg.group)
+        P = max(1, -(-cfg.max_len // PS))
+    U.note(f"multi-token full {name} ps={PS} seqs={seqs}")
+    res = run_mq(d, PS, P, split=(ps == "config"))
+    assert torch.isfinite(res["out"]).all()
+    a = (inp["query"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
+         inp["seq_lens"], inp["scale"])
+    ref = oracle.attention(*a, seqs=seqs)
+    U.assert_close(f"mq full {name}", res["out"][seqs].float(), ref[seqs])
+    for s in range(S):
+        for m in range(M):
+            n = -(-W.causal_len(int(sl[s]), M, m) // PS)
+            assert torch.all(res["ml"][s, m, :, n:] == -math.inf), (s, m)
+            assert torch.all(res["es"][s, m, :, n:] == 0), (s, m)
+            assert torch.isfinite(res["ml"][s, m, :, :n]).all(), (s, m)
+            assert torch.all(res["es"][s, m, :, :n] >= 1), (s, m)
