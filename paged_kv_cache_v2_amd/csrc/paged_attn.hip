@@ -144,8 +144,13 @@ constexpr long long kSpanBytes = 512 * 1024;
 // 16-bit GQA (MFMA kernel, two workgroups per CU, so the ranking's extra
 // round trip is poorly hidden) 186.8 -> 192.1, and uniform lengths lose
 // ~1 % (nothing to reorder). So it is taken for 8-bit caches and the vector
-// kernel only.
+// kernel, and for the 16-bit MFMA kernel only where a unit reads at least
+// kLptMinUnitBytes of K+V: there a late long unit costs more than every
+// workgroup's ranking (GQA bf16 with 2048-token units 184.7 -> 176.7 us, and
+// with 4 query tokens 209.0 -> 196.2; uniform long context 1 % slower;
+// 1024-token units of the ragged GQA batch 189.6 -> 195.5, so not there).
 constexpr int kLptMaxPairs = 4096;
+constexpr long long kLptMinUnitBytes = 1 << 20;
 // Upper bound on the LDS of a span's parked state (see span_lds_cap): 80 KiB
 // is two workgroups per CU, what the 16-bit MFMA kernel's registers allow at
 // head size 128. It admits two-partition spans for 16-column units there (66
@@ -310,7 +315,9 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   plan->fn = fn;
   plan->lds_bytes = pa::lds_layout(PS, BS, NC, D, span).total;
   const long long pairs = (long long)S * ((P + span - 1) / span);
-  plan->lpt = PA_LPT && pairs <= kLptMaxPairs && (vec || kvdt == PA_FP8_E4M3 || PA_LPT == 2);
+  const long long unit_bytes = (long long)span * PS * D * elem_size(kvdt) * 2;
+  plan->lpt = PA_LPT && pairs <= kLptMaxPairs &&
+              (vec || kvdt == PA_FP8_E4M3 || unit_bytes >= kLptMinUnitBytes || PA_LPT == 2);
   if (plan->lpt) {
     const int ord = pa::lpt_lds_bytes(S, P, PS, BS, span);
     if (ord > lds_limit) plan->lpt = 0;
