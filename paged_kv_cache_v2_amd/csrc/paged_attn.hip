@@ -115,14 +115,18 @@ struct Plan {
 #define PA_SPAN 0  // >0: force this many partitions per workgroup (measurement builds)
 #endif
 
-// Consecutive partitions per workgroup. A span of 2 amortises each
-// workgroup's prologue and epilogue and retires empty partitions together with
-// used ones (measured: GQA bf16 G=4, 512-token partitions, ~1.5 % faster; other
-// shapes neutral). It is taken only while the grid keeps at least kMinGrid
-// workgroups and a full span reads at most kSpanBytes of K+V: longer units
-// leave a tail of few, slow workgroups at the end of the launch (2048-token
-// spans measured ~6 % slower). The span's block-table slice must fit the
-// 256-thread hoist and its parked state the LDS.
+// Consecutive partitions per workgroup (1, 2 or 4). A longer span amortises
+// each workgroup's prologue and epilogue and retires empty partitions
+// together with used ones. It is taken only while the grid keeps at least
+// kMinGrid workgroups and a full span reads at most kSpanBytes of K+V; units
+// of that size take the largest-first order (see kLptMinUnitBytes), which
+// keeps their tail short. Measured against the earlier limit of two
+// partitions and 512 KiB (512-token partitions): GQA bf16 189.5 -> 185.0 us,
+// GQA fp8 94.6 -> 87.7, ALiBi GQA 190.9 -> 185.7, wide heads 506.8 -> 502.2,
+// MHA -0.5 %, long context and the multi-token windows unchanged (their grids
+// or LDS keep shorter spans); at 1024-token partitions GQA 180.8 -> 178.0.
+// The span's block-table slice must fit the 256-thread hoist and its parked
+// state the LDS.
 constexpr long long kMinGrid = 2048;
 // tmp_output store policy: device-scope stores when rows have at least
 // kThroughMinPartitions partitions, or a unit writes at least
@@ -133,7 +137,7 @@ constexpr long long kMinGrid = 2048;
 // PS=512, 2.5 % slower at PS=1024 with device-scope stores).
 constexpr int kThroughMinPartitions = 16;
 constexpr int kThroughMinColumns = 16;
-constexpr long long kSpanBytes = 512 * 1024;
+constexpr long long kSpanBytes = 1 << 20;
 #ifndef PA_LPT
 #define PA_LPT 1  // measurement builds: 0 index order everywhere, 2 largest-first everywhere
 #endif

@@ -1,11 +1,11 @@
-"""Workgroups that span two partitions, and the multi-wavefront reduce.
+"""Workgroups that span several partitions, and the multi-wavefront reduce.
 
-A partition workgroup may own two consecutive partitions of one (sequence, kv
-head); each partition is still computed and stored on its own, so every
-intermediate must match the oracle exactly as for one partition per
-workgroup. The shapes below are chosen so that the launch plan takes the
-two-partition span (asserted through paged_attn_partition_span) on every
-kernel family, with odd partition counts (a last span of one partition),
+A partition workgroup may own two or four consecutive partitions of one
+(sequence, kv head); each partition is still computed and stored on its own,
+so every intermediate must match the oracle exactly as for one partition per
+workgroup. The shapes below are chosen so that the launch plan takes spans of
+two and of four (asserted through paged_attn_partition_span) on every kernel
+family, with partition counts that leave a shorter last span,
 partitions that are not a multiple of four pages (wavefronts cross a
 partition edge between two of their pages), and sequence lengths at every
 span edge. The reduce cases cover one, two and four wavefronts per row and
@@ -31,25 +31,29 @@ def built():
 
 def span_lens(S, BS, PS, P, seed):
     edges = [0, 1, BS - 1, BS, PS - 1, PS, PS + 1, 2 * PS - 1, 2 * PS, 2 * PS + 1, 3 * PS,
-             P * PS - 1, P * PS]
+             4 * PS - 1, 4 * PS, 4 * PS + 1, P * PS - 1, P * PS]
     edges = [e for e in edges if 0 <= e <= P * PS]
     rng = np.random.default_rng(seed)
     rest = rng.integers(0, P * PS + 1, size=max(0, S - len(edges))).tolist()
     return (edges + rest)[:S]
 
 
-# dtype, H, KH, D, BS, PS, P, S
+# dtype, H, KH, D, BS, PS, P, S, span the plan takes
 SPAN_CASES = [
-    ("bf16", 32, 8, 128, 16, 64, 5, 104),   # MFMA G=4, odd P: last span has one partition
-    ("bf16", 32, 8, 128, 16, 48, 6, 96),    # MFMA G=4, 3 pages per partition
-    ("bf16", 64, 8, 128, 16, 64, 8, 64),    # MFMA G=8
-    ("bf16", 32, 2, 128, 16, 64, 8, 256),   # MFMA G=16: 66 KiB of parked state per span
-    ("f16", 32, 32, 128, 16, 64, 8, 32),    # vector G=1
-    ("bf16", 16, 8, 64, 32, 64, 4, 256),    # vector G=2, D=64, BS=32
-    ("f32", 8, 8, 64, 16, 64, 4, 128),      # vector fp32
-    ("f16", 16, 16, 256, 32, 64, 4, 64),    # vector D=256, BS=32
-    ("fp8", 32, 8, 128, 16, 64, 5, 104),    # MFMA, 8-bit cache, odd P (largest-first order)
-    ("fp8", 16, 16, 128, 16, 64, 5, 104),   # vector, 8-bit cache, odd P (largest-first order)
+    ("bf16", 32, 8, 128, 16, 64, 5, 104, 2),   # MFMA G=4, odd P: last span has one partition
+    ("bf16", 32, 8, 128, 16, 48, 6, 96, 2),    # MFMA G=4, 3 pages per partition
+    ("bf16", 64, 8, 128, 16, 64, 8, 64, 2),    # MFMA G=8
+    ("bf16", 32, 2, 128, 16, 64, 8, 256, 2),   # MFMA G=16: 66 KiB of parked state per span
+    ("bf16", 32, 8, 128, 16, 64, 5, 128, 4),   # MFMA G=4, spans of 4 + 1 partitions
+    ("bf16", 32, 8, 128, 16, 48, 7, 128, 4),   # MFMA, 3 pages per partition, spans of 4 + 3
+    ("f16", 32, 32, 128, 16, 64, 8, 32, 4),    # vector G=1
+    ("bf16", 16, 8, 64, 32, 64, 4, 256, 4),    # vector G=2, D=64, BS=32
+    ("f32", 8, 8, 64, 16, 64, 4, 128, 2),      # vector fp32
+    ("f32", 8, 8, 64, 16, 64, 6, 256, 4),      # vector fp32, spans of 4 + 2
+    ("f16", 16, 16, 256, 32, 64, 4, 64, 2),    # vector D=256, BS=32
+    ("fp8", 32, 8, 128, 16, 64, 5, 104, 2),    # MFMA, 8-bit cache, odd P (largest-first order)
+    ("fp8", 32, 8, 128, 16, 64, 6, 128, 4),    # MFMA, 8-bit cache, spans of 4 + 2
+    ("fp8", 16, 16, 128, 16, 64, 5, 104, 4),   # vector, 8-bit cache, spans of 4 + 1
 ]
 
 
@@ -62,10 +66,10 @@ def case_config(name, dtype, H, KH, D, BS, PS, P, S):
 
 @pytest.mark.parametrize("c", SPAN_CASES, ids=lambda c: "_".join(map(str, c)))
 @pytest.mark.parametrize("split", [False, True], ids=["decode", "split"])
-def test_two_partition_span(c, split):
-    dtype, H, KH, D, BS, PS, P, S = c
+def test_multi_partition_span(c, split):
+    dtype, H, KH, D, BS, PS, P, S, C = c
     span = pa.partition_span(S, H, KH, D, BS, P, PS, W.DTYPES[dtype])
-    assert span == 2, f"plan chose span {span}; the case no longer exercises two-partition spans"
+    assert span == C, f"plan chose span {span}; the case no longer exercises spans of {C}"
     cfg = case_config(f"span_{dtype}", dtype, H, KH, D, BS, PS, P, S)
     lens = span_lens(S, BS, PS, P, seed=S + P)
     inp = W.make_inputs(cfg, seed=41, lens=lens, extra_blocks=3)
@@ -107,7 +111,7 @@ def test_span_plan_keeps_occupancy():
     args = (256, 32, 2, 128, 16, 8, 512)  # G = 16: one full column tile
     assert pa.partition_span(*args, torch.bfloat16) == 2
     assert pa.partition_span(*args, torch.float8_e4m3fn) == 1
-    assert pa.partition_span(256, 32, 8, 128, 16, 8, 512, torch.float8_e4m3fn) == 2  # G = 4
+    assert pa.partition_span(256, 32, 8, 128, 16, 8, 512, torch.float8_e4m3fn) == 4  # G = 4
 
 
 def test_span_results_match_single_partition_workgroups():
