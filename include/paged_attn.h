@@ -356,7 +356,7 @@ PA_API int paged_attn_default_partition_size(int32_t head_size, int32_t block_si
 
 /* Launch plan inspection: how many consecutive partitions of one (sequence,
  * kv head) a workgroup of paged_attn_v2_partition / paged_attn_decode handles
- * for these sizes (1, 2 or 4). Results do not depend on it (each partition is
+ * for these sizes (1, 2, 4 or 8). Results do not depend on it (each partition is
  * computed and stored on its own); it only groups work. Host-side, no device
  * work; returns a PA_ERR_* code for arguments the launchers would reject on
  * shape or support grounds. */

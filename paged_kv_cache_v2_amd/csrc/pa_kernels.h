@@ -205,7 +205,7 @@ struct PartitionArgs {
 // the query); the second is the same for the whole partition, cancels in its
 // exp sum and normalised output, and is added to its max logit at the store.
 
-constexpr int kMaxSpan = 4;
+constexpr int kMaxSpan = 8;
 
 // LDS carve-up shared by both partition kernels (byte offsets): the span's
 // block-table slice, then per (partition of the span, wavefront, head) the

@@ -115,19 +115,21 @@ struct Plan {
 #define PA_SPAN 0  // >0: force this many partitions per workgroup (measurement builds)
 #endif
 
-// Consecutive partitions per workgroup (1, 2 or 4). A longer span amortises
-// each workgroup's prologue and epilogue and retires empty partitions
-// together with used ones. It is taken only while the grid keeps at least
-// kMinGrid workgroups and a full span reads at most kSpanBytes of K+V; units
-// of that size take the largest-first order (see kLptMinUnitBytes), which
-// keeps their tail short. Measured against the earlier limit of two
-// partitions and 512 KiB (512-token partitions): GQA bf16 189.5 -> 185.0 us,
-// GQA fp8 94.6 -> 87.7, ALiBi GQA 190.9 -> 185.7, wide heads 506.8 -> 502.2,
-// MHA -0.5 %, long context and the multi-token windows unchanged (their grids
-// or LDS keep shorter spans); at 1024-token partitions GQA 180.8 -> 178.0.
-// The span's block-table slice must fit the 256-thread hoist and its parked
-// state the LDS.
-constexpr long long kMinGrid = 2048;
+// Consecutive partitions per workgroup (1, 2, 4 or 8). A longer span
+// amortises each workgroup's prologue and epilogue and retires empty
+// partitions together with used ones. It is taken only while the grid keeps
+// kMinRounds workgroups per resident slot (span_min_grid) and a full span
+// reads at most kSpanBytes of K+V; units of 1 MiB or more take the
+// largest-first order (see kLptMinUnitBytes), which keeps their tail short.
+// Measured against two partitions and 512 KiB at most (512-token partitions):
+// up to four partitions and 1 MiB with a fixed floor of 2048 workgroups gave
+// GQA bf16 189.5 -> 185.0 us, GQA fp8 94.6 -> 87.7, ALiBi GQA 190.9 -> 185.7,
+// wide heads 506.8 -> 502.2, MHA -0.5 %, long context and the multi-token
+// windows unchanged; the floor of two rounds with eight partitions and 2 MiB
+// then GQA bf16 185.8 -> 182.2 and ALiBi GQA 186.8 -> 183.2, the other
+// workloads within 0.3 %. The span's block-table slice must fit the 256-thread
+// hoist and its parked state the LDS.
+constexpr int kMinRounds = 2;
 // tmp_output store policy: device-scope stores when rows have at least
 // kThroughMinPartitions partitions, or a unit writes at least
 // kThroughMinColumns rows per partition (see store_row in pa_kernels.h).
@@ -137,7 +139,7 @@ constexpr long long kMinGrid = 2048;
 // PS=512, 2.5 % slower at PS=1024 with device-scope stores).
 constexpr int kThroughMinPartitions = 16;
 constexpr int kThroughMinColumns = 16;
-constexpr long long kSpanBytes = 1 << 20;
+constexpr long long kSpanBytes = 2 << 20;
 #ifndef PA_LPT
 #define PA_LPT 1  // measurement builds: 0 index order everywhere, 2 largest-first everywhere
 #endif
@@ -162,16 +164,17 @@ constexpr long long kLptMinUnitBytes = 1 << 20;
 // 220.6 us, long context with 2 tokens 192.8 -> 185.5 us).
 constexpr int kSpanLdsCap = 80 * 1024;
 
-int pick_span(int S, int KH, int P, int PS, int BS, int NC, int D, int esz, int lds_cap) {
+int pick_span(int S, int KH, int P, int PS, int BS, int NC, int D, int esz, int lds_cap,
+              long long min_grid) {
   int best = 1;
-  for (int c = 2; c <= pa::kMaxSpan; c *= 2) {
+  for (int c = 2; c <= pa::kMaxSpan && c / 2 < P; c *= 2) {  // (c / 2 >= P: P already covered)
     const long long grid = (long long)S * KH * ((P + c - 1) / c);
     const long long bytes = (long long)c * PS * D * esz * 2;
     const int lds = pa::lds_layout(PS, BS, NC, D, c).total;
     if (c * (PS / BS) > pa::kWaves * 64 || lds > lds_cap) break;
     if (PA_SPAN > 0) {
       if (c > PA_SPAN) break;
-    } else if (grid < kMinGrid || bytes > kSpanBytes) {
+    } else if (grid < min_grid || bytes > kSpanBytes) {
       break;
     }
     best = c;
@@ -254,6 +257,28 @@ int span_lds_cap(partition_fn fn, int lds_limit) {
   return std::min(std::min(per_wg, kSpanLdsCap), lds_limit);
 }
 
+// Compute units of the current device (256 if unknown).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v < 1)
+      v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Fewest workgroups a longer span may leave in the grid: two per resident
+// slot (the workgroups per CU that the kernel's registers allow, on every
+// CU), so that the largest-first order has a second round to balance.
+long long span_min_grid(partition_fn fn) {
+  return (long long)kMinRounds * wgs_per_cu(fn) * cu_count();
+}
+
 // Host checks shared by the partition entry points; fills `plan` for a launch
 // of NC columns. The query has dtype qdt; the caches kvdt (== qdt, or
 // PA_FP8_E4M3 with a 16-bit query).
@@ -313,7 +338,8 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   if (lds1 > lds_limit)
     return fail(PA_ERR_UNSUPPORTED, "needs %d bytes of LDS per workgroup, device allows %d", lds1,
                 lds_limit);
-  const int span = pick_span(S, KH, P, PS, BS, NC, D, elem_size(kvdt), span_lds_cap(fn, lds_limit));
+  const int span = pick_span(S, KH, P, PS, BS, NC, D, elem_size(kvdt), span_lds_cap(fn, lds_limit),
+                             span_min_grid(fn));
   const long long grid = (long long)S * KH * ((P + span - 1) / span);
   if (grid > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many work units");
   plan->fn = fn;
@@ -775,7 +801,8 @@ int paged_attn_partition_span(int32_t num_seqs, int32_t num_heads, int32_t num_k
   const int rc = select_kernel(qdt, dt, 1, G, NC, D, BS, 0, &fn, &vec);
   if (rc != PA_OK) return rc;
   const int lds_limit = max_lds_per_block();
-  return pick_span(S, KH, P, PS, BS, NC, D, elem_size(dt), span_lds_cap(fn, lds_limit));
+  return pick_span(S, KH, P, PS, BS, NC, D, elem_size(dt), span_lds_cap(fn, lds_limit),
+                   span_min_grid(fn));
 }
 
 int paged_attn_default_partition_size(int32_t head_size, int32_t block_size, int32_t kv_dtype,

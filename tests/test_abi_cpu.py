@@ -55,17 +55,19 @@ def test_abi_version_and_default_partition_size():
 
 
 def test_partition_span_plan():
-    """Spans of up to 4 partitions and 1 MiB of K+V while the grid keeps 2048
-    workgroups; 1 for small grids or long partitions."""
+    """Spans of up to 8 partitions and 2 MiB of K+V while the grid keeps two
+    workgroups per resident slot; 1 for small grids or long partitions. (On a
+    host without a device the plan assumes two workgroups per CU, 256 CUs and
+    the 64 KiB per-workgroup LDS fallback.)"""
     bf, f16, f32 = torch.bfloat16, torch.float16, torch.float32
-    assert pa.partition_span(128, 32, 8, 128, 16, 8, 512, bf) == 4     # GQA, 512-token partitions
-    assert pa.partition_span(8, 64, 8, 128, 16, 64, 512, bf) == 2      # long context: grid
-    assert pa.partition_span(128, 32, 8, 128, 16, 4, 1024, bf) == 2    # 2048 tokens, 1 MiB
-    assert pa.partition_span(128, 32, 8, 128, 16, 2, 2048, bf) == 1    # 4096 tokens too long
-    assert pa.partition_span(32, 16, 16, 256, 32, 16, 512, f16) == 2   # 1 MiB, D = 256
-    assert pa.partition_span(64, 32, 32, 128, 16, 4, 512, f16) == 4    # MHA
+    assert pa.partition_span(128, 32, 8, 128, 16, 8, 512, bf) == 4     # GQA (LDS caps 8 here)
+    assert pa.partition_span(8, 64, 8, 128, 16, 64, 512, bf) == 2      # long context: LDS
+    assert pa.partition_span(128, 32, 8, 128, 16, 4, 1024, bf) == 4    # 4096 tokens, 2 MiB
+    assert pa.partition_span(128, 32, 8, 128, 16, 2, 2048, bf) == 2
+    assert pa.partition_span(32, 16, 16, 256, 32, 16, 512, f16) == 4   # 2 MiB, D = 256
+    assert pa.partition_span(64, 32, 32, 128, 16, 4, 512, f16) == 4    # MHA: all 4 partitions
     assert pa.partition_span(2, 4, 4, 64, 16, 2, 64, f32) == 1         # small grid
-    assert pa.partition_span(128, 8, 8, 64, 16, 4, 64, f32) == 2
+    assert pa.partition_span(128, 8, 8, 64, 16, 4, 64, f32) == 4
     # 32 query heads per kv head: two column tiles, whose parked state for two
     # partitions would exceed the LDS cap
     assert pa.partition_span(128, 64, 2, 128, 16, 8, 512, bf) == 1
@@ -306,8 +308,8 @@ def test_size_limits_are_rejected_before_launch():
     # one launch's tmp_output rows past 2 GiB (32-bit buffer offsets): G * P * D * 4 bytes
     assert part(H=8, KH=2, D=256, P=600_000) == binding.PA_ERR_UNSUPPORTED
     assert "2 GiB" in pa.last_error()
-    # more than 2^31 - 1 workgroups (2^22 sequences x 512 spans of four partitions)
-    assert part(S=1 << 22, H=1, KH=1, D=64, P=2048) == binding.PA_ERR_UNSUPPORTED
+    # more than 2^31 - 1 workgroups (2^30 sequences, each at least one span)
+    assert part(S=1 << 30, H=1, KH=1, D=64, P=2048) == binding.PA_ERR_UNSUPPORTED
     assert "work units" in pa.last_error()
     # more than 2^31 - 1 (query token, head) columns per kv head
     assert part_mq(M=1 << 30) == binding.PA_ERR_UNSUPPORTED

@@ -1,11 +1,11 @@
 """Workgroups that span several partitions, and the multi-wavefront reduce.
 
-A partition workgroup may own two or four consecutive partitions of one
-(sequence, kv head); each partition is still computed and stored on its own,
-so every intermediate must match the oracle exactly as for one partition per
-workgroup. The shapes below are chosen so that the launch plan takes spans of
-two and of four (asserted through paged_attn_partition_span) on every kernel
-family, with partition counts that leave a shorter last span,
+A partition workgroup may own two, four or eight consecutive partitions of
+one (sequence, kv head); each partition is still computed and stored on its
+own, so every intermediate must match the oracle exactly as for one partition
+per workgroup. The shapes below are chosen so that the launch plan takes
+spans of two, four and eight (asserted through paged_attn_partition_span) on
+every kernel family, with partition counts that leave a shorter last span,
 partitions that are not a multiple of four pages (wavefronts cross a
 partition edge between two of their pages), and sequence lengths at every
 span edge. The reduce cases cover one, two and four wavefronts per row and
@@ -31,29 +31,30 @@ def built():
 
 def span_lens(S, BS, PS, P, seed):
     edges = [0, 1, BS - 1, BS, PS - 1, PS, PS + 1, 2 * PS - 1, 2 * PS, 2 * PS + 1, 3 * PS,
-             4 * PS - 1, 4 * PS, 4 * PS + 1, P * PS - 1, P * PS]
+             4 * PS - 1, 4 * PS, 4 * PS + 1, 8 * PS - 1, 8 * PS, 8 * PS + 1, P * PS - 1, P * PS]
     edges = [e for e in edges if 0 <= e <= P * PS]
     rng = np.random.default_rng(seed)
     rest = rng.integers(0, P * PS + 1, size=max(0, S - len(edges))).tolist()
     return (edges + rest)[:S]
 
 
-# dtype, H, KH, D, BS, PS, P, S, span the plan takes
+# dtype, H, KH, D, BS, PS, P, S, span the plan takes on MI355X
 SPAN_CASES = [
-    ("bf16", 32, 8, 128, 16, 64, 5, 104, 2),   # MFMA G=4, odd P: last span has one partition
-    ("bf16", 32, 8, 128, 16, 48, 6, 96, 2),    # MFMA G=4, 3 pages per partition
-    ("bf16", 64, 8, 128, 16, 64, 8, 64, 2),    # MFMA G=8
+    ("bf16", 32, 8, 128, 16, 64, 5, 104, 4),   # MFMA G=4, spans of 4 + 1 partitions
+    ("bf16", 32, 8, 128, 16, 48, 6, 96, 4),    # MFMA G=4, 3 pages per partition, 4 + 2
+    ("bf16", 64, 8, 128, 16, 64, 8, 64, 4),    # MFMA G=8
     ("bf16", 32, 2, 128, 16, 64, 8, 256, 2),   # MFMA G=16: 66 KiB of parked state per span
-    ("bf16", 32, 8, 128, 16, 64, 5, 128, 4),   # MFMA G=4, spans of 4 + 1 partitions
-    ("bf16", 32, 8, 128, 16, 48, 7, 128, 4),   # MFMA, 3 pages per partition, spans of 4 + 3
+    ("bf16", 32, 8, 128, 16, 64, 5, 128, 8),   # MFMA G=4, one span over all 5 partitions
+    ("bf16", 32, 8, 128, 16, 48, 9, 128, 8),   # MFMA, 3 pages per partition, spans of 8 + 1
     ("f16", 32, 32, 128, 16, 64, 8, 32, 4),    # vector G=1
-    ("bf16", 16, 8, 64, 32, 64, 4, 256, 4),    # vector G=2, D=64, BS=32
+    ("bf16", 16, 8, 64, 32, 64, 8, 256, 8),    # vector G=2, D=64, BS=32
     ("f32", 8, 8, 64, 16, 64, 4, 128, 2),      # vector fp32
-    ("f32", 8, 8, 64, 16, 64, 6, 256, 4),      # vector fp32, spans of 4 + 2
-    ("f16", 16, 16, 256, 32, 64, 4, 64, 2),    # vector D=256, BS=32
+    ("f32", 8, 8, 64, 16, 64, 6, 256, 8),      # vector fp32, one span over all 6 partitions
+    ("f16", 16, 16, 256, 32, 64, 4, 64, 4),    # vector D=256, BS=32
     ("fp8", 32, 8, 128, 16, 64, 5, 104, 2),    # MFMA, 8-bit cache, odd P (largest-first order)
     ("fp8", 32, 8, 128, 16, 64, 6, 128, 4),    # MFMA, 8-bit cache, spans of 4 + 2
     ("fp8", 16, 16, 128, 16, 64, 5, 104, 4),   # vector, 8-bit cache, spans of 4 + 1
+    ("fp8", 16, 16, 128, 16, 64, 8, 160, 8),   # vector, 8-bit cache, spans of 8
 ]
 
 
@@ -126,7 +127,7 @@ def test_span_results_match_single_partition_workgroups():
                          block_size=BS, partition_size=PS, dtype=dtype, len_lo=0, len_hi=P * PS)
     lens = span_lens(S_big, BS, PS, P, seed=5)
     inp = W.make_inputs(cfg, seed=47, lens=lens)
-    assert pa.partition_span(S_big, H, KH, D, BS, P, PS, torch.bfloat16) == 2
+    assert pa.partition_span(S_big, H, KH, D, BS, P, PS, torch.bfloat16) >= 2
     assert pa.partition_span(4, H, KH, D, BS, P, PS, torch.bfloat16) == 1
     U.note("span vs single-partition plan")
     big = U.run_decode(U.to_device(inp), split=True)
