@@ -85,8 +85,11 @@ def test_multi_partition_span(c, split):
 REDUCE_CASES = [
     ("bf16", 16, 4, 128, 16, 16, 130, [2080, 1030, 5]),  # 4 wavefronts per row, 3 chunks
     ("f16", 8, 8, 256, 16, 16, 70, [1120, 1000]),        # D=256: 4 wavefronts, 2 chunks
-    ("f32", 4, 4, 64, 16, 16, 20, [320, 17]),            # D=64: one wavefront per row
-    ("bf16", 32, 8, 128, 16, 16, 24, [384, 200, 0]),     # 2 wavefronts per row
+    ("f32", 4, 4, 64, 16, 16, 20, [320, 17]),            # D=64: 2 wavefronts per row
+    ("f32", 4, 4, 64, 16, 16, 12, [192, 17]),            # D=64: one wavefront per row
+    ("bf16", 32, 8, 128, 16, 16, 24, [384, 200, 0]),     # 4 wavefronts per row
+    ("bf16", 32, 8, 128, 16, 16, 12, [192, 100, 0]),     # 2 wavefronts per row
+    ("bf16", 32, 8, 128, 16, 16, 8, [128, 100, 0]),      # one wavefront per row
 ]
 
 
