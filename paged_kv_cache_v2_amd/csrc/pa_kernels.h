@@ -6,20 +6,23 @@
 // sentinels for empty partitions) and phase-2 reduce kernel (cross-partition
 // log-sum-exp combine). That page's kernel is organised for its own GPU:
 // one program per (sequence, query head, partition), K/V gathered per query
-// head. Here a workgroup owns one (sequence, kv head, partition) unit and all
-// G query heads of the group share every K/V fetch.
+// head. Here a workgroup owns one (sequence, kv head, span of partitions) unit
+// and all the query heads (and query tokens) of a launch's columns share every
+// K/V fetch.
 //
 // Work unit and layout
 //  - A workgroup owns a span of C consecutive partitions p0 .. p0+C-1 of one
-//    (sequence, kv head); blockIdx.x = (q * S + s) * KH + kh with p0 = q * C:
-//    kv head fastest, partition span slowest, so the last-dispatched
-//    workgroups are the cheap tail/empty partitions. Each partition is still
-//    computed and stored on its own (outputs do not depend on C); spanning
-//    only amortises the unit's prologue (length and block-table loads) and
-//    epilogue (LDS merge, stores) over C partitions, lets the stores of
-//    adjacent partitions (adjacent rows of tmp_output) go out together, and
-//    retires the empty partitions of a sequence in the same workgroup as its
-//    last used one.
+//    (sequence, kv head); blockIdx.x = r * KH + kh, and the (sequence, span)
+//    pair of rank r is either pair r in index order (q * S + s, p0 = q * C:
+//    partition span slowest, so the last-dispatched workgroups are the cheap
+//    tail/empty partitions) or, where the host asks for it, the pair of rank r
+//    by page count, largest first (lpt_pair). Each partition is still
+//    computed and stored on its own (outputs do not depend on C or the
+//    order); spanning amortises the unit's prologue (length and block-table
+//    loads) and epilogue (LDS merge, stores) over C partitions, lets the
+//    stores of adjacent partitions (adjacent rows of tmp_output) go out
+//    together, and retires the empty partitions of a sequence in the same
+//    workgroup as its last used one.
 //  - Partition p covers pages [p*PS/BS, ceil(min((p+1)*PS, L)/BS)); PS % BS
 //    == 0 so partition edges are page edges, and the used pages of a span are
 //    contiguous. The span's block-table slice is loaded together with the
