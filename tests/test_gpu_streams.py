@@ -7,7 +7,8 @@ to the host or synchronises, so
 * a cascade (two decode_lse calls over a page split, then merge_states) can
   be captured in a HIP graph: every replay, with eager work and
   synchronisation between replays and new query values written in place,
-  gives the bits of the same calls run eagerly.
+  gives the bits of the same calls run eagerly;
+* so can a call that the host splits into several column launches.
 """
 import pytest
 import torch
@@ -113,3 +114,60 @@ def test_cascade_in_a_graph_matches_eager():
     ref, ref_lse = oracle.attention_lse(full["query"], full["key_cache"], full["value_cache"],
                                         full["block_tables"], full["seq_lens"], full["scale"])
     U.assert_close("graph cascade out", e_bufs["out"].cpu(), ref)
+
+
+def test_multi_launch_call_in_a_graph_matches_eager():
+    """A call that the host splits into several column launches (8 query heads
+    x 6 query tokens = 48 columns per kv head: launches of 32 and 16) captured
+    in a graph: every replay, with the query rewritten in place between
+    replays, gives the bits of the same call run eagerly."""
+    lens = [0, 5, 300, 777]
+    cfg = W.DecodeConfig("graph_mq", num_seqs=len(lens), num_heads=32, num_kv_heads=4,
+                         head_size=128, block_size=16, partition_size=256, dtype="bf16",
+                         len_lo=0, len_hi=max(lens), num_queries=6)
+    inp = W.make_inputs(cfg, seed=65, lens=lens)
+    d = U.to_device(inp)
+    q = d["query"]
+    S, M, H, D = q.shape
+    P = cfg.max_num_partitions
+
+    def alloc():
+        return dict(out=torch.zeros(S, M, H, D, device=U.DEV),
+                    lse=torch.zeros(S, M, H, device=U.DEV),
+                    tmp=torch.zeros(S, M, H, P, D, device=U.DEV),
+                    es=torch.zeros(S, M, H, P, device=U.DEV),
+                    ml=torch.zeros(S, M, H, P, device=U.DEV))
+
+    def call(b):
+        pa.paged_attn_decode_ex(b["out"], b["tmp"], b["es"], b["ml"], q, d["key_cache"],
+                                d["value_cache"], d["block_tables"], d["seq_lens"], d["scale"],
+                                cfg.partition_size, lse=b["lse"])
+
+    g_bufs, e_bufs = alloc(), alloc()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm the path outside capture
+        call(g_bufs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    U.note("capture multi-launch call")
+    with torch.cuda.graph(graph):
+        call(g_bufs)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cpu").manual_seed(66)
+    for rep in range(3):
+        q.copy_(torch.randn(S, M, H, D, generator=gen).to(torch.bfloat16).to(U.DEV))
+        torch.cuda.synchronize()
+        U.note(f"replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        call(e_bufs)
+        torch.cuda.synchronize()
+        for k in ("out", "lse", "es", "ml"):
+            assert torch.equal(g_bufs[k].view(torch.int32), e_bufs[k].view(torch.int32)), (rep, k)
+    host = dict(inp)
+    host["query"] = q.cpu()
+    ref = oracle.attention(host["query"], host["key_cache"], host["value_cache"],
+                           host["block_tables"], host["seq_lens"], host["scale"])
+    U.assert_close("graph multi-launch out", e_bufs["out"].cpu(), ref)
