@@ -405,7 +405,7 @@ def main() -> int:
                     help="also run a 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU mode)",
               file=sys.stderr)
         return 2
