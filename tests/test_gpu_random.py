@@ -7,7 +7,9 @@ runs paged_attn_decode_ex; the output, the row log-sum-exp and every
 partition intermediate are compared with the oracle. Sizes stay small so the
 oracle finishes in well under a second per case. The cases from N_NARROW on
 draw 16-bit queries with more than 16 (query token, head) columns per kv
-head: two MFMA column tiles, or several launches over the pages.
+head: two MFMA column tiles, or several launches over the pages. The
+large-batch cases draw 150-320 short sequences, enough work units that the
+launch plan takes spans of several partitions and the largest-first order.
 """
 import math
 
@@ -116,3 +118,79 @@ def test_random_config(i):
             assert torch.all(gm[idx][:, n:] == -math.inf) and torch.all(ge[idx][:, n:] == 0)
     if out16:
         assert torch.equal(out.to(q.dtype).cpu().view(torch.int16), o16.cpu().view(torch.int16))
+
+
+N_BATCH_CASES = 12
+
+
+def draw_batch(i):
+    """Larger batches of short sequences: enough units that the launch plan
+    takes spans of 2, 4 or 8 partitions (and the largest-first order)."""
+    rng = np.random.default_rng(5000 + i)
+    kv = str(rng.choice(["f32", "f16", "bf16", "fp8"], p=[0.1, 0.3, 0.35, 0.25]))
+    q = kv if kv != "fp8" else str(rng.choice(["f16", "bf16"]))
+    D = int(rng.choice([64, 128, 256], p=[0.4, 0.45, 0.15]))
+    BS = int(rng.choice([16, 32]))
+    PS = BS * int(rng.choice([1, 2, 4]))
+    P = int(rng.integers(3, 10))
+    KH = int(rng.choice([2, 4, 8]))
+    if q == "f32":
+        G, M = int(rng.choice([1, 2, 4])), 1
+    else:
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        M = 1 if rng.random() < 0.5 else int(rng.integers(2, 4))
+    while G * KH > 64:
+        KH //= 2
+    S = int(rng.integers(150, 321))
+    lens = [int(x) for x in rng.integers(0, P * PS + 1, size=S)]
+    extra = dict(q_dtype=q, k_scale=float(rng.uniform(0.01, 0.05)),
+                 v_scale=float(rng.uniform(0.01, 0.05))) if kv == "fp8" else {}
+    cfg = W.DecodeConfig(f"batch{i}", num_seqs=S, num_heads=G * KH, num_kv_heads=KH,
+                         head_size=D, block_size=BS, partition_size=PS, dtype=kv, len_lo=0,
+                         len_hi=P * PS, num_queries=M, **extra)
+    return cfg, lens, rng.random() < 0.3
+
+
+@pytest.mark.parametrize("i", range(N_BATCH_CASES))
+def test_random_large_batch(i):
+    cfg, lens, alibi = draw_batch(i)
+    inp = W.make_inputs(cfg, seed=6000 + i, lens=lens, extra_blocks=2)
+    W.poison_unused(inp)
+    d = U.to_device(inp)
+    q = d["query"]
+    lead = tuple(q.shape[:-1])
+    P, PS, D, M = cfg.max_num_partitions, cfg.partition_size, cfg.head_size, cfg.num_queries
+    slopes = W.alibi_slopes(cfg.num_heads) if alibi else None
+    span = (pa.partition_span(cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, D, cfg.block_size,
+                              P, PS, W.DTYPES[cfg.dtype]) if M == 1 else None)
+    tmp = torch.full(lead + (P, D), float("nan"), device=U.DEV)
+    es = torch.full(lead + (P,), float("nan"), device=U.DEV)
+    ml = torch.full(lead + (P,), float("nan"), device=U.DEV)
+    out = torch.full(q.shape, float("nan"), device=U.DEV)
+    lse = torch.full(lead, float("nan"), device=U.DEV)
+    U.note(f"random batch {i}: {cfg} alibi={alibi} span={span}")
+    pa.paged_attn_decode_ex(out, tmp, es, ml, q, d["key_cache"], d["value_cache"],
+                            d["block_tables"], d["seq_lens"], d["scale"], PS,
+                            k_scale=inp["k_scale"], v_scale=inp["v_scale"],
+                            alibi_slopes=slopes.to(U.DEV) if alibi else None, lse=lse)
+    torch.cuda.synchronize()
+    a = (inp["query"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
+         inp["seq_lens"], inp["scale"])
+    sc = dict(k_scale=inp["k_scale"], v_scale=inp["v_scale"], alibi_slopes=slopes)
+    ref, ref_lse = oracle.attention_lse(*a, **sc)
+    U.assert_close(f"batch {i} out", out.cpu(), ref)
+    got_lse = lse.cpu().double().numpy()
+    assert np.array_equal(np.isneginf(got_lse), np.isneginf(ref_lse)), f"batch {i} lse -inf"
+    fin = ~np.isneginf(ref_lse)
+    U.assert_close(f"batch {i} lse", got_lse[fin], ref_lse[fin])
+    # statistics of every used partition at once; sentinels past each row's prefix
+    rtmp, res_, rml = oracle.partition_stats(*a, P, PS, **sc)
+    n = np.array([[-(-W.causal_len(L, M, m) // PS) for m in range(M)] for L in lens])
+    used = np.arange(P)[None, None, :] < n[:, :, None]          # [S, M, P]
+    used = used.reshape((len(lens),) + ((M,) if M > 1 else ()) + (1, P))
+    used = np.broadcast_to(used, tuple(es.shape))
+    ge, gm, gt = es.cpu().numpy(), ml.cpu().numpy(), tmp.cpu().numpy()
+    U.assert_close(f"batch {i} es", ge[used], np.asarray(res_)[used])
+    U.assert_close(f"batch {i} ml", gm[used], np.asarray(rml)[used])
+    U.assert_close(f"batch {i} tmp", gt[used], np.asarray(rtmp)[used])
+    assert np.all(gm[~used] == -np.inf) and np.all(ge[~used] == 0), f"batch {i} sentinels"
