@@ -11,7 +11,7 @@ Prints ONE JSON line:
                size; the line also carries the % of the 8 TB/s peak and
                query-heads x tokens / s.
   tuned      = the same batch through paged_attn_decode at the partition size
-               the library recommends (paged_attn_default_partition_size);
+               the library plans for it (paged_attn_plan_partition_size);
                same K+V bytes, same output up to rounding.
   roofline   = the dominant kernel (the partition kernel): algorithmic K+V
                bytes per launch / its average duration, measured with a HIP event
@@ -280,9 +280,10 @@ def run(args) -> dict:
     red_avg_s = sum(red_ms) / len(red_ms) / 1e3
 
     # The same batch through paged_attn_decode (one ABI call, partition +
-    # reduce) at the partition size the library recommends for this geometry;
+    # reduce) at the partition size the library plans for this batch;
     # out does not depend on the partition size beyond rounding.
-    PS_t = pa.default_partition_size(D, cfg.block_size, W.DTYPES[cfg.dtype], cfg.group)
+    PS_t = pa.plan_partition_size(cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, D,
+                                  cfg.block_size, cfg.max_len, W.DTYPES[cfg.dtype])
     P_t = max(1, -(-cfg.max_len // PS_t))
     tmp_t, es_t, ml_t = work(P_t)
 

@@ -354,6 +354,23 @@ PA_API int paged_attn_abi_version(void);
 PA_API int paged_attn_default_partition_size(int32_t head_size, int32_t block_size, int32_t kv_dtype,
                                              int32_t group);
 
+/* Partition size for a single-query batch: the longest of 4096 (2048 for
+ * 8-bit caches), 2048, 1024, 512, 256 and 128 tokens whose partitions give
+ * every workgroup the current device holds at once a work unit
+ * (num_seqs * num_kv_heads * ceil(max_seq_len / size) units), else 128; never
+ * longer than the shortest candidate >= max_seq_len. Large batches get long
+ * partitions (fewer per-partition outputs to write and reduce), small ones
+ * enough parallel work. The partition kernels take any sequence lengths with
+ * any size the launchers accept: this only picks a fast one. Host-side, no
+ * device work; reads the current device's properties (fixed fallbacks
+ * without a device). Returns the size (> 0), or PA_ERR_SHAPE / PA_ERR_UNSUPPORTED
+ * for sizes, dtypes or head/block sizes the launchers reject.
+ * max_num_partitions for the call is then ceil(max_seq_len / size). */
+PA_API int paged_attn_plan_partition_size(int32_t num_seqs, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_size,
+                                          int32_t block_size, int32_t max_seq_len,
+                                          int32_t kv_dtype);
+
 /* Launch plan inspection: how many consecutive partitions of one (sequence,
  * kv head) a workgroup of paged_attn_v2_partition / paged_attn_decode handles
  * for these sizes (1, 2, 4 or 8). Results do not depend on it (each partition is

@@ -31,6 +31,7 @@ _SIGS = {
     "paged_attn_abi_version": [],
     "paged_attn_default_partition_size": [_I32, _I32, _I32, _I32],
     "paged_attn_partition_span": [_I32] * 8,
+    "paged_attn_plan_partition_size": [_I32] * 7,
     "paged_attn_v2_partition_fp8": [_P] * 8 + [_I32] * 9 + [_F32, _F32, _F32, _I32, _P],
     "paged_attn_decode_fp8": [_P] * 9 + [_I32] * 9 + [_F32, _F32, _F32, _I32, _I32, _P],
     "paged_attn_v2_partition_mq": [_P] * 8 + [_I32] * 10 + [_F32, _F32, _F32, _I32, _I32, _P],
@@ -74,6 +75,16 @@ def default_partition_size(head_size: int, block_size: int, dtype: torch.dtype, 
     rc = lib().paged_attn_default_partition_size(head_size, block_size, _CACHE_DT[dtype], group)
     if rc < 0:
         raise RuntimeError(f"paged_attn_default_partition_size: {last_error()} (code {rc})")
+    return rc
+
+
+def plan_partition_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int,
+                        block_size: int, max_seq_len: int, dtype: torch.dtype) -> int:
+    """Partition size for this batch (see paged_attn_plan_partition_size)."""
+    rc = lib().paged_attn_plan_partition_size(num_seqs, num_heads, num_kv_heads, head_size,
+                                              block_size, max_seq_len, _CACHE_DT[dtype])
+    if rc < 0:
+        raise RuntimeError(f"paged_attn_plan_partition_size: {last_error()} (code {rc})")
     return rc
 
 

@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
     names = declared_symbols()
     for n in ("paged_attn_v2_partition", "paged_attn_v2_reduce", "paged_attn_decode",
               "paged_attn_last_error", "paged_attn_abi_version",
-              "paged_attn_default_partition_size", "paged_attn_partition_span"):
+              "paged_attn_default_partition_size", "paged_attn_partition_span",
+              "paged_attn_plan_partition_size"):
         assert n in names
 
 
@@ -52,6 +53,33 @@ def test_abi_version_and_default_partition_size():
         assert ps > 0 and ps % BS == 0
     with pytest.raises(RuntimeError):
         pa.default_partition_size(96, 16, torch.float16, 1)
+
+
+def test_plan_partition_size():
+    """The longest partition (4096 tokens, 2048 for 8-bit caches) whose units
+    (sequences x kv heads x partitions) fill every resident workgroup, no
+    longer than the longest sequence needs, at least 128. (On a host without a
+    device the plan assumes two workgroups per CU and 256 CUs: 512 slots.)"""
+    bf, f16, f32, f8 = torch.bfloat16, torch.float16, torch.float32, torch.float8_e4m3fn
+    plan = pa.plan_partition_size
+    assert plan(128, 32, 8, 128, 16, 4096, bf) == 4096     # 1024 units
+    assert plan(8, 64, 8, 128, 16, 32768, bf) == 4096      # 8 x 8 x 8 = 512 units
+    assert plan(128, 32, 8, 128, 16, 4096, f8) == 2048     # 8-bit caches stop at 2048
+    assert plan(1, 32, 8, 128, 16, 32768, bf) == 512       # 8 x 64 = 512 units
+    assert plan(1, 8, 1, 128, 16, 1 << 20, bf) == 2048     # 512 partitions of 2048
+    assert plan(1, 8, 1, 128, 16, 1000, bf) == 128         # too few units at any size
+    assert plan(64, 32, 32, 128, 16, 2048, f16) == 2048    # one partition covers 2048
+    assert plan(32, 16, 16, 256, 32, 8192, f16) == 4096
+    assert plan(2, 4, 4, 64, 16, 100, f32) == 128          # never below 128
+    assert plan(0, 4, 4, 64, 16, 0, f32) == 128
+    for args in [(4, 32, 8, 96, 16, 100, bf), (4, 32, 8, 128, 64, 100, bf),
+                 (4, 32, 4, 64, 16, 100, f32)]:                 # G = 8 with fp32
+        with pytest.raises(RuntimeError, match="unsupported|group"):
+            plan(*args)
+    for args in [(4, 30, 8, 128, 16, 100, bf), (-1, 32, 8, 128, 16, 100, bf),
+                 (4, 32, 8, 128, 16, -1, bf)]:
+        with pytest.raises(RuntimeError, match="bad sizes"):
+            plan(*args)
 
 
 def test_partition_span_plan():

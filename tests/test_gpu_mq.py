@@ -174,12 +174,12 @@ _FULL = {}
 
 
 @pytest.mark.parametrize("name", W.MQ_ORDER)
-@pytest.mark.parametrize("ps", ["config", "default"])
+@pytest.mark.parametrize("ps", ["config", "planned"])
 def test_multi_token_full_size_sampled(name, ps):
     """The multi-token workloads at full size, in the launch configurations
     bench.py times (the configured partition size through the two calls, the
-    recommended one through paged_attn_decode_mq): sampled sequences against
-    the oracle, properties at every row."""
+    size the library plans for the batch through paged_attn_decode_mq):
+    sampled sequences against the oracle, properties at every row."""
     cfg = W.CONFIGS[name]
     if name not in _FULL:
         _FULL.clear()
@@ -193,8 +193,9 @@ def test_multi_token_full_size_sampled(name, ps):
     if ps == "config":
         PS, P = cfg.partition_size, cfg.max_num_partitions
     else:
-        PS = pa.default_partition_size(cfg.head_size, cfg.block_size, W.DTYPES[cfg.dtype],
-                                       cfg.group)
+        PS = pa.plan_partition_size(cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads,
+                                    cfg.head_size, cfg.block_size, cfg.max_len,
+                                    W.DTYPES[cfg.dtype])
         P = max(1, -(-cfg.max_len // PS))
     U.note(f"multi-token full {name} ps={PS} seqs={seqs}")
     res = run_mq(d, PS, P, split=(ps == "config"))

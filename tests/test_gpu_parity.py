@@ -77,18 +77,19 @@ def sample_seqs(inp, k=3, seed=0):
 
 
 @pytest.mark.parametrize("name", ALL)
-@pytest.mark.parametrize("ps", ["config", "default"])
+@pytest.mark.parametrize("ps", ["config", "planned"])
 def test_parity_full_size_sampled(name, ps):
     """Full-size inputs, in the launch configurations bench.py times: the
     configured partition size through the two calls, and the library's
-    recommended partition size through paged_attn_decode."""
+    partition size the library plans for the batch through paged_attn_decode."""
     inp, d = full_inputs(name)
     cfg = W.CONFIGS[name]
     seqs = sample_seqs(inp, k=1 if name == "longctx_bf16_g8" else 3)
     PS = None
-    if ps == "default":
-        PS = pa.default_partition_size(cfg.head_size, cfg.block_size, W.DTYPES[cfg.dtype],
-                                       cfg.group)
+    if ps == "planned":
+        PS = pa.plan_partition_size(cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads,
+                                    cfg.head_size, cfg.block_size, cfg.max_len,
+                                    W.DTYPES[cfg.dtype])
     U.note(f"parity full {name} ps={ps} S={inp['num_seqs']} blocks={inp['num_blocks']} "
            f"seqs={seqs}")
     res = U.run_decode(d, PS=PS, P=max(1, -(-cfg.max_len // PS)) if PS else None,
