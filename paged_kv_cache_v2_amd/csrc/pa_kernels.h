@@ -1202,6 +1202,41 @@ __global__ void __launch_bounds__(kWaves * 64) reduce_kernel(ReduceArgs a) {
   }
 }
 
+// The same combine when every row has one partition (P = 1): its normalised
+// row is the output (weight e^(m - m) l / l = 1, so out = tmp exactly) and the
+// row's lse is m + ln l. The length, the statistics and the row are loaded
+// together, one round trip; 256 / D rows per wavefront (D / 4 lanes each, one
+// 16-byte piece per lane). A row with no keys (the partition left unwritten)
+// gives out = 0 and lse = -inf.
+template <int D, int ODT>
+__global__ void __launch_bounds__(kWaves * 64) reduce_one_kernel(ReduceArgs a) {
+  constexpr int LPR = D / 4;   // lanes per row
+  constexpr int R = 64 / LPR;  // rows per wavefront
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / LPR, c4 = lane % LPR;
+  const long long sh = ((long long)blockIdx.x * kWaves + wave) * R + sub;
+  if (sh >= (long long)a.S * a.M * a.H) return;
+  const int sm = (int)(sh / a.H);
+  const int s = sm / a.M, qm = sm - s * a.M;
+  const int L0 = a.sl[s];
+  const f32x4 v = *(const f32x4*)(a.tmp_out + sh * D + 4 * c4);
+  float m = 0.0f, l = 1.0f;
+  if (a.lse && c4 == 0) {
+    m = a.max_logits[sh];
+    l = a.exp_sums[sh];
+  }
+  const int L = min(L0, max(0, L0 - a.M + qm + 1));  // keys query token qm sees
+  const f32x4 acc = L > 0 ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+  if (a.lse && c4 == 0) a.lse[sh] = L > 0 ? m + __builtin_amdgcn_logf(l) * kLn2 : kNegInf;
+  const size_t o = (size_t)sh * D + 4 * c4;
+  if constexpr (ODT == DT_F32) {
+    *(f32x4*)((float*)a.out + o) = acc;
+  } else {
+    using Cd = codec<ODT>;
+    *(u32x2*)((uint16_t*)a.out + o) = u32x2{Cd::pack(acc[0], acc[1]), Cd::pack(acc[2], acc[3])};
+  }
+}
+
 // ---------------------------------------------------------------- merge states
 // Two attention results of the same rows over disjoint key sets, each with its
 // rows' log-sum-exps, merge into one: with Mx = max(la, lb), w = e^(l - Mx),

@@ -68,6 +68,16 @@ const reduce_fn kReduce[3][3] = {
      pa::reduce_kernel<256, pa::DT_BF16>},
 };
 
+// P = 1: [out dtype][D]
+const reduce_fn kReduceOne[3][3] = {
+    {pa::reduce_one_kernel<64, pa::DT_F32>, pa::reduce_one_kernel<128, pa::DT_F32>,
+     pa::reduce_one_kernel<256, pa::DT_F32>},
+    {pa::reduce_one_kernel<64, pa::DT_F16>, pa::reduce_one_kernel<128, pa::DT_F16>,
+     pa::reduce_one_kernel<256, pa::DT_F16>},
+    {pa::reduce_one_kernel<64, pa::DT_BF16>, pa::reduce_one_kernel<128, pa::DT_BF16>,
+     pa::reduce_one_kernel<256, pa::DT_BF16>},
+};
+
 // [dtype]
 const merge_fn kMerge[3] = {pa::merge_states_kernel<pa::DT_F32>,
                             pa::merge_states_kernel<pa::DT_F16>,
@@ -416,7 +426,7 @@ int check_reduce(void* out, const float* tmp_output, const float* exp_sums,
   if (!aligned16(out) || !aligned16(tmp_output))
     return fail(PA_ERR_ALIGN, "out and tmp_output must be 16-byte aligned");
   if ((long long)S * M * H > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many rows");
-  *fn = kReduce[odt][di];
+  *fn = P == 1 ? kReduceOne[odt][di] : kReduce[odt][di];
   return PA_OK;
 }
 
@@ -438,7 +448,8 @@ int launch_reduce(reduce_fn fn, void* out, float* lse, const float* tmp_output,
   a.M = M;
   a.WPI = pa::reduce_waves_per_row(P, D);
   const long long rows = (long long)S * M * H;
-  const int rows_per_block = pa::kWaves / a.WPI;
+  // (reduce_one_kernel for P = 1: 256 / D rows per wavefront)
+  const int rows_per_block = P == 1 ? pa::kWaves * (256 / D) : pa::kWaves / a.WPI;
   hipLaunchKernelGGL(fn, dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
                      dim3(pa::kWaves * 64), 0, stream, a);
   const hipError_t e = hipGetLastError();

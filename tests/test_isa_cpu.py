@@ -57,7 +57,7 @@ def spill_exempt(name):
 
 def test_hot_kernels_use_no_scratch(kernels):
     bad = {k: sum(o.startswith("scratch_") for o in ops(v)) for k, v in kernels.items()
-           if ("partition_" in k or "reduce_kernel" in k) and not spill_exempt(k)}
+           if ("partition_" in k or "reduce_kernel" in k or "reduce_one_kernel" in k) and not spill_exempt(k)}
     bad = {k: v for k, v in bad.items() if v}
     assert not bad, f"scratch traffic in {bad}"
 
