@@ -107,7 +107,11 @@ PA_API int paged_attn_v2_partition(float* tmp_output, float* exp_sums, float* ma
  * n = ceil(seq_lens[s] / PS) partitions the sequence uses:
  *   M = max_p max_logits, Z = sum_p exp(max_logits - M) * exp_sums,
  *   out[s][h] = sum_p exp(max_logits - M) * exp_sums / Z * tmp_output[s][h][p]
- * and out[s][h] = 0 when n == 0. Entries of partitions p >= n are not read.
+ * and out[s][h] = 0 when n == 0. Entries of partitions p >= n never affect
+ * the result (NaN there is fine); they are not read, except that with
+ * max_num_partitions == 1 each row's single entry is loaded together with its
+ * statistics (one round trip) and discarded when n == 0. With one partition
+ * the weight is exactly 1: out[s][h] is tmp_output[s][h][0], cast.
  *
  *   out          [S, H, D] in out_dtype (PA_F32, or the kv dtype: round to
  *                nearest even from the fp32 result), written

@@ -845,11 +845,14 @@ int paged_attn_plan_partition_size(int32_t num_seqs, int32_t num_heads, int32_t 
       select_kernel(qdt, dt, 1, G, launch_columns(G, 1, D, top, BS), D, BS, 0, &fn, &vec);
   if (rc != PA_OK) return rc;
   const long long slots = (long long)wgs_per_cu(fn) * cu_count();
-  // The longest candidate whose units fill every resident workgroup, else 128.
+  // The longest candidate whose units (S * KH * parts) fill every resident
+  // workgroup, else 128; compared as parts >= ceil(slots / (S * KH)), which
+  // cannot overflow.
+  const long long sk = (long long)S * KH;
   int ps = top;
   for (; ps > 128; ps /= 2) {
     const long long parts = L > ps ? (L + ps - 1) / ps : 1;
-    if ((long long)S * KH * parts >= slots) break;
+    if (sk > 0 && parts >= (slots + sk - 1) / sk) break;
   }
   return ps;
 }
