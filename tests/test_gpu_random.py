@@ -10,6 +10,7 @@ draw 16-bit queries with more than 16 (query token, head) columns per kv
 head: two MFMA column tiles, or several launches over the pages. The
 large-batch cases draw 150-320 short sequences, enough work units that the
 launch plan takes spans of several partitions and the largest-first order.
+The planned cases run at the partition size the library plans for the batch.
 """
 import math
 
@@ -194,3 +195,62 @@ def test_random_large_batch(i):
     U.assert_close(f"batch {i} ml", gm[used], np.asarray(rml)[used])
     U.assert_close(f"batch {i} tmp", gt[used], np.asarray(rtmp)[used])
     assert np.all(gm[~used] == -np.inf) and np.all(ge[~used] == 0), f"batch {i} sentinels"
+
+
+N_PLANNED = 8
+
+
+@pytest.mark.parametrize("i", range(N_PLANNED))
+def test_random_planned_partition_size(i):
+    """The partition size paged_attn_plan_partition_size picks for the batch
+    (one partition per row for the large batches of short sequences, several
+    for the small batches of long ones), through the one-call form: out and lse
+    against the oracle."""
+    if i < N_PLANNED // 2:
+        cfg, lens, alibi = draw_batch(i)
+    else:
+        rng = np.random.default_rng(7000 + i)
+        kv = str(rng.choice(["f16", "bf16", "fp8"]))
+        q = kv if kv != "fp8" else "bf16"
+        if i < N_PLANNED - 2:   # a few long sequences: many short partitions
+            KH, G = int(rng.choice([1, 2])), int(rng.choice([1, 4, 8]))
+            S, hi = int(rng.integers(1, 4)), 6000
+        else:                   # a dozen: a few partitions of 2048 or 4096 tokens
+            KH, G, S, hi = 8, 4, 12, 12000
+        lens = [int(x) for x in rng.integers(1, hi + 1, size=S)]
+        extra = dict(q_dtype=q, k_scale=0.03, v_scale=0.04) if kv == "fp8" else {}
+        cfg = W.DecodeConfig(f"planned{i}", num_seqs=S, num_heads=G * KH, num_kv_heads=KH,
+                             head_size=128, block_size=16, partition_size=128, dtype=kv,
+                             len_lo=0, len_hi=max(lens), **extra)
+        alibi = False
+    L = max(lens)
+    PS = pa.plan_partition_size(cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_size,
+                                cfg.block_size, L, W.DTYPES[cfg.dtype])
+    P = max(1, -(-L // PS))
+    inp = W.make_inputs(cfg, seed=8000 + i, lens=lens, extra_blocks=2)
+    W.poison_unused(inp)
+    d = U.to_device(inp)
+    q = d["query"]
+    lead = tuple(q.shape[:-1])
+    D = cfg.head_size
+    slopes = W.alibi_slopes(cfg.num_heads) if alibi else None
+    tmp = torch.full(lead + (P, D), float("nan"), device=U.DEV)
+    es = torch.full(lead + (P,), float("nan"), device=U.DEV)
+    ml = torch.full(lead + (P,), float("nan"), device=U.DEV)
+    out = torch.full(q.shape, float("nan"), device=U.DEV)
+    lse = torch.full(lead, float("nan"), device=U.DEV)
+    U.note(f"planned {i}: {cfg} PS={PS} P={P} alibi={alibi}")
+    pa.paged_attn_decode_ex(out, tmp, es, ml, q, d["key_cache"], d["value_cache"],
+                            d["block_tables"], d["seq_lens"], d["scale"], PS,
+                            k_scale=inp["k_scale"], v_scale=inp["v_scale"],
+                            alibi_slopes=slopes.to(U.DEV) if alibi else None, lse=lse)
+    torch.cuda.synchronize()
+    a = (inp["query"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
+         inp["seq_lens"], inp["scale"])
+    ref, ref_lse = oracle.attention_lse(*a, k_scale=inp["k_scale"], v_scale=inp["v_scale"],
+                                        alibi_slopes=slopes)
+    U.assert_close(f"planned {i} out", out.cpu(), ref)
+    got_lse = lse.cpu().double().numpy()
+    assert np.array_equal(np.isneginf(got_lse), np.isneginf(ref_lse)), f"planned {i} lse -inf"
+    fin = ~np.isneginf(ref_lse)
+    U.assert_close(f"planned {i} lse", got_lse[fin], ref_lse[fin])
