@@ -116,14 +116,16 @@ def test_cascade_in_a_graph_matches_eager():
     U.assert_close("graph cascade out", e_bufs["out"].cpu(), ref)
 
 
-def test_multi_launch_call_in_a_graph_matches_eager():
+@pytest.mark.parametrize("ps", [256, 1024], ids=["four_partitions", "one_partition"])
+def test_multi_launch_call_in_a_graph_matches_eager(ps):
     """A call that the host splits into several column launches (8 query heads
     x 6 query tokens = 48 columns per kv head: launches of 32 and 16) captured
     in a graph: every replay, with the query rewritten in place between
-    replays, gives the bits of the same call run eagerly."""
+    replays, gives the bits of the same call run eagerly. With 1024-token
+    partitions every row has one partition (the reduce's one-partition form)."""
     lens = [0, 5, 300, 777]
     cfg = W.DecodeConfig("graph_mq", num_seqs=len(lens), num_heads=32, num_kv_heads=4,
-                         head_size=128, block_size=16, partition_size=256, dtype="bf16",
+                         head_size=128, block_size=16, partition_size=ps, dtype="bf16",
                          len_lo=0, len_hi=max(lens), num_queries=6)
     inp = W.make_inputs(cfg, seed=65, lens=lens)
     d = U.to_device(inp)
@@ -151,7 +153,7 @@ def test_multi_launch_call_in_a_graph_matches_eager():
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
-    U.note("capture multi-launch call")
+    U.note(f"capture multi-launch call ps={ps}")
     with torch.cuda.graph(graph):
         call(g_bufs)
     torch.cuda.synchronize()
