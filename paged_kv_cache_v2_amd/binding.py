@@ -71,8 +71,14 @@ def abi_version() -> int:
     return lib().paged_attn_abi_version()
 
 
+def _cache_dt(dtype: torch.dtype) -> int:
+    _need(dtype in _CACHE_DT, f"cache dtype must be float32, float16, bfloat16 or "
+          f"float8_e4m3fn, got {dtype}")
+    return _CACHE_DT[dtype]
+
+
 def default_partition_size(head_size: int, block_size: int, dtype: torch.dtype, group: int) -> int:
-    rc = lib().paged_attn_default_partition_size(head_size, block_size, _CACHE_DT[dtype], group)
+    rc = lib().paged_attn_default_partition_size(head_size, block_size, _cache_dt(dtype), group)
     if rc < 0:
         raise RuntimeError(f"paged_attn_default_partition_size: {last_error()} (code {rc})")
     return rc
@@ -82,7 +88,7 @@ def plan_partition_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_s
                         block_size: int, max_seq_len: int, dtype: torch.dtype) -> int:
     """Partition size for this batch (see paged_attn_plan_partition_size)."""
     rc = lib().paged_attn_plan_partition_size(num_seqs, num_heads, num_kv_heads, head_size,
-                                              block_size, max_seq_len, _CACHE_DT[dtype])
+                                              block_size, max_seq_len, _cache_dt(dtype))
     if rc < 0:
         raise RuntimeError(f"paged_attn_plan_partition_size: {last_error()} (code {rc})")
     return rc
@@ -93,7 +99,7 @@ def partition_span(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: 
                    dtype: torch.dtype) -> int:
     """Partitions per workgroup the launchers use for these sizes (plan inspection)."""
     rc = lib().paged_attn_partition_span(num_seqs, num_heads, num_kv_heads, head_size, block_size,
-                                         max_num_partitions, partition_size, _CACHE_DT[dtype])
+                                         max_num_partitions, partition_size, _cache_dt(dtype))
     if rc < 0:
         raise RuntimeError(f"paged_attn_partition_span: {last_error()} (code {rc})")
     return rc

@@ -71,3 +71,12 @@ def test_multi_token_calls_check_their_ranks():
     with pytest.raises(ValueError):
         pa.paged_attn_decode_mq(t["out"], t["tmp"], t["es"], t["ml"], t["q"], t["kc"], t["vc"],
                                 t["bt"], t["sl"], 0.125, 64)
+
+
+def test_host_helpers_reject_unknown_dtypes():
+    with pytest.raises(ValueError, match="cache dtype"):
+        pa.plan_partition_size(4, 8, 2, 128, 16, 100, torch.int8)
+    with pytest.raises(ValueError, match="cache dtype"):
+        pa.default_partition_size(128, 16, torch.float64, 4)
+    with pytest.raises(ValueError, match="cache dtype"):
+        pa.partition_span(4, 8, 2, 128, 16, 1, 512, torch.int32)
