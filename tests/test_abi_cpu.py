@@ -82,6 +82,27 @@ def test_plan_partition_size():
             plan(*args)
 
 
+def test_planned_sizes_are_accepted_by_the_launch_plan():
+    """Every size the planner returns is one the launchers take: a multiple of
+    the block size, at most 256 pages, and a valid launch plan for
+    ceil(max_seq_len / size) partitions."""
+    dts = [torch.float32, torch.float16, torch.bfloat16, torch.float8_e4m3fn]
+    for S in (0, 1, 7, 128, 4096):
+        for H, KH in ((4, 4), (32, 8), (64, 1)):
+            for D in (64, 128, 256):
+                for BS in (16, 32):
+                    for L in (0, 1, 100, 4096, 100_000):
+                        for dt in dts:
+                            if dt == torch.float32 and H // KH > 4:
+                                continue
+                            ps = pa.plan_partition_size(S, H, KH, D, BS, L, dt)
+                            assert 128 <= ps <= 4096 and ps % BS == 0 and ps // BS <= 256
+                            assert ps <= 2048 or dt != torch.float8_e4m3fn
+                            P = max(1, -(-L // ps))
+                            span = pa.partition_span(S, H, KH, D, BS, P, ps, dt)
+                            assert span in (1, 2, 4, 8)
+
+
 def test_partition_span_plan():
     """Spans of up to 8 partitions and 2 MiB of K+V while the grid keeps two
     workgroups per resident slot; 1 for small grids or long partitions. (On a
