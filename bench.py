@@ -1,38 +1,44 @@
 #!/usr/bin/env python3
 """Benchmark of paged single-query decode attention (V2 split, GQA) on one MI355X.
 
-One step is the whole hot path over one batch: paged_attn_v2_partition then
-paged_attn_v2_reduce on one stream, inputs already resident in HBM. W warmup
-steps, then exactly K timed steps between two torch.cuda.synchronize() calls.
-Prints ONE JSON line:
+One step is the whole hot path over one batch: one paged_attn_decode call at
+the workload's configured partition size (512 tokens for the GQA batch),
+inputs already resident in HBM. Every 512-token partition is computed on its
+own and the partitions are combined with the log-sum-exp rule, inside the
+partition kernel where one workgroup holds all of a row's partitions (the GQA
+batch: no reduce launch, no per-partition rows), else by the reduce over the
+workgroups' span entries. W warmup steps, then exactly K timed steps between
+two torch.cuda.synchronize() calls. Prints ONE JSON line:
 
-  value      = algorithmic K+V bytes per step / step time (GB/s), the metric's
-               "achieved HBM GB/s", at the workload's configured partition
-               size; the line also carries the % of the 8 TB/s peak and
-               query-heads x tokens / s.
+  value      = algorithmic K+V bytes per step / step time (GB/s), steps back to
+               back; also as % of the 8 TB/s peak and query-heads x tokens / s.
+  flushed    = the protocol the metric is defined on: each call timed by its
+               own HIP event pair after a 512 MiB scratch write that evicts
+               the 256 MB Infinity Cache (outside the events); median and
+               p10 / p90 over the calls, as GB/s and % of peak.
+  roofline   = the decode call's kernels (the partition kernel, plus the reduce
+               when a row spans several workgroups): K+V bytes / their average
+               duration from a HIP event pair on the launch stream around every
+               call of a second pass of K steps; `traffic` = HBM bytes per call
+               from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary when
+               it was taken on the current kernel source (else null).
+  two_call   = the same batch through paged_attn_v2_partition + paged_attn_v2_reduce
+               (every partition's row stored, then reduced): step time, and the
+               two kernels' event-timed averages.
   tuned      = the same batch through paged_attn_decode at the partition size
-               the library plans for it (paged_attn_plan_partition_size);
-               same K+V bytes, same output up to rounding.
-  roofline   = the dominant kernel (the partition kernel): algorithmic K+V
-               bytes per launch / its average duration, measured with a HIP event
-               pair on the launch stream around every partition launch of a
-               second pass of the same K steps; `traffic` = HBM bytes per launch
-               from the committed
-               rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the
-               current kernel source (else null).
-  cpu_baseline = the fp64 oracle (partition stats + combine) timed on this
-               host's cores over the same workload: one warm run, then the
-               median of at least three timed runs (at least 10 s in all).
-  flushed    = the same two calls timed one by one with their own event
-               pairs after a 512 MiB scratch write (evicts the Infinity
-               Cache): median and p10 / p90 over 100 calls.
-  copy_context = a 1 GiB device-to-device copy's bandwidth (context for the
-               8 TB/s peak).
-  merge_states = paged_attn_merge_states timed with HIP events: on the
-               batch's own rows (two query-dtype states of every (sequence,
-               query token, head) row, as a cascade merges them) and on a
-               2^20-row stream that shows the kernel's bandwidth; bytes are
-               2 inputs + 1 output row plus 3 lse words per row.
+               the library plans for it (paged_attn_plan_partition_size).
+  workloads  = the same measurements (value, flushed, roofline, tuned) for the
+               other configurations named by --also (the long-context GQA batch
+               by default).
+  ceiling    = a read-only kernel that gathers the same K/V pages through the
+               same block tables with the same loads and computes nothing
+               (libpa_ceiling.so): the page-gather read bandwidth of this chip.
+  copy_context = a 1 GiB device-to-device copy's bandwidth.
+  merge_states = paged_attn_merge_states on the batch's own rows and on a
+               2^20-row stream.
+  cpu_baseline = the fp64 oracle (partition statistics + combine) timed on this
+               host's cores over the whole headline batch: one warm run, then
+               the median of at least three timed runs (at least 10 s in all).
 
 Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -53,6 +59,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "decode attention achieved HBM GB/s (% of peak) + query-heads×tokens/s, GQA cfg"
 DEFAULT_WORKLOAD = "gqa_bf16_g4"
+DEFAULT_ALSO = "longctx_bf16_g8"
 TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "*hbm_traffic*.md")
 
 
@@ -67,7 +74,7 @@ def source_hash() -> str:
 
 
 def committed_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from a committed counter summary taken on this source."""
+    """HBM bytes per call from a committed counter summary taken on this source."""
     want = source_hash()
     for path in sorted(glob.glob(TRAFFIC_GLOB)):
         text = open(path).read()
@@ -78,9 +85,25 @@ def committed_traffic(workload: str, kernel: str):
     return None, None
 
 
-def cpu_baseline(inp, W, min_seconds: float):
+def kv_bytes(inp) -> int:
+    """Algorithmic K+V bytes of one step: each token's K and V row of each kv
+    head read once, 2 * D * sizeof bytes per (token, kv head)."""
+    esz = inp["key_cache"].element_size()
+    return int(inp["seq_lens"].to("cpu").long().sum()) * inp["num_kv_heads"] * 2 * \
+        inp["head_size"] * esz
+
+
+def qhead_tokens(inp) -> int:
+    """(query token, query head, key) triples one step scores: with M query
+    tokens per sequence (its last M positions), token m sees L - M + m + 1 keys."""
+    M = inp.get("num_queries", 1)
+    lens = [int(x) for x in inp["seq_lens"].tolist()]
+    keys = sum(max(0, min(L, L - M + m + 1)) for L in lens for m in range(M))
+    return keys * inp["num_heads"]
+
+
+def cpu_baseline(inp, min_seconds: float):
     import oracle
-    import torch  # noqa: F401
     threads = oracle.default_threads()
     args = (inp["query"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
             inp["seq_lens"], inp["scale"])
@@ -100,12 +123,236 @@ def cpu_baseline(inp, W, min_seconds: float):
         times.append(one())
     per_run = sorted(times)[len(times) // 2]
     return {
-        "value": round(W.kv_bytes(inp) / per_run / 1e9, 4), "unit": "GB/s", "cores": threads,
+        "value": round(kv_bytes(inp) / per_run / 1e9, 4), "unit": "GB/s", "cores": threads,
         "kind": "oracle",
         "sample": (f"whole workload ({inp['num_seqs']} sequences, "
                    f"{int(inp['seq_lens'].sum())} tokens), fp64 partition stats + combine: "
                    f"1 warm run, median of {len(times)} timed runs, {per_run:.2f} s per run"),
     }
+
+
+def quantile(v, f):
+    v = sorted(v)
+    return v[min(len(v) - 1, int(f * len(v)))]
+
+
+def pct(gbs):
+    return round(100.0 * gbs / PEAK_HBM_GBS, 2)
+
+
+class Batch:
+    """One workload's inputs on the GPU and its launch forms."""
+
+    def __init__(self, name, pa, W, torch, PS=None):
+        self.name, self.pa, self.torch = name, pa, torch
+        cfg = W.CONFIGS[name]
+        self.cfg = cfg
+        self.seed = W.workload_seed(name)
+        inp = W.make_inputs(cfg, seed=self.seed)
+        self.inp = inp
+        self.PS = PS or cfg.partition_size
+        P = max(1, -(-int(inp["seq_lens"].max()) // self.PS))
+        self.P = max(P, cfg.max_num_partitions) if self.PS == cfg.partition_size else P
+        dev = torch.device("cuda", 0)
+        self.dev = dev
+        self.q, self.kc, self.vc = (inp[k].to(dev) for k in ("query", "key_cache", "value_cache"))
+        self.bt, self.sl = inp["block_tables"].to(dev), inp["seq_lens"].to(dev)
+        self.MQ = cfg.num_queries
+        self.S, self.H, self.D = self.q.shape[0], self.q.shape[-2], self.q.shape[-1]
+        self.lead = (self.S,) if self.MQ == 1 else (self.S, self.MQ)
+        self.out = torch.empty(*self.lead, self.H, self.D, dtype=torch.float32, device=dev)
+        self.ws = self.work(self.P)
+        self.stream = torch.cuda.current_stream(dev)
+        self.fp8 = cfg.dtype == "fp8"
+        self.al = inp["alibi_slopes"].to(dev) if cfg.alibi else None
+        self.kvb = kv_bytes(inp)
+        self.qht = qhead_tokens(inp)
+        self.PS_t = pa.plan_partition_size(cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads,
+                                           self.D, cfg.block_size, cfg.max_len,
+                                           W.DTYPES[cfg.dtype])
+        self.P_t = max(1, -(-cfg.max_len // self.PS_t))
+        self.ws_t = self.work(self.P_t)
+        self.dtype_name = W.DTYPES[cfg.dtype]
+
+    def work(self, P_):
+        t, dev = self.torch, self.dev
+        return (t.empty(*self.lead, self.H, P_, self.D, dtype=t.float32, device=dev),
+                t.empty(*self.lead, self.H, P_, dtype=t.float32, device=dev),
+                t.empty(*self.lead, self.H, P_, dtype=t.float32, device=dev))
+
+    def entry(self):
+        return ("paged_attn_decode_ex" if self.al is not None else
+                "paged_attn_decode_mq" if self.MQ > 1 else
+                "paged_attn_decode_fp8" if self.fp8 else "paged_attn_decode")
+
+    def decode(self, ws=None, PS=None):
+        pa, i = self.pa, self.inp
+        tmp, es, ml = ws or self.ws
+        PS = PS or self.PS
+        a = (self.q, self.kc, self.vc, self.bt, self.sl, i["scale"])
+        if self.al is not None:
+            pa.paged_attn_decode_ex(self.out, tmp, es, ml, *a, PS, i["k_scale"], i["v_scale"],
+                                    self.al, stream=self.stream)
+        elif self.MQ > 1:
+            pa.paged_attn_decode_mq(self.out, tmp, es, ml, *a, PS, i["k_scale"], i["v_scale"],
+                                    stream=self.stream)
+        elif self.fp8:
+            pa.paged_attn_decode_fp8(self.out, tmp, es, ml, *a, i["k_scale"], i["v_scale"], PS,
+                                     stream=self.stream)
+        else:
+            pa.paged_attn_decode(self.out, tmp, es, ml, *a, PS, stream=self.stream)
+
+    def partition(self):
+        pa, i = self.pa, self.inp
+        tmp, es, ml = self.ws
+        a = (self.q, self.kc, self.vc, self.bt, self.sl, i["scale"])
+        if self.al is not None:
+            pa.paged_attn_v2_partition_ex(tmp, es, ml, *a, self.PS, i["k_scale"], i["v_scale"],
+                                          self.al, self.stream)
+        elif self.MQ > 1:
+            pa.paged_attn_v2_partition_mq(tmp, es, ml, *a, self.PS, i["k_scale"], i["v_scale"],
+                                          self.stream)
+        elif self.fp8:
+            pa.paged_attn_v2_partition_fp8(tmp, es, ml, *a, i["k_scale"], i["v_scale"], self.PS,
+                                           self.stream)
+        else:
+            pa.paged_attn_v2_partition(tmp, es, ml, *a, self.PS, self.stream)
+
+    def reduce(self):
+        tmp, es, ml = self.ws
+        if self.MQ > 1:
+            self.pa.paged_attn_v2_reduce_mq(self.out, tmp, es, ml, self.sl, self.PS, self.stream)
+        else:
+            self.pa.paged_attn_v2_reduce(self.out, tmp, es, ml, self.sl, self.PS, self.stream)
+
+    # ---- timing
+    def back_to_back(self, fn, K, W_):
+        """Seconds per step of K back-to-back steps between two synchronisations."""
+        torch = self.torch
+        for _ in range(W_):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / K
+
+    def events(self, fns, K):
+        """K rounds of the calls in `fns`, a HIP event pair on the launch stream
+        around each call: per call, the list of K durations in microseconds."""
+        torch = self.torch
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+              for _ in range(K)]
+        for k in range(K):
+            ev[k][0].record(self.stream)
+            for j, fn in enumerate(fns):
+                fn()
+                ev[k][j + 1].record(self.stream)
+        torch.cuda.synchronize()
+        return [[ev[k][j].elapsed_time(ev[k][j + 1]) * 1e3 for k in range(K)]
+                for j in range(len(fns))]
+
+    def flushed(self, n):
+        """Each decode call timed by its own event pair after a 512 MiB scratch
+        write (outside the events) that evicts the Infinity Cache; 10 warm-up
+        calls, then n."""
+        torch = self.torch
+        scratch = torch.empty(1 << 27, dtype=torch.float32, device=self.dev)  # 512 MiB
+        times = []
+        for i in range(n + 10):
+            scratch.fill_(float(i))
+            e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+            e0.record(self.stream)
+            self.decode()
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            if i >= 10:
+                times.append(e0.elapsed_time(e1) * 1e3)
+        del scratch
+        med = quantile(times, 0.5)
+        gbs = self.kvb / med / 1e3
+        return {"calls": n, "step_median_us": round(med, 3),
+                "step_p10_us": round(quantile(times, 0.1), 3),
+                "step_p90_us": round(quantile(times, 0.9), 3),
+                "value": round(gbs, 2), "unit": "GB/s", "pct_of_peak_hbm": pct(gbs),
+                "qheads_tokens_per_s": round(self.qht / med * 1e6, 1)}
+
+    def span(self, P, PS):
+        if self.MQ > 1:
+            return None
+        c = self.cfg
+        return self.pa.partition_span(self.S, self.H, c.num_kv_heads, self.D, c.block_size, P,
+                                      PS, self.dtype_name)
+
+    def kernel_name(self):
+        c = self.cfg
+        return ("partition_mfma_kernel" if c.query_dtype != "f32" and (c.group >= 4 or self.MQ > 1)
+                else "partition_vec_kernel")
+
+    def measure(self, K, W_, flushed_calls, two_call=True):
+        """value (back to back), roofline (events), flushed, tuned; two_call optional."""
+        step_s = self.back_to_back(self.decode, K, W_)
+        call_us = self.events([self.decode], K)[0]
+        call_avg = sum(call_us) / len(call_us)
+        gbs = self.kvb / step_s / 1e9
+        achieved = self.kvb / call_avg / 1e3
+        traffic, traffic_src = committed_traffic(self.name, self.kernel_name())
+        c = self.cfg
+        res = {
+            "value": round(gbs, 2), "unit": "GB/s", "ms_per_step": round(step_s * 1e3, 5),
+            "pct_of_peak_hbm": pct(gbs),
+            "qheads_tokens_per_s": round(self.qht / step_s, 1),
+            "entry": self.entry(), "partition_size": self.PS, "max_num_partitions": self.P,
+            "partition_span": self.span(self.P, self.PS),
+            "roofline": {
+                "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "kernel": self.kernel_name(), "call_avg_us": round(call_avg, 3),
+                "call_p10_us": round(quantile(call_us, 0.1), 3),
+                "call_p90_us": round(quantile(call_us, 0.9), 3),
+                "bytes_per_launch": self.kvb, "traffic_source": traffic_src,
+                "kernel_source_hash": source_hash(),
+            },
+        }
+        if flushed_calls > 0:
+            res["flushed"] = self.flushed(flushed_calls)
+        if two_call:
+            two_s = self.back_to_back(lambda: (self.partition(), self.reduce()), K, W_)
+            part_us, red_us = self.events([self.partition, self.reduce], K)
+            pavg = sum(part_us) / len(part_us)
+            res["two_call"] = {
+                "entries": "paged_attn_v2_partition + paged_attn_v2_reduce",
+                "ms_per_step": round(two_s * 1e3, 5),
+                "value": round(self.kvb / two_s / 1e9, 2),
+                "pct_of_peak_hbm": pct(self.kvb / two_s / 1e9),
+                "partition_avg_us": round(pavg, 3),
+                "partition_frac": round(self.kvb / pavg / 1e3 / PEAK_HBM_GBS, 4),
+                "reduce_avg_us": round(sum(red_us) / len(red_us), 3),
+            }
+        tuned_s = self.back_to_back(lambda: self.decode(self.ws_t, self.PS_t), K, W_)
+        res["tuned"] = {
+            "entry": self.entry(), "partition_size": self.PS_t, "max_num_partitions": self.P_t,
+            "partition_span": self.span(self.P_t, self.PS_t),
+            "ms_per_step": round(tuned_s * 1e3, 5), "value": round(self.kvb / tuned_s / 1e9, 2),
+            "unit": "GB/s", "pct_of_peak_hbm": pct(self.kvb / tuned_s / 1e9),
+            "qheads_tokens_per_s": round(self.qht / tuned_s, 1),
+        }
+        res["config"] = {
+            "workload": self.name, "num_seqs": self.S, "num_heads": self.H,
+            "num_kv_heads": c.num_kv_heads, "head_size": self.D, "block_size": c.block_size,
+            "partition_size": self.PS, "max_num_partitions": self.P,
+            "seq_lens": (f"fixed {list(c.fixed_lens)[:2]}..." if c.fixed_lens else
+                         f"uniform[{c.len_lo},{c.len_hi}] seed {self.seed}"),
+            "total_tokens": int(self.inp["seq_lens"].sum()), "kv_bytes_per_step": self.kvb,
+            "num_blocks": self.inp["num_blocks"],
+            **({"k_scale": self.inp["k_scale"], "v_scale": self.inp["v_scale"]}
+               if self.fp8 else {}),
+            **({"num_queries": self.MQ} if self.MQ > 1 else {}),
+            **({"alibi": "slopes 2^(-8(h+1)/H)"} if self.al is not None else {}),
+        }
+        res["dtype"] = (c.dtype if not self.fp8 else f"fp8_e4m3 cache, {c.query_dtype} query")
+        return res
 
 
 def merge_bench(pa, torch, dev, stream, rows: int, D: int, dtype, K: int) -> dict:
@@ -123,7 +370,7 @@ def merge_bench(pa, torch, dev, stream, rows: int, D: int, dtype, K: int) -> dic
         # microseconds, less than an event pair between every launch would add
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record(stream)
-        for i in range(K):
+        for _ in range(K):
             pa.paged_attn_merge_states(out, lse, a, la, b, lb, stream)
         ev[1].record(stream)
         torch.cuda.synchronize()
@@ -141,38 +388,6 @@ def merge_bench(pa, torch, dev, stream, rows: int, D: int, dtype, K: int) -> dic
         "stream_avg_us": round(t_s * 1e6, 3), "stream_achieved": round(nb_s / t_s / 1e9, 2),
         "stream_frac": round(nb_s / t_s / 1e9 / PEAK_HBM_GBS, 4), "unit": "GB/s",
     }
-
-
-def flushed_calls(torch, dev, stream, partition, reduce, tmp, es, ml, PS, kvb, n) -> dict:
-    """Each call timed by its own event pairs (partition, reduce) after a
-    512 MiB scratch write that evicts the 256 MB Infinity Cache (outside the
-    events): median and p10 / p90 of the step and of each kernel."""
-    scratch = torch.empty(1 << 27, dtype=torch.float32, device=dev)  # 512 MiB
-    steps, parts, reds = [], [], []
-    for i in range(n + 10):
-        scratch.fill_(float(i))
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        e[0].record(stream)
-        partition(tmp, es, ml, PS)
-        e[1].record(stream)
-        reduce(tmp, es, ml, PS)
-        e[2].record(stream)
-        torch.cuda.synchronize()
-        if i >= 10:  # 10 warm-up calls
-            parts.append(e[0].elapsed_time(e[1]) * 1e3)
-            reds.append(e[1].elapsed_time(e[2]) * 1e3)
-            steps.append(e[0].elapsed_time(e[2]) * 1e3)
-    del scratch
-
-    def q(v, f):
-        v = sorted(v)
-        return round(v[min(len(v) - 1, int(f * len(v)))], 3)
-
-    med = q(steps, 0.5)
-    return {"calls": n, "step_median_us": med, "step_p10_us": q(steps, 0.1),
-            "step_p90_us": q(steps, 0.9), "partition_median_us": q(parts, 0.5),
-            "reduce_median_us": q(reds, 0.5), "value": round(kvb / med / 1e3, 2), "unit": "GB/s",
-            "pct_of_peak_hbm": round(100.0 * kvb / med / 1e3 / PEAK_HBM_GBS, 2)}
 
 
 def copy_bandwidth(torch, dev, stream) -> dict:
@@ -194,6 +409,24 @@ def copy_bandwidth(torch, dev, stream) -> dict:
             "unit": "GB/s", "pct_of_peak_hbm": round(100.0 * 2 * 4 * n / t / 1e9 / PEAK_HBM_GBS, 2)}
 
 
+def gather_ceiling(pa, torch, b: Batch, K: int) -> dict:
+    """The read-only page-gather kernel over the batch's own pages: GB/s."""
+    from paged_kv_cache_v2_amd import ceiling
+    sink = torch.empty(ceiling.sink_words(b.S, b.cfg.num_kv_heads, b.bt.shape[1]),
+                       dtype=torch.int32, device=b.dev)
+
+    def run():
+        ceiling.gather_ceiling(sink, b.kc, b.vc, b.bt, b.sl, stream=b.stream)
+
+    for _ in range(5):
+        run()
+    us = b.events([run], K)[0]
+    avg = sum(us) / len(us)
+    gbs = b.kvb / avg / 1e3
+    return {"kernel": "gather_ceiling_kernel", "workload": b.name, "avg_us": round(avg, 3),
+            "value": round(gbs, 2), "unit": "GB/s", "pct_of_peak_hbm": pct(gbs)}
+
+
 def run(args) -> dict:
     import torch
 
@@ -201,193 +434,62 @@ def run(args) -> dict:
     from paged_kv_cache_v2_amd import workloads as W
 
     pa.ensure_built()
-    cfg = W.CONFIGS[args.workload]
-    seed = W.workload_seed(args.workload)
-    inp = W.make_inputs(cfg, seed=seed)
-    PS = args.partition_size or cfg.partition_size
-    P = max(1, -(-int(inp["seq_lens"].max()) // PS))
-    P = max(P, cfg.max_num_partitions) if PS == cfg.partition_size else P
-    dev = torch.device("cuda", 0)
-    q, kc, vc = (inp[k].to(dev) for k in ("query", "key_cache", "value_cache"))
-    bt, sl = inp["block_tables"].to(dev), inp["seq_lens"].to(dev)
-    MQ = cfg.num_queries
-    S, H, D = q.shape[0], q.shape[-2], q.shape[-1]
-    lead = (S,) if MQ == 1 else (S, MQ)
-
-    def work(P_):
-        return (torch.empty(*lead, H, P_, D, dtype=torch.float32, device=dev),
-                torch.empty(*lead, H, P_, dtype=torch.float32, device=dev),
-                torch.empty(*lead, H, P_, dtype=torch.float32, device=dev))
-
-    out = torch.empty(*lead, H, D, dtype=torch.float32, device=dev)
-    tmp, es, ml = work(P)
-    stream = torch.cuda.current_stream(dev)
-
-    fp8 = cfg.dtype == "fp8"
-    ks, vs = inp["k_scale"], inp["v_scale"]
-    al = inp["alibi_slopes"].to(dev) if cfg.alibi else None
-
-    def partition(tmp_, es_, ml_, PS_):
-        if al is not None:
-            pa.paged_attn_v2_partition_ex(tmp_, es_, ml_, q, kc, vc, bt, sl, inp["scale"], PS_,
-                                          ks, vs, al, stream)
-        elif MQ > 1:
-            pa.paged_attn_v2_partition_mq(tmp_, es_, ml_, q, kc, vc, bt, sl, inp["scale"], PS_,
-                                          ks, vs, stream)
-        elif fp8:
-            pa.paged_attn_v2_partition_fp8(tmp_, es_, ml_, q, kc, vc, bt, sl, inp["scale"], ks, vs,
-                                           PS_, stream)
-        else:
-            pa.paged_attn_v2_partition(tmp_, es_, ml_, q, kc, vc, bt, sl, inp["scale"], PS_,
-                                       stream)
-
-    def reduce(tmp_, es_, ml_, PS_):
-        if MQ > 1:
-            pa.paged_attn_v2_reduce_mq(out, tmp_, es_, ml_, sl, PS_, stream)
-        else:
-            pa.paged_attn_v2_reduce(out, tmp_, es_, ml_, sl, PS_, stream)
-
-    def step():
-        partition(tmp, es, ml, PS)
-        reduce(tmp, es, ml, PS)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    K = args.steps
-    # Timed region: exactly K whole-path steps between two synchronisations.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(K):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    # Kernel timing: the same K steps again, with a HIP event pair on the launch
-    # stream around every partition launch (events inside the timed region above
-    # would add their own gaps to the step time).
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    for i in range(K):
-        ev[i][0].record(stream)
-        partition(tmp, es, ml, PS)
-        ev[i][1].record(stream)
-        reduce(tmp, es, ml, PS)
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    part_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
-    red_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
-    part_avg_s = sum(part_ms) / len(part_ms) / 1e3
-    red_avg_s = sum(red_ms) / len(red_ms) / 1e3
-
-    # The same batch through paged_attn_decode (one ABI call, partition +
-    # reduce) at the partition size the library plans for this batch;
-    # out does not depend on the partition size beyond rounding.
-    PS_t = pa.plan_partition_size(cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, D,
-                                  cfg.block_size, cfg.max_len, W.DTYPES[cfg.dtype])
-    P_t = max(1, -(-cfg.max_len // PS_t))
-    tmp_t, es_t, ml_t = work(P_t)
-
-    def step_tuned():
-        if al is not None:
-            pa.paged_attn_decode_ex(out, tmp_t, es_t, ml_t, q, kc, vc, bt, sl, inp["scale"], PS_t,
-                                    ks, vs, al, stream=stream)
-        elif MQ > 1:
-            pa.paged_attn_decode_mq(out, tmp_t, es_t, ml_t, q, kc, vc, bt, sl, inp["scale"], PS_t,
-                                    ks, vs, stream=stream)
-        elif fp8:
-            pa.paged_attn_decode_fp8(out, tmp_t, es_t, ml_t, q, kc, vc, bt, sl, inp["scale"], ks,
-                                     vs, PS_t, stream=stream)
-        else:
-            pa.paged_attn_decode(out, tmp_t, es_t, ml_t, q, kc, vc, bt, sl, inp["scale"], PS_t,
-                                 stream=stream)
-
-    for _ in range(args.warmup):
-        step_tuned()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(K):
-        step_tuned()
-    torch.cuda.synchronize()
-    tuned_s = (time.perf_counter() - t0) / K
-    del tmp_t, es_t, ml_t
-
-    kvb = W.kv_bytes(inp)
-    step_s = elapsed / K
-    gbs = kvb / step_s / 1e9
-    achieved = kvb / part_avg_s / 1e9
-    kernel = ("partition_mfma_kernel"
-              if (cfg.query_dtype != "f32" and (cfg.group >= 4 or MQ > 1))
-              else "partition_vec_kernel")
-    traffic, traffic_src = committed_traffic(args.workload, kernel)
+    K, W_ = args.steps, args.warmup
+    b = Batch(args.workload, pa, W, torch, args.partition_size)
+    # Timed region: exactly K whole-path steps (one decode call each) between
+    # two synchronisations, inside Batch.measure.
+    m = b.measure(K, W_, args.flushed_calls, two_call=True)
     res = {
         "metric": METRIC,
-        "value": round(gbs, 2),
+        "value": m["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_s * 1e3, 5),
+        "warmup": W_,
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype if not fp8 else f"fp8_e4m3 cache, {cfg.query_dtype} query",
+        "dtype": m["dtype"],
         "data": "synthetic",
-        "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
-        "qheads_tokens_per_s": round(W.qhead_tokens(inp) / step_s, 1),
-        "config": {
-            "workload": args.workload, "num_seqs": S, "num_heads": H,
-            "num_kv_heads": cfg.num_kv_heads, "head_size": D, "block_size": cfg.block_size,
-            "partition_size": PS, "max_num_partitions": P,
-            "seq_lens": (f"fixed {list(cfg.fixed_lens)[:2]}..." if cfg.fixed_lens else
-                         f"uniform[{cfg.len_lo},{cfg.len_hi}] seed {seed}"),
-            "total_tokens": int(inp["seq_lens"].sum()), "kv_bytes_per_step": kvb,
-            "num_blocks": inp["num_blocks"],
-            **({"k_scale": inp["k_scale"], "v_scale": inp["v_scale"]} if fp8 else {}),
-            **({"num_queries": MQ} if MQ > 1 else {}),
-            **({"alibi": "slopes 2^(-8(h+1)/H)"} if al is not None else {}),
-        },
-        "tuned": {
-            "entry": ("paged_attn_decode_ex" if al is not None else
-                      "paged_attn_decode_mq" if MQ > 1 else
-                      "paged_attn_decode_fp8" if fp8 else "paged_attn_decode"),
-            "partition_size": PS_t, "max_num_partitions": P_t,
-            "partition_span": (None if MQ > 1 else
-                               pa.partition_span(S, H, cfg.num_kv_heads, D, cfg.block_size, P_t,
-                                                 PS_t, W.DTYPES[cfg.dtype])),
-            "ms_per_step": round(tuned_s * 1e3, 5), "value": round(kvb / tuned_s / 1e9, 2),
-            "unit": "GB/s", "pct_of_peak_hbm": round(100.0 * kvb / tuned_s / 1e9 / PEAK_HBM_GBS, 2),
-            "qheads_tokens_per_s": round(W.qhead_tokens(inp) / tuned_s, 1),
-        },
-        "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
-            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "kernel": kernel, "kernel_avg_us": round(part_avg_s * 1e6, 3),
-            "kernel_p10_us": round(part_ms[len(part_ms) // 10] * 1e3, 3),
-            "kernel_p90_us": round(part_ms[(9 * len(part_ms)) // 10] * 1e3, 3),
-            "bytes_per_launch": kvb, "traffic_source": traffic_src,
-            "kernel_source_hash": source_hash(),
-            "reduce_avg_us": round(red_avg_s * 1e6, 3),
-            "partition_span": (None if MQ > 1 else
-                               pa.partition_span(S, H, cfg.num_kv_heads, D, cfg.block_size, P,
-                                                 PS, W.DTYPES[cfg.dtype])),
-        },
+        "pct_of_peak_hbm": m["pct_of_peak_hbm"],
+        "qheads_tokens_per_s": m["qheads_tokens_per_s"],
+        "config": m["config"],
+        "entry": m["entry"],
+        "partition_span": m["partition_span"],
+        "roofline": m["roofline"],
     }
-    res["merge_states"] = merge_bench(pa, torch, dev, stream, S * MQ * H, D,
-                                      W.DTYPES[cfg.query_dtype], K)
-    if args.flushed_calls > 0:
-        res["flushed"] = flushed_calls(torch, dev, stream, partition, reduce, tmp, es, ml, PS,
-                                       kvb, args.flushed_calls)
-    res["copy_context"] = copy_bandwidth(torch, dev, stream)
+    for k in ("flushed", "two_call", "tuned"):
+        if k in m:
+            res[k] = m[k]
+    if not args.no_ceiling:
+        res["ceiling"] = gather_ceiling(pa, torch, b, K)
+    if not args.no_extras:
+        res["merge_states"] = merge_bench(pa, torch, b.dev, b.stream, b.S * b.MQ * b.H, b.D,
+                                          W.DTYPES[b.cfg.query_dtype], K)
+        res["copy_context"] = copy_bandwidth(torch, b.dev, b.stream)
     if args.calibrate_copy:
         n = 1 << 28  # 1 GiB of fp32: FETCH_SIZE / WRITE_SIZE calibration for the counters
-        a = torch.ones(n, device=dev)
-        b = torch.empty_like(a)
+        a = torch.ones(n, device=b.dev)
+        c = torch.empty_like(a)
         for _ in range(3):
-            b.copy_(a)
+            c.copy_(a)
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = 4 * n
+    host_inp = b.inp
+    del b
+    torch.cuda.empty_cache()
+    also = [w for w in (args.also.split(",") if args.also else []) if w and w != args.workload]
+    if also:
+        res["workloads"] = {}
+        for name in also:
+            o = Batch(name, pa, W, torch)
+            r = o.measure(K, W_, args.flushed_calls, two_call=False)
+            res["workloads"][name] = r
+            del o
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp, W, args.cpu_min_seconds)
+        res["cpu_baseline"] = cpu_baseline(host_inp, args.cpu_min_seconds)
     return res
 
 
@@ -397,8 +499,13 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--also", default=DEFAULT_ALSO,
+                    help="comma-separated further workloads measured into `workloads` ('' for none)")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip merge_states and copy_context")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
     ap.add_argument("--flushed-calls", type=int, default=100,
                     help="calls timed one by one after an Infinity Cache flush")

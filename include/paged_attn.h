@@ -108,10 +108,12 @@ PA_API int paged_attn_v2_partition(float* tmp_output, float* exp_sums, float* ma
  *   M = max_p max_logits, Z = sum_p exp(max_logits - M) * exp_sums,
  *   out[s][h] = sum_p exp(max_logits - M) * exp_sums / Z * tmp_output[s][h][p]
  * and out[s][h] = 0 when n == 0. Entries of partitions p >= n never affect
- * the result (NaN there is fine); they are not read, except that with
- * max_num_partitions == 1 each row's single entry is loaded together with its
- * statistics (one round trip) and discarded when n == 0. With one partition
- * the weight is exactly 1: out[s][h] is tmp_output[s][h][0], cast.
+ * the result (NaN there is fine): the statistics of a row's first 64
+ * partitions are loaded together with its length, before n is known, and
+ * those past n are discarded; tmp_output rows past n are never read, except
+ * that with max_num_partitions == 1 each row's single row is loaded together
+ * with its statistics (one round trip) and discarded when n == 0. With one
+ * partition the weight is exactly 1: out[s][h] is tmp_output[s][h][0], cast.
  *
  *   out          [S, H, D] in out_dtype (PA_F32, or the kv dtype: round to
  *                nearest even from the fp32 result), written
@@ -126,9 +128,23 @@ PA_API int paged_attn_v2_reduce(void* out, const float* tmp_output, const float*
 
 /*
  * Phase 1 then phase 2 on one stream (the page's host launcher): the same
- * arguments as the two calls above. tmp_output / exp_sums / max_logits are
- * workspace the caller allocates ([S,H,P,D], [S,H,P], [S,H,P] fp32) and may
- * reuse across calls on the same stream.
+ * arguments and the same `out` as the two calls above, up to fp32 rounding.
+ * Every partition of PS tokens is still computed on its own (its max logit,
+ * exp sum and normalised row, exactly as phase 1 defines them), and the
+ * partitions are combined with phase 2's log-sum-exp rule, but the combine
+ * runs where the data already is: a workgroup that holds C consecutive
+ * partitions of a (sequence, kv head) combines them in on-chip memory. When
+ * its C partitions are all of a row's (P <= C), it writes `out` itself and
+ * no second kernel runs; otherwise it stores one combined entry per span of
+ * C partitions (statistics and row, in the first ceil(P / C) entries of each
+ * row of the workspace) and the reduce combines those entries as partitions
+ * of C * PS tokens. C is the launch plan's span (paged_attn_partition_span).
+ *
+ * tmp_output / exp_sums / max_logits are workspace the caller allocates
+ * ([S,H,P,D], [S,H,P], [S,H,P] fp32) and may reuse across calls on the same
+ * stream; their contents after this call are unspecified (they may be left
+ * unwritten). Phase 1's per-partition rows and statistics are produced by
+ * paged_attn_v2_partition.
  */
 PA_API int paged_attn_decode(void* out, float* tmp_output, float* exp_sums, float* max_logits,
                              const void* query, const void* key_cache, const void* value_cache,
@@ -349,7 +365,8 @@ PA_API int paged_attn_merge_states(void* out, float* out_lse, const void* a, con
  * library; valid until the next call on the same thread. */
 PA_API const char* paged_attn_last_error(void);
 
-/* Version of this ABI (incremented on any incompatible change). */
+/* Version of this ABI (incremented on any incompatible change). 2: the decode
+ * calls leave their workspace unspecified (partitions combined in the kernel). */
 PA_API int paged_attn_abi_version(void);
 
 /* Partition size the library is tuned for at this geometry (a multiple of

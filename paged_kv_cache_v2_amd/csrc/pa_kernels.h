@@ -197,6 +197,13 @@ struct PartitionArgs {
   float v_scale;   // 1, or v_scale for an 8-bit cache (applied once, at the merge)
   const float* alibi;  // [H] ALiBi slopes (read by the AL kernels only)
   int lpt;             // 1: workgroups take units largest first (see lpt_pair)
+  // One-call decode (combine_store): the workgroup combines its span's
+  // partitions itself instead of storing a row per partition.
+  int fuse;            // 0: a row per partition (phase 1 alone); 1: combine the span
+  int Pq;              // fuse: span entries per row, ceil(P / C); 1: the span is the row
+  void* out;           // fuse, Pq == 1: out [S * Mq * H, D] in odt
+  float* lse;          // fuse, Pq == 1: optional [S * Mq * H] row log-sum-exp (NULL: none)
+  int odt;             // DT_F32, DT_F16 or DT_BF16
 };
 
 // ALiBi: a query at position i adds slope_h * (j - i) to its scaled score for
@@ -299,6 +306,109 @@ __device__ __forceinline__ void merge_store(const PartitionArgs& a, const float*
       }
       a.exp_sums[row] = Z;
       a.max_logits[row] = mx * kLn2;
+    }
+  }
+}
+
+// Store four fp32 values of an output row in the output dtype (round to
+// nearest even for the 16-bit types).
+__device__ __forceinline__ void store_out4(void* out, int odt, size_t off, f32x4 v) {
+  if (odt == DT_F32) {
+    *(f32x4*)((float*)out + off) = v;
+  } else if (odt == DT_F16) {
+    *(u32x2*)((uint16_t*)out + off) =
+        u32x2{codec<DT_F16>::pack(v[0], v[1]), codec<DT_F16>::pack(v[2], v[3])};
+  } else {
+    *(u32x2*)((uint16_t*)out + off) =
+        u32x2{codec<DT_BF16>::pack(v[0], v[1]), codec<DT_BF16>::pack(v[2], v[3])};
+  }
+}
+
+// One-call decode epilogue. Each of the span's ne used partitions is first
+// merged over the wavefronts exactly as merge_store does it -- partition j's
+// max m_j (log2 units, plus its share of the ALiBi bias), exp sum l_j and
+// normalised row o_j -- and the partitions are then combined with the
+// reduce's log-sum-exp rule: M = max_j m_j, Z = sum_j e^(m_j - M) l_j,
+// row = sum_j (e^(m_j - M) l_j / Z) o_j. When the span holds every partition
+// of the row (Pq == 1) that row is the attention output: it goes to `out` in
+// its dtype, with lse = M + ln Z if asked for, and nothing is written to the
+// workspace. Otherwise the span's (M, Z, row) is entry q = p0 / C of a
+// [rows, Pq] workspace, which the reduce combines exactly like partitions of
+// C * PS tokens. A column with no keys in the span (several query tokens,
+// causal prefix ended earlier) gets M = -inf, Z = 0 and a zero row.
+template <int D, bool AL>
+__device__ __forceinline__ void combine_store(const PartitionArgs& a, const float* s_m,
+                                              const float* s_l, const float* s_acc, int s,
+                                              int kh, int p0, int ne, int G, int NC, int L) {
+  constexpr int D4 = D / 4;
+  const int q = p0 / a.C;
+  const int mf = a.c0 / G, ml = (a.c0 + NC - 1) / G;  // first and last query token here
+  const size_t row0 = ((size_t)s * a.Mq + mf) * a.H + kh * G;  // row of (mf, head kh*G)
+  const __amdgpu_buffer_rsrc_t tmp = __builtin_amdgcn_make_buffer_rsrc(
+      a.tmp_out + row0 * a.Pq * D, (short)0, ((ml - mf) * a.H + G) * a.Pq * D * 4, kRsrcFlags);
+  for (int i = threadIdx.x; i < NC * D4; i += kWaves * 64) {
+    const int c = i / D4, d4 = i - c * D4;
+    const int m = (a.c0 + c) / G, h = a.c0 + c - m * G;
+    float slope2 = 0.0f;
+    if constexpr (AL) slope2 = a.alibi[kh * G + h] * kLog2e;
+    // Partition j's wavefront-common max mu (0 if no wavefront saw a key), its
+    // exp sum l and its max logit mx (log2 units, with its share of the bias).
+    // Recomputed from LDS in each pass below instead of being held in arrays.
+    auto part = [&](int j, float& mu, float& l, float& mx) {
+      float Mx = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[slot(j, w, c, NC)]);
+      mu = Mx == kNegInf ? 0.0f : Mx;
+      l = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int k = slot(j, w, c, NC);
+        l += fast_exp2(s_m[k] - mu) * s_l[k];
+      }
+      mx = Mx;
+      if constexpr (AL) mx += slope2 * (float)((p0 + j) * a.PS - (L - a.Mq + m));
+    };
+    float M = kNegInf;
+    for (int j = 0; j < ne; ++j) {
+      float mu, l, mx;
+      part(j, mu, l, mx);
+      M = fmaxf(M, mx);
+    }
+    const float Mu = M == kNegInf ? 0.0f : M;
+    float Z = 0.0f;
+    for (int j = 0; j < ne; ++j) {
+      float mu, l, mx;
+      part(j, mu, l, mx);
+      Z += l > 0.0f ? fast_exp2(mx - Mu) * l : 0.0f;
+    }
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < ne; ++j) {
+      float mu, l, mx;
+      part(j, mu, l, mx);
+      if (l > 0.0f) {  // (a partition without keys for this column has weight 0)
+        f32x4 oj = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const int k = slot(j, w, c, NC);
+          oj += fast_exp2(s_m[k] - mu) * *(const f32x4*)&s_acc[k * D + 4 * d4];
+        }
+        oj *= a.v_scale / l;  // partition j's normalised row
+        o += (fast_exp2(mx - Mu) * l / Z) * oj;
+      }
+    }
+    const int hrow = (m - mf) * a.H + h;  // row of this column relative to row0
+    if (a.Pq == 1) {
+      const size_t row = row0 + hrow;
+      store_out4(a.out, a.odt, row * D + 4 * d4, o);
+      if (a.lse && d4 == 0)
+        a.lse[row] = Z > 0.0f ? fmaf(__builtin_amdgcn_logf(Z), kLn2, M * kLn2) : kNegInf;
+    } else {
+      store_row(tmp, (uint32_t)(((hrow * a.Pq + q) * D + 4 * d4) * 4), o, a.through);
+      if (d4 == 0) {
+        const size_t e = (row0 + hrow) * a.Pq + q;
+        a.exp_sums[e] = Z;
+        a.max_logits[e] = M * kLn2;
+      }
     }
   }
 }
@@ -427,19 +537,36 @@ __device__ __forceinline__ void unit_begin(const PartitionArgs& a, Unit& u, uint
 // After unit_begin: sentinels (max -inf, sum 0) for the span's empty
 // partitions; false if the whole span is empty, otherwise publish the span's
 // block-table slice to LDS for the whole workgroup.
-template <int BS>
+template <int BS, int D>
 __device__ __forceinline__ bool unit_hoist(const PartitionArgs& a, int32_t* s_bt, Unit& u) {
-  if ((int)threadIdx.x < u.nparts * u.NC) {
-    const int j = threadIdx.x / u.NC, c = a.c0 + threadIdx.x % u.NC;
-    const int m = c / u.G, h = c - m * u.G;
-    if ((u.p0 + j) * a.PS >= u.L) {
-      const size_t row =
-          (((size_t)u.s * a.Mq + m) * a.H + u.kh * u.G + h) * a.P + u.p0 + j;
-      a.max_logits[row] = kNegInf;
-      a.exp_sums[row] = 0.0f;
+  const int t0 = u.p0 * a.PS;
+  if (!a.fuse) {
+    if ((int)threadIdx.x < u.nparts * u.NC) {
+      const int j = threadIdx.x / u.NC, c = a.c0 + threadIdx.x % u.NC;
+      const int m = c / u.G, h = c - m * u.G;
+      if ((u.p0 + j) * a.PS >= u.L) {
+        const size_t row =
+            (((size_t)u.s * a.Mq + m) * a.H + u.kh * u.G + h) * a.P + u.p0 + j;
+        a.max_logits[row] = kNegInf;
+        a.exp_sums[row] = 0.0f;
+      }
+    }
+  } else if (t0 >= u.L) {
+    // An empty span of the one-call decode: the sentinel entry (Pq > 1), or,
+    // when the span is the whole row (an empty sequence), out = 0, lse = -inf.
+    for (int i = threadIdx.x; i < u.NC * (a.Pq > 1 ? 1 : D / 4); i += kWaves * 64) {
+      const int ci = a.Pq > 1 ? i : i / (D / 4), d4 = a.Pq > 1 ? 0 : i % (D / 4);
+      const int c = a.c0 + ci, m = c / u.G, h = c - m * u.G;
+      const size_t row = ((size_t)u.s * a.Mq + m) * a.H + u.kh * u.G + h;
+      if (a.Pq > 1) {
+        a.max_logits[row * a.Pq + u.p0 / a.C] = kNegInf;
+        a.exp_sums[row * a.Pq + u.p0 / a.C] = 0.0f;
+      } else {
+        store_out4(a.out, a.odt, row * D + 4 * d4, f32x4{0.f, 0.f, 0.f, 0.f});
+        if (a.lse && d4 == 0) a.lse[row] = kNegInf;
+      }
     }
   }
-  const int t0 = u.p0 * a.PS;
   if (t0 >= u.L) return false;
   const int t1 = min(t0 + u.nparts * a.PS, u.L);
   u.npages = (t1 - t0 + BS - 1) / BS;
@@ -519,10 +646,16 @@ constexpr int prefetch_fp8(int page_regs) { return page_regs <= 16 ? PA_PREFETCH
 constexpr int fp8_waves(int D, int BS, bool AL) {
   return PA_FP8_WAVES > 0 ? PA_FP8_WAVES : D * BS <= 2048 && !AL ? 4 : D <= 128 ? 3 : 2;
 }
-// Register budget (wavefronts per SIMD) of the MFMA kernel: two column tiles
-// hold two accumulators and two query operands, which only fit at 2.
+// Register budget (wavefronts per SIMD) of the MFMA kernel: 2 for 16-bit
+// caches (one or two column tiles; left unbounded, the one-tile kernel at head
+// size 128 took 288 registers, one wavefront per SIMD, and ran ~1 % slower on
+// the GQA and long-context batches than at 2) except the largest page (head
+// size 256, 32-token blocks), which would spill at 2; the 8-bit budget above
+// otherwise.
 constexpr int mfma_waves(int D, int BS, bool KV8, bool AL, int CT) {
-  return CT > 1 ? 2 : KV8 ? fp8_waves(D, BS, AL) : (PA_MIN_WAVES > 0 ? PA_MIN_WAVES : 1);
+  return CT > 1 ? 2
+         : KV8  ? fp8_waves(D, BS, AL)
+                : (PA_MIN_WAVES > 0 ? PA_MIN_WAVES : D * BS <= 4096 ? 2 : 1);
 }
 
 template <int DT, int D, int BS, bool KV8, bool AL, int CT>
@@ -574,7 +707,7 @@ partition_mfma_kernel(PartitionArgs a) {
       qb[t][mk] = live ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  if (!unit_hoist<BS>(a, (int32_t*)smem, u)) return;
+  if (!unit_hoist<BS, D>(a, (int32_t*)smem, u)) return;
   const LdsLayout lay = lds_layout(a.PS, BS, NC, D, a.C);
   const int32_t* s_bt = (const int32_t*)(smem + lay.bt_off);
   float* s_m = (float*)(smem + lay.m_off);
@@ -818,7 +951,10 @@ partition_mfma_kernel(PartitionArgs a) {
   pipeline<PF>(npg, ring, fetch, process);
   while (jcur < u.ne) park();
   __syncthreads();
-  merge_store<D, AL>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G, NC, u.L);
+  if (a.fuse)
+    combine_store<D, AL>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G, NC, u.L);
+  else
+    merge_store<D, AL>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G, NC, u.L);
 }
 
 // =====================================================================
@@ -885,7 +1021,7 @@ partition_vec_kernel(PartitionArgs a) {
   float slope2[GM];
 #pragma unroll
   for (int gg = 0; gg < GM; ++gg) slope2[gg] = AL && gg < G ? a.alibi[u.kh * G + gg] * kLog2e : 0.0f;
-  if (!unit_hoist<BS>(a, (int32_t*)smem, u)) return;
+  if (!unit_hoist<BS, D>(a, (int32_t*)smem, u)) return;
   const LdsLayout lay = lds_layout(a.PS, BS, G, D, a.C);
   const int32_t* s_bt = (const int32_t*)(smem + lay.bt_off);
   float* s_m = (float*)(smem + lay.m_off);
@@ -1063,7 +1199,10 @@ partition_vec_kernel(PartitionArgs a) {
   pipeline<PF>(npg, ring, fetch, process);
   while (jcur < u.ne) park();
   __syncthreads();
-  merge_store<D, AL>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G, G, u.L);
+  if (a.fuse)
+    combine_store<D, AL>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G, G, u.L);
+  else
+    merge_store<D, AL>(a, s_m, s_l, s_acc, u.s, u.kh, u.p0, u.ne, G, G, u.L);
 }
 
 // =====================================================================
@@ -1149,7 +1288,7 @@ __global__ void __launch_bounds__(kWaves * 64) reduce_kernel(ReduceArgs a) {
       for (int i = lane + 64; i < n; i += 64) Z += fast_exp2((mlr[i] - M) * kLog2e) * esr[i];
       Z = wave_sum(Z);
       // Z >= 1 (the partition holding the row's max contributes its l >= 1)
-      lse = M + __builtin_amdgcn_logf(Z) * kLn2;
+      lse = fmaf(__builtin_amdgcn_logf(Z), kLn2, M);
       for (int base = 0; base < n; base += 64) {
         // Weight of partition base + lane.
         float wl;
@@ -1227,7 +1366,7 @@ __global__ void __launch_bounds__(kWaves * 64) reduce_one_kernel(ReduceArgs a) {
   }
   const int L = min(L0, max(0, L0 - a.M + qm + 1));  // keys query token qm sees
   const f32x4 acc = L > 0 ? v : f32x4{0.f, 0.f, 0.f, 0.f};
-  if (a.lse && c4 == 0) a.lse[sh] = L > 0 ? m + __builtin_amdgcn_logf(l) * kLn2 : kNegInf;
+  if (a.lse && c4 == 0) a.lse[sh] = L > 0 ? fmaf(__builtin_amdgcn_logf(l), kLn2, m) : kNegInf;
   const size_t o = (size_t)sh * D + 4 * c4;
   if constexpr (ODT == DT_F32) {
     *(f32x4*)((float*)a.out + o) = acc;

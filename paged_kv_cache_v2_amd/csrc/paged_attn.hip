@@ -121,6 +121,16 @@ struct Plan {
   int lpt;  // largest-first unit order
 };
 
+// One-call decode: the partition launches combine each span's partitions
+// themselves (combine_store in pa_kernels.h) and, when one span covers a
+// whole row, write the output directly.
+struct Fuse {
+  int on = 0;
+  void* out = nullptr;
+  float* lse = nullptr;
+  int odt = PA_F32;
+};
+
 #ifndef PA_SPAN
 #define PA_SPAN 0  // >0: force this many partitions per workgroup (measurement builds)
 #endif
@@ -296,7 +306,8 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
                     const void* key_cache, const void* value_cache, const int32_t* block_tables,
                     const int32_t* seq_lens, int32_t S, int32_t H, int32_t KH, int32_t D,
                     int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS, int32_t qdt,
-                    int32_t kvdt, int32_t M, int32_t NC, const float* alibi, Plan* plan) {
+                    int32_t kvdt, int32_t M, int32_t NC, const float* alibi, Plan* plan,
+                    int force_span = 0) {
   if (S < 0 || H < 0 || KH < 0 || D < 0 || BS < 0 || NB < 0 || MB < 0 || P < 0)
     return fail(PA_ERR_SHAPE, "negative size argument");
   if (M < 1) return fail(PA_ERR_SHAPE, "num_queries must be >= 1");
@@ -348,8 +359,9 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   if (lds1 > lds_limit)
     return fail(PA_ERR_UNSUPPORTED, "needs %d bytes of LDS per workgroup, device allows %d", lds1,
                 lds_limit);
-  const int span = pick_span(S, KH, P, PS, BS, NC, D, elem_size(kvdt), span_lds_cap(fn, lds_limit),
-                             span_min_grid(fn));
+  const int span = force_span > 0 ? force_span
+                                  : pick_span(S, KH, P, PS, BS, NC, D, elem_size(kvdt),
+                                              span_lds_cap(fn, lds_limit), span_min_grid(fn));
   const long long grid = (long long)S * KH * ((P + span - 1) / span);
   if (grid > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many work units");
   plan->fn = fn;
@@ -373,7 +385,7 @@ int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float
                      const int32_t* block_tables, const int32_t* seq_lens, int32_t S, int32_t H,
                      int32_t KH, int32_t NB, int32_t MB, int32_t P, int32_t PS, float scale,
                      float k_scale, float v_scale, int32_t NC, int32_t Mq, int32_t c0,
-                     const float* alibi, hipStream_t stream) {
+                     const float* alibi, const Fuse& fz, hipStream_t stream) {
   PartitionArgs a;
   a.tmp_out = tmp_output;
   a.exp_sums = exp_sums;
@@ -399,6 +411,13 @@ int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float
   a.v_scale = v_scale;
   a.alibi = alibi;
   a.lpt = plan.lpt;
+  // (With one-partition spans and several spans per row, the span entries are
+  // the partition rows themselves: the plain phase-1 epilogue writes them.)
+  a.Pq = fz.on ? (P + plan.span - 1) / plan.span : P;
+  a.fuse = fz.on && (plan.span > 1 || a.Pq == 1);
+  a.out = fz.out;
+  a.lse = fz.lse;
+  a.odt = fz.odt;
   hipLaunchKernelGGL(plan.fn, dim3(plan.grid), dim3(pa::kWaves * 64), plan.lds_bytes, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "partition launch failed: %s", hipGetErrorString(e));
@@ -466,7 +485,7 @@ int plan_partitions(float* tmp_output, float* exp_sums, float* max_logits, const
                     const int32_t* seq_lens, int32_t S, int32_t H, int32_t KH, int32_t D,
                     int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS, int32_t qdt,
                     int32_t kvdt, int32_t M, const float* alibi, Plan* full, Plan* last,
-                    int* nc) {
+                    int* nc, bool same_span = false) {
   const int G = KH > 0 && H >= KH && H % KH == 0 ? H / KH : 1;  // (validated by check_partition)
   const long long total = (long long)G * (M > 0 ? M : 1);
   *nc = launch_columns(G, M > 0 ? M : 1, D, PS, BS);
@@ -480,6 +499,15 @@ int plan_partitions(float* tmp_output, float* exp_sums, float* max_logits, const
     rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                          block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt, M,
                          (int)(total % *nc), alibi, last);
+  if (rc == PA_OK && same_span && last->span != full->span) {
+    // One span for every column launch (their span entries share one layout):
+    // the shorter of the two, which fits both launches' LDS.
+    const int span = std::min(full->span, last->span);
+    Plan* re = full->span > span ? full : last;
+    rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
+                         block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt, M,
+                         re == full ? *nc : (int)(total % *nc), alibi, re, span);
+  }
   return rc;
 }
 
@@ -489,14 +517,14 @@ int launch_partitions(const Plan& full, const Plan& last, int nc, float* tmp_out
                       const int32_t* block_tables, const int32_t* seq_lens, int32_t S,
                       int32_t H, int32_t KH, int32_t NB, int32_t MB, int32_t P, int32_t PS,
                       float scale, float k_scale, float v_scale, int32_t M, const float* alibi,
-                      hipStream_t stream) {
+                      const Fuse& fz, hipStream_t stream) {
   const int total = H / KH * M;  // (bounded by plan_partitions)
   for (int c0 = 0; c0 < total; c0 += nc) {
     const int n = total - c0 < nc ? total - c0 : nc;
     const int rc = launch_partition(n == nc ? full : last, tmp_output, exp_sums, max_logits,
                                     query, key_cache, value_cache, block_tables, seq_lens, S, H,
                                     KH, NB, MB, P, PS, scale, k_scale, v_scale, n, M, c0, alibi,
-                                    stream);
+                                    fz, stream);
     if (rc != PA_OK) return rc;
   }
   return PA_OK;
@@ -519,7 +547,7 @@ int partition_entry(float* tmp_output, float* exp_sums, float* max_logits, const
   if (rc != PA_OK || S == 0) return rc;
   return launch_partitions(full, last, nc, tmp_output, exp_sums, max_logits, query, key_cache,
                            value_cache, block_tables, seq_lens, S, H, KH, NB, MB, P, PS, scale,
-                           k_scale, v_scale, M, alibi, (hipStream_t)stream);
+                           k_scale, v_scale, M, alibi, Fuse(), (hipStream_t)stream);
 }
 
 int decode_entry(void* out, float* lse, float* tmp_output, float* exp_sums, float* max_logits,
@@ -536,20 +564,32 @@ int decode_entry(void* out, float* lse, float* tmp_output, float* exp_sums, floa
   int nc = 1;
   int rc = plan_partitions(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                            block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt, M,
-                           alibi, &full, &last, &nc);
+                           alibi, &full, &last, &nc, /*same_span=*/true);
   if (rc != PA_OK || S == 0) return rc;
   if (out_dtype != PA_F32 && out_dtype != qdt)
     return fail(PA_ERR_UNSUPPORTED, "out dtype must be PA_F32 or the query dtype");
+  // The partition launches combine each span's partitions (Fuse); with one
+  // span per row they write out (and lse) themselves and no reduce runs,
+  // otherwise the reduce combines the Pq span entries of each row, which
+  // stand for partitions of span * PS tokens.
+  const int span = full.span;
+  const int Pq = (P + span - 1) / span;
   reduce_fn fn = nullptr;
-  rc = check_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, S, M, H, D, P, PS,
+  rc = check_reduce(out, tmp_output, exp_sums, max_logits, seq_lens, S, M, H, D, Pq, PS * span,
                     out_dtype, &fn);
   if (rc != PA_OK) return rc;
+  if ((long long)PS * span > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "partition too long");
+  Fuse fz;
+  fz.on = 1;
+  fz.out = out;
+  fz.lse = lse;
+  fz.odt = out_dtype;
   rc = launch_partitions(full, last, nc, tmp_output, exp_sums, max_logits, query, key_cache,
                          value_cache, block_tables, seq_lens, S, H, KH, NB, MB, P, PS, scale,
-                         k_scale, v_scale, M, alibi, (hipStream_t)stream);
-  if (rc != PA_OK) return rc;
-  return launch_reduce(fn, out, lse, tmp_output, exp_sums, max_logits, seq_lens, S, M, H, D, P,
-                       PS, (hipStream_t)stream);
+                         k_scale, v_scale, M, alibi, fz, (hipStream_t)stream);
+  if (rc != PA_OK || Pq == 1) return rc;
+  return launch_reduce(fn, out, lse, tmp_output, exp_sums, max_logits, seq_lens, S, M, H, D, Pq,
+                       PS * span, (hipStream_t)stream);
 }
 
 int reduce_entry(void* out, float* lse, const float* tmp_output, const float* exp_sums,
@@ -790,7 +830,7 @@ int paged_attn_merge_states(void* out, float* out_lse, const void* a, const floa
 
 const char* paged_attn_last_error(void) { return g_err; }
 
-int paged_attn_abi_version(void) { return 1; }
+int paged_attn_abi_version(void) { return 2; }
 
 int paged_attn_partition_span(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                               int32_t head_size, int32_t block_size, int32_t max_num_partitions,

@@ -323,25 +323,3 @@ def poison_unused(inp: Dict[str, object], value: float = float("nan")) -> None:
             vc[last, :, :, n % BS:] = value
     kc[~referenced] = value
     vc[~referenced] = value
-
-
-def kv_bytes(inp: Dict[str, object]) -> int:
-    """Algorithmic K+V bytes one decode step reads: 2*D*sizeof per (token, kv-head)."""
-    esz = inp["key_cache"].element_size()
-    return int(inp["seq_lens"].to(torch.int64).sum()) * inp["num_kv_heads"] * 2 * \
-        inp["head_size"] * esz
-
-
-def causal_len(L: int, M: int, m: int) -> int:
-    """Keys query token m (of M, the sequence's last positions) sees in a
-    length-L sequence: positions t <= L - M + m, clamped to [0, L]."""
-    return max(0, min(L, L - M + m + 1))
-
-
-def qhead_tokens(inp: Dict[str, object]) -> int:
-    """(query token, query head, key token) triples one step scores."""
-    M = inp.get("num_queries", 1)
-    if M == 1:
-        return int(inp["seq_lens"].to(torch.int64).sum()) * inp["num_heads"]
-    return sum(causal_len(int(L), M, m) for L in inp["seq_lens"].tolist()
-               for m in range(M)) * inp["num_heads"]

@@ -41,31 +41,51 @@ def num_partitions(inp, PS: int) -> int:
 
 def run_decode(dinp: Dict[str, object], PS: Optional[int] = None, P: Optional[int] = None,
                out_dtype=torch.float32, split: bool = False) -> Dict[str, torch.Tensor]:
-    """One decode through the C ABI; workspace pre-filled with NaN. Host copies back."""
+    """One batch through the C ABI; workspaces pre-filled with NaN. Host copies back.
+
+    split=True: paged_attn_v2_partition then paged_attn_v2_reduce only.
+    split=False: the same two calls (phase 1's per-partition rows and
+    statistics are what `tmp`, `es` and `ml` hold, and their output is
+    `out_split`), then paged_attn_decode on its own NaN-filled workspace:
+    `out` is the one-call result, which combines partitions inside the kernel
+    and leaves its workspace unspecified (`ws_tmp`, `ws_es`, `ws_ml`)."""
     q = dinp["query"]
     S, H, D = q.shape
     PS = PS or dinp["partition_size"]
     P = P or max(dinp["max_num_partitions"] if PS == dinp["partition_size"] else 1,
                  num_partitions(dinp, PS))
-    tmp = torch.full((S, H, P, D), float("nan"), device=DEV)
-    es = torch.full((S, H, P), float("nan"), device=DEV)
-    ml = torch.full((S, H, P), float("nan"), device=DEV)
-    out = torch.full((S, H, D), float("nan"), device=DEV).to(out_dtype)
+
+    def ws():
+        return (torch.full((S, H, P, D), float("nan"), device=DEV),
+                torch.full((S, H, P), float("nan"), device=DEV),
+                torch.full((S, H, P), float("nan"), device=DEV))
+
+    def new_out():
+        return torch.full((S, H, D), float("nan"), device=DEV).to(out_dtype)
+
     args = (q, dinp["key_cache"], dinp["value_cache"], dinp["block_tables"], dinp["seq_lens"])
-    if dinp["key_cache"].dtype == torch.float8_e4m3fn:
-        ks, vs = dinp["k_scale"], dinp["v_scale"]
-        if split:
-            pa.paged_attn_v2_partition_fp8(tmp, es, ml, *args, dinp["scale"], ks, vs, PS)
-            pa.paged_attn_v2_reduce(out, tmp, es, ml, dinp["seq_lens"], PS)
-        else:
-            pa.paged_attn_decode_fp8(out, tmp, es, ml, *args, dinp["scale"], ks, vs, PS)
-    elif split:
-        pa.paged_attn_v2_partition(tmp, es, ml, *args, dinp["scale"], PS)
-        pa.paged_attn_v2_reduce(out, tmp, es, ml, dinp["seq_lens"], PS)
+    fp8 = dinp["key_cache"].dtype == torch.float8_e4m3fn
+    ks, vs = dinp.get("k_scale", 1.0), dinp.get("v_scale", 1.0)
+    tmp, es, ml = ws()
+    out_s = new_out()
+    if fp8:
+        pa.paged_attn_v2_partition_fp8(tmp, es, ml, *args, dinp["scale"], ks, vs, PS)
     else:
-        pa.paged_attn_decode(out, tmp, es, ml, *args, dinp["scale"], PS)
+        pa.paged_attn_v2_partition(tmp, es, ml, *args, dinp["scale"], PS)
+    pa.paged_attn_v2_reduce(out_s, tmp, es, ml, dinp["seq_lens"], PS)
+    res = dict(tmp=tmp, es=es, ml=ml, P=P, PS=PS)
+    if split:
+        res["out"] = out_s
+    else:
+        wt, we, wm = ws()
+        out = new_out()
+        if fp8:
+            pa.paged_attn_decode_fp8(out, wt, we, wm, *args, dinp["scale"], ks, vs, PS)
+        else:
+            pa.paged_attn_decode(out, wt, we, wm, *args, dinp["scale"], PS)
+        res.update(out=out, out_split=out_s, ws_tmp=wt, ws_es=we, ws_ml=wm)
     torch.cuda.synchronize()
-    return dict(out=out.cpu(), tmp=tmp.cpu(), es=es.cpu(), ml=ml.cpu(), P=P, PS=PS)
+    return {k: v.cpu() if isinstance(v, torch.Tensor) else v for k, v in res.items()}
 
 
 def assert_close(name: str, got, ref, atol: float = ATOL, rtol: float = RTOL) -> float:
@@ -83,27 +103,38 @@ def assert_close(name: str, got, ref, atol: float = ATOL, rtol: float = RTOL) ->
 
 
 def check_against_oracle(inp: Dict[str, object], res: Dict[str, torch.Tensor],
-                         seqs: Optional[Sequence[int]] = None, label: str = "") -> None:
-    """Compare out and the partition intermediates of `seqs` (all if None) with the oracle."""
+                         seqs: Optional[Sequence[int]] = None, label: str = "") -> Dict[str, float]:
+    """Compare out (and out_split) and the partition intermediates of `seqs` (all if
+    None) with the oracle; returns the worst err/limit ratio per quantity (< 1 passes)."""
     S = inp["query"].shape[0]
     rows = list(range(S)) if seqs is None else sorted(set(int(s) for s in seqs))
     args = (inp["query"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
             inp["seq_lens"], inp["scale"])
     sc = dict(k_scale=inp.get("k_scale", 1.0), v_scale=inp.get("v_scale", 1.0))
     ref = oracle.attention(*args, seqs=rows, **sc)
-    assert_close(f"{label} out", res["out"][rows].float(), ref[rows])
+    worst = {"out": assert_close(f"{label} out", res["out"][rows].float(), ref[rows])}
+    if "out_split" in res:
+        worst["out_split"] = assert_close(f"{label} out (two calls)",
+                                          res["out_split"][rows].float(), ref[rows])
     tmp, es, ml = oracle.partition_stats(*args, res["P"], res["PS"], seqs=rows, **sc)
     sl = inp["seq_lens"].tolist()
+    ml_w = es_w = tmp_w = 0.0
     for s in rows:
         n = -(-sl[s] // res["PS"]) if sl[s] > 0 else 0
         if n:
-            assert_close(f"{label} max_logits s={s}", res["ml"][s, :, :n], ml[s, :, :n])
-            assert_close(f"{label} exp_sums s={s}", res["es"][s, :, :n], es[s, :, :n])
-            assert_close(f"{label} tmp_output s={s}", res["tmp"][s, :, :n], tmp[s, :, :n])
+            ml_w = max(ml_w, assert_close(f"{label} max_logits s={s}", res["ml"][s, :, :n],
+                                          ml[s, :, :n]))
+            es_w = max(es_w, assert_close(f"{label} exp_sums s={s}", res["es"][s, :, :n],
+                                          es[s, :, :n]))
+            tmp_w = max(tmp_w, assert_close(f"{label} tmp_output s={s}", res["tmp"][s, :, :n],
+                                            tmp[s, :, :n]))
         # empty partitions: exact sentinels, tmp_output untouched (still NaN)
         assert torch.all(res["ml"][s, :, n:] == -math.inf), f"{label} sentinel max s={s}"
         assert torch.all(res["es"][s, :, n:] == 0), f"{label} sentinel sum s={s}"
         assert torch.all(torch.isnan(res["tmp"][s, :, n:])), f"{label} tmp written s={s}"
+    worst.update(max_logits=ml_w, exp_sums=es_w, tmp_output=tmp_w)
+    note(f"{label}: worst err/limit " + " ".join(f"{k}={v:.3g}" for k, v in worst.items()))
+    return worst
 
 
 def small_config(name: str) -> W.DecodeConfig:

@@ -45,8 +45,31 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def test_ceiling_library_exports_its_symbols():
+    """libpa_ceiling.so (the benchmark's read-only page-gather instrument)
+    exports what include/pa_ceiling.h declares, and rejects bad sizes on the
+    host (nothing is launched)."""
+    from paged_kv_cache_v2_amd import ceiling
+    text = open(os.path.join(ROOT, "include", "pa_ceiling.h")).read()
+    names = re.findall(r"PA_CEILING_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+    assert sorted(names) == ["pa_gather_ceiling", "pa_gather_ceiling_sink_words"]
+    L = ceiling.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert ceiling.sink_words(3, 2, 65) == 3 * 2 * 3 * 4
+    assert L.pa_gather_ceiling(FAKE, 1, FAKE, FAKE, FAKE, FAKE, 2, 2, 4096, 16, 10, 8, None) == -2
+    assert L.pa_gather_ceiling(FAKE, 1 << 20, FAKE, FAKE, FAKE, FAKE, 2, 2, 3000, 16, 10, 8,
+                               None) == -2
+    assert L.pa_gather_ceiling(None, 1 << 20, FAKE, FAKE, FAKE, FAKE, 2, 2, 4096, 16, 10, 8,
+                               None) == -1
+    assert L.pa_gather_ceiling(FAKE, 1 << 20, FAKE + 4, FAKE, FAKE, FAKE, 2, 2, 4096, 16, 10, 8,
+                               None) == -4
+    assert L.pa_gather_ceiling(FAKE, 0, FAKE, FAKE, FAKE, FAKE, 0, 2, 4096, 16, 10, 8,
+                               None) == 0  # no sequences: a no-op
+
+
 def test_abi_version_and_default_partition_size():
-    assert pa.abi_version() == 1
+    assert pa.abi_version() == 2
     for D, BS, dt, G in [(128, 16, torch.bfloat16, 4), (256, 32, torch.float16, 1),
                          (64, 16, torch.float32, 1), (128, 16, torch.bfloat16, 32)]:
         ps = pa.default_partition_size(D, BS, dt, G)

@@ -106,6 +106,7 @@ def test_fp8_seq_len_one_returns_scaled_v(name):
                            inp["block_tables"], inp["seq_lens"], inp["scale"],
                            k_scale=inp["k_scale"], v_scale=inp["v_scale"])
     assert np.array_equal(res["out"].double().numpy(), ref)
+    assert np.array_equal(res["out_split"].double().numpy(), ref)
     v = inp["value_cache"].to(torch.float32) / 32
     G = cfg.group
     for s in range(cfg.num_seqs):

@@ -112,10 +112,11 @@ class Selector:
 
 
 def check(res, expect, label):
-    got = res["out"][:, :, :expect.shape[-1]]
-    if not torch.equal(got, expect):
-        bad = (got != expect).any(-1).nonzero()[:5].tolist()
-        raise AssertionError(f"{label}: gathered indices differ at (s, h) {bad}")
+    for k in ("out", "out_split"):  # the one call, and the two calls
+        got = res[k][:, :, :expect.shape[-1]]
+        if not torch.equal(got, expect):
+            bad = (got != expect).any(-1).nonzero()[:5].tolist()
+            raise AssertionError(f"{label} ({k}): gathered indices differ at (s, h) {bad}")
 
 
 def test_selector_exhaustive_tiny():
@@ -165,6 +166,7 @@ def test_seq_len_one_returns_v(name):
     ref = oracle.attention(inp["query"], inp["key_cache"], inp["value_cache"],
                            inp["block_tables"], inp["seq_lens"], inp["scale"])
     assert np.array_equal(res["out"].double().numpy(), ref)
+    assert np.array_equal(res["out_split"].double().numpy(), ref)
     v = inp["value_cache"].float()
     G = cfg.group
     for s in range(cfg.num_seqs):
@@ -191,7 +193,7 @@ def test_block_relabelling_bit_identical(name):
     U.note(f"T3 {name}")
     a = U.run_decode(U.to_device(inp))
     b = U.run_decode(U.to_device(inp2))
-    for k in ("out", "es", "ml"):
+    for k in ("out", "out_split", "es", "ml"):
         assert torch.equal(a[k], b[k]), k
     assert torch.equal(a["tmp"].nan_to_num(nan=3.0), b["tmp"].nan_to_num(nan=3.0))
 
@@ -204,5 +206,5 @@ def test_run_to_run_bit_identical(name):
     U.note(f"determinism {name}")
     a = U.run_decode(d)
     b = U.run_decode(d)
-    for k in ("out", "es", "ml"):
+    for k in ("out", "out_split", "es", "ml"):
         assert torch.equal(a[k], b[k]), k

@@ -18,6 +18,7 @@ import torch
 import oracle
 import paged_kv_cache_v2_amd as pa
 from paged_kv_cache_v2_amd import workloads as W
+from tests import rows as R
 from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
@@ -30,21 +31,30 @@ def built():
 
 
 def run_mq(d, PS, P, split=False, out_dtype=torch.float32):
+    """The two calls (paged_attn_v2_partition_mq + paged_attn_v2_reduce_mq: `tmp`,
+    `es`, `ml` and their output); with split=False also paged_attn_decode_mq on
+    its own workspace, whose output is `out` (the two calls' is `out_split`)."""
     q = d["query"]
     S, M, H, D = q.shape
-    tmp = torch.full((S, M, H, P, D), float("nan"), device=U.DEV)
-    es = torch.full((S, M, H, P), float("nan"), device=U.DEV)
-    ml = torch.full((S, M, H, P), float("nan"), device=U.DEV)
-    out = torch.full((S, M, H, D), float("nan"), device=U.DEV).to(out_dtype)
+
+    def ws():
+        return (torch.full((S, M, H, P, D), float("nan"), device=U.DEV),
+                torch.full((S, M, H, P), float("nan"), device=U.DEV),
+                torch.full((S, M, H, P), float("nan"), device=U.DEV))
+
     args = (q, d["key_cache"], d["value_cache"], d["block_tables"], d["seq_lens"], d["scale"], PS)
     sc = dict(k_scale=d.get("k_scale", 1.0), v_scale=d.get("v_scale", 1.0))
-    if split:
-        pa.paged_attn_v2_partition_mq(tmp, es, ml, *args, **sc)
-        pa.paged_attn_v2_reduce_mq(out, tmp, es, ml, d["seq_lens"], PS)
-    else:
-        pa.paged_attn_decode_mq(out, tmp, es, ml, *args, **sc)
+    tmp, es, ml = ws()
+    out_s = torch.full((S, M, H, D), float("nan"), device=U.DEV).to(out_dtype)
+    pa.paged_attn_v2_partition_mq(tmp, es, ml, *args, **sc)
+    pa.paged_attn_v2_reduce_mq(out_s, tmp, es, ml, d["seq_lens"], PS)
+    res = dict(tmp=tmp, es=es, ml=ml, out=out_s)
+    if not split:
+        out = torch.full((S, M, H, D), float("nan"), device=U.DEV).to(out_dtype)
+        pa.paged_attn_decode_mq(out, *ws(), *args, **sc)
+        res.update(out=out, out_split=out_s)
     torch.cuda.synchronize()
-    return dict(out=out.cpu(), tmp=tmp.cpu(), es=es.cpu(), ml=ml.cpu())
+    return {k: v.cpu() for k, v in res.items()}
 
 
 def check(inp, res, PS, P, label):
@@ -53,11 +63,13 @@ def check(inp, res, PS, P, label):
     sc = dict(k_scale=inp["k_scale"], v_scale=inp["v_scale"])
     ref = oracle.attention(*a, **sc)
     U.assert_close(f"{label} out", res["out"].float(), ref)
+    if "out_split" in res:
+        U.assert_close(f"{label} out (two calls)", res["out_split"].float(), ref)
     tmp, es, ml = oracle.partition_stats(*a, P, PS, **sc)
     M = inp["query"].shape[1]
     for s, L in enumerate(inp["seq_lens"].tolist()):
         for m in range(M):
-            n = -(-W.causal_len(L, M, m) // PS)
+            n = -(-R.causal_len(L, M, m) // PS)
             if n:
                 U.assert_close(f"{label} ml s={s} m={m}", res["ml"][s, m, :, :n], ml[s, m, :, :n])
                 U.assert_close(f"{label} es s={s} m={m}", res["es"][s, m, :, :n], es[s, m, :, :n])
@@ -175,21 +187,17 @@ _FULL = {}
 
 @pytest.mark.parametrize("name", W.MQ_ORDER)
 @pytest.mark.parametrize("ps", ["config", "planned"])
-def test_multi_token_full_size_sampled(name, ps):
-    """The multi-token workloads at full size, in the launch configurations
-    bench.py times (the configured partition size through the two calls, the
-    size the library plans for the batch through paged_attn_decode_mq):
-    sampled sequences against the oracle, properties at every row."""
+def test_multi_token_full_size(name, ps):
+    """The multi-token workloads at full size, at the configured and at the
+    planned partition size, through the one call and the two calls: every
+    output row and every used partition's row and statistics against the
+    oracle, sentinels exact past each row's causal prefix."""
     cfg = W.CONFIGS[name]
     if name not in _FULL:
         _FULL.clear()
         inp = W.make_inputs(cfg, seed=W.workload_seed(name))
         _FULL[name] = (inp, U.to_device(inp))
     inp, d = _FULL[name]
-    sl = inp["seq_lens"].numpy()
-    S, M = len(sl), cfg.num_queries
-    # the longest and shortest sequence and one more (one if all lengths are equal)
-    seqs = sorted({int(np.argmax(sl)), int(np.argmin(sl)), 1 % S}) if sl.min() < sl.max() else [0]
     if ps == "config":
         PS, P = cfg.partition_size, cfg.max_num_partitions
     else:
@@ -197,17 +205,7 @@ def test_multi_token_full_size_sampled(name, ps):
                                     cfg.head_size, cfg.block_size, cfg.max_len,
                                     W.DTYPES[cfg.dtype])
         P = max(1, -(-cfg.max_len // PS))
-    U.note(f"multi-token full {name} ps={PS} seqs={seqs}")
-    res = run_mq(d, PS, P, split=(ps == "config"))
+    U.note(f"multi-token full {name} ps={PS}")
+    res = run_mq(d, PS, P)
     assert torch.isfinite(res["out"]).all()
-    a = (inp["query"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
-         inp["seq_lens"], inp["scale"])
-    ref = oracle.attention(*a, seqs=seqs)
-    U.assert_close(f"mq full {name}", res["out"][seqs].float(), ref[seqs])
-    for s in range(S):
-        for m in range(M):
-            n = -(-W.causal_len(int(sl[s]), M, m) // PS)
-            assert torch.all(res["ml"][s, m, :, n:] == -math.inf), (s, m)
-            assert torch.all(res["es"][s, m, :, n:] == 0), (s, m)
-            assert torch.isfinite(res["ml"][s, m, :, :n]).all(), (s, m)
-            assert torch.all(res["es"][s, m, :, :n] >= 1), (s, m)
+    check(inp, res, PS, P, f"mq full {name} PS={PS}")

@@ -21,6 +21,7 @@ import torch
 import oracle
 import paged_kv_cache_v2_amd as pa
 from paged_kv_cache_v2_amd import workloads as W
+from tests import rows as R
 from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
@@ -85,16 +86,16 @@ def test_random_config(i):
     out = torch.full(q.shape, float("nan"), device=U.DEV)
     lse = torch.full(lead, float("nan"), device=U.DEV)
     U.note(f"random case {i}: {cfg} lens={lens} alibi={alibi}")
-    pa.paged_attn_decode_ex(out, tmp, es, ml, q, d["key_cache"], d["value_cache"],
-                            d["block_tables"], d["seq_lens"], d["scale"], PS,
-                            k_scale=inp["k_scale"], v_scale=inp["v_scale"],
-                            alibi_slopes=slopes.to(U.DEV) if alibi else None, lse=lse)
+    call = (q, d["key_cache"], d["value_cache"], d["block_tables"], d["seq_lens"], d["scale"], PS)
+    sc = dict(k_scale=inp["k_scale"], v_scale=inp["v_scale"],
+              alibi_slopes=slopes.to(U.DEV) if alibi else None)
+    # the one call (its workspace: a copy of the NaN-filled buffers), then phase
+    # 1 alone for the per-partition rows and statistics
+    pa.paged_attn_decode_ex(out, tmp.clone(), es.clone(), ml.clone(), *call, lse=lse, **sc)
     if out16:  # the same call with a 16-bit output is the RNE cast of the fp32 one
         o16 = torch.empty(q.shape, dtype=q.dtype, device=U.DEV)
-        pa.paged_attn_decode_ex(o16, tmp, es, ml, q, d["key_cache"], d["value_cache"],
-                                d["block_tables"], d["seq_lens"], d["scale"], PS,
-                                k_scale=inp["k_scale"], v_scale=inp["v_scale"],
-                                alibi_slopes=slopes.to(U.DEV) if alibi else None)
+        pa.paged_attn_decode_ex(o16, tmp.clone(), es.clone(), ml.clone(), *call, **sc)
+    pa.paged_attn_v2_partition_ex(tmp, es, ml, *call, **sc)
     torch.cuda.synchronize()
     a = (inp["query"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
          inp["seq_lens"], inp["scale"])
@@ -110,7 +111,7 @@ def test_random_config(i):
     gt, ge, gm = tmp.cpu(), es.cpu(), ml.cpu()
     for s, L in enumerate(lens):
         for m in range(M):
-            n = -(-W.causal_len(L, M, m) // PS)
+            n = -(-R.causal_len(L, M, m) // PS)
             idx = (s, m) if M > 1 else (s,)
             if n:
                 U.assert_close(f"case {i} ml {s},{m}", gm[idx][:, :n], rml[idx][:, :n])
@@ -170,10 +171,11 @@ def test_random_large_batch(i):
     out = torch.full(q.shape, float("nan"), device=U.DEV)
     lse = torch.full(lead, float("nan"), device=U.DEV)
     U.note(f"random batch {i}: {cfg} alibi={alibi} span={span}")
-    pa.paged_attn_decode_ex(out, tmp, es, ml, q, d["key_cache"], d["value_cache"],
-                            d["block_tables"], d["seq_lens"], d["scale"], PS,
-                            k_scale=inp["k_scale"], v_scale=inp["v_scale"],
-                            alibi_slopes=slopes.to(U.DEV) if alibi else None, lse=lse)
+    call = (q, d["key_cache"], d["value_cache"], d["block_tables"], d["seq_lens"], d["scale"], PS)
+    sc = dict(k_scale=inp["k_scale"], v_scale=inp["v_scale"],
+              alibi_slopes=slopes.to(U.DEV) if alibi else None)
+    pa.paged_attn_decode_ex(out, tmp.clone(), es.clone(), ml.clone(), *call, lse=lse, **sc)
+    pa.paged_attn_v2_partition_ex(tmp, es, ml, *call, **sc)   # phase 1 alone
     torch.cuda.synchronize()
     a = (inp["query"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
          inp["seq_lens"], inp["scale"])
@@ -186,7 +188,7 @@ def test_random_large_batch(i):
     U.assert_close(f"batch {i} lse", got_lse[fin], ref_lse[fin])
     # statistics of every used partition at once; sentinels past each row's prefix
     rtmp, res_, rml = oracle.partition_stats(*a, P, PS, **sc)
-    n = np.array([[-(-W.causal_len(L, M, m) // PS) for m in range(M)] for L in lens])
+    n = np.array([[-(-R.causal_len(L, M, m) // PS) for m in range(M)] for L in lens])
     used = np.arange(P)[None, None, :] < n[:, :, None]          # [S, M, P]
     used = used.reshape((len(lens),) + ((M,) if M > 1 else ()) + (1, P))
     used = np.broadcast_to(used, tuple(es.shape))

@@ -17,6 +17,7 @@ import torch
 import oracle
 import paged_kv_cache_v2_amd as pa
 from paged_kv_cache_v2_amd import workloads as W
+from tests import rows as R
 from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
@@ -54,7 +55,7 @@ def inputs(c, seed):
 
 def keys_seen(lens, M):
     """[S, M] keys each query token sees (its causal prefix)."""
-    return np.array([[W.causal_len(L, M, m) for m in range(M)] for L in lens])
+    return np.array([[R.causal_len(L, M, m) for m in range(M)] for L in lens])
 
 
 @pytest.mark.parametrize("c", CASES, ids=lambda c: "_".join(map(str, c)))

@@ -62,23 +62,33 @@ def case(label, seed):
 
 
 def run(d, PS, P, split, slopes=None):
+    """The two calls (paged_attn_v2_partition_ex + paged_attn_v2_reduce_lse: `tmp`,
+    `es`, `ml`, their output and lse); unless split, also paged_attn_decode_ex on
+    its own workspace, whose output and lse are `out` and `lse`."""
     q = d["query"]
     S, H, D = q.shape
-    tmp = torch.full((S, H, P, D), float("nan"), device=U.DEV)
-    es = torch.full((S, H, P), float("nan"), device=U.DEV)
-    ml = torch.full((S, H, P), float("nan"), device=U.DEV)
-    out = torch.full((S, H, D), float("nan"), device=U.DEV)
-    lse = torch.full((S, H), float("nan"), device=U.DEV)
+
+    def ws():
+        return (torch.full((S, H, P, D), float("nan"), device=U.DEV),
+                torch.full((S, H, P), float("nan"), device=U.DEV),
+                torch.full((S, H, P), float("nan"), device=U.DEV))
+
     args = (q, d["key_cache"], d["value_cache"], d["block_tables"], d["seq_lens"], d["scale"], PS)
     sc = dict(k_scale=d.get("k_scale", 1.0), v_scale=d.get("v_scale", 1.0),
               alibi_slopes=slopes.to(U.DEV) if slopes is not None else None)
-    if split:
-        pa.paged_attn_v2_partition_ex(tmp, es, ml, *args, **sc)
-        pa.paged_attn_v2_reduce_lse(out, lse, tmp, es, ml, d["seq_lens"], PS)
-    else:
-        pa.paged_attn_decode_ex(out, tmp, es, ml, *args, lse=lse, **sc)
+    tmp, es, ml = ws()
+    out_s = torch.full((S, H, D), float("nan"), device=U.DEV)
+    lse_s = torch.full((S, H), float("nan"), device=U.DEV)
+    pa.paged_attn_v2_partition_ex(tmp, es, ml, *args, **sc)
+    pa.paged_attn_v2_reduce_lse(out_s, lse_s, tmp, es, ml, d["seq_lens"], PS)
+    res = dict(tmp=tmp, es=es, ml=ml, out=out_s, lse=lse_s)
+    if not split:
+        out = torch.full((S, H, D), float("nan"), device=U.DEV)
+        lse = torch.full((S, H), float("nan"), device=U.DEV)
+        pa.paged_attn_decode_ex(out, *ws(), *args, lse=lse, **sc)
+        res.update(out=out, lse=lse, out_split=out_s, lse_split=lse_s)
     torch.cuda.synchronize()
-    return dict(out=out.cpu(), lse=lse.cpu(), tmp=tmp.cpu(), es=es.cpu(), ml=ml.cpu())
+    return {k: v.cpu() for k, v in res.items()}
 
 
 def check(inp, res, PS, P, label, slopes=None):
@@ -86,11 +96,14 @@ def check(inp, res, PS, P, label, slopes=None):
          inp["seq_lens"], inp["scale"])
     sc = dict(k_scale=inp["k_scale"], v_scale=inp["v_scale"], alibi_slopes=slopes)
     ref, ref_lse = oracle.attention_lse(*a, **sc)
-    U.assert_close(f"{label} out", res["out"], ref)
-    got_lse = res["lse"].double().numpy()
     empty = np.isneginf(ref_lse)
-    assert np.array_equal(np.isneginf(got_lse), empty), f"{label} lse -inf rows"
-    U.assert_close(f"{label} lse", got_lse[~empty], ref_lse[~empty])
+    for o, l in (("out", "lse"), ("out_split", "lse_split")):
+        if o not in res:
+            continue
+        U.assert_close(f"{label} {o}", res[o], ref)
+        got_lse = res[l].double().numpy()
+        assert np.array_equal(np.isneginf(got_lse), empty), f"{label} {l} -inf rows"
+        U.assert_close(f"{label} {l}", got_lse[~empty], ref_lse[~empty])
     tmp, es, ml = oracle.partition_stats(*a, P, PS, **sc)
     for s, L in enumerate(inp["seq_lens"].tolist()):
         n = -(-L // PS)
@@ -131,12 +144,16 @@ def test_single_query_equals_one_token_window(label):
     single = run(d, PS, P, False)
     q4 = d["query"][:, None].contiguous()
     S, _, H, D = q4.shape
-    tmp = torch.full((S, 1, H, P, D), float("nan"), device=U.DEV)
-    es = torch.full((S, 1, H, P), float("nan"), device=U.DEV)
-    ml = torch.full((S, 1, H, P), float("nan"), device=U.DEV)
+    def ws():
+        return (torch.full((S, 1, H, P, D), float("nan"), device=U.DEV),
+                torch.full((S, 1, H, P), float("nan"), device=U.DEV),
+                torch.full((S, 1, H, P), float("nan"), device=U.DEV))
+
+    a = (q4, d["key_cache"], d["value_cache"], d["block_tables"], d["seq_lens"], d["scale"], PS)
     out = torch.full((S, 1, H, D), float("nan"), device=U.DEV)
-    pa.paged_attn_decode_mq(out, tmp, es, ml, q4, d["key_cache"], d["value_cache"],
-                            d["block_tables"], d["seq_lens"], d["scale"], PS)
+    pa.paged_attn_decode_mq(out, *ws(), *a)           # the one-call form
+    tmp, es, ml = ws()
+    pa.paged_attn_v2_partition_mq(tmp, es, ml, *a)    # phase 1 alone
     torch.cuda.synchronize()
     assert torch.equal(out[:, 0].cpu(), single["out"])
     assert torch.equal(es[:, 0].cpu(), single["es"])

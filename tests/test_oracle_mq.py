@@ -20,6 +20,7 @@ import torch
 
 import oracle
 from paged_kv_cache_v2_amd import workloads as W
+from tests import rows as R
 from tests import dense_views as DV
 
 
@@ -127,7 +128,7 @@ def test_partition_combine_equals_dense(PS):
     # sentinels exactly where a query row's causal prefix ends
     for s, L in enumerate(inp["seq_lens"].tolist()):
         for m in range(M):
-            n = -(-W.causal_len(L, M, m) // PS)
+            n = -(-R.causal_len(L, M, m) // PS)
             assert np.all(ml[s, m, :, n:] == -np.inf) and np.all(es[s, m, :, n:] == 0)
             assert np.all(np.isfinite(ml[s, m, :, :n]))
 

@@ -84,10 +84,3 @@ def test_poison_unused_leaves_read_slots():
         if L % 16:
             b = int(bt[s, (L - 1) // 16])
             assert torch.isnan(inp["value_cache"][b, :, :, L % 16:].float()).all()
-
-
-def test_kv_bytes():
-    inp = W.make_inputs(W.CONFIGS["tiny_f32_d64"], seed=1)
-    assert W.kv_bytes(inp) == 137 * 4 * 2 * 64 * 4
-    assert W.qhead_tokens(inp) == 137 * 4
-    assert np.isclose(280_576, W.kv_bytes(inp))
