@@ -403,6 +403,20 @@ PA_API int paged_attn_partition_span(int32_t num_seqs, int32_t num_heads, int32_
                                      int32_t max_num_partitions, int32_t partition_size,
                                      int32_t kv_dtype);
 
+/* Launch plan inspection for the one-call decode (paged_attn_decode*): writes
+ * plan_out[0] = partitions per workgroup (the span C), plan_out[1] = ring
+ * slots of the rolling merge (0: the span's parked states are combined at the
+ * end; 1 or 2: partitions are merged as the span streams, for spans whose
+ * parked states would not fit on chip), plan_out[2] = span entries per row
+ * (ceil(P / C); 1: no reduce runs), plan_out[3] = column launches. Results do
+ * not depend on the plan beyond fp32 rounding. Host-side, no device work;
+ * returns PA_OK or the PA_ERR_* code the decode calls would return for these
+ * sizes and dtypes (plan_out NULL: PA_ERR_NULL; num_seqs < 1: PA_ERR_SHAPE). */
+PA_API int paged_attn_decode_plan(int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                  int32_t max_num_partitions, int32_t partition_size,
+                                  int32_t q_dtype, int32_t kv_dtype, int32_t* plan_out);
+
 #ifdef __cplusplus
 }
 #endif

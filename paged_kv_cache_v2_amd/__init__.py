@@ -6,7 +6,7 @@ plus the seeded synthetic-input generator.
 """
 from .binding import (PA_BF16, PA_FP8_E4M3, PA_ERR_ALIGN, PA_ERR_HIP, PA_ERR_NULL, PA_ERR_SHAPE,  # noqa: F401
                       PA_ERR_UNSUPPORTED, PA_F16, PA_F32, PA_OK, abi_version,
-                      default_partition_size, ensure_built, last_error, lib, paged_attn_decode,
+                      decode_plan, default_partition_size, ensure_built, last_error, lib, paged_attn_decode,
                       paged_attn_decode_fp8, paged_attn_v2_partition_fp8,
                       paged_attn_decode_mq, paged_attn_v2_partition_mq, paged_attn_v2_reduce_mq,
                       paged_attn_decode_lse, paged_attn_v2_reduce_lse, paged_attn_merge_states,

@@ -32,6 +32,7 @@ _SIGS = {
     "paged_attn_default_partition_size": [_I32, _I32, _I32, _I32],
     "paged_attn_partition_span": [_I32] * 8,
     "paged_attn_plan_partition_size": [_I32] * 7,
+    "paged_attn_decode_plan": [_I32] * 10 + [_P],
     "paged_attn_v2_partition_fp8": [_P] * 8 + [_I32] * 9 + [_F32, _F32, _F32, _I32, _P],
     "paged_attn_decode_fp8": [_P] * 9 + [_I32] * 9 + [_F32, _F32, _F32, _I32, _I32, _P],
     "paged_attn_v2_partition_mq": [_P] * 8 + [_I32] * 10 + [_F32, _F32, _F32, _I32, _I32, _P],
@@ -103,6 +104,22 @@ def partition_span(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: 
     if rc < 0:
         raise RuntimeError(f"paged_attn_partition_span: {last_error()} (code {rc})")
     return rc
+
+
+def decode_plan(num_seqs: int, num_queries: int, num_heads: int, num_kv_heads: int,
+                head_size: int, block_size: int, max_num_partitions: int, partition_size: int,
+                q_dtype: torch.dtype, kv_dtype: torch.dtype) -> dict:
+    """The one-call decode's launch plan for these sizes (host-side query):
+    span (partitions per workgroup), roll (ring slots of the rolling merge, 0:
+    none), entries (span entries per row; 1: no reduce), launches (column
+    launches)."""
+    _need(q_dtype in _DT, f"query dtype must be float32, float16 or bfloat16, got {q_dtype}")
+    out = (ctypes.c_int32 * 4)()
+    _check("paged_attn_decode_plan",
+           lib().paged_attn_decode_plan(num_seqs, num_queries, num_heads, num_kv_heads,
+                                        head_size, block_size, max_num_partitions,
+                                        partition_size, _DT[q_dtype], _cache_dt(kv_dtype), out))
+    return dict(span=out[0], roll=out[1], entries=out[2], launches=out[3])
 
 
 def _check(name: str, rc: int) -> None:

@@ -103,10 +103,12 @@ __device__ __forceinline__ T stream_load(const void* p) {
 
 // Software pipeline over a wavefront's pages: fetch(i, buf) is issued PF pages
 // ahead of process(i, buf); buffers rotate through a ring whose indices are
-// compile-time constants after unrolling, so they stay in registers.
-template <int PF, typename Buf, typename Fetch, typename Process>
+// compile-time constants after unrolling, so they stay in registers. pre(i)
+// runs before page i + PF is fetched (page i is then already in flight and
+// the ring slot of page i + PF still free: the fewest registers are live).
+template <int PF, typename Buf, typename Fetch, typename Process, typename Pre>
 __device__ __forceinline__ void pipeline(int n, Buf (&buf)[PF + 1], Fetch&& fetch,
-                                         Process&& process) {
+                                         Process&& process, Pre&& pre) {
   constexpr int NB = PF + 1;
 #pragma unroll
   for (int b = 0; b < PF; ++b)
@@ -119,6 +121,7 @@ __device__ __forceinline__ void pipeline(int n, Buf (&buf)[PF + 1], Fetch&& fetc
   for (; PF > 0 && t0 + NB + PF <= n; t0 += NB) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
+      pre(t0 + b);
       fetch(t0 + b + PF, buf[(b + PF) % NB]);
 #if PA_PIN_PREFETCH
       __builtin_amdgcn_sched_barrier(0);
@@ -132,6 +135,7 @@ __device__ __forceinline__ void pipeline(int n, Buf (&buf)[PF + 1], Fetch&& fetc
     for (int b = 0; b < NB; ++b) {
       const int t = t0 + b;
       if (t < n) {
+        pre(t);
         if (t + PF < n) fetch(t + PF, buf[(b + PF) % NB]);
 #if PA_PIN_PREFETCH
         // Keep the prefetch loads ahead of this page's compute: left free, the
@@ -204,6 +208,10 @@ struct PartitionArgs {
   void* out;           // fuse, Pq == 1: out [S * Mq * H, D] in odt
   float* lse;          // fuse, Pq == 1: optional [S * Mq * H] row log-sum-exp (NULL: none)
   int odt;             // DT_F32, DT_F16 or DT_BF16
+  int roll;            // fuse, MFMA kernel: 0 (combine_store) or R = 1, 2 ring slots of
+                       // the rolling merge (see roll_layout)
+  int lds_bytes;       // dynamic LDS of the launch: a kernel whose layout needs more
+                       // returns at once, writing nothing (a host planning error)
 };
 
 // ALiBi: a query at position i adds slope_h * (j - i) to its scaled score for
@@ -232,6 +240,28 @@ __host__ __device__ inline LdsLayout lds_layout(int PS, int BS, int NC, int D, i
   o.l_off = o.m_off + up16(C * kWaves * NC * 4);
   o.acc_off = o.l_off + up16(C * kWaves * NC * 4);
   o.total = o.acc_off + C * kWaves * NC * D * 4;
+  return o;
+}
+
+// LDS of the rolling merge (the MFMA kernel's one-call decode, a.roll = R):
+// the span's block-table slice; R ring slots, each holding per wavefront and
+// column tile its 16 columns' running max and exp sum, then, per owning
+// wavefront, source wavefront (the three others), column tile and owned
+// d-block, the source's 64 lanes x 16 bytes of accumulator; then each
+// wavefront's running rows (per tile and owned d-block, 64 lanes x 16 bytes).
+// A wavefront owns D / 64 of the D / 16 d-blocks of 16 rows.
+struct RollLayout {
+  int bt_off, slot_off, slot_bytes, stat_bytes, run_off, total;
+};
+__host__ __device__ inline RollLayout roll_layout(int PS, int BS, int CT, int D, int C, int R) {
+  RollLayout o;
+  const int VQ = D / 64;
+  o.bt_off = 0;
+  o.slot_off = (C * (PS / BS) * 4 + 15) & ~15;
+  o.stat_bytes = kWaves * CT * 16 * 4 * 2;
+  o.slot_bytes = o.stat_bytes + kWaves * 3 * CT * VQ * 1024;
+  o.run_off = o.slot_off + R * o.slot_bytes;
+  o.total = o.run_off + kWaves * CT * VQ * 1024;
   return o;
 }
 
@@ -658,11 +688,26 @@ constexpr int mfma_waves(int D, int BS, bool KV8, bool AL, int CT) {
                 : (PA_MIN_WAVES > 0 ? PA_MIN_WAVES : D * BS <= 4096 ? 2 : 1);
 }
 
-template <int DT, int D, int BS, bool KV8, bool AL, int CT>
+// Pages in flight for the rolling-merge kernels: as the others, except with
+// two column tiles, whose registers (two accumulators, two query operands,
+// the merge) only fit two wavefronts per SIMD without a page of prefetch.
+#ifndef PA_ROLL_CT2_PREFETCH
+#define PA_ROLL_CT2_PREFETCH 0
+#endif
+template <bool ROLL, int CT>
+constexpr int roll_prefetch(int pf) {
+  return ROLL && CT > 1 ? (pf < PA_ROLL_CT2_PREFETCH ? pf : PA_ROLL_CT2_PREFETCH) : pf;
+}
+
+// ROLL: the one-call decode's rolling merge (16-bit caches only; see
+// park_roll), a separate instantiation so that the other kernels carry none
+// of its code or registers.
+template <int DT, int D, int BS, bool KV8, bool AL, int CT, bool ROLL>
 __global__ void __launch_bounds__(kWaves * 64)
 __attribute__((amdgpu_waves_per_eu(mfma_waves(D, BS, KV8, AL, CT))))
 partition_mfma_kernel(PartitionArgs a) {
   static_assert(CT == 1 || CT == 2, "one or two column tiles");
+  static_assert(!(ROLL && KV8), "the rolling merge is built for 16-bit caches");
   constexpr int SUB = BS / 16;  // 16-token sub-tiles per page
   constexpr int KS = D / 32;    // QK k-steps (32 d each) per sub-tile
   constexpr int KL = KV8 ? D / 64 : D / 32;  // K 16-byte loads per lane per sub-tile
@@ -670,7 +715,7 @@ partition_mfma_kernel(PartitionArgs a) {
   constexpr int ESZ = KV8 ? 1 : 2;
   constexpr size_t PAGE = (size_t)D * BS * ESZ;  // bytes of one (block, kv head) page
   constexpr int PREGS = SUB * (KL * 4 + VB * (KV8 ? 1 : 2));
-  constexpr int PF = KV8 ? prefetch_fp8(PREGS) : prefetch_for(PREGS);
+  constexpr int PF = KV8 ? prefetch_fp8(PREGS) : roll_prefetch<ROLL, CT>(prefetch_for(PREGS));
   using C = codec<DT>;
   using M = mma<DT>;
   using Page = MfmaPage<KV8, SUB, D>;
@@ -688,6 +733,7 @@ partition_mfma_kernel(PartitionArgs a) {
   // running max stays put like a live column's.
   int lim[CT];
   float slope2[CT];  // ALiBi slope of the column, log2 units
+  int qpos[CT];      // the column's query position (ALiBi, rolling merge)
   u32x4 qb[CT][KS];  // Q columns as the QK B operand
 #pragma unroll
   for (int t = 0; t < CT; ++t) {
@@ -695,6 +741,7 @@ partition_mfma_kernel(PartitionArgs a) {
     const int c = a.c0 + (live ? 16 * t + g : 0);
     const int qm = c / G, h = c - qm * G;
     lim[t] = min(u.L, max(0, u.L - a.Mq + qm + 1));
+    qpos[t] = u.L - a.Mq + qm;
     slope2[t] = AL && live ? a.alibi[u.kh * G + h] * kLog2e : 0.0f;
     // k-step mk: lane holds 8 consecutive d of its column, d = 32mk + 8*grp
     // (16-bit cache) or 16*(4*(mk/2) + grp) + 8*(mk%2) (8-bit).
@@ -707,8 +754,11 @@ partition_mfma_kernel(PartitionArgs a) {
       qb[t][mk] = live ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  if (!unit_hoist<BS, D>(a, (int32_t*)smem, u)) return;
   const LdsLayout lay = lds_layout(a.PS, BS, NC, D, a.C);
+  if ((ROLL ? roll_layout(a.PS, BS, CT, D, a.C, a.roll == 2 ? 2 : 1).total : lay.total) >
+      a.lds_bytes)
+    return;  // (uniform: the launch's LDS does not hold this kernel's layout)
+  if (!unit_hoist<BS, D>(a, (int32_t*)smem, u)) return;
   const int32_t* s_bt = (const int32_t*)(smem + lay.bt_off);
   float* s_m = (float*)(smem + lay.m_off);
   float* s_l = (float*)(smem + lay.l_off);
@@ -741,7 +791,7 @@ partition_mfma_kernel(PartitionArgs a) {
   // Park this wavefront's state of partition jcur of the span in LDS and
   // start the next partition empty (wavefront-uniform control flow).
   int jcur = 0, next_edge = pps;  // next_edge: first page of partition jcur + 1
-  auto park = [&]() {
+  auto park = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < CT; ++t) {
       const float ls = rows_sum(lsum[t]);
@@ -758,6 +808,114 @@ partition_mfma_kernel(PartitionArgs a) {
           for (int r = 0; r < 4; ++r) dst[16 * mb + r] = acc[t][mb][r];
         }
       }
+      m[t] = kNegInf;
+      lsum[t] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < VB; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    ++jcur;
+    next_edge += pps;
+  };
+
+  // Rolling merge (one-call decode, a.roll = R ring slots; roll_layout). At
+  // each partition edge every wavefront hands the three quarters of its
+  // accumulator that it does not own (d-blocks mb with mb / VQ != wave) to
+  // their owners through LDS, with its columns' max and exp sum; after a
+  // barrier each wavefront merges its own quarter of the partition over the
+  // four wavefronts -- the partition's max logit, exp sum and normalised row,
+  // exactly what the plain epilogue stores for it -- and folds that into its
+  // running combination of the span's partitions with the log-sum-exp rule
+  // (running max rM, sum rZ = sum_j e^(m_j - rM) l_j, rows sum_j e^(m_j - rM)
+  // l_j o_j in LDS; the span's row is their ratio). With one slot, a second
+  // barrier keeps the next partition's writes behind this one's merge; with
+  // two, the next edge's barrier does. Every wavefront parks every used
+  // partition of the span once, so all reach the same barriers.
+  constexpr int VQ = VB / 4;
+  static_assert(kWaves == 4 && VB % 4 == 0, "the rolling merge splits d-blocks over 4 wavefronts");
+  float rM[CT], rZ[CT];
+#pragma unroll
+  for (int t = 0; t < CT; ++t) {
+    rM[t] = kNegInf;
+    rZ[t] = 0.0f;
+  }
+  const int R = a.roll == 2 ? 2 : 1;  // ring slots (the host plans 1 or 2)
+  const RollLayout rl = roll_layout(a.PS, BS, CT, D, a.C, R);
+  f32x4* s_run = (f32x4*)(smem + rl.run_off) + wave * CT * VQ * 64 + lane;  // [t][mbl] x 64 lanes
+  auto park_roll = [&]() __attribute__((always_inline)) {
+    uint8_t* slotp = smem + rl.slot_off + (R == 2 ? (jcur & 1) : 0) * rl.slot_bytes;
+    float* st_m = (float*)slotp;                 // [wave][t][16]
+    float* st_l = st_m + kWaves * CT * 16;
+    f32x4* xch = (f32x4*)(slotp + rl.stat_bytes);  // [owner][source 0..2][t][mbl][64 lanes]
+    if (R == 1 && jcur > 0) __syncthreads();  // the slot's last merge is done
+#pragma unroll
+    for (int t = 0; t < CT; ++t) {
+      const float ls = rows_sum(lsum[t]);
+      if (grp == 0) {
+        st_m[(wave * CT + t) * 16 + g] = m[t];
+        st_l[(wave * CT + t) * 16 + g] = ls;
+      }
+#pragma unroll
+      for (int mb = 0; mb < VB; ++mb) {
+        const int owner = mb / VQ;
+        if (owner != wave)  // source index of this wavefront as the owner counts them
+          xch[(((owner * 3 + ((wave - owner - 1) & 3)) * CT + t) * VQ + mb % VQ) * 64 + lane] =
+              acc[t][mb];
+      }
+    }
+    __syncthreads();  // the partition's four wavefront states are in the slot
+    // The merge of this wavefront's quarter; WQ = wave as a compile-time
+    // constant, so the accumulator's d-blocks are selected by register name
+    // (a runtime index would put the accumulator in scratch memory).
+    auto merge_quarter = [&](auto WQ) __attribute__((always_inline)) {
+      constexpr int wq = decltype(WQ)::value;
+#pragma unroll
+      for (int t = 0; t < CT; ++t) {
+        // (statistics are re-read from LDS where needed rather than held in
+        // registers: this runs with a page in flight and one being computed)
+        float Mx = kNegInf;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, st_m[(w * CT + t) * 16 + g]);
+        const float mu = Mx == kNegInf ? 0.0f : Mx;
+        float Z = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)  // 0 for a wavefront with no keys
+          Z += fast_exp2(st_m[(w * CT + t) * 16 + g] - mu) * st_l[(w * CT + t) * 16 + g];
+        // The partition's max logit (log2 units, with its share of the bias)
+        // and its weight in the running combination; a column with no keys
+        // in it (Z = 0) leaves the running state as it is.
+        float mj = Mx;
+        if constexpr (AL) mj += slope2[t] * (float)((u.p0 + jcur) * a.PS - qpos[t]);
+        const bool has = Z > 0.0f;
+        const float nM = has ? fmaxf(rM[t], mj) : rM[t];
+        const float al = has ? fast_exp2(rM[t] - nM) : 1.0f;
+        const float be = has ? fast_exp2(mj - nM) * Z : 0.0f;
+        const float inv = has ? a.v_scale / Z : 0.0f;
+        rM[t] = nM;
+        rZ[t] = rZ[t] * al + be;
+#pragma unroll
+        for (int mbl = 0; mbl < VQ; ++mbl) {
+          f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) {  // sources in wavefront order
+            const f32x4 v =
+                w == wq ? acc[t][wq * VQ + mbl]
+                        : xch[(((wq * 3 + ((w - wq - 1) & 3)) * CT + t) * VQ + mbl) * 64 + lane];
+            o += fast_exp2(st_m[(w * CT + t) * 16 + g] - mu) * v;
+          }
+          const f32x4 oj = o * inv;  // the partition's normalised row (this lane's 4 d)
+          f32x4* r = s_run + (t * VQ + mbl) * 64;
+          *r = (jcur == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : *r * al) + be * oj;
+        }
+      }
+    };
+    switch (wave) {
+      case 0: merge_quarter(std::integral_constant<int, 0>{}); break;
+      case 1: merge_quarter(std::integral_constant<int, 1>{}); break;
+      case 2: merge_quarter(std::integral_constant<int, 2>{}); break;
+      default: merge_quarter(std::integral_constant<int, 3>{}); break;
+    }
+#pragma unroll
+    for (int t = 0; t < CT; ++t) {
       m[t] = kNegInf;
       lsum[t] = 0.0f;
 #pragma unroll
@@ -814,7 +972,7 @@ partition_mfma_kernel(PartitionArgs a) {
 
   auto process = [&](int i, const Page& pg) {
     const int page = wave + i * kWaves;  // page of the span
-    while (page >= next_edge) park();
+    while (page >= next_edge) park();  // (the rolling merge has parked in pre)
     const int tok0 = (u.pg0 + page) * BS;  // first token of the page
     float s2[CT][SUB][4];
 #pragma unroll
@@ -947,8 +1105,51 @@ partition_mfma_kernel(PartitionArgs a) {
     }
   };
 
+  // The rolling merge parks before the next page's fetch is issued, so that
+  // its merge runs with one page fewer of registers live.
+  auto pre = [&](int i) __attribute__((always_inline)) {
+    if constexpr (ROLL) {
+      const int page = wave + i * kWaves;
+      while (page >= next_edge) park_roll();
+    }
+  };
   Page ring[PF + 1];
-  pipeline<PF>(npg, ring, fetch, process);
+  pipeline<PF>(npg, ring, fetch, process, pre);
+  if constexpr (ROLL) {
+    while (jcur < u.ne) park_roll();
+    // Each wavefront writes its quarter of every live column's combined row.
+    const int q = u.p0 / a.C;
+    const int mf = a.c0 / G;
+    const size_t row0 = ((size_t)u.s * a.Mq + mf) * a.H + u.kh * G;
+#pragma unroll
+    for (int t = 0; t < CT; ++t) {
+      const int cl = 16 * t + g;
+      if (cl >= NC) continue;
+      const int c = a.c0 + cl, qm = c / G, h = c - qm * G;
+      const size_t row = row0 + (size_t)(qm - mf) * a.H + h;
+      const bool has = rZ[t] > 0.0f;
+      const float inv = has ? 1.0f / rZ[t] : 0.0f;
+#pragma unroll
+      for (int mbl = 0; mbl < VQ; ++mbl) {
+        const f32x4 o = s_run[(t * VQ + mbl) * 64] * inv;
+        const int d = 16 * (wave * VQ + mbl) + 4 * grp;
+        if (a.Pq == 1)
+          store_out4(a.out, a.odt, row * D + d, o);
+        else
+          *(f32x4*)(a.tmp_out + (row * a.Pq + q) * D + d) = o;
+      }
+      if (wave == 0 && grp == 0) {
+        if (a.Pq == 1) {
+          if (a.lse)
+            a.lse[row] = has ? fmaf(__builtin_amdgcn_logf(rZ[t]), kLn2, rM[t] * kLn2) : kNegInf;
+        } else {
+          a.exp_sums[row * a.Pq + q] = rZ[t];
+          a.max_logits[row * a.Pq + q] = rM[t] * kLn2;
+        }
+      }
+    }
+    return;
+  }
   while (jcur < u.ne) park();
   __syncthreads();
   if (a.fuse)
@@ -1021,8 +1222,9 @@ partition_vec_kernel(PartitionArgs a) {
   float slope2[GM];
 #pragma unroll
   for (int gg = 0; gg < GM; ++gg) slope2[gg] = AL && gg < G ? a.alibi[u.kh * G + gg] * kLog2e : 0.0f;
-  if (!unit_hoist<BS, D>(a, (int32_t*)smem, u)) return;
   const LdsLayout lay = lds_layout(a.PS, BS, G, D, a.C);
+  if (lay.total > a.lds_bytes) return;  // (uniform: the launch's LDS does not hold the layout)
+  if (!unit_hoist<BS, D>(a, (int32_t*)smem, u)) return;
   const int32_t* s_bt = (const int32_t*)(smem + lay.bt_off);
   float* s_m = (float*)(smem + lay.m_off);
   float* s_l = (float*)(smem + lay.l_off);
@@ -1196,7 +1398,7 @@ partition_vec_kernel(PartitionArgs a) {
   };
 
   Page ring[PF + 1];
-  pipeline<PF>(npg, ring, fetch, process);
+  pipeline<PF>(npg, ring, fetch, process, [](int) {});
   while (jcur < u.ne) park();
   __syncthreads();
   if (a.fuse)

@@ -55,6 +55,9 @@ const pa::partition_fn (*const kMfma[2][2])[3][2] = {{pa::kMfma_al0, pa::kMfmaW_
                                                      {pa::kMfma_al1, pa::kMfmaW_al1}};
 const pa::partition_fn (*const kMfma8[2][2])[3][2] = {{pa::kMfma8_al0, pa::kMfma8W_al0},
                                                       {pa::kMfma8_al1, pa::kMfma8W_al1}};
+// the rolling-merge instantiations of the 16-bit kernels (one-call decode)
+const pa::partition_fn (*const kMfmaR[2][2])[3][2] = {{pa::kMfmaR_al0, pa::kMfmaRW_al0},
+                                                      {pa::kMfmaR_al1, pa::kMfmaRW_al1}};
 const pa::partition_fn (*const kVec[2])[3][2][3] = {pa::kVec_al0, pa::kVec_al1};
 const pa::partition_fn (*const kVec8[2])[3][2][3] = {pa::kVec8_al0, pa::kVec8_al1};
 
@@ -118,7 +121,8 @@ struct Plan {
   int lds_bytes;
   int grid;
   int span;
-  int lpt;  // largest-first unit order
+  int lpt;   // largest-first unit order
+  int roll;  // one-call decode on the MFMA kernel: ring slots of the rolling merge (0: none)
 };
 
 // One-call decode: the partition launches combine each span's partitions
@@ -184,14 +188,31 @@ constexpr long long kLptMinUnitBytes = 1 << 20;
 // 220.6 us, long context with 2 tokens 192.8 -> 185.5 us).
 constexpr int kSpanLdsCap = 80 * 1024;
 
+#ifndef PA_ROLL
+#define PA_ROLL 1  // measurement builds: 0 never the rolling merge, 2 always (one-call MFMA spans)
+#endif
+
+// Ring slots of the rolling merge for a one-call MFMA span of c partitions
+// (roll_ct = the launch's column tiles; 0: not an MFMA one-call launch): 0
+// where the span's parked states fit lds_cap (combine_store), else 2 or 1 slots
+// as they fit; -1 if nothing fits.
+int span_roll(int PS, int BS, int NC, int D, int c, int roll_ct, int lds_cap) {
+  const bool park = pa::lds_layout(PS, BS, NC, D, c).total <= lds_cap;
+  if (roll_ct == 0 || c < 2 || (park && PA_ROLL < 2)) return park ? 0 : -1;
+  if (PA_ROLL == 0) return park ? 0 : -1;
+  if (pa::roll_layout(PS, BS, roll_ct, D, c, 2).total <= lds_cap) return 2;
+  if (pa::roll_layout(PS, BS, roll_ct, D, c, 1).total <= lds_cap) return 1;
+  return park ? 0 : -1;
+}
+
 int pick_span(int S, int KH, int P, int PS, int BS, int NC, int D, int esz, int lds_cap,
-              long long min_grid) {
+              long long min_grid, int roll_ct = 0) {
   int best = 1;
   for (int c = 2; c <= pa::kMaxSpan && c / 2 < P; c *= 2) {  // (c / 2 >= P: P already covered)
     const long long grid = (long long)S * KH * ((P + c - 1) / c);
     const long long bytes = (long long)c * PS * D * esz * 2;
-    const int lds = pa::lds_layout(PS, BS, NC, D, c).total;
-    if (c * (PS / BS) > pa::kWaves * 64 || lds > lds_cap) break;
+    if (c * (PS / BS) > pa::kWaves * 64 || span_roll(PS, BS, NC, D, c, roll_ct, lds_cap) < 0)
+      break;
     if (PA_SPAN > 0) {
       if (c > PA_SPAN) break;
     } else if (grid < min_grid || bytes > kSpanBytes) {
@@ -307,7 +328,7 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
                     const int32_t* seq_lens, int32_t S, int32_t H, int32_t KH, int32_t D,
                     int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS, int32_t qdt,
                     int32_t kvdt, int32_t M, int32_t NC, const float* alibi, Plan* plan,
-                    int force_span = 0) {
+                    int force_span = 0, bool fuse = false) {
   if (S < 0 || H < 0 || KH < 0 || D < 0 || BS < 0 || NB < 0 || MB < 0 || P < 0)
     return fail(PA_ERR_SHAPE, "negative size argument");
   if (M < 1) return fail(PA_ERR_SHAPE, "num_queries must be >= 1");
@@ -359,13 +380,23 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   if (lds1 > lds_limit)
     return fail(PA_ERR_UNSUPPORTED, "needs %d bytes of LDS per workgroup, device allows %d", lds1,
                 lds_limit);
+  // One-call launches of the MFMA kernel may span more partitions than their
+  // parked states fit, with the rolling merge.
+  const int roll_ct = fuse && !vec && kvdt != PA_FP8_E4M3 ? (NC > 16 ? 2 : 1) : 0;
+  const int cap = span_lds_cap(fn, lds_limit);
   const int span = force_span > 0 ? force_span
-                                  : pick_span(S, KH, P, PS, BS, NC, D, elem_size(kvdt),
-                                              span_lds_cap(fn, lds_limit), span_min_grid(fn));
+                                  : pick_span(S, KH, P, PS, BS, NC, D, elem_size(kvdt), cap,
+                                              span_min_grid(fn), roll_ct);
   const long long grid = (long long)S * KH * ((P + span - 1) / span);
   if (grid > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many work units");
+  // (a longer span was admitted by pick_span, or is a forced shorter one;
+  // one partition's parked state fits lds_limit, checked above)
+  plan->roll = roll_ct && span > 1 ? span_roll(PS, BS, NC, D, span, roll_ct, cap) : 0;
+  if (plan->roll < 0) return fail(PA_ERR_UNSUPPORTED, "no LDS layout for a span of %d", span);
+  if (plan->roll > 0) fn = kMfmaR[al][roll_ct - 1][qdt - 1][d_index(D)][bs_index(BS)];
   plan->fn = fn;
-  plan->lds_bytes = pa::lds_layout(PS, BS, NC, D, span).total;
+  plan->lds_bytes = plan->roll > 0 ? pa::roll_layout(PS, BS, roll_ct, D, span, plan->roll).total
+                                   : pa::lds_layout(PS, BS, NC, D, span).total;
   const long long pairs = (long long)S * ((P + span - 1) / span);
   const long long unit_bytes = (long long)span * PS * D * elem_size(kvdt) * 2;
   plan->lpt = PA_LPT && pairs <= kLptMaxPairs &&
@@ -415,6 +446,8 @@ int launch_partition(const Plan& plan, float* tmp_output, float* exp_sums, float
   // the partition rows themselves: the plain phase-1 epilogue writes them.)
   a.Pq = fz.on ? (P + plan.span - 1) / plan.span : P;
   a.fuse = fz.on && (plan.span > 1 || a.Pq == 1);
+  a.roll = a.fuse ? plan.roll : 0;
+  a.lds_bytes = plan.lds_bytes;
   a.out = fz.out;
   a.lse = fz.lse;
   a.odt = fz.odt;
@@ -478,6 +511,13 @@ int launch_reduce(reduce_fn fn, void* out, float* lse, const float* tmp_output,
 
 bool finite(float v) { return v == v && v - v == 0.0f; }
 
+// Block-table row length that holds P partitions of PS tokens (at least 1).
+int32_t max_blocks_for(int32_t P, int32_t PS, int32_t BS) {
+  if (P < 1 || PS < 1 || BS < 1) return 1;
+  const long long mb = ((long long)P * PS + BS - 1) / BS;
+  return mb > 0x7fffffffLL ? 0x7fffffff : (int32_t)mb;
+}
+
 // Plans for the column launches of a phase-1 call: `full` for launches of nc
 // columns, `last` for a narrower final one (all validated before any launch).
 int plan_partitions(float* tmp_output, float* exp_sums, float* max_logits, const void* query,
@@ -485,28 +525,28 @@ int plan_partitions(float* tmp_output, float* exp_sums, float* max_logits, const
                     const int32_t* seq_lens, int32_t S, int32_t H, int32_t KH, int32_t D,
                     int32_t BS, int32_t NB, int32_t MB, int32_t P, int32_t PS, int32_t qdt,
                     int32_t kvdt, int32_t M, const float* alibi, Plan* full, Plan* last,
-                    int* nc, bool same_span = false) {
+                    int* nc, bool fuse = false) {
   const int G = KH > 0 && H >= KH && H % KH == 0 ? H / KH : 1;  // (validated by check_partition)
   const long long total = (long long)G * (M > 0 ? M : 1);
   *nc = launch_columns(G, M > 0 ? M : 1, D, PS, BS);
   int rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                            block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt, M,
-                           *nc, alibi, full);
+                           *nc, alibi, full, 0, fuse);
   if (rc != PA_OK || S == 0) return rc;
   if (total > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many query columns");
   *last = *full;
   if (total % *nc)
     rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                          block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt, M,
-                         (int)(total % *nc), alibi, last);
-  if (rc == PA_OK && same_span && last->span != full->span) {
+                         (int)(total % *nc), alibi, last, 0, fuse);
+  if (rc == PA_OK && fuse && last->span != full->span) {
     // One span for every column launch (their span entries share one layout):
     // the shorter of the two, which fits both launches' LDS.
     const int span = std::min(full->span, last->span);
     Plan* re = full->span > span ? full : last;
     rc = check_partition(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                          block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt, M,
-                         re == full ? *nc : (int)(total % *nc), alibi, re, span);
+                         re == full ? *nc : (int)(total % *nc), alibi, re, span, fuse);
   }
   return rc;
 }
@@ -564,7 +604,7 @@ int decode_entry(void* out, float* lse, float* tmp_output, float* exp_sums, floa
   int nc = 1;
   int rc = plan_partitions(tmp_output, exp_sums, max_logits, query, key_cache, value_cache,
                            block_tables, seq_lens, S, H, KH, D, BS, NB, MB, P, PS, qdt, kvdt, M,
-                           alibi, &full, &last, &nc, /*same_span=*/true);
+                           alibi, &full, &last, &nc, /*fuse=*/true);
   if (rc != PA_OK || S == 0) return rc;
   if (out_dtype != PA_F32 && out_dtype != qdt)
     return fail(PA_ERR_UNSUPPORTED, "out dtype must be PA_F32 or the query dtype");
@@ -854,6 +894,35 @@ int paged_attn_partition_span(int32_t num_seqs, int32_t num_heads, int32_t num_k
   const int lds_limit = max_lds_per_block();
   return pick_span(S, KH, P, PS, BS, NC, D, elem_size(dt), span_lds_cap(fn, lds_limit),
                    span_min_grid(fn));
+}
+
+int paged_attn_decode_plan(int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                           int32_t max_num_partitions, int32_t partition_size, int32_t q_dtype,
+                           int32_t kv_dtype, int32_t* plan_out) {
+  g_err[0] = 0;
+  if (!plan_out) return fail(PA_ERR_NULL, "plan_out is NULL");
+  if (num_seqs < 1) return fail(PA_ERR_SHAPE, "num_seqs must be >= 1");
+  // The launch checks, with a stand-in for every tensor (never dereferenced:
+  // nothing is launched).
+  alignas(16) static const char stand_in[16] = {};
+  void* p = (void*)stand_in;
+  Plan full, last;
+  int nc = 1;
+  const int rc = plan_partitions((float*)p, (float*)p, (float*)p, p, p, p, (const int32_t*)p,
+                                 (const int32_t*)p, num_seqs, num_heads, num_kv_heads, head_size,
+                                 block_size, 1, max_blocks_for(max_num_partitions, partition_size,
+                                                               block_size),
+                                 max_num_partitions, partition_size, q_dtype, kv_dtype,
+                                 num_queries, nullptr, &full, &last, &nc, /*fuse=*/true);
+  if (rc != PA_OK) return rc;
+  const int span = full.span;
+  plan_out[0] = span;
+  plan_out[1] = full.roll;
+  plan_out[2] = (max_num_partitions + span - 1) / span;
+  const long long cols = (long long)(num_heads / num_kv_heads) * num_queries;
+  plan_out[3] = (int)((cols + nc - 1) / nc);
+  return PA_OK;
 }
 
 int paged_attn_plan_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,

@@ -77,7 +77,7 @@ def test_no_scalar_cache_writes(kernels):
 
 def test_kv_loads_are_dwordx4_or_dwordx2_streaming(kernels):
     """K/V pages are fetched with 16-byte (K, vector-path V, 8-bit MFMA-path V) or
-    8-byte (16-bit MFMA-path V) non-temporal loads; the 8-bit MFMA path then
+    8-byte (16-bit MFMA-path V, also in the rolling-merge instantiations) non-temporal loads; the 8-bit MFMA path then
     transposes its V words across lane rows with the gfx950 permlane swaps."""
     seen = 0
     for k, v in kernels.items():
@@ -94,7 +94,10 @@ def test_kv_loads_are_dwordx4_or_dwordx2_streaming(kernels):
         if "partition_vec_kernelILi2ELi128ELi16ELi1ELb1" in k:
             assert any(l.startswith("global_load_dwordx4") for l in nt)
             seen += 1
-    assert seen == 10  # each with ALiBi off and on; the MFMA ones with one and two column tiles
+    # each with ALiBi off and on; the 16-bit MFMA ones with one and two column
+    # tiles, with and without the rolling merge; the 8-bit MFMA ones with one
+    # and two column tiles
+    assert seen == 14
 
 
 def test_fp8_kernels_convert_with_gfx950_instructions(kernels):
