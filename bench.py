@@ -278,12 +278,15 @@ class Batch:
                 "value": round(gbs, 2), "unit": "GB/s", "pct_of_peak_hbm": pct(gbs),
                 "qheads_tokens_per_s": round(self.qht / med * 1e6, 1)}
 
-    def span(self, P, PS):
-        if self.MQ > 1:
-            return None
+    def plan(self, P, PS):
+        """The one-call decode's launch plan (span, ring slots, span entries per row)."""
         c = self.cfg
-        return self.pa.partition_span(self.S, self.H, c.num_kv_heads, self.D, c.block_size, P,
-                                      PS, self.dtype_name)
+        return self.pa.decode_plan(self.S, self.MQ, self.H, c.num_kv_heads, self.D, c.block_size,
+                                   P, PS, self.torch_dtype(c.query_dtype), self.dtype_name)
+
+    def torch_dtype(self, name):
+        from paged_kv_cache_v2_amd import workloads as W
+        return W.DTYPES[name]
 
     def kernel_name(self):
         c = self.cfg
@@ -304,7 +307,7 @@ class Batch:
             "pct_of_peak_hbm": pct(gbs),
             "qheads_tokens_per_s": round(self.qht / step_s, 1),
             "entry": self.entry(), "partition_size": self.PS, "max_num_partitions": self.P,
-            "partition_span": self.span(self.P, self.PS),
+            "plan": self.plan(self.P, self.PS),
             "roofline": {
                 "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
@@ -333,7 +336,7 @@ class Batch:
         tuned_s = self.back_to_back(lambda: self.decode(self.ws_t, self.PS_t), K, W_)
         res["tuned"] = {
             "entry": self.entry(), "partition_size": self.PS_t, "max_num_partitions": self.P_t,
-            "partition_span": self.span(self.P_t, self.PS_t),
+            "plan": self.plan(self.P_t, self.PS_t),
             "ms_per_step": round(tuned_s * 1e3, 5), "value": round(self.kvb / tuned_s / 1e9, 2),
             "unit": "GB/s", "pct_of_peak_hbm": pct(self.kvb / tuned_s / 1e9),
             "qheads_tokens_per_s": round(self.qht / tuned_s, 1),
@@ -412,11 +415,11 @@ def copy_bandwidth(torch, dev, stream) -> dict:
 def gather_ceiling(pa, torch, b: Batch, K: int) -> dict:
     """The read-only page-gather kernel over the batch's own pages: GB/s."""
     from paged_kv_cache_v2_amd import ceiling
-    sink = torch.empty(ceiling.sink_words(b.S, b.cfg.num_kv_heads, b.bt.shape[1]),
-                       dtype=torch.int32, device=b.dev)
+    sink = torch.empty(ceiling.sink_words(), dtype=torch.int32, device=b.dev)
+    blocks = ceiling.page_list(b.bt, b.sl, b.cfg.block_size)
 
     def run():
-        ceiling.gather_ceiling(sink, b.kc, b.vc, b.bt, b.sl, stream=b.stream)
+        ceiling.gather_ceiling(sink, b.kc, b.vc, blocks, stream=b.stream)
 
     for _ in range(5):
         run()
@@ -456,7 +459,7 @@ def run(args) -> dict:
         "qheads_tokens_per_s": m["qheads_tokens_per_s"],
         "config": m["config"],
         "entry": m["entry"],
-        "partition_span": m["partition_span"],
+        "plan": m["plan"],
         "roofline": m["roofline"],
     }
     for k in ("flushed", "two_call", "tuned"):

@@ -27,30 +27,26 @@ extern "C" {
 #define PA_CEILING_API
 #endif
 
-/* Words of `sink` a call needs: 4 per workgroup, one workgroup per (sequence,
- * kv head, run of 32 blocks of the block-table row). */
-PA_CEILING_API int64_t pa_gather_ceiling_sink_words(int32_t num_seqs, int32_t num_kv_heads,
-                                                    int32_t max_blocks_per_seq);
+/* Words of `sink` a call needs (4 per workgroup of the fixed grid). */
+PA_CEILING_API int64_t pa_gather_ceiling_sink_words(void);
 
 /*
- * Read every (block, kv head) page of key_cache and value_cache that the
- * sequences use: blocks block_tables[s][i] for i < ceil(seq_lens[s] / BS),
- * kv heads 0 .. KH-1, page_bytes bytes each (D * BS * element size; a
- * multiple of 1024). Each workgroup folds what it read into four words of
- * `sink` (int32 [pa_gather_ceiling_sink_words]); their values mean nothing.
+ * Read the K and V page of every (block, kv head) item of a flat page list:
+ * blocks[j] for j < num_pages (each used block of each sequence once; the
+ * caller gathers them from its block tables), kv heads 0 .. KH-1, page_bytes
+ * bytes each (D * BS * element size; 1, 2, 4, 8 or 16 KiB). Each workgroup
+ * folds what it read into four words of `sink` (int32
+ * [pa_gather_ceiling_sink_words()]); their values mean nothing.
  *
  *   key_cache, value_cache   [B, KH, page_bytes] bytes, 16-byte aligned
- *   block_tables [S, MB] int32, entries of used blocks in [0, B)
- *   seq_lens     [S] int32, 0 <= seq_lens[s] <= MB * BS
+ *   blocks                   [num_pages] int32 in [0, B) (clamped into it)
  * Returns 0, or -1 (NULL pointer), -2 (bad size), -4 (misaligned), -5 (launch
- * rejected by the HIP runtime).
+ * rejected by the HIP runtime). num_pages == 0 is a no-op.
  */
 PA_CEILING_API int pa_gather_ceiling(int32_t* sink, int64_t sink_words, const void* key_cache,
-                                     const void* value_cache, const int32_t* block_tables,
-                                     const int32_t* seq_lens, int32_t num_seqs,
-                                     int32_t num_kv_heads, int32_t page_bytes,
-                                     int32_t block_size, int32_t num_blocks,
-                                     int32_t max_blocks_per_seq, void* stream);
+                                     const void* value_cache, const int32_t* blocks,
+                                     int64_t num_pages, int32_t num_kv_heads,
+                                     int32_t page_bytes, int32_t num_blocks, void* stream);
 
 #ifdef __cplusplus
 }

@@ -343,8 +343,8 @@ PA_API int paged_attn_decode_ex(void* out, float* lse, float* tmp_output, float*
  *   out_lse = Mx + ln(w_a + w_b)
  *
  * both lse -inf (no keys on either side) -> out = 0, out_lse = -inf; one side
- * -inf -> the other side's row. fp32 arithmetic, one rounding to `dtype` at
- * the end.
+ * -inf -> the other side's row (the -inf side's row is never used, whatever it
+ * holds, NaN included). fp32 arithmetic, one rounding to `dtype` at the end.
  *
  *   a, b, out          [num_rows, head_size] of `dtype` (PA_F32, PA_F16 or
  *                      PA_BF16), 16-byte aligned

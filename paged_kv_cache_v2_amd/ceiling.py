@@ -20,29 +20,34 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run `python -m paged_kv_cache_v2_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
-        L.pa_gather_ceiling_sink_words.argtypes = [ctypes.c_int32] * 3
+        L.pa_gather_ceiling_sink_words.argtypes = []
         L.pa_gather_ceiling_sink_words.restype = ctypes.c_int64
-        L.pa_gather_ceiling.argtypes = ([ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 4 +
-                                        [ctypes.c_int32] * 6 + [ctypes.c_void_p])
+        L.pa_gather_ceiling.argtypes = ([ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 3 +
+                                        [ctypes.c_int64] + [ctypes.c_int32] * 3 +
+                                        [ctypes.c_void_p])
         L.pa_gather_ceiling.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
 
-def sink_words(num_seqs: int, num_kv_heads: int, max_blocks_per_seq: int) -> int:
-    return int(lib().pa_gather_ceiling_sink_words(num_seqs, num_kv_heads, max_blocks_per_seq))
+def sink_words() -> int:
+    return int(lib().pa_gather_ceiling_sink_words())
+
+
+def page_list(block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int) -> torch.Tensor:
+    """The used blocks of every sequence, in sequence order (a flat int32 list)."""
+    nb = (seq_lens.to(torch.int64) + block_size - 1) // block_size
+    cols = torch.arange(block_tables.shape[1], device=block_tables.device)
+    return block_tables[cols[None, :] < nb[:, None]].to(torch.int32).contiguous()
 
 
 def gather_ceiling(sink: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
-                   block_tables: torch.Tensor, seq_lens: torch.Tensor, stream=None) -> None:
-    """Read every used (block, kv head) page of both caches once."""
+                   blocks: torch.Tensor, stream=None) -> None:
+    """Read the K and V page of every (block in `blocks`, kv head) once."""
     B, KH = key_cache.shape[0], key_cache.shape[1]
     page = key_cache[0, 0].numel() * key_cache.element_size()
-    S, MB = block_tables.shape
-    BS = value_cache.shape[-1]
     rc = lib().pa_gather_ceiling(sink.data_ptr(), sink.numel(), key_cache.data_ptr(),
-                                 value_cache.data_ptr(), block_tables.data_ptr(),
-                                 seq_lens.data_ptr(), S, KH, page, BS, B, MB,
-                                 _stream(key_cache, stream))
+                                 value_cache.data_ptr(), blocks.data_ptr(), blocks.numel(), KH,
+                                 page, B, _stream(key_cache, stream))
     if rc != 0:
         raise RuntimeError(f"pa_gather_ceiling failed with status {rc}")

@@ -1619,17 +1619,22 @@ __global__ void __launch_bounds__(256) merge_states_kernel(MergeArgs g) {
     pb = wb * inv;
     ol = mx + __builtin_amdgcn_logf(wa + wb) * kLn2;
   }
+  // A side with lse -inf (no keys) is selected out, not multiplied by its zero
+  // weight: its row is unspecified and may hold NaN.
+  const bool ua = la != kNegInf, ub = lb != kNegInf;
+  auto mix = [&](float x, float y) {
+    return (ua ? pa * x : 0.0f) + (ub ? pb * y : 0.0f);
+  };
   u32x4 vo;
   if constexpr (DT == DT_F32) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      vo[e] = __float_as_uint(pa * __uint_as_float(va[e]) + pb * __uint_as_float(vb[e]));
+      vo[e] = __float_as_uint(mix(__uint_as_float(va[e]), __uint_as_float(vb[e])));
   } else {
     using Cd = codec<DT>;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      vo[e] = Cd::pack(pa * Cd::lo(va[e]) + pb * Cd::lo(vb[e]),
-                       pa * Cd::hi(va[e]) + pb * Cd::hi(vb[e]));
+      vo[e] = Cd::pack(mix(Cd::lo(va[e]), Cd::lo(vb[e])), mix(Cd::hi(va[e]), Cd::hi(vb[e])));
   }
   ((u32x4*)g.out)[i] = vo;
   if (g.out_lse && (i & ((1 << g.tpr_shift) - 1)) == 0) g.out_lse[r] = ol;

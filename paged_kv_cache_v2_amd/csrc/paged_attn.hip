@@ -316,9 +316,17 @@ int cu_count() {
 // Fewest workgroups a longer span may leave in the grid: two per resident
 // slot (the workgroups per CU that the kernel's registers allow, on every
 // CU), so that the largest-first order has a second round to balance.
-long long span_min_grid(partition_fn fn) {
-  return (long long)kMinRounds * wgs_per_cu(fn) * cu_count();
+long long span_min_grid(partition_fn fn, int rounds = kMinRounds) {
+  return (long long)rounds * wgs_per_cu(fn) * cu_count();
 }
+
+// The one-call decode's spans need only one workgroup per resident slot:
+// a longer span also means fewer span entries to store and reduce. Measured
+// on MI355X against two rounds (eight-partition spans instead of four, one
+// round of 512 workgroups): long context 172.4 -> 168.9 us, with 2 query
+// tokens 181.0 -> 170.5, with 4 query tokens 189 -> 175; spans of 8 over 2 MiB
+// (head size 256) were slower, so the byte limit stays.
+constexpr int kMinRoundsFused = 1;
 
 // Host checks shared by the partition entry points; fills `plan` for a launch
 // of NC columns. The query has dtype qdt; the caches kvdt (== qdt, or
@@ -386,7 +394,9 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   const int cap = span_lds_cap(fn, lds_limit);
   const int span = force_span > 0 ? force_span
                                   : pick_span(S, KH, P, PS, BS, NC, D, elem_size(kvdt), cap,
-                                              span_min_grid(fn), roll_ct);
+                                              span_min_grid(fn, fuse ? kMinRoundsFused
+                                                                     : kMinRounds),
+                                              roll_ct);
   const long long grid = (long long)S * KH * ((P + span - 1) / span);
   if (grid > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many work units");
   // (a longer span was admitted by pick_span, or is a forced shorter one;
@@ -642,6 +652,19 @@ int reduce_entry(void* out, float* lse, const float* tmp_output, const float* ex
   if (rc != PA_OK || S == 0) return rc;
   return launch_reduce(fn, out, lse, tmp_output, exp_sums, max_logits, seq_lens, S, M, H, D, P,
                        PS, (hipStream_t)stream);
+}
+
+// The one-call decode's launch plan for these sizes, checked as a call would
+// check it, with a stand-in for every tensor (never dereferenced: nothing is
+// launched). Returns PA_OK or the call's error code.
+int plan_with_stand_ins(int32_t S, int32_t M, int32_t H, int32_t KH, int32_t D, int32_t BS,
+                        int32_t P, int32_t PS, int32_t qdt, int32_t kvdt, Plan* full,
+                        Plan* last, int* nc) {
+  alignas(16) static const char stand_in[16] = {};
+  void* p = (void*)stand_in;
+  return plan_partitions((float*)p, (float*)p, (float*)p, p, p, p, (const int32_t*)p,
+                         (const int32_t*)p, S, H, KH, D, BS, 1, max_blocks_for(P, PS, BS), P, PS,
+                         qdt, kvdt, M, nullptr, full, last, nc, /*fuse=*/true);
 }
 
 }  // namespace
@@ -903,18 +926,11 @@ int paged_attn_decode_plan(int32_t num_seqs, int32_t num_queries, int32_t num_he
   g_err[0] = 0;
   if (!plan_out) return fail(PA_ERR_NULL, "plan_out is NULL");
   if (num_seqs < 1) return fail(PA_ERR_SHAPE, "num_seqs must be >= 1");
-  // The launch checks, with a stand-in for every tensor (never dereferenced:
-  // nothing is launched).
-  alignas(16) static const char stand_in[16] = {};
-  void* p = (void*)stand_in;
   Plan full, last;
   int nc = 1;
-  const int rc = plan_partitions((float*)p, (float*)p, (float*)p, p, p, p, (const int32_t*)p,
-                                 (const int32_t*)p, num_seqs, num_heads, num_kv_heads, head_size,
-                                 block_size, 1, max_blocks_for(max_num_partitions, partition_size,
-                                                               block_size),
-                                 max_num_partitions, partition_size, q_dtype, kv_dtype,
-                                 num_queries, nullptr, &full, &last, &nc, /*fuse=*/true);
+  const int rc = plan_with_stand_ins(num_seqs, num_queries, num_heads, num_kv_heads, head_size,
+                                     block_size, max_num_partitions, partition_size, q_dtype,
+                                     kv_dtype, &full, &last, &nc);
   if (rc != PA_OK) return rc;
   const int span = full.span;
   plan_out[0] = span;
@@ -956,13 +972,31 @@ int paged_attn_plan_partition_size(int32_t num_seqs, int32_t num_heads, int32_t 
   const long long slots = (long long)wgs_per_cu(fn) * cu_count();
   // The longest candidate whose units (S * KH * parts) fill every resident
   // workgroup, else 128; compared as parts >= ceil(slots / (S * KH)), which
-  // cannot overflow.
+  // cannot overflow. A candidate the decode call would reject on this device
+  // (the LDS of one partition's parked state, the 32-bit workspace offsets) is
+  // skipped.
   const long long sk = (long long)S * KH;
+  auto ok = [&](int ps) {
+    if (S == 0) return true;
+    Plan full, last;
+    int nc = 1;
+    const int P = L > ps ? (int)((L + (long long)ps - 1) / ps) : 1;
+    return plan_with_stand_ins(S, 1, H, KH, D, BS, P, ps, qdt, dt, &full, &last, &nc) == PA_OK;
+  };
   int ps = top;
   for (; ps > 128; ps /= 2) {
+    if (!ok(ps)) continue;
     const long long parts = L > ps ? (L + ps - 1) / ps : 1;
     if (sk > 0 && parts >= (slots + sk - 1) / sk) break;
   }
+  if (!ok(ps)) {
+    Plan full, last;
+    int nc = 1;
+    const int P = L > ps ? (int)((L + (long long)ps - 1) / ps) : 1;
+    const int rc2 = plan_with_stand_ins(S, 1, H, KH, D, BS, P, ps, qdt, dt, &full, &last, &nc);
+    return rc2 != PA_OK ? rc2 : ps;
+  }
+  g_err[0] = 0;
   return ps;
 }
 

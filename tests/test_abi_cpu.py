@@ -56,16 +56,17 @@ def test_ceiling_library_exports_its_symbols():
     L = ceiling.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert ceiling.sink_words(3, 2, 65) == 3 * 2 * 3 * 4
-    assert L.pa_gather_ceiling(FAKE, 1, FAKE, FAKE, FAKE, FAKE, 2, 2, 4096, 16, 10, 8, None) == -2
-    assert L.pa_gather_ceiling(FAKE, 1 << 20, FAKE, FAKE, FAKE, FAKE, 2, 2, 3000, 16, 10, 8,
-                               None) == -2
-    assert L.pa_gather_ceiling(None, 1 << 20, FAKE, FAKE, FAKE, FAKE, 2, 2, 4096, 16, 10, 8,
-                               None) == -1
-    assert L.pa_gather_ceiling(FAKE, 1 << 20, FAKE + 4, FAKE, FAKE, FAKE, 2, 2, 4096, 16, 10, 8,
-                               None) == -4
-    assert L.pa_gather_ceiling(FAKE, 0, FAKE, FAKE, FAKE, FAKE, 0, 2, 4096, 16, 10, 8,
-                               None) == 0  # no sequences: a no-op
+    W = ceiling.sink_words()
+    assert W > 0
+    assert L.pa_gather_ceiling(FAKE, 1, FAKE, FAKE, FAKE, 10, 2, 4096, 10, None) == -2  # sink
+    assert L.pa_gather_ceiling(FAKE, W, FAKE, FAKE, FAKE, 10, 2, 3000, 10, None) == -2  # page
+    assert L.pa_gather_ceiling(None, W, FAKE, FAKE, FAKE, 10, 2, 4096, 10, None) == -1
+    assert L.pa_gather_ceiling(FAKE, W, FAKE + 4, FAKE, FAKE, 10, 2, 4096, 10, None) == -4
+    assert L.pa_gather_ceiling(FAKE, W, FAKE, FAKE, FAKE, -1, 2, 4096, 10, None) == -2
+    assert L.pa_gather_ceiling(FAKE, W, FAKE, FAKE, FAKE, 0, 2, 4096, 10, None) == 0  # no-op
+    bt = torch.tensor([[3, 1, 7, -1], [5, -1, -1, -1], [0, 0, 0, 0]], dtype=torch.int32)
+    sl = torch.tensor([40, 16, 0], dtype=torch.int32)
+    assert ceiling.page_list(bt, sl, 16).tolist() == [3, 1, 7, 5]
 
 
 def test_abi_version_and_default_partition_size():
@@ -107,8 +108,10 @@ def test_plan_partition_size():
 
 def test_planned_sizes_are_accepted_by_the_launch_plan():
     """Every size the planner returns is one the launchers take: a multiple of
-    the block size, at most 256 pages, and a valid launch plan for
-    ceil(max_seq_len / size) partitions."""
+    the block size, at most 256 pages, and a launch plan that passes every
+    check a decode call makes (the LDS of a partition's parked state, the
+    32-bit workspace offsets) for ceil(max_seq_len / size) partitions, on this
+    host's device limits (64 KiB of LDS per workgroup without a device)."""
     dts = [torch.float32, torch.float16, torch.bfloat16, torch.float8_e4m3fn]
     for S in (0, 1, 7, 128, 4096):
         for H, KH in ((4, 4), (32, 8), (64, 1)):
@@ -118,12 +121,25 @@ def test_planned_sizes_are_accepted_by_the_launch_plan():
                         for dt in dts:
                             if dt == torch.float32 and H // KH > 4:
                                 continue
-                            ps = pa.plan_partition_size(S, H, KH, D, BS, L, dt)
+                            qdt = torch.bfloat16 if dt == torch.float8_e4m3fn else dt
+                            try:
+                                ps = pa.plan_partition_size(S, H, KH, D, BS, L, dt)
+                            except RuntimeError as e:
+                                # a geometry no partition size makes fit this device's
+                                # LDS: the decode call rejects it the same way
+                                assert "LDS" in str(e) and S > 0, e
+                                with pytest.raises(RuntimeError, match="LDS"):
+                                    pa.decode_plan(S, 1, H, KH, D, BS, max(1, -(-L // 128)),
+                                                   128, qdt, dt)
+                                continue
                             assert 128 <= ps <= 4096 and ps % BS == 0 and ps // BS <= 256
                             assert ps <= 2048 or dt != torch.float8_e4m3fn
                             P = max(1, -(-L // ps))
                             span = pa.partition_span(S, H, KH, D, BS, P, ps, dt)
                             assert span in (1, 2, 4, 8)
+                            if S > 0:  # the whole launch check a decode call makes
+                                plan = pa.decode_plan(S, 1, H, KH, D, BS, P, ps, qdt, dt)
+                                assert plan["span"] in (1, 2, 4, 8) and plan["entries"] >= 1
 
 
 def test_partition_span_plan():

@@ -150,6 +150,32 @@ ROUND = {torch.float32: 0.0, torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+def test_merge_states_ignores_the_rows_of_empty_sides(dtype):
+    """A side whose lse is -inf has no keys; its row is unspecified (a decode
+    leaves it 0, a caller's buffer may hold anything) and must not reach the
+    output: NaN-filled rows there give the other side's row, or 0 when both
+    sides are empty."""
+    R, D = 96, 128
+    a, la, b, lb, k = random_states(R, D, dtype, seed=7)
+    a[:k] = float("nan")              # la = -inf on these rows
+    b[k:2 * k] = float("inf")         # lb = -inf on these rows
+    a[2 * k:3 * k] = float("nan")     # both -inf
+    b[2 * k:3 * k] = float("nan")
+    U.note(f"merge empty sides {dtype}")
+    ga, gb, gla, glb = (t.to(U.DEV) for t in (a, b, la, lb))
+    out = torch.full_like(ga, float("nan"))
+    out_lse = torch.full_like(gla, float("nan"))
+    pa.paged_attn_merge_states(out, out_lse, ga, gla, gb, glb)
+    torch.cuda.synchronize()
+    got, got_lse = out.cpu(), out_lse.cpu()
+    bits = torch.int32 if dtype == torch.float32 else torch.int16
+    assert torch.equal(got[:k].view(bits), b[:k].view(bits))
+    assert torch.equal(got[k:2 * k].view(bits), a[k:2 * k].view(bits))
+    assert torch.all(got[2 * k:3 * k] == 0) and torch.all(got_lse[2 * k:3 * k] == -math.inf)
+    assert torch.isfinite(got[:3 * k]).all()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_merge_states_matches_oracle(dtype, D):
     R = 200  # rows; several workgroups for every head size, plus a ragged last one

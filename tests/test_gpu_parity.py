@@ -55,9 +55,10 @@ def test_one_call_matches_two_calls(name):
     r = U.run_decode(d)
     U.assert_close(f"{name} one call vs two", r["out"], r["out_split"].double().numpy())
     S, H, D = inp["query"].shape
-    span = pa.partition_span(S, H, inp["num_kv_heads"], D, cfg.block_size, r["P"], r["PS"],
-                             W.DTYPES[cfg.dtype])
-    Pq = -(-r["P"] // span)
+    plan = pa.decode_plan(S, 1, H, inp["num_kv_heads"], D, cfg.block_size, r["P"], r["PS"],
+                          W.DTYPES[cfg.query_dtype], W.DTYPES[cfg.dtype])
+    Pq = plan["entries"]
+    assert Pq == -(-r["P"] // plan["span"])
     if Pq == 1:
         for k in ("ws_tmp", "ws_es", "ws_ml"):
             assert torch.isnan(r[k]).all(), k
