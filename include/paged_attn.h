@@ -333,6 +333,34 @@ PA_API int paged_attn_decode_ex(void* out, float* lse, float* tmp_output, float*
                                 int32_t kv_dtype, int32_t out_dtype, void* stream);
 
 /*
+ * paged_attn_decode_ex without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the span entries live in a static
+ * 32 MiB array of device memory that each GPU the library is loaded on holds
+ * until the process ends. Nothing is allocated or freed by the call. Same
+ * arguments as paged_attn_decode_ex minus tmp_output / exp_sums / max_logits,
+ * same results bit for bit.
+ *  - The workspace the launch plan needs, num_seqs * num_queries * num_heads *
+ *    entries * (head_size + 2) * 4 bytes (entries = span entries per row,
+ *    paged_attn_decode_plan; with one span per row it is never touched),
+ *    must fit the 32 MiB: larger calls return PA_ERR_UNSUPPORTED and enqueue
+ *    nothing.
+ *  - Every call on one GPU shares that GPU's array: calls that overlap on a
+ *    GPU (other streams, other host threads) race and must be serialised by
+ *    the caller. Nothing in the array needs to start at zero.
+ */
+PA_API int paged_attn_decode_noalloc(void* out, float* lse, const void* query,
+                                     const void* key_cache, const void* value_cache,
+                                     const int32_t* block_tables, const int32_t* seq_lens,
+                                     int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                                     int32_t num_kv_heads, int32_t head_size,
+                                     int32_t block_size, int32_t num_blocks,
+                                     int32_t max_blocks_per_seq, int32_t max_num_partitions,
+                                     int32_t partition_size, float scale, float k_scale,
+                                     float v_scale, const float* alibi_slopes, int32_t q_dtype,
+                                     int32_t kv_dtype, int32_t out_dtype, void* stream);
+
+/*
  * Merge two attention states of the same rows computed over disjoint key sets
  * (a shared prefix and a per-request suffix, or two shards of one long
  * sequence) into the state over their union: the Triton PagedAttention V2

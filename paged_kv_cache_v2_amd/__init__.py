@@ -10,6 +10,6 @@ from .binding import (PA_BF16, PA_FP8_E4M3, PA_ERR_ALIGN, PA_ERR_HIP, PA_ERR_NUL
                       paged_attn_decode_fp8, paged_attn_v2_partition_fp8,
                       paged_attn_decode_mq, paged_attn_v2_partition_mq, paged_attn_v2_reduce_mq,
                       paged_attn_decode_lse, paged_attn_v2_reduce_lse, paged_attn_merge_states,
-                      paged_attn_decode_ex, paged_attn_v2_partition_ex,
+                      paged_attn_decode_ex, paged_attn_decode_noalloc, paged_attn_v2_partition_ex,
                       paged_attn_v2_partition, paged_attn_v2_reduce, partition_span,
                       plan_partition_size, workspace)

@@ -33,6 +33,8 @@ _SIGS = {
     "paged_attn_partition_span": [_I32] * 8,
     "paged_attn_plan_partition_size": [_I32] * 7,
     "paged_attn_decode_plan": [_I32] * 10 + [_P],
+    "paged_attn_decode_noalloc": [_P] * 7 + [_I32] * 10 + [_F32, _F32, _F32, _P, _I32, _I32,
+                                                          _I32, _P],
     "paged_attn_v2_partition_fp8": [_P] * 8 + [_I32] * 9 + [_F32, _F32, _F32, _I32, _P],
     "paged_attn_decode_fp8": [_P] * 9 + [_I32] * 9 + [_F32, _F32, _F32, _I32, _I32, _P],
     "paged_attn_v2_partition_mq": [_P] * 8 + [_I32] * 10 + [_F32, _F32, _F32, _I32, _I32, _P],
@@ -476,6 +478,30 @@ def paged_attn_decode_ex(out, tmp_output, exp_sums, max_logits, query, key_cache
             _slopes_arg(alibi_slopes, H), _DT[query.dtype], _CACHE_DT[key_cache.dtype],
             _DT[out.dtype], _stream(query, stream))
     _check("paged_attn_decode_ex", rc)
+
+
+def paged_attn_decode_noalloc(out, query, key_cache, value_cache, block_tables, seq_lens,
+                              scale: float, partition_size: int, max_num_partitions: int,
+                              k_scale: float = 1.0, v_scale: float = 1.0, alibi_slopes=None,
+                              lse=None, stream=None) -> None:
+    """paged_attn_decode_ex with the library's static per-GPU scratch as the
+    workspace: allocates nothing (calls that overlap on one GPU race)."""
+    _need(query.dim() in (3, 4), "query [S, H, D] or [S, M, H, D] expected")
+    q4 = _rows4(query, "query")
+    S, M, H, KH, D, BS, B, MB = _mq_geometry(q4, key_cache, value_cache, block_tables, seq_lens)
+    _need(out.dim() == query.dim() and tuple(out.shape) == tuple(query.shape) and
+          out.dtype in _DT and out.is_cuda and out.is_contiguous(),
+          "out must be a contiguous tensor shaped like query")
+    lse_ptr = _lse_arg(lse, _rows4(out, "out")) if lse is not None else None
+    _one_device(out, lse, query, key_cache, value_cache, block_tables, seq_lens, alibi_slopes)
+    with _device(query):
+        rc = lib().paged_attn_decode_noalloc(
+            out.data_ptr(), lse_ptr, query.data_ptr(), key_cache.data_ptr(),
+            value_cache.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), S, M, H, KH,
+            D, BS, B, MB, int(max_num_partitions), partition_size, float(scale), float(k_scale),
+            float(v_scale), _slopes_arg(alibi_slopes, H), _DT[query.dtype],
+            _CACHE_DT[key_cache.dtype], _DT[out.dtype], _stream(query, stream))
+    _check("paged_attn_decode_noalloc", rc)
 
 
 def paged_attn_merge_states(out, out_lse, a, lse_a, b, lse_b, stream=None) -> None:

@@ -667,6 +667,38 @@ int plan_with_stand_ins(int32_t S, int32_t M, int32_t H, int32_t KH, int32_t D, 
                          qdt, kvdt, M, nullptr, full, last, nc, /*fuse=*/true);
 }
 
+// ---------------------------------------------------------------- scratch
+// The allocation-free decode's workspace: one array per GPU the library is
+// loaded on, held until the process ends. Its address on the current device
+// comes from hipGetSymbolAddress once per device (in host code `scratch` only
+// names the symbol; it is never used as an address).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The current device's scratch address, or nullptr (with the error set).
+uint8_t* scratch_address() {
+  static std::mutex mu;
+  static uint8_t* addr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    fail(PA_ERR_HIP, "no current HIP device for the scratch workspace");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    addr[dev] = (uint8_t*)p;
+  }
+  return addr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -852,6 +884,47 @@ int paged_attn_decode_ex(void* out, float* lse, float* tmp_output, float* exp_su
                       head_size, block_size, num_blocks, max_blocks_per_seq, max_num_partitions,
                       partition_size, scale, k_scale, v_scale, q_dtype, kv_dtype, out_dtype,
                       stream, alibi_slopes);
+}
+
+int paged_attn_decode_noalloc(void* out, float* lse, const void* query, const void* key_cache,
+                              const void* value_cache, const int32_t* block_tables,
+                              const int32_t* seq_lens, int32_t num_seqs, int32_t num_queries,
+                              int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                              int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t max_num_partitions,
+                              int32_t partition_size, float scale, float k_scale,
+                              float v_scale, const float* alibi_slopes, int32_t q_dtype,
+                              int32_t kv_dtype, int32_t out_dtype, void* stream) {
+  g_err[0] = 0;
+  const int32_t S = num_seqs, M = num_queries, H = num_heads, D = head_size,
+                P = max_num_partitions;
+  if (S == 0 && M >= 1)  // the documented no-op (decode_entry checks the rest)
+    return decode_entry(out, lse, nullptr, nullptr, nullptr, query, key_cache, value_cache,
+                        block_tables, seq_lens, S, M, H, num_kv_heads, D, block_size,
+                        num_blocks, max_blocks_per_seq, P, partition_size, scale, k_scale,
+                        v_scale, q_dtype, kv_dtype, out_dtype, stream, alibi_slopes);
+  // The plan fixes how many span entries per row the workspace holds.
+  Plan full, last;
+  int nc = 1;
+  int rc = plan_with_stand_ins(S, M, H, num_kv_heads, D, block_size, P, partition_size, q_dtype,
+                               kv_dtype, &full, &last, &nc);
+  if (rc != PA_OK) return rc;
+  const long long Pq = (P + full.span - 1) / full.span;
+  const long long rows = (long long)S * M * H;
+  auto up = [](long long b) { return (b + 255) & ~255LL; };
+  const long long tmp_bytes = up(rows * Pq * D * 4), stat_bytes = up(rows * Pq * 4);
+  if (tmp_bytes + 2 * stat_bytes > (long long)kScratchBytes)
+    return fail(PA_ERR_UNSUPPORTED,
+                "workspace of %lld bytes exceeds the %zu-byte scratch of the allocation-free "
+                "call (use paged_attn_decode_ex with a caller workspace)",
+                tmp_bytes + 2 * stat_bytes, kScratchBytes);
+  uint8_t* base = scratch_address();
+  if (!base) return PA_ERR_HIP;
+  return decode_entry(out, lse, (float*)base, (float*)(base + tmp_bytes),
+                      (float*)(base + tmp_bytes + stat_bytes), query, key_cache, value_cache,
+                      block_tables, seq_lens, S, M, H, num_kv_heads, D, block_size, num_blocks,
+                      max_blocks_per_seq, P, partition_size, scale, k_scale, v_scale, q_dtype,
+                      kv_dtype, out_dtype, stream, alibi_slopes);
 }
 
 int paged_attn_merge_states(void* out, float* out_lse, const void* a, const float* lse_a,
