@@ -19,24 +19,34 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "paged_decode_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# PA_ORACLE_LIB: load another build of the same source instead (the sanitizer
+# test points it at an AddressSanitizer / UndefinedBehaviorSanitizer build).
+_LIB_PATH = os.environ.get("PA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _LIB = None
 
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
 
 
-def compile_source(src: str, out: str) -> str:
-    """gcc a C source of the oracle into a shared library (IEEE semantics: no fast-math)."""
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def compile_source(src: str, out: str, sanitize: bool = False) -> str:
+    """gcc a C source of the oracle into a shared library (IEEE semantics: no
+    fast-math); with sanitize, instrumented by AddressSanitizer and
+    UndefinedBehaviorSanitizer (load it with the sanitizer runtime preloaded)."""
     tmp = out + f".tmp{os.getpid()}"
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-Wall",
-           "-Wno-unused-function", src, "-o", tmp, "-lm"]
+           "-Wno-unused-function", *(SANITIZE_FLAGS if sanitize else []), src, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
 
 
 def build(force: bool = True) -> str:
-    """Compile liboracle.so next to its source."""
+    """Compile liboracle.so next to its source (not when PA_ORACLE_LIB names another build)."""
+    if os.environ.get("PA_ORACLE_LIB"):
+        return _LIB_PATH
     if force or not os.path.exists(_LIB_PATH):
         compile_source(_SRC, _LIB_PATH)
     return _LIB_PATH

@@ -19,7 +19,10 @@ PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_ALIGN, PA_ERR_HIP =
 _DT = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 _CACHE_DT = {**_DT, torch.float8_e4m3fn: PA_FP8_E4M3}
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpaged_attn.so")
+# PAGED_ATTN_LIB: load another build of the same sources (e.g. one whose host
+# code is instrumented by sanitizers) instead of the in-tree library.
+LIB_PATH = os.environ.get("PAGED_ATTN_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpaged_attn.so")
 _LIB = None
 
 _P, _I32, _I64, _F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
