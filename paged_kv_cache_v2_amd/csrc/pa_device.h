@@ -26,6 +26,22 @@ constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// threadIdx.x as a value the compiler cannot form earlier than this point (an
+// empty asm statement that claims to modify it): index arithmetic of an
+// epilogue that starts from it then stays after the streaming loop instead of
+// being hoisted above it and holding registers through it.
+__device__ __forceinline__ int late_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+// A wavefront-uniform value made opaque the same way (kept in a scalar
+// register), so that arithmetic on it is not hoisted either.
+__device__ __forceinline__ int late_uniform(int v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
 // ---------------------------------------------------------------- codecs
 // Two 16-bit elements packed in one 32-bit word: element 0 in the low half.
 template <int DT> struct codec;

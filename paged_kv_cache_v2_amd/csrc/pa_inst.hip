@@ -5,6 +5,8 @@
 //             5: MFMA, two column tiles, 8-bit caches
 //             6: MFMA, rolling merge (one-call decode), 16-bit caches
 //             7: MFMA, rolling merge, two column tiles, 16-bit caches
+//             8: MFMA, rolling merge, 8-bit caches
+//             9: MFMA, rolling merge, two column tiles, 8-bit caches
 //   PA_AL     0: no position bias        1: ALiBi
 // The build compiles this file once per (family, ALiBi) pair in parallel.
 #include <hip/hip_runtime.h>
@@ -28,13 +30,13 @@ namespace pa {
 constexpr bool kAL = PA_AL != 0;
 
 #if PA_FAMILY != 2 && PA_FAMILY != 3
-constexpr bool kKV8 = PA_FAMILY == 1 || PA_FAMILY == 5;
-constexpr int kCT = PA_FAMILY == 4 || PA_FAMILY == 5 || PA_FAMILY == 7 ? 2 : 1;
+constexpr bool kKV8 = PA_FAMILY == 1 || PA_FAMILY == 5 || PA_FAMILY == 8 || PA_FAMILY == 9;
+constexpr int kCT = PA_FAMILY == 4 || PA_FAMILY == 5 || PA_FAMILY == 7 || PA_FAMILY == 9 ? 2 : 1;
 constexpr bool kRoll = PA_FAMILY >= 6;
 #define PA_MFMA_BS(DT, D)                                        \
   {partition_mfma_kernel<DT, D, 16, kKV8, kAL, kCT, kRoll>,      \
    partition_mfma_kernel<DT, D, 32, kKV8, kAL, kCT, kRoll>}
-#if PA_FAMILY != 4 && PA_FAMILY != 5 && PA_FAMILY != 7  // one column tile
+#if PA_FAMILY != 4 && PA_FAMILY != 5 && PA_FAMILY != 7 && PA_FAMILY != 9  // one column tile
 #define PA_MFMA_D(DT) {PA_MFMA_BS(DT, 64), PA_MFMA_BS(DT, 128), PA_MFMA_BS(DT, 256)}
 #else
 #define PA_MFMA_D(DT) {PA_MFMA_BS(DT, 64), PA_MFMA_BS(DT, 128), {nullptr, nullptr}}
@@ -49,8 +51,12 @@ const partition_fn PA_TABLE(kMfmaW)[2][3][2] = {PA_MFMA_D(DT_F16), PA_MFMA_D(DT_
 const partition_fn PA_TABLE(kMfma8W)[2][3][2] = {PA_MFMA_D(DT_F16), PA_MFMA_D(DT_BF16)};
 #elif PA_FAMILY == 6
 const partition_fn PA_TABLE(kMfmaR)[2][3][2] = {PA_MFMA_D(DT_F16), PA_MFMA_D(DT_BF16)};
-#else
+#elif PA_FAMILY == 7
 const partition_fn PA_TABLE(kMfmaRW)[2][3][2] = {PA_MFMA_D(DT_F16), PA_MFMA_D(DT_BF16)};
+#elif PA_FAMILY == 8
+const partition_fn PA_TABLE(kMfma8R)[2][3][2] = {PA_MFMA_D(DT_F16), PA_MFMA_D(DT_BF16)};
+#else
+const partition_fn PA_TABLE(kMfma8RW)[2][3][2] = {PA_MFMA_D(DT_F16), PA_MFMA_D(DT_BF16)};
 #endif
 #undef PA_MFMA_D
 #undef PA_MFMA_BS

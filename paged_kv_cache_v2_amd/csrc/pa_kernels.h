@@ -291,52 +291,73 @@ __device__ __forceinline__ int slot(int j, int w, int c, int NC) { return (j * k
 // normalised outputs. Local column c of the launch is column a.c0 + c = m*G + h
 // of the unit: query token m (of Mq) and query head kh*G + h; its output rows
 // are ((s*Mq + m)*H + kh*G + h) of the [S*Mq*H, P] statistics and
-// [S*Mq*H, P, D] tmp_output. Threads walk (column, partition, d) in memory
-// order, so the rows of adjacent partitions of one head are written together.
+// [S*Mq*H, P, D] tmp_output. Two steps with a barrier between them:
+//  1. one thread per (column, partition) forms the partition's max Mx over
+//     the wavefronts, its exp sum Z = sum_w e^(m_w - Mx) l_w and its
+//     statistics, and each wavefront's row weight e^(m_w - Mx) v_scale / Z,
+//     which it writes over that wavefront's parked max (a thread touches only
+//     its own slots);
+//  2. threads walk (column, partition, d) in memory order, so the rows of
+//     adjacent partitions of one head are written together; a row is the
+//     weighted sum of the wavefronts' accumulators.
 // A column whose causal prefix ends before a used partition merges to max
-// -inf, sum 0 (the empty-partition sentinels).
+// -inf, sum 0 and a zero row (the empty-partition sentinels).
+// The caller has synchronised the workgroup after parking; all its threads
+// call this (it contains a barrier).
 template <int D, bool AL>
-__device__ __forceinline__ void merge_store(const PartitionArgs& a, const float* s_m,
-                                            const float* s_l, const float* s_acc, int s, int kh,
-                                            int p0, int ne, int G, int NC, int L) {
+__device__ __forceinline__ void merge_store(const PartitionArgs& a, float* s_m, const float* s_l,
+                                            const float* s_acc, int s, int kh, int p0, int ne,
+                                            int G, int NC, int L) {
   constexpr int D4 = D / 4;
   const int per_col = ne * D4;
   const int mf = a.c0 / G, ml = (a.c0 + NC - 1) / G;  // first and last query token here
   const size_t row0 = ((size_t)s * a.Mq + mf) * a.H + kh * G;  // row of (mf, head kh*G)
+  for (int i = late_tid(); i < NC * ne; i += kWaves * 64) {
+    const int c = i / ne, j = i - c * ne;
+    const int m = (a.c0 + c) / G, h = a.c0 + c - m * G;
+    float mw[kWaves];
+    float Mx = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = s_m[slot(j, w, c, NC)];
+      Mx = fmaxf(Mx, mw[w]);
+    }
+    const float Mu = Mx == kNegInf ? 0.0f : Mx;  // a column with no keys here: all weights 0
+    float e[kWaves];
+    float Z = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      e[w] = fast_exp2(mw[w] - Mu);  // 0 for a wavefront with no tokens
+      Z += e[w] * s_l[slot(j, w, c, NC)];
+    }
+    const float f = Z > 0.0f ? a.v_scale / Z : 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s_m[slot(j, w, c, NC)] = e[w] * f;
+    float mx = Mx;
+    if constexpr (AL) {  // the partition's share of the ALiBi bias (see PartitionArgs)
+      const float slope2 = a.alibi[kh * G + h] * kLog2e;
+      mx += slope2 * (float)((p0 + j) * a.PS - (L - a.Mq + m));
+    }
+    const size_t row = (row0 + (m - mf) * a.H + h) * a.P + p0 + j;
+    a.exp_sums[row] = Z;
+    a.max_logits[row] = mx * kLn2;
+  }
+  __syncthreads();
   // The launch's rows of tmp_output (query tokens mf..ml x heads x P), 32-bit offsets.
   const __amdgpu_buffer_rsrc_t tmp = __builtin_amdgcn_make_buffer_rsrc(
       a.tmp_out + row0 * a.P * D, (short)0, ((ml - mf) * a.H + G) * a.P * D * 4, kRsrcFlags);
-  for (int i = threadIdx.x; i < NC * per_col; i += kWaves * 64) {
+  for (int i = late_tid(); i < NC * per_col; i += kWaves * 64) {
     const int c = i / per_col, rem = i - c * per_col;
     const int j = rem / D4, d4 = rem - j * D4;
     const int m = (a.c0 + c) / G, h = a.c0 + c - m * G;
-    float Mx = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[slot(j, w, c, NC)]);
-    const float Mu = Mx == kNegInf ? 0.0f : Mx;  // a column with no keys here: all weights 0
-    float Z = 0.0f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const int k = slot(j, w, c, NC);
-      const float e = fast_exp2(s_m[k] - Mu);  // 0 for a wavefront with no tokens
-      Z += e * s_l[k];
-      const f32x4 v = *(const f32x4*)&s_acc[k * D + 4 * d4];
-      o += e * v;
+      o += s_m[k] * *(const f32x4*)&s_acc[k * D + 4 * d4];
     }
-    const float inv = a.v_scale / Z;
     const int hrow = (m - mf) * a.H + h;  // row of this column relative to row0
-    const size_t row = (row0 + hrow) * a.P + p0 + j;
-    store_row(tmp, (uint32_t)(((hrow * a.P + p0 + j) * D + 4 * d4) * 4), o * inv, a.through);
-    if (d4 == 0) {
-      float mx = Mx;
-      if constexpr (AL) {  // the partition's share of the ALiBi bias (see PartitionArgs)
-        const float slope2 = a.alibi[kh * G + h] * kLog2e;
-        mx += slope2 * (float)((p0 + j) * a.PS - (L - a.Mq + m));
-      }
-      a.exp_sums[row] = Z;
-      a.max_logits[row] = mx * kLn2;
-    }
+    store_row(tmp, (uint32_t)(((hrow * a.P + p0 + j) * D + 4 * d4) * 4), o, a.through);
   }
 }
 
@@ -354,92 +375,109 @@ __device__ __forceinline__ void store_out4(void* out, int odt, size_t off, f32x4
   }
 }
 
-// One-call decode epilogue. Each of the span's ne used partitions is first
-// merged over the wavefronts exactly as merge_store does it -- partition j's
-// max m_j (log2 units, plus its share of the ALiBi bias), exp sum l_j and
-// normalised row o_j -- and the partitions are then combined with the
-// reduce's log-sum-exp rule: M = max_j m_j, Z = sum_j e^(m_j - M) l_j,
-// row = sum_j (e^(m_j - M) l_j / Z) o_j. When the span holds every partition
-// of the row (Pq == 1) that row is the attention output: it goes to `out` in
-// its dtype, with lse = M + ln Z if asked for, and nothing is written to the
-// workspace. Otherwise the span's (M, Z, row) is entry q = p0 / C of a
-// [rows, Pq] workspace, which the reduce combines exactly like partitions of
-// C * PS tokens. A column with no keys in the span (several query tokens,
-// causal prefix ended earlier) gets M = -inf, Z = 0 and a zero row.
+// One-call decode epilogue. Each of the span's ne used partitions is merged
+// over the wavefronts as merge_store does it -- partition j's max m_j (log2
+// units, plus its share of the ALiBi bias), exp sum l_j and normalised row
+// o_j = sum_w e^(m_jw - max_w m_jw) acc_jw / l_j -- and the partitions are
+// combined with the reduce's log-sum-exp rule: M = max_j m_j,
+// Z = sum_j e^(m_j - M) l_j, row = sum_j (e^(m_j - M) l_j / Z) o_j. The two
+// weights of a wavefront's accumulator are folded into one,
+// e^(m_jw - max_w m_jw) e^(m_j - M) v_scale / Z, in three steps separated by
+// barriers, each thread touching only its own parked slots until the last:
+//  1. one thread per (column, partition): the partition's maxima, l_j and m_j
+//     (kept in its first two exp-sum slots) and the wavefront factors
+//     e^(m_jw - max_w m_jw) (over the parked maxima);
+//  2. the same threads: M and Z of the column from every partition's l_j and
+//     m_j, and the factors scaled by e^(m_j - M) v_scale / Z; one thread per
+//     column stores the span's statistics;
+//  3. threads walk (column, d) and sum the weighted accumulators.
+// When the span holds every partition of the row (Pq == 1) that row is the
+// attention output: it goes to `out` in its dtype, with lse = M + ln Z if
+// asked for, and nothing is written to the workspace. Otherwise the span's
+// (M, Z, row) is entry q = p0 / C of a [rows, Pq] workspace, which the reduce
+// combines exactly like partitions of C * PS tokens. A column with no keys in
+// the span (several query tokens, causal prefix ended earlier) gets M = -inf,
+// Z = 0 and a zero row. The caller has synchronised the workgroup after
+// parking; all its threads call this (it contains barriers).
 template <int D, bool AL>
-__device__ __forceinline__ void combine_store(const PartitionArgs& a, const float* s_m,
-                                              const float* s_l, const float* s_acc, int s,
-                                              int kh, int p0, int ne, int G, int NC, int L) {
+__device__ __forceinline__ void combine_store(const PartitionArgs& a, float* s_m, float* s_l,
+                                              const float* s_acc, int s, int kh, int p0, int ne,
+                                              int G, int NC, int L) {
   constexpr int D4 = D / 4;
   const int q = p0 / a.C;
   const int mf = a.c0 / G, ml = (a.c0 + NC - 1) / G;  // first and last query token here
   const size_t row0 = ((size_t)s * a.Mq + mf) * a.H + kh * G;  // row of (mf, head kh*G)
+  for (int i = late_tid(); i < NC * ne; i += kWaves * 64) {
+    const int c = i / ne, j = i - c * ne;
+    float mw[kWaves];
+    float Mx = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = s_m[slot(j, w, c, NC)];
+      Mx = fmaxf(Mx, mw[w]);
+    }
+    const float mu = Mx == kNegInf ? 0.0f : Mx;  // 0 if no wavefront saw a key
+    float l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float e = fast_exp2(mw[w] - mu);
+      l += e * s_l[slot(j, w, c, NC)];
+      s_m[slot(j, w, c, NC)] = e;
+    }
+    float mx = Mx;
+    if constexpr (AL) {
+      const int m = (a.c0 + c) / G, h = a.c0 + c - m * G;
+      mx += a.alibi[kh * G + h] * kLog2e * (float)((p0 + j) * a.PS - (L - a.Mq + m));
+    }
+    s_l[slot(j, 0, c, NC)] = l;
+    s_l[slot(j, 1, c, NC)] = mx;
+  }
+  __syncthreads();
+  for (int i = late_tid(); i < NC * ne; i += kWaves * 64) {
+    const int c = i / ne, j = i - c * ne;
+    float M = kNegInf;
+    for (int k = 0; k < ne; ++k) M = fmaxf(M, s_l[slot(k, 1, c, NC)]);
+    const float Mu = M == kNegInf ? 0.0f : M;
+    float Z = 0.0f;
+    for (int k = 0; k < ne; ++k) {
+      const float lk = s_l[slot(k, 0, c, NC)];
+      Z += lk > 0.0f ? fast_exp2(s_l[slot(k, 1, c, NC)] - Mu) * lk : 0.0f;
+    }
+    // (a partition without keys for this column has weight 0)
+    const float lj = s_l[slot(j, 0, c, NC)];
+    const float f = lj > 0.0f ? fast_exp2(s_l[slot(j, 1, c, NC)] - Mu) * a.v_scale / Z : 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s_m[slot(j, w, c, NC)] *= f;
+    if (j == 0) {
+      const int m = (a.c0 + c) / G, h = a.c0 + c - m * G;
+      const size_t row = row0 + (m - mf) * a.H + h;
+      if (a.Pq == 1) {
+        if (a.lse) a.lse[row] = Z > 0.0f ? fmaf(__builtin_amdgcn_logf(Z), kLn2, M * kLn2) : kNegInf;
+      } else {
+        a.exp_sums[row * a.Pq + q] = Z;
+        a.max_logits[row * a.Pq + q] = M * kLn2;
+      }
+    }
+  }
+  __syncthreads();
   const __amdgpu_buffer_rsrc_t tmp = __builtin_amdgcn_make_buffer_rsrc(
       a.tmp_out + row0 * a.Pq * D, (short)0, ((ml - mf) * a.H + G) * a.Pq * D * 4, kRsrcFlags);
-  for (int i = threadIdx.x; i < NC * D4; i += kWaves * 64) {
+  for (int i = late_tid(); i < NC * D4; i += kWaves * 64) {
     const int c = i / D4, d4 = i - c * D4;
     const int m = (a.c0 + c) / G, h = a.c0 + c - m * G;
-    float slope2 = 0.0f;
-    if constexpr (AL) slope2 = a.alibi[kh * G + h] * kLog2e;
-    // Partition j's wavefront-common max mu (0 if no wavefront saw a key), its
-    // exp sum l and its max logit mx (log2 units, with its share of the bias).
-    // Recomputed from LDS in each pass below instead of being held in arrays.
-    auto part = [&](int j, float& mu, float& l, float& mx) {
-      float Mx = kNegInf;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[slot(j, w, c, NC)]);
-      mu = Mx == kNegInf ? 0.0f : Mx;
-      l = 0.0f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < ne; ++j) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const int k = slot(j, w, c, NC);
-        l += fast_exp2(s_m[k] - mu) * s_l[k];
-      }
-      mx = Mx;
-      if constexpr (AL) mx += slope2 * (float)((p0 + j) * a.PS - (L - a.Mq + m));
-    };
-    float M = kNegInf;
-    for (int j = 0; j < ne; ++j) {
-      float mu, l, mx;
-      part(j, mu, l, mx);
-      M = fmaxf(M, mx);
-    }
-    const float Mu = M == kNegInf ? 0.0f : M;
-    float Z = 0.0f;
-    for (int j = 0; j < ne; ++j) {
-      float mu, l, mx;
-      part(j, mu, l, mx);
-      Z += l > 0.0f ? fast_exp2(mx - Mu) * l : 0.0f;
-    }
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < ne; ++j) {
-      float mu, l, mx;
-      part(j, mu, l, mx);
-      if (l > 0.0f) {  // (a partition without keys for this column has weight 0)
-        f32x4 oj = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const int k = slot(j, w, c, NC);
-          oj += fast_exp2(s_m[k] - mu) * *(const f32x4*)&s_acc[k * D + 4 * d4];
-        }
-        oj *= a.v_scale / l;  // partition j's normalised row
-        o += (fast_exp2(mx - Mu) * l / Z) * oj;
+        o += s_m[k] * *(const f32x4*)&s_acc[k * D + 4 * d4];
       }
     }
     const int hrow = (m - mf) * a.H + h;  // row of this column relative to row0
-    if (a.Pq == 1) {
-      const size_t row = row0 + hrow;
-      store_out4(a.out, a.odt, row * D + 4 * d4, o);
-      if (a.lse && d4 == 0)
-        a.lse[row] = Z > 0.0f ? fmaf(__builtin_amdgcn_logf(Z), kLn2, M * kLn2) : kNegInf;
-    } else {
+    if (a.Pq == 1)
+      store_out4(a.out, a.odt, (row0 + hrow) * D + 4 * d4, o);
+    else
       store_row(tmp, (uint32_t)(((hrow * a.Pq + q) * D + 4 * d4) * 4), o, a.through);
-      if (d4 == 0) {
-        const size_t e = (row0 + hrow) * a.Pq + q;
-        a.exp_sums[e] = Z;
-        a.max_logits[e] = M * kLn2;
-      }
-    }
   }
 }
 
@@ -551,7 +589,10 @@ __device__ __forceinline__ int lpt_pair(const PartitionArgs& a, uint8_t* smem) {
 template <int BS>
 __device__ __forceinline__ void unit_begin(const PartitionArgs& a, Unit& u, uint8_t* smem) {
   u.kh = blockIdx.x % a.KH;
-  const int pair = a.lpt ? lpt_pair<BS>(a, smem) : (int)(blockIdx.x / a.KH);
+  // (uniform; read out of lane 0 so that the unit's indices live in scalar
+  // registers rather than vector ones)
+  const int pair =
+      __builtin_amdgcn_readfirstlane(a.lpt ? lpt_pair<BS>(a, smem) : (int)(blockIdx.x / a.KH));
   u.s = pair % a.S;
   u.p0 = (pair / a.S) * a.C;
   u.nparts = min(a.C, a.P - u.p0);
@@ -569,6 +610,7 @@ __device__ __forceinline__ void unit_begin(const PartitionArgs& a, Unit& u, uint
 // block-table slice to LDS for the whole workgroup.
 template <int BS, int D>
 __device__ __forceinline__ bool unit_hoist(const PartitionArgs& a, int32_t* s_bt, Unit& u) {
+  u.L = __builtin_amdgcn_readfirstlane(u.L);  // (uniform, as the unit's indices)
   const int t0 = u.p0 * a.PS;
   if (!a.fuse) {
     if ((int)threadIdx.x < u.nparts * u.NC) {
@@ -676,15 +718,22 @@ constexpr int prefetch_fp8(int page_regs) { return page_regs <= 16 ? PA_PREFETCH
 constexpr int fp8_waves(int D, int BS, bool AL) {
   return PA_FP8_WAVES > 0 ? PA_FP8_WAVES : D * BS <= 2048 && !AL ? 4 : D <= 128 ? 3 : 2;
 }
+// Wavefronts per SIMD of the 8-bit rolling-merge kernel (one column tile): its
+// running combination and merge do not fit the plain 8-bit kernel's budget.
+#ifndef PA_FP8_ROLL_WAVES
+#define PA_FP8_ROLL_WAVES 2
+#endif
 // Register budget (wavefronts per SIMD) of the MFMA kernel: 2 for 16-bit
 // caches (one or two column tiles; left unbounded, the one-tile kernel at head
 // size 128 took 288 registers, one wavefront per SIMD, and ran ~1 % slower on
 // the GQA and long-context batches than at 2) except the largest page (head
-// size 256, 32-token blocks), which would spill at 2; the 8-bit budget above
+// size 256, 32-token blocks), which would spill at 2; the 8-bit budgets above
 // otherwise.
-constexpr int mfma_waves(int D, int BS, bool KV8, bool AL, int CT) {
+constexpr int mfma_waves(int D, int BS, bool KV8, bool AL, int CT, bool ROLL) {
   return CT > 1 ? 2
-         : KV8  ? fp8_waves(D, BS, AL)
+         : KV8  ? (ROLL ? (PA_FP8_ROLL_WAVES < fp8_waves(D, BS, AL) ? PA_FP8_ROLL_WAVES
+                                                                     : fp8_waves(D, BS, AL))
+                        : fp8_waves(D, BS, AL))
                 : (PA_MIN_WAVES > 0 ? PA_MIN_WAVES : D * BS <= 4096 ? 2 : 1);
 }
 
@@ -699,15 +748,13 @@ constexpr int roll_prefetch(int pf) {
   return ROLL && CT > 1 ? (pf < PA_ROLL_CT2_PREFETCH ? pf : PA_ROLL_CT2_PREFETCH) : pf;
 }
 
-// ROLL: the one-call decode's rolling merge (16-bit caches only; see
-// park_roll), a separate instantiation so that the other kernels carry none
-// of its code or registers.
+// ROLL: the one-call decode's rolling merge (see park_roll), a separate
+// instantiation so that the other kernels carry none of its code or registers.
 template <int DT, int D, int BS, bool KV8, bool AL, int CT, bool ROLL>
 __global__ void __launch_bounds__(kWaves * 64)
-__attribute__((amdgpu_waves_per_eu(mfma_waves(D, BS, KV8, AL, CT))))
+__attribute__((amdgpu_waves_per_eu(mfma_waves(D, BS, KV8, AL, CT, ROLL))))
 partition_mfma_kernel(PartitionArgs a) {
   static_assert(CT == 1 || CT == 2, "one or two column tiles");
-  static_assert(!(ROLL && KV8), "the rolling merge is built for 16-bit caches");
   constexpr int SUB = BS / 16;  // 16-token sub-tiles per page
   constexpr int KS = D / 32;    // QK k-steps (32 d each) per sub-tile
   constexpr int KL = KV8 ? D / 64 : D / 32;  // K 16-byte loads per lane per sub-tile

@@ -22,6 +22,8 @@ extern const partition_fn kMfmaW_al0[2][3][2], kMfmaW_al1[2][3][2];
 extern const partition_fn kMfma8W_al0[2][3][2], kMfma8W_al1[2][3][2];
 extern const partition_fn kMfmaR_al0[2][3][2], kMfmaR_al1[2][3][2];    // rolling merge
 extern const partition_fn kMfmaRW_al0[2][3][2], kMfmaRW_al1[2][3][2];  // rolling, two tiles
+extern const partition_fn kMfma8R_al0[2][3][2], kMfma8R_al1[2][3][2];    // rolling, 8-bit
+extern const partition_fn kMfma8RW_al0[2][3][2], kMfma8RW_al1[2][3][2];  // rolling, 8-bit, two
 extern const partition_fn kVec_al0[3][3][2][3], kVec_al1[3][3][2][3];
 extern const partition_fn kVec8_al0[2][3][2][3], kVec8_al1[2][3][2][3];
 

@@ -55,9 +55,11 @@ const pa::partition_fn (*const kMfma[2][2])[3][2] = {{pa::kMfma_al0, pa::kMfmaW_
                                                      {pa::kMfma_al1, pa::kMfmaW_al1}};
 const pa::partition_fn (*const kMfma8[2][2])[3][2] = {{pa::kMfma8_al0, pa::kMfma8W_al0},
                                                       {pa::kMfma8_al1, pa::kMfma8W_al1}};
-// the rolling-merge instantiations of the 16-bit kernels (one-call decode)
+// the rolling-merge instantiations (one-call decode), 16-bit and 8-bit caches
 const pa::partition_fn (*const kMfmaR[2][2])[3][2] = {{pa::kMfmaR_al0, pa::kMfmaRW_al0},
                                                       {pa::kMfmaR_al1, pa::kMfmaRW_al1}};
+const pa::partition_fn (*const kMfma8R[2][2])[3][2] = {{pa::kMfma8R_al0, pa::kMfma8RW_al0},
+                                                       {pa::kMfma8R_al1, pa::kMfma8RW_al1}};
 const pa::partition_fn (*const kVec[2])[3][2][3] = {pa::kVec_al0, pa::kVec_al1};
 const pa::partition_fn (*const kVec8[2])[3][2][3] = {pa::kVec8_al0, pa::kVec8_al1};
 
@@ -191,14 +193,23 @@ constexpr int kSpanLdsCap = 80 * 1024;
 #ifndef PA_ROLL
 #define PA_ROLL 1  // measurement builds: 0 never the rolling merge, 2 always (one-call MFMA spans)
 #endif
+// The 8-bit one-call decode's spans of two or more partitions run the
+// rolling-merge kernel: the plain 8-bit kernel's register budget (4 wavefronts
+// per SIMD) leaves each workgroup 40 KiB of LDS, two partitions' parked states
+// at 8 columns, so its spans stay short.
+#ifndef PA_ROLL8
+#define PA_ROLL8 1  // measurement builds: 0 keeps 8-bit caches on combine_store spans
+#endif
+constexpr bool kRoll8 = PA_ROLL8 != 0;
 
 // Ring slots of the rolling merge for a one-call MFMA span of c partitions
 // (roll_ct = the launch's column tiles; 0: not an MFMA one-call launch): 0
-// where the span's parked states fit lds_cap (combine_store), else 2 or 1 slots
-// as they fit; -1 if nothing fits.
-int span_roll(int PS, int BS, int NC, int D, int c, int roll_ct, int lds_cap) {
+// where the span's parked states fit lds_cap (combine_store) and the rolling
+// merge is not preferred, else 2 or 1 slots as they fit; -1 if nothing fits.
+int span_roll(int PS, int BS, int NC, int D, int c, int roll_ct, int lds_cap,
+              bool prefer = false) {
   const bool park = pa::lds_layout(PS, BS, NC, D, c).total <= lds_cap;
-  if (roll_ct == 0 || c < 2 || (park && PA_ROLL < 2)) return park ? 0 : -1;
+  if (roll_ct == 0 || c < 2 || (park && !prefer && PA_ROLL < 2)) return park ? 0 : -1;
   if (PA_ROLL == 0) return park ? 0 : -1;
   if (pa::roll_layout(PS, BS, roll_ct, D, c, 2).total <= lds_cap) return 2;
   if (pa::roll_layout(PS, BS, roll_ct, D, c, 1).total <= lds_cap) return 1;
@@ -389,21 +400,28 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
     return fail(PA_ERR_UNSUPPORTED, "needs %d bytes of LDS per workgroup, device allows %d", lds1,
                 lds_limit);
   // One-call launches of the MFMA kernel may span more partitions than their
-  // parked states fit, with the rolling merge.
-  const int roll_ct = fuse && !vec && kvdt != PA_FP8_E4M3 ? (NC > 16 ? 2 : 1) : 0;
-  const int cap = span_lds_cap(fn, lds_limit);
+  // parked states fit, with the rolling merge. With an 8-bit cache every
+  // one-call span of two or more partitions takes it (kRoll8), and spans are
+  // sized for that kernel's occupancy.
+  const bool kv8 = kvdt == PA_FP8_E4M3;
+  const int roll_ct = fuse && !vec && (!kv8 || kRoll8) ? (NC > 16 ? 2 : 1) : 0;
+  const partition_fn rfn =
+      roll_ct ? (kv8 ? kMfma8R : kMfmaR)[al][roll_ct - 1][qdt - 1][d_index(D)][bs_index(BS)]
+              : nullptr;
+  const partition_fn sized = kv8 && rfn ? rfn : fn;
+  const int cap = span_lds_cap(sized, lds_limit);
   const int span = force_span > 0 ? force_span
                                   : pick_span(S, KH, P, PS, BS, NC, D, elem_size(kvdt), cap,
-                                              span_min_grid(fn, fuse ? kMinRoundsFused
-                                                                     : kMinRounds),
+                                              span_min_grid(sized, fuse ? kMinRoundsFused
+                                                                        : kMinRounds),
                                               roll_ct);
   const long long grid = (long long)S * KH * ((P + span - 1) / span);
   if (grid > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many work units");
   // (a longer span was admitted by pick_span, or is a forced shorter one;
   // one partition's parked state fits lds_limit, checked above)
-  plan->roll = roll_ct && span > 1 ? span_roll(PS, BS, NC, D, span, roll_ct, cap) : 0;
+  plan->roll = roll_ct && span > 1 ? span_roll(PS, BS, NC, D, span, roll_ct, cap, kv8) : 0;
   if (plan->roll < 0) return fail(PA_ERR_UNSUPPORTED, "no LDS layout for a span of %d", span);
-  if (plan->roll > 0) fn = kMfmaR[al][roll_ct - 1][qdt - 1][d_index(D)][bs_index(BS)];
+  if (plan->roll > 0) fn = rfn;
   plan->fn = fn;
   plan->lds_bytes = plan->roll > 0 ? pa::roll_layout(PS, BS, roll_ct, D, span, plan->roll).total
                                    : pa::lds_layout(PS, BS, NC, D, span).total;

@@ -9,7 +9,9 @@ four owned d-blocks per wavefront), one and two column tiles, spans that hold
 a whole row (the output written by the partition kernel) and spans that do
 not (span entries, then the reduce), lengths at partition and span edges,
 rows shorter than the query window and empty sequences, ALiBi, the row
-log-sum-exp and a 16-bit output. Every output row and lse is compared with
+log-sum-exp and a 16-bit output; with 16-bit and 8-bit (E4M3, scaled) caches
+(an 8-bit cache takes the rolling merge for every span of two or more
+partitions). Every output row and lse is compared with
 the oracle, and with the two calls (paged_attn_v2_partition_ex +
 paged_attn_v2_reduce_lse), whose per-partition rows the other tests compare.
 """
@@ -31,7 +33,8 @@ def built():
     oracle.build(force=False)
 
 
-# label, (dtype, H, KH, D, BS, PS, M, S, P)
+# label, (cache dtype, H, KH, D, BS, PS, M, S, P); 8-bit caches with a bf16
+# or f16 query (the q_dtype column of FP8_QUERY)
 CASES = [
     ("g4m4_d128", ("bf16", 32, 8, 128, 16, 64, 4, 128, 8)),
     ("g4m4_d128_entries", ("bf16", 32, 8, 128, 16, 64, 4, 128, 16)),
@@ -39,7 +42,14 @@ CASES = [
     ("g8m2_d64_bs32", ("f16", 32, 4, 64, 32, 64, 2, 256, 8)),
     ("g8_d256", ("bf16", 16, 2, 256, 16, 32, 1, 512, 8)),
     ("g16_d128_single", ("f16", 64, 4, 128, 16, 64, 1, 256, 8)),
+    ("fp8_g8_d128", ("fp8", 64, 8, 128, 16, 64, 1, 64, 8)),
+    ("fp8_g4_d128_entries", ("fp8", 32, 8, 128, 16, 64, 1, 128, 16)),
+    ("fp8_g8m4_two_tiles", ("fp8", 64, 8, 128, 16, 64, 4, 64, 8)),
+    ("fp8_g4_d64_bs32", ("fp8", 16, 4, 64, 32, 64, 1, 256, 8)),
+    ("fp8_g8_d256", ("fp8", 16, 2, 256, 16, 32, 1, 256, 8)),
 ]
+FP8_QUERY = {"fp8_g4_d64_bs32": "f16"}  # the others: bf16
+FP8_SCALES = (0.015, 0.02)  # k_scale, v_scale
 BY = {c[0]: c for c in CASES}
 
 
@@ -53,9 +63,13 @@ def lens_for(S, BS, PS, P, M, seed):
 
 def cfg_of(label):
     _, (dtype, H, KH, D, BS, PS, M, S, P) = BY[label]
+    extra = {}
+    if dtype == "fp8":
+        extra = dict(q_dtype=FP8_QUERY.get(label, "bf16"), k_scale=FP8_SCALES[0],
+                     v_scale=FP8_SCALES[1])
     cfg = W.DecodeConfig(f"roll_{label}", num_seqs=S, num_heads=H, num_kv_heads=KH,
                          head_size=D, block_size=BS, partition_size=PS, dtype=dtype, len_lo=0,
-                         len_hi=P * PS, num_queries=M)
+                         len_hi=P * PS, num_queries=M, **extra)
     return cfg, PS, P
 
 
@@ -82,11 +96,14 @@ def test_cases_cover_the_plans():
     assert all(p["roll"] in (1, 2) and p["span"] >= 2 for p in plans), plans
     assert {p["roll"] for p in plans} == {1, 2}, plans
     assert any(p["entries"] == 1 for p in plans) and any(p["entries"] > 1 for p in plans), plans
+    fp8 = [p for c, p in zip(CASES, plans) if c[1][0] == "fp8"]
+    assert any(p["entries"] == 1 for p in fp8) and any(p["entries"] > 1 for p in fp8), fp8
 
 
 def run(d, PS, P, slopes, out_dtype):
     """The one call (with lse), then the two calls; host copies."""
     q = d["query"]
+    scales = dict(k_scale=d["k_scale"], v_scale=d["v_scale"]) if "k_scale" in d else {}
     lead = tuple(q.shape[:-1])
     D = q.shape[-1]
 
@@ -99,11 +116,11 @@ def run(d, PS, P, slopes, out_dtype):
     al = slopes.to(U.DEV) if slopes is not None else None
     out = torch.full(q.shape, float("nan"), device=U.DEV).to(out_dtype)
     lse = torch.full(lead, float("nan"), device=U.DEV)
-    pa.paged_attn_decode_ex(out, *ws(), *args, alibi_slopes=al, lse=lse)
+    pa.paged_attn_decode_ex(out, *ws(), *args, alibi_slopes=al, lse=lse, **scales)
     tmp, es, ml = ws()
     out_s = torch.full(q.shape, float("nan"), device=U.DEV).to(out_dtype)
     lse_s = torch.full(lead, float("nan"), device=U.DEV)
-    pa.paged_attn_v2_partition_ex(tmp, es, ml, *args, alibi_slopes=al)
+    pa.paged_attn_v2_partition_ex(tmp, es, ml, *args, alibi_slopes=al, **scales)
     pa.paged_attn_v2_reduce_lse(out_s, lse_s, tmp, es, ml, d["seq_lens"], PS)
     torch.cuda.synchronize()
     return out.cpu(), lse.cpu(), out_s.cpu(), lse_s.cpu()
@@ -131,7 +148,8 @@ def test_rolling_merge_matches_oracle(label, variant):
     out, lse, out_s, lse_s = run(d, PS, P, slopes, out_dtype)
     a = (inp["query"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
          inp["seq_lens"], inp["scale"])
-    ref, ref_lse = oracle.attention_lse(*a, alibi_slopes=slopes)
+    scales = {k: inp[k] for k in ("k_scale", "v_scale") if k in inp}
+    ref, ref_lse = oracle.attention_lse(*a, alibi_slopes=slopes, **scales)
     if out_dtype == torch.float32:
         w = U.assert_close(f"{label} {variant} out", out, ref)
         U.assert_close(f"{label} {variant} out (two calls)", out_s, ref)
@@ -146,7 +164,7 @@ def test_rolling_merge_matches_oracle(label, variant):
     assert np.all(out.float().numpy()[empty] == 0)
 
 
-@pytest.mark.parametrize("label", ["g4m4_d128", "g8m4_two_tiles"])
+@pytest.mark.parametrize("label", ["g4m4_d128", "g8m4_two_tiles", "fp8_g8_d128"])
 def test_rolling_merge_run_to_run_identical(label):
     cfg, inp, PS, P = case(label, seed=92)
     d = U.to_device(inp)

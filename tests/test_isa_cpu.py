@@ -94,10 +94,9 @@ def test_kv_loads_are_dwordx4_or_dwordx2_streaming(kernels):
         if "partition_vec_kernelILi2ELi128ELi16ELi1ELb1" in k:
             assert any(l.startswith("global_load_dwordx4") for l in nt)
             seen += 1
-    # each with ALiBi off and on; the 16-bit MFMA ones with one and two column
-    # tiles, with and without the rolling merge; the 8-bit MFMA ones with one
-    # and two column tiles
-    assert seen == 14
+    # each with ALiBi off and on; the MFMA ones (16-bit and 8-bit caches) with
+    # one and two column tiles, with and without the rolling merge
+    assert seen == 18
 
 
 def test_fp8_kernels_convert_with_gfx950_instructions(kernels):
