@@ -27,9 +27,9 @@ two torch.cuda.synchronize() calls. Prints ONE JSON line:
                two kernels' event-timed averages.
   tuned      = the same batch through paged_attn_decode at the partition size
                the library plans for it (paged_attn_plan_partition_size).
-  workloads  = the same measurements (value, flushed, roofline, tuned) for the
-               other configurations named by --also (the long-context GQA batch
-               by default).
+  workloads  = the same measurements (value, flushed, roofline, tuned, ceiling)
+               for the other configurations named by --also (the long-context
+               GQA batch by default).
   ceiling    = a read-only kernel that gathers the same K/V pages through the
                same block tables with the same loads and computes nothing
                (libpa_ceiling.so): the page-gather read bandwidth of this chip.
@@ -489,6 +489,8 @@ def run(args) -> dict:
         for name in also:
             o = Batch(name, pa, W, torch)
             r = o.measure(K, W_, args.flushed_calls, two_call=False)
+            if not args.no_ceiling:
+                r["ceiling"] = gather_ceiling(pa, torch, o, K)
             res["workloads"][name] = r
             del o
             torch.cuda.empty_cache()

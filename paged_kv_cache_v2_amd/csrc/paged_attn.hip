@@ -338,6 +338,11 @@ long long span_min_grid(partition_fn fn, int rounds = kMinRounds) {
 // tokens 181.0 -> 170.5, with 4 query tokens 189 -> 175; spans of 8 over 2 MiB
 // (head size 256) were slower, so the byte limit stays.
 constexpr int kMinRoundsFused = 1;
+// The 8-bit rolling-merge kernel (three workgroups per CU) takes its spans
+// down to a grid of kMinWgsPerCuRoll8 workgroups per CU rather than a full
+// round: on the long-context batch at 512-token partitions, spans of eight
+// (512 workgroups) against four (1024) measured 90.9 -> 88.7 us.
+constexpr int kMinWgsPerCuRoll8 = 2;
 
 // Host checks shared by the partition entry points; fills `plan` for a launch
 // of NC columns. The query has dtype qdt; the caches kvdt (== qdt, or
@@ -410,11 +415,11 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
               : nullptr;
   const partition_fn sized = kv8 && rfn ? rfn : fn;
   const int cap = span_lds_cap(sized, lds_limit);
+  long long min_grid = span_min_grid(sized, fuse ? kMinRoundsFused : kMinRounds);
+  if (kv8 && rfn) min_grid = std::min(min_grid, (long long)kMinWgsPerCuRoll8 * cu_count());
   const int span = force_span > 0 ? force_span
                                   : pick_span(S, KH, P, PS, BS, NC, D, elem_size(kvdt), cap,
-                                              span_min_grid(sized, fuse ? kMinRoundsFused
-                                                                        : kMinRounds),
-                                              roll_ct);
+                                              min_grid, roll_ct);
   const long long grid = (long long)S * KH * ((P + span - 1) / span);
   if (grid > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many work units");
   // (a longer span was admitted by pick_span, or is a forced shorter one;
