@@ -29,7 +29,8 @@ two torch.cuda.synchronize() calls. Prints ONE JSON line:
                the library plans for it (paged_attn_plan_partition_size).
   workloads  = the same measurements (value, flushed, roofline, tuned, ceiling)
                for the other configurations named by --also (the long-context
-               GQA batch by default).
+               GQA batch by default), each after 0.1 s of untimed calls (the
+               clocks ramp up again after the idle gap of building the batch).
   ceiling    = a read-only kernel that gathers the same K/V pages through the
                same block tables with the same loads and computes nothing
                (libpa_ceiling.so): the page-gather read bandwidth of this chip.
@@ -294,6 +295,17 @@ class Batch:
         return ("partition_mfma_kernel" if c.query_dtype != "f32" and (c.group >= 4 or self.MQ > 1)
                 else "partition_vec_kernel")
 
+    def settle(self, seconds):
+        """Untimed decode calls for at least `seconds`: the GPU's clocks ramp up
+        over the first ~20 ms of load after an idle gap (the 8-bit batches, whose
+        kernels issue more instructions per byte, run ~10 % slower until then)."""
+        torch = self.torch
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(20):
+                self.decode()
+            torch.cuda.synchronize()
+
     def measure(self, K, W_, flushed_calls, two_call=True):
         """value (back to back), roofline (events), flushed, tuned; two_call optional."""
         step_s = self.back_to_back(self.decode, K, W_)
@@ -488,6 +500,7 @@ def run(args) -> dict:
         res["workloads"] = {}
         for name in also:
             o = Batch(name, pa, W, torch)
+            o.settle(0.1)  # (building the batch left the GPU idle for seconds)
             r = o.measure(K, W_, args.flushed_calls, two_call=False)
             if not args.no_ceiling:
                 r["ceiling"] = gather_ceiling(pa, torch, o, K)
