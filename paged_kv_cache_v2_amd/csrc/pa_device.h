@@ -140,6 +140,23 @@ template <> struct mma<DT_F16> {
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// v_max_f32 / v_max3_f32 as single instructions. fmaxf makes the compiler
+// quiet possible signalling NaNs first (one v_max_f32 x, x, x per operand it
+// cannot prove canonical: every value that comes out of a cross-lane swap or
+// a select). The scores and running maxima maxed here are products, sums and
+// selects of finite values and -inf, and the instruction's result is the
+// same; the quieting is dropped. (ALU instructions only; nothing is loaded.)
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Exchange across 16-lane rows with gfx950's v_permlane16_swap / v_permlane32_swap
 // (register-to-register, no LDS round trip). Called with the same value in
 // both operands, each returns, in every lane l, the pair (x_a, x_b) = the
@@ -163,8 +180,15 @@ __device__ __forceinline__ void pair32(float v, float& a, float& b) {
 __device__ __forceinline__ float rows_max(float v) {
   float a, b;
   pair16(v, a, b);
-  pair32(fmaxf(a, b), a, b);
-  return fmaxf(a, b);
+  pair32(max_raw(a, b), a, b);
+  return max_raw(a, b);
+}
+// max(m, rows_max(v)) with the last step fused into one v_max3_f32.
+__device__ __forceinline__ float rows_max_with(float v, float m) {
+  float a, b;
+  pair16(v, a, b);
+  pair32(max_raw(a, b), a, b);
+  return max3_raw(m, a, b);
 }
 __device__ __forceinline__ float rows_sum(float v) {
   float a, b;
@@ -174,10 +198,10 @@ __device__ __forceinline__ float rows_sum(float v) {
 }
 // Max / sum within each 16-lane row.
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, shfl_xor(v, 1));
-  v = fmaxf(v, shfl_xor(v, 2));
-  v = fmaxf(v, shfl_xor(v, 4));
-  return fmaxf(v, shfl_xor(v, 8));
+  v = max_raw(v, shfl_xor(v, 1));
+  v = max_raw(v, shfl_xor(v, 2));
+  v = max_raw(v, shfl_xor(v, 4));
+  return max_raw(v, shfl_xor(v, 8));
 }
 __device__ __forceinline__ float row16_sum(float v) {
   v += shfl_xor(v, 1);
@@ -201,6 +225,15 @@ __device__ __forceinline__ bool e_valid(int e, int nvalid) { return e < nvalid; 
 // of keep_first.
 __device__ __forceinline__ uint32_t keep_first_bytes(uint32_t w, int nvalid) {
   const uint32_t m = nvalid >= 4 ? 0xffffffffu : nvalid <= 0 ? 0u : (1u << (8 * nvalid)) - 1u;
+  return w & m;
+}
+
+// Zero the elements (ESZ bytes each: 1, 2 or 4) of a word at positions >=
+// nvalid; nvalid may be negative or past the word's elements.
+template <int ESZ>
+__device__ __forceinline__ uint32_t keep_first_elems(uint32_t w, int nvalid) {
+  constexpr int N = 4 / ESZ;
+  const uint32_t m = nvalid >= N ? 0xffffffffu : nvalid <= 0 ? 0u : (1u << (8 * ESZ * nvalid)) - 1u;
   return w & m;
 }
 

@@ -100,6 +100,17 @@ __device__ __forceinline__ T stream_load(const void* p) {
   return *(const T*)p;
 #endif
 }
+// The same through a global-memory (address space 1) pointer.
+typedef const __attribute__((address_space(1))) uint8_t* gbytes;
+template <typename T>
+__device__ __forceinline__ T stream_load(gbytes p) {
+  typedef const __attribute__((address_space(1))) T* gT;
+#if PA_NT_LOADS
+  return __builtin_nontemporal_load((gT)p);
+#else
+  return *(gT)p;
+#endif
+}
 
 // Software pipeline over a wavefront's pages: fetch(i, buf) is issued PF pages
 // ahead of process(i, buf); buffers rotate through a ring whose indices are
@@ -771,7 +782,10 @@ partition_mfma_kernel(PartitionArgs a) {
   Unit u;
   unit_begin<BS>(a, u, smem);
   const int G = u.G, NC = u.NC;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // (read out of lane 0: the compiler then knows it is wavefront-uniform, so
+  // the page index and the branches on it are scalar)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane & 15, grp = lane >> 4;  // g: this lane's column in a tile (and token row)
   // Column 16t + g of the launch (tile t) is column a.c0 + 16t + g = qm*G + h
   // of the unit: query head kh*G + h of query token qm, which sees tokens
@@ -779,6 +793,9 @@ partition_mfma_kernel(PartitionArgs a) {
   // (>= NC) take the launch's first column with a zero query, so their
   // running max stays put like a live column's.
   int lim[CT];
+  // The smallest of the launch's limits: that of its first column's query
+  // token (the padding columns take the first column too).
+  const int lim_lo = min(u.L, max(0, u.L - a.Mq + a.c0 / G + 1));
   float slope2[CT];  // ALiBi slope of the column, log2 units
   int qpos[CT];      // the column's query position (ALiBi, rolling merge)
   u32x4 qb[CT][KS];  // Q columns as the QK B operand
@@ -972,24 +989,33 @@ partition_mfma_kernel(PartitionArgs a) {
     next_edge += pps;
   };
 
+  // The page's base is wavefront-uniform (scalar registers) and each lane adds
+  // a 32-bit offset: the loads take the scalar-base form, with no per-page
+  // 64-bit address arithmetic in vector registers.
   auto fetch = [&](int i, Page& pg) {
     const int blk = min(max(__builtin_amdgcn_readfirstlane(s_bt[wave + i * kWaves]), 0), a.NB - 1);
-    const uint8_t* kp = kbase + (size_t)blk * blk_stride + k_lane;
-    const uint8_t* vp = vbase + (size_t)blk * blk_stride + v_lane;
+    gbytes kpage = (gbytes)(kbase + (size_t)blk * blk_stride);
+    gbytes vpage = (gbytes)(vbase + (size_t)blk * blk_stride);
+    // (opaque scalar values from here: the compiler would otherwise fold the
+    // lane offsets into the base once, outside the loop, and redo the page
+    // arithmetic per lane)
+    asm volatile("" : "+s"(kpage), "+s"(vpage));
 #pragma unroll
     for (int j = 0; j < KL; ++j) {
 #pragma unroll
       for (int st = 0; st < SUB; ++st)
-        pg.k[st][j] = stream_load<u32x4>(kp + j * 4 * BS * 16 + st * 256);
+        pg.k[st][j] = stream_load<u32x4>(kpage + (k_lane + (uint32_t)(j * 4 * BS * 16 + st * 256)));
     }
 #pragma unroll
     for (int mb = 0; mb < VB; ++mb) {
 #pragma unroll
       for (int st = 0; st < SUB; ++st) {
         if constexpr (KV8) {
-          if (mb % 4 == 0) pg.v[st][mb / 4] = stream_load<u32x4>(vp + mb * 16 * BS + st * 16);
+          if (mb % 4 == 0)
+            pg.v[st][mb / 4] =
+                stream_load<u32x4>(vpage + (v_lane + (uint32_t)(mb * 16 * BS + st * 16)));
         } else {
-          pg.v[st][mb] = stream_load<u32x2>(vp + mb * 16 * BS * 2 + st * 32);
+          pg.v[st][mb] = stream_load<u32x2>(vpage + (v_lane + (uint32_t)(mb * 16 * BS * 2 + st * 32)));
         }
       }
     }
@@ -1021,6 +1047,7 @@ partition_mfma_kernel(PartitionArgs a) {
     const int page = wave + i * kWaves;  // page of the span
     while (page >= next_edge) park();  // (the rolling merge has parked in pre)
     const int tok0 = (u.pg0 + page) * BS;  // first token of the page
+    const bool full = tok0 + BS <= lim_lo;
     float s2[CT][SUB][4];
 #pragma unroll
     for (int st = 0; st < SUB; ++st) {
@@ -1035,39 +1062,53 @@ partition_mfma_kernel(PartitionArgs a) {
       }
 #pragma unroll
       for (int t = 0; t < CT; ++t) {
-        const int nvalid = lim[t] - (tok0 + 16 * st + 4 * grp);  // row 4*grp+r valid iff r < nvalid
-        if constexpr (AL) {  // position relative to the page's partition start
-          const float base =
-              slope2[t] * (float)(tok0 + 16 * st + 4 * grp - (u.p0 + jcur) * a.PS);
+        // score of row 4*grp+r (log2 units, with this page's share of the bias)
+        auto score = [&](int r) {
+          if constexpr (AL) {  // position relative to the page's partition start
+            const float base =
+                slope2[t] * (float)(tok0 + 16 * st + 4 * grp - (u.p0 + jcur) * a.PS);
+            return fmaf(sc[t][r], a.qk_scale, fmaf(slope2[t], (float)r, base));
+          } else {
+            return sc[t][r] * a.qk_scale;
+          }
+        };
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s2[t][st][r] = score(r);
+      }
+    }
+    // Rows past a column's limit (the sequence's end, or a query token's causal
+    // prefix): only on pages that reach a limit (wavefront-uniform branch).
+    if (!full) {
+#pragma unroll
+      for (int st = 0; st < SUB; ++st) {
+#pragma unroll
+        for (int t = 0; t < CT; ++t) {
+          const int nvalid = lim[t] - (tok0 + 16 * st + 4 * grp);  // row 4*grp+r valid iff r < nvalid
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            s2[t][st][r] = r < nvalid ? fmaf(sc[t][r], a.qk_scale, fmaf(slope2[t], (float)r, base))
-                                      : kNegInf;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) s2[t][st][r] = r < nvalid ? sc[t][r] * a.qk_scale : kNegInf;
+            if (r >= nvalid) s2[t][st][r] = kNegInf;
         }
       }
     }
     u32x2 phi[CT][SUB], plo[CT][SUB];
 #pragma unroll
     for (int t = 0; t < CT; ++t) {
-      float mt = kNegInf;
+      float mt = max_raw(max3_raw(s2[t][0][0], s2[t][0][1], s2[t][0][2]), s2[t][0][3]);
 #pragma unroll
-      for (int st = 0; st < SUB; ++st)
-        mt = fmaxf(mt, fmaxf(fmaxf(s2[t][st][0], s2[t][st][1]), fmaxf(s2[t][st][2], s2[t][st][3])));
-      mt = rows_max(mt);
-      const float mn = fmaxf(m[t], mt);
+      for (int st = 1; st < SUB; ++st)
+        mt = max3_raw(mt, max3_raw(s2[t][st][0], s2[t][st][1], s2[t][st][2]), s2[t][st][3]);
+      const float mn = rows_max_with(mt, m[t]);
       const float mu = mn == kNegInf ? 0.0f : mn;
       const float alpha = fast_exp2(m[t] - mu);
       m[t] = mn;
-      float psum = 0.0f;
+      float psum = 0.0f;  // (the first term is assigned, not added to 0: the same value, one add fewer)
 #pragma unroll
       for (int st = 0; st < SUB; ++st) {
         float pr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(s2[t][st][r] - mu);
-        psum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        const float ps = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        psum = st == 0 ? ps : psum + ps;
         const uint32_t h01 = C::pack(pr[0], pr[1]), h23 = C::pack(pr[2], pr[3]);
         phi[t][st] = u32x2{h01, h23};
         plo[t][st] = u32x2{C::pack(pr[0] - C::lo(h01), pr[1] - C::hi(h01)),
@@ -1244,7 +1285,8 @@ partition_vec_kernel(PartitionArgs a) {
   unit_begin<BS>(a, u, smem);
   const int G = u.G;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // (uniform, scalar)
   const int t = lane & 15, grp = lane >> 4;     // K: token, chunk row
   const int h = lane % CPR, dl = lane / CPR;    // V: token chunk, d offset
 
@@ -1352,6 +1394,7 @@ partition_vec_kernel(PartitionArgs a) {
     const int page = wave + i * kWaves;  // page of the span
     while (page >= next_edge) park();
     const int tok0 = (u.pg0 + page) * BS;  // first token of the page
+    const bool tail = tok0 + BS > u.L;     // the sequence's last page (uniform)
     float p[GM][SUB];
 #pragma unroll
     for (int gg = 0; gg < GM; ++gg) {
@@ -1379,21 +1422,27 @@ partition_vec_kernel(PartitionArgs a) {
         dot = rows_sum(dot);
         const int tk = tok0 + 16 * st + t;  // this lane's token
         if constexpr (AL)  // position relative to the page's partition start
-          s2[st] = tk < u.L ? fmaf(dot, a.qk_scale, slope2[gg] * (float)(tk - (u.p0 + jcur) * a.PS))
-                            : kNegInf;
+          s2[st] = fmaf(dot, a.qk_scale, slope2[gg] * (float)(tk - (u.p0 + jcur) * a.PS));
         else
-          s2[st] = tk < u.L ? dot * a.qk_scale : kNegInf;
-        mt = fmaxf(mt, s2[st]);
+          s2[st] = dot * a.qk_scale;
       }
+      // Tokens past the sequence's end: only on its last page (wavefront-uniform branch).
+      if (tail) {
+#pragma unroll
+        for (int st = 0; st < SUB; ++st)
+          if (tok0 + 16 * st + t >= u.L) s2[st] = kNegInf;
+      }
+#pragma unroll
+      for (int st = 0; st < SUB; ++st) mt = max_raw(mt, s2[st]);
       mt = row16_max(mt);
-      const float mn = fmaxf(m[gg], mt);
+      const float mn = max_raw(m[gg], mt);
       const float mu = mn == kNegInf ? 0.0f : mn;
       const float alpha = fast_exp2(m[gg] - mu);
       float ps = 0.0f;
 #pragma unroll
       for (int st = 0; st < SUB; ++st) {
         p[gg][st] = fast_exp2(s2[st] - mu);
-        ps += p[gg][st];
+        ps = st == 0 ? p[gg][st] : ps + p[gg][st];
       }
       lpart[gg] = lpart[gg] * alpha + ps;
       m[gg] = mn;
@@ -1402,7 +1451,19 @@ partition_vec_kernel(PartitionArgs a) {
         for (int j = 0; j < VJ; ++j) acc[gg][j] *= alpha;
       }
     }
-    const int nv = u.L - (tok0 + h * X);  // valid tokens among this lane's X
+    // V tail slots past the sequence's end are zeroed (not multiplied by a zero
+    // weight: they may hold NaN), only on its last page.
+    u32x4 vw[VJ];
+#pragma unroll
+    for (int j = 0; j < VJ; ++j) vw[j] = pg.v[j];
+    if (tail) {
+      const int nv = u.L - (tok0 + h * X);  // valid tokens among this lane's X
+#pragma unroll
+      for (int j = 0; j < VJ; ++j) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) vw[j][w] = keep_first_elems<ESZ>(vw[j][w], nv - w * (4 / ESZ));
+      }
+    }
 #pragma unroll
     for (int gg = 0; gg < GM; ++gg) {
       // p of page token 16*st + k sits in lane k (rows repeat it); this lane
@@ -1420,23 +1481,16 @@ partition_vec_kernel(PartitionArgs a) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           if constexpr (KV8) {
-            const f32x2 lo = fp8_pair_f32<false>(pg.v[j][w]), hi = fp8_pair_f32<true>(pg.v[j][w]);
-            const float v0 = e_valid(4 * w, nv) ? lo[0] : 0.0f;
-            const float v1 = e_valid(4 * w + 1, nv) ? lo[1] : 0.0f;
-            const float v2 = e_valid(4 * w + 2, nv) ? hi[0] : 0.0f;
-            const float v3 = e_valid(4 * w + 3, nv) ? hi[1] : 0.0f;
-            sum = fmaf(pw[4 * w], v0, sum);
-            sum = fmaf(pw[4 * w + 1], v1, sum);
-            sum = fmaf(pw[4 * w + 2], v2, sum);
-            sum = fmaf(pw[4 * w + 3], v3, sum);
+            const f32x2 lo = fp8_pair_f32<false>(vw[j][w]), hi = fp8_pair_f32<true>(vw[j][w]);
+            sum = fmaf(pw[4 * w], lo[0], sum);
+            sum = fmaf(pw[4 * w + 1], lo[1], sum);
+            sum = fmaf(pw[4 * w + 2], hi[0], sum);
+            sum = fmaf(pw[4 * w + 3], hi[1], sum);
           } else if constexpr (DT == DT_F32) {
-            const float v = e_valid(w, nv) ? __uint_as_float(pg.v[j][w]) : 0.0f;
-            sum = fmaf(pw[w], v, sum);
+            sum = fmaf(pw[w], __uint_as_float(vw[j][w]), sum);
           } else {
-            const float v0 = e_valid(2 * w, nv) ? codec<DT>::lo(pg.v[j][w]) : 0.0f;
-            const float v1 = e_valid(2 * w + 1, nv) ? codec<DT>::hi(pg.v[j][w]) : 0.0f;
-            sum = fmaf(pw[2 * w], v0, sum);
-            sum = fmaf(pw[2 * w + 1], v1, sum);
+            sum = fmaf(pw[2 * w], codec<DT>::lo(vw[j][w]), sum);
+            sum = fmaf(pw[2 * w + 1], codec<DT>::hi(vw[j][w]), sum);
           }
         }
         acc[gg][j] = sum;

@@ -304,8 +304,8 @@ int wgs_per_cu(partition_fn fn) {
 // LDS a span's parked state may take: the CU's LDS shared by the workgroups
 // the kernel's registers allow (a longer span must not cost occupancy), at
 // most kSpanLdsCap and the per-workgroup limit.
-int span_lds_cap(partition_fn fn, int lds_limit) {
-  const int per_wg = max_lds_per_cu() / wgs_per_cu(fn);
+int span_lds_cap(partition_fn fn, int lds_limit, int wgs = 0) {
+  const int per_wg = max_lds_per_cu() / (wgs > 0 ? wgs : wgs_per_cu(fn));
   return std::min(std::min(per_wg, kSpanLdsCap), lds_limit);
 }
 
@@ -327,8 +327,8 @@ int cu_count() {
 // Fewest workgroups a longer span may leave in the grid: two per resident
 // slot (the workgroups per CU that the kernel's registers allow, on every
 // CU), so that the largest-first order has a second round to balance.
-long long span_min_grid(partition_fn fn, int rounds = kMinRounds) {
-  return (long long)rounds * wgs_per_cu(fn) * cu_count();
+long long span_min_grid(partition_fn fn, int rounds = kMinRounds, int wgs = 0) {
+  return (long long)rounds * (wgs > 0 ? wgs : wgs_per_cu(fn)) * cu_count();
 }
 
 // The one-call decode's spans need only one workgroup per resident slot:
@@ -343,6 +343,20 @@ constexpr int kMinRoundsFused = 1;
 // round: on the long-context batch at 512-token partitions, spans of eight
 // (512 workgroups) against four (1024) measured 90.9 -> 88.7 us.
 constexpr int kMinWgsPerCuRoll8 = 2;
+// ... and runs at most kRoll8WgsPerCu workgroups per CU: its 128 registers
+// would allow four, which measured 3 % slower on the GQA fp8 batch (84.4
+// against 82.0 us, same box); the launch asks for enough LDS to keep a fourth
+// workgroup off the CU.
+constexpr int kRoll8WgsPerCu = 3;
+// The 16-bit MFMA kernels run at most kMfma16WgsPerCu workgroups per CU (the
+// one-tile kernel's 168 registers would allow three; at three the planned
+// spans shrink and the long-context batch measured 2 % slower, the two-call
+// GQA step 1.8 % slower).
+constexpr int kMfma16WgsPerCu = 2;
+
+// LDS a launch asks for so that at most `wgs` of its workgroups share a CU
+// (1 KiB multiples, so that allocation rounding cannot lose one).
+int occupancy_lds(int wgs) { return (max_lds_per_cu() / wgs) & ~1023; }
 
 // Host checks shared by the partition entry points; fills `plan` for a launch
 // of NC columns. The query has dtype qdt; the caches kvdt (== qdt, or
@@ -414,8 +428,10 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
       roll_ct ? (kv8 ? kMfma8R : kMfmaR)[al][roll_ct - 1][qdt - 1][d_index(D)][bs_index(BS)]
               : nullptr;
   const partition_fn sized = kv8 && rfn ? rfn : fn;
-  const int cap = span_lds_cap(sized, lds_limit);
-  long long min_grid = span_min_grid(sized, fuse ? kMinRoundsFused : kMinRounds);
+  const int cap_wgs = vec ? 0 : !kv8 ? kMfma16WgsPerCu : rfn ? kRoll8WgsPerCu : 0;
+  const int wgs = cap_wgs ? std::min(wgs_per_cu(sized), cap_wgs) : wgs_per_cu(sized);
+  const int cap = span_lds_cap(sized, lds_limit, wgs);
+  long long min_grid = span_min_grid(sized, fuse ? kMinRoundsFused : kMinRounds, wgs);
   if (kv8 && rfn) min_grid = std::min(min_grid, (long long)kMinWgsPerCuRoll8 * cu_count());
   const int span = force_span > 0 ? force_span
                                   : pick_span(S, KH, P, PS, BS, NC, D, elem_size(kvdt), cap,
@@ -430,6 +446,12 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   plan->fn = fn;
   plan->lds_bytes = plan->roll > 0 ? pa::roll_layout(PS, BS, roll_ct, D, span, plan->roll).total
                                    : pa::lds_layout(PS, BS, NC, D, span).total;
+  // (the occupancy caps above, on the kernel that runs: the 8-bit kernel
+  // without the rolling merge keeps its four workgroups per CU)
+  if (cap_wgs && (!kv8 || plan->roll > 0) && wgs_per_cu(fn) > cap_wgs) {
+    const int floor_lds = std::min(lds_limit, occupancy_lds(cap_wgs));
+    if (plan->lds_bytes < floor_lds) plan->lds_bytes = floor_lds;
+  }
   const long long pairs = (long long)S * ((P + span - 1) / span);
   const long long unit_bytes = (long long)span * PS * D * elem_size(kvdt) * 2;
   plan->lpt = PA_LPT && pairs <= kLptMaxPairs &&
@@ -682,12 +704,12 @@ int reduce_entry(void* out, float* lse, const float* tmp_output, const float* ex
 // launched). Returns PA_OK or the call's error code.
 int plan_with_stand_ins(int32_t S, int32_t M, int32_t H, int32_t KH, int32_t D, int32_t BS,
                         int32_t P, int32_t PS, int32_t qdt, int32_t kvdt, Plan* full,
-                        Plan* last, int* nc) {
+                        Plan* last, int* nc, bool fuse = true) {
   alignas(16) static const char stand_in[16] = {};
   void* p = (void*)stand_in;
   return plan_partitions((float*)p, (float*)p, (float*)p, p, p, p, (const int32_t*)p,
                          (const int32_t*)p, S, H, KH, D, BS, 1, max_blocks_for(P, PS, BS), P, PS,
-                         qdt, kvdt, M, nullptr, full, last, nc, /*fuse=*/true);
+                         qdt, kvdt, M, nullptr, full, last, nc, fuse);
 }
 
 // ---------------------------------------------------------------- scratch
@@ -1004,15 +1026,15 @@ int paged_attn_partition_span(int32_t num_seqs, int32_t num_heads, int32_t num_k
     return fail(PA_ERR_UNSUPPORTED, "unsupported head_size / block_size");
   if (PS <= 0 || PS % BS || PS / BS > pa::kWaves * 64 || P < 1)
     return fail(PA_ERR_SHAPE, "bad partition size / count");
-  const int G = H / KH, NC = launch_columns(G, 1, D, PS, BS);
-  partition_fn fn = nullptr;
-  bool vec = false;
+  if (S == 0) return 1;
+  // the phase-1 launch plan itself (check_partition, on stand-in pointers)
   const int qdt = dt == PA_FP8_E4M3 ? PA_BF16 : dt;  // (an 8-bit cache's f16 query: same plan)
-  const int rc = select_kernel(qdt, dt, 1, G, NC, D, BS, 0, &fn, &vec);
+  Plan full, last;
+  int nc = 1;
+  const int rc = plan_with_stand_ins(S, 1, H, KH, D, BS, P, PS, qdt, dt, &full, &last, &nc,
+                                     /*fuse=*/false);
   if (rc != PA_OK) return rc;
-  const int lds_limit = max_lds_per_block();
-  return pick_span(S, KH, P, PS, BS, NC, D, elem_size(dt), span_lds_cap(fn, lds_limit),
-                   span_min_grid(fn));
+  return full.span;
 }
 
 int paged_attn_decode_plan(int32_t num_seqs, int32_t num_queries, int32_t num_heads,

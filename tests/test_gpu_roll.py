@@ -47,7 +47,13 @@ CASES = [
     ("fp8_g8m4_two_tiles", ("fp8", 64, 8, 128, 16, 64, 4, 64, 8)),
     ("fp8_g4_d64_bs32", ("fp8", 16, 4, 64, 32, 64, 1, 256, 8)),
     ("fp8_g8_d256", ("fp8", 16, 2, 256, 16, 32, 1, 256, 8)),
+    ("fp8_g8_d256_bs32", ("fp8", 16, 2, 256, 32, 64, 1, 256, 8)),
 ]
+# Head size 256 with an 8-bit cache and 16-token blocks: the rolling kernel's
+# ring slot (~66 KiB) exceeds the LDS its register occupancy leaves a
+# workgroup, so the host may plan one-partition spans there instead; the case
+# checks whichever plan it takes.
+MAY_NOT_ROLL = {"fp8_g8_d256"}
 FP8_QUERY = {"fp8_g4_d64_bs32": "f16"}  # the others: bf16
 FP8_SCALES = (0.015, 0.02)  # k_scale, v_scale
 BY = {c[0]: c for c in CASES}
@@ -93,11 +99,15 @@ def test_cases_cover_the_plans():
     """The cases take the rolling merge with one and with two ring slots, with
     spans that hold whole rows and spans whose entries the reduce combines."""
     plans = [plan_of(cfg, P, PS) for cfg, PS, P in (cfg_of(c[0]) for c in CASES)]
-    assert all(p["roll"] in (1, 2) and p["span"] >= 2 for p in plans), plans
-    assert {p["roll"] for p in plans} == {1, 2}, plans
-    assert any(p["entries"] == 1 for p in plans) and any(p["entries"] > 1 for p in plans), plans
-    fp8 = [p for c, p in zip(CASES, plans) if c[1][0] == "fp8"]
+    assert all(p["roll"] in (1, 2) and p["span"] >= 2
+               for c, p in zip(CASES, plans) if c[0] not in MAY_NOT_ROLL), plans
+    rolling = [p for c, p in zip(CASES, plans) if c[0] not in MAY_NOT_ROLL]
+    assert {p["roll"] for p in rolling} == {1, 2}, plans
+    assert any(p["entries"] == 1 for p in rolling) and any(p["entries"] > 1 for p in rolling), plans
+    fp8 = [p for c, p in zip(CASES, plans) if c[1][0] == "fp8" and c[0] not in MAY_NOT_ROLL]
     assert any(p["entries"] == 1 for p in fp8) and any(p["entries"] > 1 for p in fp8), fp8
+    assert any(p["launches"] == 1 and c[1][6] * c[1][1] // c[1][2] > 16
+               for c, p in zip(CASES, plans) if c[1][0] == "fp8"), fp8  # two column tiles
 
 
 def run(d, PS, P, slopes, out_dtype):
@@ -140,7 +150,8 @@ def test_rolling_merge_matches_oracle(label, variant):
     S, H, D = cfg.num_seqs, cfg.num_heads, cfg.head_size
     qdt = W.DTYPES[cfg.query_dtype]
     plan = plan_of(cfg, P, PS)
-    assert plan["span"] >= 2 and plan["roll"] in (1, 2), plan
+    if label not in MAY_NOT_ROLL:
+        assert plan["span"] >= 2 and plan["roll"] in (1, 2), plan
     slopes = W.alibi_slopes(H) if variant == "alibi" else None
     out_dtype = qdt if variant == "bf16_out" else torch.float32
     U.note(f"rolling merge {label} {variant} plan={plan}")
