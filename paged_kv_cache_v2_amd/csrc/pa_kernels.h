@@ -48,6 +48,13 @@
 //  - Masked tokens (t >= seq_len in the last page) are selected out: score
 //    -inf and value 0, never multiplied by a zero weight, so NaN in unread
 //    cache slots cannot leak.
+//  - The one-call decode (PartitionArgs::fuse) computes every partition the
+//    same way but does not store it: the workgroup combines its span's
+//    partitions with the reduce's log-sum-exp rule, either at the end from
+//    the parked states (combine_store) or as the span streams, one partition
+//    at a time (park_roll, the ROLL instantiations), and writes the output
+//    itself when the span is the whole row, else one span entry per row for
+//    the reduce.
 #pragma once
 
 #include <type_traits>

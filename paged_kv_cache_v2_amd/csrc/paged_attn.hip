@@ -216,8 +216,15 @@ int span_roll(int PS, int BS, int NC, int D, int c, int roll_ct, int lds_cap,
   return park ? 0 : -1;
 }
 
+// A one-call batch whose K+V (at the longest length, every sequence) is at
+// most kSmallBatchBytes is launch- and latency-bound: there a span covering
+// the whole row (no reduce launch) beats any split. The tiny fp32 batch (two
+// sequences, 1 MiB at most): 9.0 -> 6.x us per call.
+constexpr long long kSmallBatchBytes = 4 << 20;
+
 int pick_span(int S, int KH, int P, int PS, int BS, int NC, int D, int esz, int lds_cap,
-              long long min_grid, int roll_ct = 0) {
+              long long min_grid, int roll_ct = 0, bool fuse = false) {
+  const bool small = fuse && (long long)S * KH * P * PS * D * esz * 2 <= kSmallBatchBytes;
   int best = 1;
   for (int c = 2; c <= pa::kMaxSpan && c / 2 < P; c *= 2) {  // (c / 2 >= P: P already covered)
     const long long grid = (long long)S * KH * ((P + c - 1) / c);
@@ -226,7 +233,7 @@ int pick_span(int S, int KH, int P, int PS, int BS, int NC, int D, int esz, int 
       break;
     if (PA_SPAN > 0) {
       if (c > PA_SPAN) break;
-    } else if (grid < min_grid || bytes > kSpanBytes) {
+    } else if (!small && (grid < min_grid || bytes > kSpanBytes)) {
       break;
     }
     best = c;
@@ -435,7 +442,7 @@ int check_partition(float* tmp_output, float* exp_sums, float* max_logits, const
   if (kv8 && rfn) min_grid = std::min(min_grid, (long long)kMinWgsPerCuRoll8 * cu_count());
   const int span = force_span > 0 ? force_span
                                   : pick_span(S, KH, P, PS, BS, NC, D, elem_size(kvdt), cap,
-                                              min_grid, roll_ct);
+                                              min_grid, roll_ct, fuse);
   const long long grid = (long long)S * KH * ((P + span - 1) / span);
   if (grid > 0x7fffffffLL) return fail(PA_ERR_UNSUPPORTED, "too many work units");
   // (a longer span was admitted by pick_span, or is a forced shorter one;
