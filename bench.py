@@ -34,6 +34,10 @@ two torch.cuda.synchronize() calls. Prints ONE JSON line:
   ceiling    = a read-only kernel that gathers the same K/V pages through the
                same block tables with the same loads and computes nothing
                (libpa_ceiling.so): the page-gather read bandwidth of this chip.
+  ceiling_units = (16-bit MFMA workloads) the same reads with the decode's work
+               structure: one workgroup per (sequence, span, kv head) unit of
+               the one-call plan, largest first, wavefronts taking every fourth
+               page, two workgroups per CU as the 16-bit MFMA decode runs.
   copy_context = a 1 GiB device-to-device copy's bandwidth.
   merge_states = paged_attn_merge_states on the batch's own rows and on a
                2^20-row stream.
@@ -445,6 +449,39 @@ def gather_ceiling(pa, torch, b: Batch, K: int) -> dict:
             "value": round(gbs, 2), "unit": "GB/s", "pct_of_peak_hbm": pct(gbs)}
 
 
+# Workgroups per CU of the 16-bit MFMA decode kernel (the host caps it there).
+MFMA16_WGS_PER_CU = 2
+
+
+def units_ceiling(pa, torch, b: Batch, K: int) -> dict:
+    """The read-only gather with the one-call decode's work units (same spans,
+    same largest-first order, same residency): GB/s."""
+    from paged_kv_cache_v2_amd import ceiling
+    span = b.plan(b.P, b.PS)["span"]
+    span_pages = span * b.PS // b.cfg.block_size
+    pages, off, n = ceiling.unit_pages(b.inp["block_tables"], b.inp["seq_lens"],
+                                       b.cfg.block_size, b.cfg.num_kv_heads, span_pages)
+    pages, off = pages.to(b.dev), off.to(b.dev)
+    sink = torch.empty(max(1, 4 * n), dtype=torch.int32, device=b.dev)
+
+    def run():
+        ceiling.gather_units(sink, b.kc, b.vc, pages, off, n, MFMA16_WGS_PER_CU, stream=b.stream)
+
+    for _ in range(5):
+        run()
+    us = b.events([run], K)[0]
+    avg = sum(us) / len(us)
+    gbs = b.kvb / avg / 1e3
+    return {"kernel": "gather_units_kernel", "workload": b.name, "units": n,
+            "span_pages": span_pages, "workgroups_per_cu": MFMA16_WGS_PER_CU,
+            "avg_us": round(avg, 3), "value": round(gbs, 2), "unit": "GB/s",
+            "pct_of_peak_hbm": pct(gbs)}
+
+
+def mfma16(b: Batch) -> bool:
+    return b.kernel_name() == "partition_mfma_kernel" and not b.fp8
+
+
 def run(args) -> dict:
     import torch
 
@@ -482,6 +519,8 @@ def run(args) -> dict:
             res[k] = m[k]
     if not args.no_ceiling:
         res["ceiling"] = gather_ceiling(pa, torch, b, K)
+        if mfma16(b):
+            res["ceiling_units"] = units_ceiling(pa, torch, b, K)
     if not args.no_extras:
         res["merge_states"] = merge_bench(pa, torch, b.dev, b.stream, b.S * b.MQ * b.H, b.D,
                                           W.DTYPES[b.cfg.query_dtype], K)
@@ -506,6 +545,8 @@ def run(args) -> dict:
             r = o.measure(K, W_, args.flushed_calls, two_call=False)
             if not args.no_ceiling:
                 r["ceiling"] = gather_ceiling(pa, torch, o, K)
+                if mfma16(o):
+                    r["ceiling_units"] = units_ceiling(pa, torch, o, K)
             res["workloads"][name] = r
             del o
             torch.cuda.empty_cache()

@@ -78,6 +78,65 @@ __global__ void __launch_bounds__(256) gather_ceiling_kernel(
 typedef void (*ceiling_fn)(int32_t*, const uint8_t*, const uint8_t*, const int32_t*, long long,
                            int, int);
 
+// The same reads with the decode kernels' work structure: workgroup u owns
+// the pages pages[unit_off[u] .. unit_off[u + 1]) (page p = block * KH + kv
+// head, p < num_cache_pages; clamped into range) and its four wavefronts take
+// every fourth of them, each with two pages' K and V loads in flight. The
+// dynamic LDS request (a launch argument) bounds the workgroups per CU.
+template <int CH>  // 16-byte chunks per lane per page: page_bytes / 1024
+__global__ void __launch_bounds__(256) gather_units_kernel(
+    int32_t* sink, const uint8_t* kc, const uint8_t* vc, const int32_t* pages,
+    const int32_t* unit_off, long long num_cache_pages) {
+  extern __shared__ int32_t lds[];
+  constexpr int NIF = 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t page = (size_t)CH * 1024;
+  const int i1 = unit_off[blockIdx.x + 1];
+  uint32_t acc = 0;
+  auto base = [&](int i) {
+    long long p = __builtin_amdgcn_readfirstlane(pages[i]);
+    p = p < 0 ? 0 : (p >= num_cache_pages ? num_cache_pages - 1 : p);
+    return (size_t)p * page + lane * 16;
+  };
+  int i = unit_off[blockIdx.x] + wave;
+  for (; i + 4 * (NIF - 1) < i1; i += 4 * NIF) {
+    u32x4 k[NIF][CH], v[NIF][CH];
+#pragma unroll
+    for (int j = 0; j < NIF; ++j) {
+      const size_t off = base(i + 4 * j);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        k[j][c] = __builtin_nontemporal_load((const u32x4*)(kc + off + c * 1024));
+        v[j][c] = __builtin_nontemporal_load((const u32x4*)(vc + off + c * 1024));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NIF; ++j)
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        acc ^= k[j][c].x ^ k[j][c].y ^ k[j][c].z ^ k[j][c].w ^ v[j][c].x ^ v[j][c].y ^
+               v[j][c].z ^ v[j][c].w;
+  }
+  for (; i < i1; i += 4) {
+    const size_t off = base(i);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const u32x4 k = __builtin_nontemporal_load((const u32x4*)(kc + off + c * 1024));
+      const u32x4 v = __builtin_nontemporal_load((const u32x4*)(vc + off + c * 1024));
+      acc ^= k.x ^ k.y ^ k.z ^ k.w ^ v.x ^ v.y ^ v.z ^ v.w;
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) acc ^= __shfl_xor(acc, o, 64);
+  if (lane == 0) {
+    lds[wave] = (int32_t)acc;
+    sink[(size_t)blockIdx.x * 4 + wave] = lds[wave];
+  }
+}
+
+typedef void (*units_fn)(int32_t*, const uint8_t*, const uint8_t*, const int32_t*,
+                         const int32_t*, long long);
+
 }  // namespace
 
 extern "C" {
@@ -106,6 +165,39 @@ int pa_gather_ceiling(int32_t* sink, int64_t sink_words, const void* key_cache,
   hipLaunchKernelGGL(fn, dim3(kGrid), dim3(256), 0, (hipStream_t)stream, sink,
                      (const uint8_t*)key_cache, (const uint8_t*)value_cache, blocks,
                      (long long)num_pages * num_kv_heads, num_kv_heads, num_blocks);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int pa_gather_units(int32_t* sink, int64_t sink_words, const void* key_cache,
+                    const void* value_cache, const int32_t* pages, const int32_t* unit_off,
+                    int32_t num_units, int64_t num_cache_pages, int32_t page_bytes,
+                    int32_t workgroups_per_cu, void* stream) {
+  if (num_units < 0 || num_cache_pages < 1 || workgroups_per_cu < 1) return -2;
+  if (num_units == 0) return 0;
+  if (!sink || !key_cache || !value_cache || !pages || !unit_off) return -1;
+  if (((uintptr_t)key_cache | (uintptr_t)value_cache) & 15u) return -4;
+  if (sink_words < (int64_t)num_units * 4) return -2;
+  units_fn fn;
+  switch (page_bytes) {
+    case 1024: fn = gather_units_kernel<1>; break;
+    case 2048: fn = gather_units_kernel<2>; break;
+    case 4096: fn = gather_units_kernel<4>; break;
+    case 8192: fn = gather_units_kernel<8>; break;
+    default: return -2;
+  }
+  int dev = 0, per_cu = 0, per_block = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+          hipSuccess ||
+      hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+          hipSuccess)
+    return -5;
+  // the LDS share that leaves room for workgroups_per_cu workgroups on a CU
+  int lds = (per_cu / workgroups_per_cu) & ~1023;
+  lds = lds < 16 ? 16 : lds > per_block ? per_block : lds;
+  hipLaunchKernelGGL(fn, dim3(num_units), dim3(256), lds, (hipStream_t)stream, sink,
+                     (const uint8_t*)key_cache, (const uint8_t*)value_cache, pages, unit_off,
+                     (long long)num_cache_pages);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

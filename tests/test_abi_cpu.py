@@ -52,7 +52,7 @@ def test_ceiling_library_exports_its_symbols():
     from paged_kv_cache_v2_amd import ceiling
     text = open(os.path.join(ROOT, "include", "pa_ceiling.h")).read()
     names = re.findall(r"PA_CEILING_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
-    assert sorted(names) == ["pa_gather_ceiling", "pa_gather_ceiling_sink_words"]
+    assert sorted(names) == ["pa_gather_ceiling", "pa_gather_ceiling_sink_words", "pa_gather_units"]
     L = ceiling.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -67,6 +67,20 @@ def test_ceiling_library_exports_its_symbols():
     bt = torch.tensor([[3, 1, 7, -1], [5, -1, -1, -1], [0, 0, 0, 0]], dtype=torch.int32)
     sl = torch.tensor([40, 16, 0], dtype=torch.int32)
     assert ceiling.page_list(bt, sl, 16).tolist() == [3, 1, 7, 5]
+    # the unit-structured gather: host-side rejections, nothing launched
+    assert L.pa_gather_units(FAKE, 8, FAKE, FAKE, FAKE, FAKE, 0, 10, 4096, 2, None) == 0  # no-op
+    assert L.pa_gather_units(FAKE, 8, FAKE, FAKE, FAKE, FAKE, -1, 10, 4096, 2, None) == -2
+    assert L.pa_gather_units(FAKE, 8, FAKE, FAKE, FAKE, FAKE, 2, 10, 4096, 0, None) == -2  # wgs
+    assert L.pa_gather_units(FAKE, 8, FAKE, FAKE, FAKE, FAKE, 2, 0, 4096, 2, None) == -2  # pages
+    assert L.pa_gather_units(None, 8, FAKE, FAKE, FAKE, FAKE, 2, 10, 4096, 2, None) == -1
+    assert L.pa_gather_units(FAKE, 8, FAKE, FAKE, None, FAKE, 2, 10, 4096, 2, None) == -1
+    assert L.pa_gather_units(FAKE, 8, FAKE + 4, FAKE, FAKE, FAKE, 2, 10, 4096, 2, None) == -4
+    assert L.pa_gather_units(FAKE, 7, FAKE, FAKE, FAKE, FAKE, 2, 10, 4096, 2, None) == -2  # sink
+    assert L.pa_gather_units(FAKE, 8, FAKE, FAKE, FAKE, FAKE, 2, 10, 16384, 2, None) == -2  # page
+    # units: (sequence, span of 2 pages) pairs by page count, then kv head
+    pages, off, n = ceiling.unit_pages(bt, sl, 16, 2, 2)
+    assert n == 6 and off.tolist() == [0, 2, 4, 5, 6, 7, 8]
+    assert pages.tolist() == [3 * 2, 1 * 2, 3 * 2 + 1, 1 * 2 + 1, 5 * 2, 5 * 2 + 1, 7 * 2, 7 * 2 + 1]
 
 
 def test_abi_version_and_default_partition_size():
