@@ -5,9 +5,10 @@ partition size, batch, lengths with empty and partial partitions, query
 tokens, ALiBi on or off, output dtype) within what the launchers accept and
 runs paged_attn_decode_ex; the output, the row log-sum-exp and every
 partition intermediate are compared with the oracle. Sizes stay small so the
-oracle finishes in well under a second per case. The cases from N_NARROW on
-draw 16-bit queries with more than 16 (query token, head) columns per kv
-head: two MFMA column tiles, or several launches over the pages. The
+oracle finishes in well under a second per case. The cases from N_NARROW to
+N_FIRST, and the odd ones after it, draw 16-bit queries with more than 16
+(query token, head) columns per kv head: two MFMA column tiles, or several
+launches over the pages. The
 large-batch cases draw 150-320 short sequences, enough work units that the
 launch plan takes spans of several partitions and the largest-first order.
 The planned cases run at the partition size the library plans for the batch.
@@ -27,7 +28,8 @@ from tests import gpu_util as U
 pytestmark = pytest.mark.gpu
 
 N_NARROW = 40
-N_CASES = 56
+N_FIRST = 56   # cases before this one: narrow below N_NARROW, wide from it
+N_CASES = 120  # cases from N_FIRST on alternate: even narrow, odd wide
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -38,7 +40,7 @@ def built():
 
 def draw(i):
     rng = np.random.default_rng(1000 + i)
-    wide = i >= N_NARROW
+    wide = i >= N_NARROW if i < N_FIRST else i % 2 == 1
     kv = rng.choice(["f32", "f16", "bf16", "fp8"], p=[0, 0.35, 0.35, 0.3] if wide else
                     [0.15, 0.3, 0.3, 0.25])
     q = kv if kv != "fp8" else str(rng.choice(["f16", "bf16"]))
@@ -122,7 +124,7 @@ def test_random_config(i):
         assert torch.equal(out.to(q.dtype).cpu().view(torch.int16), o16.cpu().view(torch.int16))
 
 
-N_BATCH_CASES = 12
+N_BATCH_CASES = 24
 
 
 def draw_batch(i):
