@@ -18,10 +18,13 @@ two torch.cuda.synchronize() calls. Prints ONE JSON line:
                p10 / p90 over the calls, as GB/s and % of peak.
   roofline   = the decode call's kernels (the partition kernel, plus the reduce
                when a row spans several workgroups): K+V bytes / their average
-               duration from a HIP event pair on the launch stream around every
-               call of a second pass of K steps; `traffic` = HBM bytes per call
-               from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary when
-               it was taken on the current kernel source (else null).
+               duration, from one HIP event pair on the launch stream around a
+               second pass of K back-to-back calls (the timed region / K); the
+               per-call distribution from an event pair around each call of a
+               third pass (event_pair_*: each pair also times its launch);
+               `traffic` = HBM bytes per call from the committed rocprofv3
+               FETCH_SIZE / WRITE_SIZE summary when it was taken on the current
+               kernel source (else null).
   two_call   = the same batch through paged_attn_v2_partition + paged_attn_v2_reduce
                (every partition's row stored, then reduced): step time, and the
                two kernels' event-timed averages.
@@ -246,6 +249,18 @@ class Batch:
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / K
 
+    def region(self, fn, K):
+        """Microseconds per call of K back-to-back calls of `fn`, from one HIP
+        event pair on the launch stream around them."""
+        torch = self.torch
+        e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        e0.record(self.stream)
+        for _ in range(K):
+            fn()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / K
+
     def events(self, fns, K):
         """K rounds of the calls in `fns`, a HIP event pair on the launch stream
         around each call: per call, the list of K durations in microseconds."""
@@ -315,8 +330,8 @@ class Batch:
     def measure(self, K, W_, flushed_calls, two_call=True):
         """value (back to back), roofline (events), flushed, tuned; two_call optional."""
         step_s = self.back_to_back(self.decode, K, W_)
+        call_avg = self.region(self.decode, K)
         call_us = self.events([self.decode], K)[0]
-        call_avg = sum(call_us) / len(call_us)
         gbs = self.kvb / step_s / 1e9
         achieved = self.kvb / call_avg / 1e3
         traffic, traffic_src = committed_traffic(self.name, self.kernel_name())
@@ -331,8 +346,9 @@ class Batch:
                 "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "kernel": self.kernel_name(), "call_avg_us": round(call_avg, 3),
-                "call_p10_us": round(quantile(call_us, 0.1), 3),
-                "call_p90_us": round(quantile(call_us, 0.9), 3),
+                "event_pair_avg_us": round(sum(call_us) / len(call_us), 3),
+                "event_pair_p10_us": round(quantile(call_us, 0.1), 3),
+                "event_pair_p90_us": round(quantile(call_us, 0.9), 3),
                 "bytes_per_launch": self.kvb, "traffic_source": traffic_src,
                 "kernel_source_hash": source_hash(),
             },
@@ -442,8 +458,7 @@ def gather_ceiling(pa, torch, b: Batch, K: int) -> dict:
 
     for _ in range(5):
         run()
-    us = b.events([run], K)[0]
-    avg = sum(us) / len(us)
+    avg = b.region(run, K)
     gbs = b.kvb / avg / 1e3
     return {"kernel": "gather_ceiling_kernel", "workload": b.name, "avg_us": round(avg, 3),
             "value": round(gbs, 2), "unit": "GB/s", "pct_of_peak_hbm": pct(gbs)}
@@ -469,8 +484,7 @@ def units_ceiling(pa, torch, b: Batch, K: int) -> dict:
 
     for _ in range(5):
         run()
-    us = b.events([run], K)[0]
-    avg = sum(us) / len(us)
+    avg = b.region(run, K)
     gbs = b.kvb / avg / 1e3
     return {"kernel": "gather_units_kernel", "workload": b.name, "units": n,
             "span_pages": span_pages, "workgroups_per_cu": MFMA16_WGS_PER_CU,
